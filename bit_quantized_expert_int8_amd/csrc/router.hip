@@ -1,0 +1,351 @@
+// moe_rmsnorm, moe_router_topk and moe_combine.
+//
+// Router: each block holds the token's activation in LDS as fp32 and each of its four wavefronts
+// computes one expert's logit with 16-byte int8 loads (coalesced along the row) and a wave reduction.
+// The last block to finish for a token (agent-scope ticket counter in the caller's workspace) reads the
+// token's logits back into LDS, ranks every candidate against all logits (ties: lower id first), keeps
+// the k best in rank order and takes the softmax over them.  It resets the counter, so the workspace is
+// reusable.  Logits travel between blocks by device-coherent stores and loads.
+#include "common.h"
+
+namespace moeq4 {
+namespace {
+
+constexpr int kRouterWaves = 4;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxK = 32;
+constexpr int kRouterChunks = 8;    // 16-byte chunks per lane: rows of up to 8192 int8
+
+template <typename T>
+__device__ __forceinline__ float load_act(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_act<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_act<uint16_t>(const uint16_t* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
+
+// 8 consecutive activations (16- or 32-byte aligned) as fp32
+__device__ __forceinline__ void load8(const uint16_t* p, float v[8]) {
+  const uint4 r = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float v[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+__device__ __forceinline__ void store_act(void* out, bool bf16, int64_t i, float v) {
+  if (bf16)
+    reinterpret_cast<uint16_t*>(out)[i] = (uint16_t)f32_to_bf16_bits(v);
+  else
+    reinterpret_cast<float*>(out)[i] = v;
+}
+
+// ------------------------------------------------------------------------------------------------
+// RMSNorm: one block per token
+// ------------------------------------------------------------------------------------------------
+template <typename XT>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const XT* __restrict__ x, const float* __restrict__ gamma, float eps,
+                                                      int d, void* __restrict__ out, bool out_bf16) {
+  __shared__ float partial[4];
+  const int64_t t = blockIdx.x;
+  const XT* xt = x + t * d;
+  // 8 elements per thread and pass, every load issued before the first use; values stay in registers
+  constexpr int kPasses = 16384 / (8 * 256);
+  float v[kPasses][8];
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int j0 = (threadIdx.x + 256 * p) * 8;
+    if (j0 < d) load8(xt + j0, v[p]);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int j0 = (threadIdx.x + 256 * p) * 8;
+    if (j0 < d)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss += v[p][i] * v[p][i];
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) partial[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = (partial[0] + partial[1]) + (partial[2] + partial[3]);
+  const float r = 1.0f / sqrtf(tot / (float)d + eps);
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int j0 = (threadIdx.x + 256 * p) * 8;
+    if (j0 < d) {
+      const float4 g0 = reinterpret_cast<const float4*>(gamma + j0)[0], g1 = reinterpret_cast<const float4*>(gamma + j0)[1];
+      const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) store_act(out, out_bf16, t * d + j0 + i, (v[p][i] * r) * g[i]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Router GEMV + last-block top-k
+// ------------------------------------------------------------------------------------------------
+struct RouterArgs {
+  const void* x;
+  int d, E, k;
+  const int8_t* w;
+  const float* scale;
+  const int32_t* forced;
+  int32_t* ids;
+  float* weights;
+  float* logits;         // [T][E]: caller's buffer or workspace
+  uint32_t* counters;    // [T], zero between calls
+};
+
+__device__ __forceinline__ bool better(float v, int i, float v2, int i2) { return v > v2 || (v == v2 && i < i2); }
+
+template <typename XT>
+__global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
+  extern __shared__ float xs[];                      // [d] fp32 activation
+  __shared__ uint32_t last_flag;
+  const int64_t t = blockIdx.y;
+  const XT* x = reinterpret_cast<const XT*>(a.x) + t * a.d;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e = blockIdx.x * kRouterWaves + wave;
+  const int nch = a.d / 16;                          // 16-byte chunks of one int8 row
+  const int8_t* row = a.w + (int64_t)(e < a.E ? e : 0) * a.d;
+  // every load of the block in one round trip: this wave's weight chunks, then the activation
+  int4 q[kRouterChunks];
+#pragma unroll
+  for (int m = 0; m < kRouterChunks; ++m) {
+    const int c = lane + 64 * m;
+    if (c < nch) q[m] = *reinterpret_cast<const int4*>(row + c * 16);
+  }
+  // activation: 8 elements per thread and pass, all passes issued before any is used
+  {
+    constexpr int kPasses = 8192 / (8 * 256);
+    float v[kPasses][8];
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int j0 = (threadIdx.x + 256 * p) * 8;
+      if (j0 < a.d) load8(x + j0, v[p]);
+    }
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int j0 = (threadIdx.x + 256 * p) * 8;
+      if (j0 < a.d) {
+        *reinterpret_cast<float4*>(xs + j0) = make_float4(v[p][0], v[p][1], v[p][2], v[p][3]);
+        *reinterpret_cast<float4*>(xs + j0 + 4) = make_float4(v[p][4], v[p][5], v[p][6], v[p][7]);
+      }
+    }
+  }
+  __syncthreads();
+
+  if (e < a.E) {
+    float acc = 0.f;
+#pragma unroll
+    for (int m = 0; m < kRouterChunks; ++m) {
+      const int c = lane + 64 * m;
+      if (c >= nch) break;
+      const float4* xv = reinterpret_cast<const float4*>(xs + c * 16);
+      const int qw[4] = {q[m].x, q[m].y, q[m].z, q[m].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 xx = xv[i];
+        acc += (float)(int8_t)(qw[i] & 0xff) * xx.x;
+        acc += (float)(int8_t)((qw[i] >> 8) & 0xff) * xx.y;
+        acc += (float)(int8_t)((qw[i] >> 16) & 0xff) * xx.z;
+        acc += (float)(int8_t)((qw[i] >> 24) & 0xff) * xx.w;
+      }
+    }
+    acc = wave_sum(acc);
+    // device-coherent store (bypasses the non-coherent per-XCD L2 state), so no L2 writeback is needed
+    if (lane == 0) __hip_atomic_store(a.logits + t * a.E + e, acc * a.scale[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // Publish this block's logits, then take a ticket; the last block selects.  Agent-scope fences would
+  // write back and invalidate the whole L2 of every XCD from every wave; instead the logits travel by
+  // device-coherent stores/loads and each wave waits for its stores to complete before the barrier.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t ticket = __hip_atomic_fetch_add(a.counters + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_flag = (ticket == gridDim.x - 1) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (!last_flag) return;
+
+  // The last block selects.  Top-k by rank: candidate e is kept iff fewer than k logits beat it
+  // (larger value, or equal value and lower id), and its rank is its position in the output.  Every
+  // comparison reads LDS by broadcast; there are no dependent cross-lane shuffle chains.
+  __shared__ float lgs[kMaxExperts];
+  __shared__ float sel_v[kMaxK];
+  __shared__ int sel_i[kMaxK];
+  const float* lg = a.logits + t * a.E;
+#pragma unroll
+  for (int p = 0; p < kMaxExperts / 256; ++p) {
+    const int e2 = threadIdx.x + 256 * p;
+    if (e2 < a.E) lgs[e2] = __hip_atomic_load(lg + e2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (a.forced) {
+    if (threadIdx.x < a.k) {
+      const int i = a.forced[t * a.k + threadIdx.x];
+      sel_i[threadIdx.x] = i;
+      sel_v[threadIdx.x] = (i >= 0 && i < a.E) ? lgs[i] : NAN;
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < kMaxExperts / 256; ++p) {
+      const int c = threadIdx.x + 256 * p;
+      if (c < a.E) {
+        const float v = lgs[c];
+        int rank = 0;
+        for (int e2 = 0; e2 < a.E; ++e2) {
+          const float u = lgs[e2];
+          rank += (u > v) | ((u == v) & (e2 < c));
+        }
+        if (rank < a.k) {
+          sel_i[rank] = c;
+          sel_v[rank] = v;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // softmax over the k kept logits; every lane sums the same terms in the same order
+  if (threadIdx.x < a.k) {
+    float mx = sel_v[0];
+    for (int r = 1; r < a.k; ++r) mx = fmaxf(mx, sel_v[r]);
+    float den = 0.f;
+    for (int r = 0; r < a.k; ++r) den += expf(sel_v[r] - mx);
+    a.ids[t * a.k + threadIdx.x] = sel_i[threadIdx.x];
+    a.weights[t * a.k + threadIdx.x] = expf(sel_v[threadIdx.x] - mx) / den;
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(a.counters + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------------------------------------------
+// combine
+// ------------------------------------------------------------------------------------------------
+template <typename RT, int KT>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const float* __restrict__ w,
+                                                      const float* __restrict__ ys, const RT* __restrict__ res, int k,
+                                                      int d, void* __restrict__ out, bool out_bf16) {
+  const int64_t t = blockIdx.y;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= d) return;
+  // all loads first (one memory round trip), then the sum in the fixed order i = 0..k-1; loads past k
+  // are clamped to a valid row and weighted by 0, so the code has no data-dependent branches
+  float yv[KT], wv[KT];
+  if (k > 0) {
+#pragma unroll
+    for (int i = 0; i < KT; ++i) {
+      const int ic = i < k ? i : k - 1;
+      yv[i] = y[(t * k + ic) * d + j];
+      wv[i] = w[t * k + ic];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < KT; ++i) yv[i] = wv[i] = 0.f;
+  }
+  const float s = ys ? ys[t * d + j] : 0.f;
+  const float r = res ? load_act(res, t * d + j) : 0.f;
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < KT; ++i) acc += (i < k ? wv[i] : 0.f) * yv[i];
+  acc += s;
+  acc += r;
+  store_act(out, out_bf16, t * d + j, acc);
+}
+
+}  // namespace
+}  // namespace moeq4
+
+using namespace moeq4;
+
+extern "C" moe_status moe_rmsnorm(const void* x_dev, moe_dtype x_dtype, const float* gamma_dev, float eps, int32_t T,
+                                  int32_t d, void* out_dev, moe_dtype out_dtype, void* stream) {
+  if (!x_dev || !gamma_dev || !out_dev) return fail(MOE_ERR_INVALID_ARG, "moe_rmsnorm: NULL pointer");
+  if (T < 1 || d < 8 || d % 8 || d > 16384) return fail(MOE_ERR_INVALID_ARG, "moe_rmsnorm: T=%d d=%d (multiple of 8, <= 16384)", T, d);
+  if (!aligned(x_dev, 16) || !aligned(gamma_dev, 16)) return fail(MOE_ERR_INVALID_ARG, "moe_rmsnorm: x or gamma not 16-byte aligned");
+  if ((x_dtype != MOE_F32 && x_dtype != MOE_BF16) || (out_dtype != MOE_F32 && out_dtype != MOE_BF16))
+    return fail(MOE_ERR_INVALID_ARG, "moe_rmsnorm: bad dtype");
+  if (!(eps >= 0.f)) return fail(MOE_ERR_INVALID_ARG, "moe_rmsnorm: eps must be >= 0");
+  hipStream_t s = as_stream(stream);
+  if (x_dtype == MOE_BF16)
+    hipLaunchKernelGGL(rmsnorm_kernel<uint16_t>, dim3(T), dim3(256), 0, s, (const uint16_t*)x_dev, gamma_dev, eps, d,
+                       out_dev, out_dtype == MOE_BF16);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(T), dim3(256), 0, s, (const float*)x_dev, gamma_dev, eps, d, out_dev,
+                       out_dtype == MOE_BF16);
+  return check_launch("moe_rmsnorm");
+}
+
+extern "C" size_t moe_router_workspace_bytes(int32_t T, int32_t E) {
+  if (T < 1 || E < 1) return 0;
+  const size_t counters = ((size_t)T * 4 + 255) / 256 * 256;
+  return counters + (size_t)T * E * 4;
+}
+
+extern "C" moe_status moe_router_topk(const void* x_dev, moe_dtype x_dtype, int32_t T, int32_t d, const int8_t* w_dev,
+                                      const float* row_scale_dev, int32_t E, int32_t k, const int32_t* forced_ids_dev,
+                                      int32_t* ids_dev, float* weights_dev, float* logits_dev, void* workspace_dev,
+                                      size_t workspace_bytes, void* stream) {
+  if (!x_dev || !w_dev || !row_scale_dev || !ids_dev || !weights_dev || !workspace_dev)
+    return fail(MOE_ERR_INVALID_ARG, "moe_router_topk: NULL pointer");
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "moe_router_topk: bad x_dtype");
+  if (T < 1 || T > 65535) return fail(MOE_ERR_INVALID_ARG, "moe_router_topk: T=%d", T);
+  if (E < 1 || E > kMaxExperts || k < 1 || k > E || k > kMaxK)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_router_topk: E=%d k=%d (need 1 <= k <= min(E, 32), E <= 1024)", E, k);
+  if (d < 16 || d % 16 || d > 8192) return fail(MOE_ERR_UNSUPPORTED, "moe_router_topk: d=%d (multiple of 16, <= 8192)", d);
+  if (!aligned(w_dev, 16) || !aligned(x_dev, 16))
+    return fail(MOE_ERR_INVALID_ARG, "moe_router_topk: router weights or x not 16-byte aligned");
+  const size_t need = moe_router_workspace_bytes(T, E);
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_INVALID_ARG, "moe_router_topk: workspace %zu bytes < %zu", workspace_bytes, need);
+  if (!aligned(workspace_dev, 256)) return fail(MOE_ERR_INVALID_ARG, "moe_router_topk: workspace not 256-byte aligned");
+  RouterArgs a;
+  a.x = x_dev;
+  a.d = d;
+  a.E = E;
+  a.k = k;
+  a.w = w_dev;
+  a.scale = row_scale_dev;
+  a.forced = forced_ids_dev;
+  a.ids = ids_dev;
+  a.weights = weights_dev;
+  a.counters = static_cast<uint32_t*>(workspace_dev);
+  a.logits = logits_dev ? logits_dev
+                        : reinterpret_cast<float*>(static_cast<char*>(workspace_dev) + ((size_t)T * 4 + 255) / 256 * 256);
+  dim3 grid((E + kRouterWaves - 1) / kRouterWaves, T);
+  const size_t lds = (size_t)d * sizeof(float);
+  hipStream_t s = as_stream(stream);
+  if (x_dtype == MOE_BF16)
+    hipLaunchKernelGGL(router_kernel<uint16_t>, grid, dim3(256), lds, s, a);
+  else
+    hipLaunchKernelGGL(router_kernel<float>, grid, dim3(256), lds, s, a);
+  return check_launch("moe_router_topk");
+}
+
+extern "C" moe_status moe_combine(const float* y_routed_dev, const float* weights_dev, const float* y_shared_dev,
+                                  const void* residual_dev, moe_dtype residual_dtype, int32_t T, int32_t k, int32_t d,
+                                  void* out_dev, moe_dtype out_dtype, void* stream) {
+  if (!out_dev || (k > 0 && (!y_routed_dev || !weights_dev))) return fail(MOE_ERR_INVALID_ARG, "moe_combine: NULL pointer");
+  if (T < 1 || T > 65535 || k < 0 || k > kMaxK || d < 1) return fail(MOE_ERR_INVALID_ARG, "moe_combine: T=%d k=%d d=%d", T, k, d);
+  if ((out_dtype != MOE_F32 && out_dtype != MOE_BF16) || (residual_dev && residual_dtype != MOE_F32 && residual_dtype != MOE_BF16))
+    return fail(MOE_ERR_INVALID_ARG, "moe_combine: bad dtype");
+  dim3 grid((d + 255) / 256, T);
+  hipStream_t s = as_stream(stream);
+  const bool rb = residual_dev && residual_dtype == MOE_BF16, ob = out_dtype == MOE_BF16;
+  const uint16_t* r16 = (const uint16_t*)residual_dev;
+  const float* r32 = (const float*)residual_dev;
+  if (k <= 8) {
+    if (rb) hipLaunchKernelGGL((combine_kernel<uint16_t, 8>), grid, dim3(256), 0, s, y_routed_dev, weights_dev, y_shared_dev, r16, k, d, out_dev, ob);
+    else hipLaunchKernelGGL((combine_kernel<float, 8>), grid, dim3(256), 0, s, y_routed_dev, weights_dev, y_shared_dev, r32, k, d, out_dev, ob);
+  } else {
+    if (rb) hipLaunchKernelGGL((combine_kernel<uint16_t, kMaxK>), grid, dim3(256), 0, s, y_routed_dev, weights_dev, y_shared_dev, r16, k, d, out_dev, ob);
+    else hipLaunchKernelGGL((combine_kernel<float, kMaxK>), grid, dim3(256), 0, s, y_routed_dev, weights_dev, y_shared_dev, r32, k, d, out_dev, ob);
+  }
+  return check_launch("moe_combine");
+}

@@ -1,0 +1,138 @@
+"""Decode-step runtime over the C ABI: device-resident weights of a stack of MoE layers, caller-owned
+workspaces, and the per-token sequence of library calls (RMSNorm -> router/top-k -> expert GEMVs ->
+combine), optionally captured into one HIP graph per token.
+
+PyTorch is used only to own device memory and streams; every step of the path runs in libmoeq4.so.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Callable, Optional
+
+import torch
+
+from . import moeq4 as q
+
+
+@dataclasses.dataclass
+class Shape:
+    d: int
+    n_experts: int
+    k: int
+    F: int
+    S: int
+    sb_dtype: int = q.MOE_BF16
+    x_dtype: int = q.MOE_BF16
+    act: int = q.MOE_ACT_GELU_TANH
+    rms_norm: bool = False
+    eps: float = 1e-6
+
+
+@dataclasses.dataclass
+class LayerWeights:
+    pool: torch.Tensor            # uint8 [E][record_bytes]
+    shared: Optional[torch.Tensor]  # uint8 [1][shared_record_bytes]
+    router_w: torch.Tensor        # int8 [E][d]
+    router_s: torch.Tensor        # float32 [E]
+    gamma: Optional[torch.Tensor]  # float32 [d]
+
+
+def _torch_dtype(dt: int):
+    return torch.bfloat16 if dt == q.MOE_BF16 else torch.float32
+
+
+def pack_layer(shape: Shape, fill_expert: Callable, fill_shared: Optional[Callable], router_w: torch.Tensor,
+               router_s: torch.Tensor, gamma: Optional[torch.Tensor], device="cuda", stream=None) -> LayerWeights:
+    """Quantize one layer's experts into device records with the library's encoder.
+
+    ``fill_expert(e, w_gate_up, w_down)`` writes expert e's fp32 weights ([2F][d] and [d][F] CUDA tensors)
+    in place; ``fill_shared(w_gate_up, w_down)`` the same for the shared expert (width S)."""
+    d, F, S, E = shape.d, shape.F, shape.S, shape.n_experts
+    rb = q.moe_record_bytes(d, F, shape.sb_dtype)
+    pool = torch.empty((E, rb), dtype=torch.uint8, device=device)
+    wgu = torch.empty((2 * F, d), dtype=torch.float32, device=device)
+    wd = torch.empty((d, F), dtype=torch.float32, device=device)
+    for e in range(E):
+        fill_expert(e, wgu, wd)
+        q.q4_pack_expert(wgu, wd, d, F, shape.sb_dtype, pool[e].data_ptr(), stream)
+    shared = None
+    if fill_shared is not None:
+        srb = q.moe_record_bytes(d, S, shape.sb_dtype)
+        shared = torch.empty((1, srb), dtype=torch.uint8, device=device)
+        sgu = torch.empty((2 * S, d), dtype=torch.float32, device=device)
+        sd = torch.empty((d, S), dtype=torch.float32, device=device)
+        fill_shared(sgu, sd)
+        q.q4_pack_expert(sgu, sd, d, S, shape.sb_dtype, shared.data_ptr(), stream)
+    torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
+    return LayerWeights(pool, shared, router_w.to(device).contiguous(), router_s.to(device).contiguous(),
+                        None if gamma is None else gamma.to(device).contiguous())
+
+
+class MoEDecoder:
+    """Runs T tokens through a stack of MoE layers (T = 1 is decode)."""
+
+    def __init__(self, shape: Shape, layers: list, T: int = 1, device="cuda"):
+        self.shape, self.layers, self.T = shape, layers, T
+        s = shape
+        self.device = device
+        self.routed_pools = [q.pool(L.pool, L.pool.shape[1], s.n_experts, s.d, s.F, s.sb_dtype) for L in layers]
+        self.shared_pools = [None if L.shared is None else q.pool(L.shared, L.shared.shape[1], 1, s.d, s.S, s.sb_dtype)
+                             for L in layers]
+        xdt = _torch_dtype(s.x_dtype)
+        self.u = torch.empty((T, s.d), dtype=xdt, device=device)            # expert/router input
+        L = len(layers)
+        # routing of every layer is kept (the last token's), so it can be inspected or replayed
+        self.ids_all = torch.empty((L, T, s.k), dtype=torch.int32, device=device)
+        self.weights_all = torch.empty((L, T, s.k), dtype=torch.float32, device=device)
+        self.logits_all = torch.empty((L, T, s.n_experts), dtype=torch.float32, device=device)
+        self.ids, self.weights, self.logits = self.ids_all[0], self.weights_all[0], self.logits_all[0]
+        self.y_routed = torch.empty((T, s.k, s.d), dtype=torch.float32, device=device)
+        self.y_shared = torch.empty((T, s.d), dtype=torch.float32, device=device)
+        self.router_ws_bytes = q.moe_router_workspace_bytes(T, s.n_experts)
+        self.router_ws = torch.zeros(self.router_ws_bytes, dtype=torch.uint8, device=device)
+        self.gemv_ws_bytes = max(q.q4_expert_gemv_workspace_bytes(rp, s.k, sp, T)
+                                 for rp, sp in zip(self.routed_pools, self.shared_pools))
+        self.gemv_ws = torch.empty(max(self.gemv_ws_bytes, 256), dtype=torch.uint8, device=device)
+        self.graph = None
+
+    # one layer: x_in -> x_out (both [T][d] in the activation dtype)
+    def layer(self, l: int, x_in: torch.Tensor, x_out: torch.Tensor, forced_ids: Optional[torch.Tensor] = None,
+              routed_pool=None, ids: Optional[torch.Tensor] = None, stream=None) -> None:
+        s, L, T = self.shape, self.layers[l], self.T
+        if s.rms_norm:
+            q.moe_rmsnorm(x_in, s.x_dtype, L.gamma, s.eps, T, s.d, self.u, s.x_dtype, stream)
+            u = self.u
+        else:
+            u = x_in
+        lid, lw, lg = self.ids_all[l], self.weights_all[l], self.logits_all[l]
+        q.moe_router_topk(u, s.x_dtype, T, s.d, L.router_w, L.router_s, s.n_experts, s.k, forced_ids, lid, lw, lg,
+                          self.router_ws, self.router_ws_bytes, stream)
+        q.q4_expert_gemv(routed_pool or self.routed_pools[l], lid if ids is None else ids, s.k, self.shared_pools[l],
+                         u, s.x_dtype, T, s.act, self.y_routed, self.y_shared, self.gemv_ws, self.gemv_ws_bytes, stream)
+        q.moe_combine(self.y_routed, lw, self.y_shared if self.shared_pools[l] is not None else None,
+                      x_in if s.rms_norm else None, s.x_dtype, T, s.k, s.d, x_out, s.x_dtype, stream)
+
+    def step(self, x: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+        """Run every layer: x -> out, ping-ponging between `out` and an internal buffer."""
+        n = len(self.layers)
+        if not hasattr(self, "_tmp"):
+            self._tmp = torch.empty_like(out)
+        bufs = [self._tmp, out] if n % 2 == 0 else [out, self._tmp]
+        src = x
+        for l in range(n):
+            dst = bufs[l % 2]
+            self.layer(l, src, dst, stream=stream)
+            src = dst
+
+    def capture(self, x: torch.Tensor, out: torch.Tensor) -> torch.cuda.CUDAGraph:
+        """Capture one whole-stack step into a HIP graph (replay with graph.replay())."""
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.step(x, out, stream=s)          # warm-up outside capture
+        torch.cuda.current_stream().wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step(x, out, stream=torch.cuda.current_stream())
+        self.graph = g
+        return g

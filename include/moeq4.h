@@ -1,0 +1,236 @@
+/*
+ * moeq4.h — C ABI of libmoeq4.so: the per-token Mixture-of-Experts decode step on MI355X (gfx950).
+ *
+ * The step, as the pages describe it for Gemma 4 26B-A4B: per token and per layer an 8-bit router picks
+ * the top 8 of 128 experts, the selected experts run as quantized matrix-vector products on 4-bit
+ * MLX-style affine weights, a shared expert runs for every token, and the two branches are combined;
+ * routed experts live in a small per-layer LFU cache fed from slower storage.
+ *
+ * Pages cited (by title):
+ *   [G26]   "Gemma 4 26B : Comment faire tourner un LLM en 2 Go de RAM" (lhusser.fr)
+ *   [LEAF]  romain.leaflet.pub article on TurboFieldfare (untitled page)
+ *   [DAILY] "TurboFieldfare" event page, daily.steinslab.io
+ *   [REMIO] "TurboFieldfare exécute Mac Gemma 4 26B dans 2 Go, mais la vitesse du SSD devient le compromis"
+ *   [DEVT]  "Een model met 26 miljard parameters uitvoeren in twee gigabyte geheugen op een gewone Mac"
+ *
+ * Conventions for every entry point:
+ *   - Pointers named *_dev are device pointers (hipMalloc'd or torch CUDA tensors); *_host are host pointers.
+ *   - The caller owns every buffer.  The library allocates no device memory inside these calls; scratch
+ *     space comes from a caller workspace sized by the matching *_workspace_bytes() query.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Compute calls only enqueue work.
+ *   - Arguments are validated on the host before anything is enqueued; a non-MOE_OK status means nothing
+ *     was enqueued (except MOE_ERR_HIP, raised by a failed launch).  moe_last_error() then returns a
+ *     thread-local message.  Device-side data errors (an expert id outside the pool) cannot be checked on
+ *     the host: the affected outputs are written as NaN.
+ *   - Results are deterministic: fixed reduction orders, no floating-point atomics.
+ */
+#ifndef MOEQ4_H
+#define MOEQ4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,   /* null pointer, bad size, bad enum */
+  MOE_ERR_UNSUPPORTED = 2,   /* shape outside what the kernels support (see each call) */
+  MOE_ERR_OUT_OF_RANGE = 3,  /* a host-visible id or index is outside its range */
+  MOE_ERR_CACHE = 4,         /* cache policy refused the request (duplicate ids, more ids than slots) */
+  MOE_ERR_HIP = 5            /* a HIP runtime call or launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Gated activation of the expert FFN.  The pages name no activation; GELU (tanh form) is the reading for
+ * Gemma-style experts, SiLU the common alternative. */
+typedef enum { MOE_ACT_GELU_TANH = 0, MOE_ACT_SILU = 1 } moe_act;
+
+/* ---------------------------------------------------------------------------------------------------
+ * Expert record format ([REMIO] "L'affirmation des 2 Go fait de la bande passante SSD la nouvelle
+ * contrainte": experts in MLX affine 4-bit layout; [DAILY] "1. Compression par 4").
+ *
+ * One expert (hidden size d, FFN width F) is one contiguous record — the unit the expert cache copies.
+ * Sections, each starting on a 256-byte boundary, record size rounded up to 256 bytes:
+ *   gate_up codes   uint32 [2F][d/8]       rows 0..F-1 = gate matrix, rows F..2F-1 = up matrix
+ *   gate_up scale/bias  sb [2F][d/64][2]   (scale, bias) per group of 64 input columns
+ *   down codes      uint32 [d][F/8]
+ *   down scale/bias     sb [d][F/64][2]
+ * Code of column c of a row: word c/8 of that row, bits 4*(c%8) .. 4*(c%8)+3 (low nibble first).
+ * Dequantized weight: w = scale * code + bias, code in 0..15.  sb is bf16 or fp32 (moe_dtype).
+ * d and F must be multiples of 64.
+ * ------------------------------------------------------------------------------------------------- */
+
+/* Byte size of one expert record; 0 if d or F is not a positive multiple of 64 or sb_dtype is invalid. */
+size_t moe_record_bytes(int32_t d, int32_t F, moe_dtype sb_dtype);
+
+/* Byte offsets of the four sections (gate_up codes, gate_up s/b, down codes, down s/b) into offsets[4]. */
+moe_status moe_record_layout(int32_t d, int32_t F, moe_dtype sb_dtype, size_t offsets[4]);
+
+/* A pool of expert records in device memory: record i at base + i * record_bytes. */
+typedef struct {
+  const void* base_dev;    /* device pointer to record 0 (256-byte aligned) */
+  size_t record_bytes;     /* stride between records, >= moe_record_bytes(d, F, sb_dtype), multiple of 256 */
+  int32_t n_records;       /* experts in the pool (or cache slots) */
+  int32_t d;               /* hidden size, multiple of 64, <= 8192 */
+  int32_t F;               /* FFN width, multiple of 64, <= 8192 */
+  moe_dtype sb_dtype;      /* scale/bias dtype */
+} moe_q4_pool;
+
+/* ---------------------------------------------------------------------------------------------------
+ * q4_quantize — encode fp32 weights W [N][K] (row-major, device) into 4-bit codes and scale/bias.
+ * The pages list quantization among the engine's own GPU kernels ([DEVT] "Geen afhankelijkheden van
+ * llama.cpp en MLX").  Min-max per group of 64 along K (the plainest affine reading):
+ *   scale = (max - min)/15 (fp32), bias = min, both rounded to sb_dtype (round-to-nearest-even);
+ *   code = clamp(round_half_even((w - bias) / scale), 0, 15) in IEEE fp32; code = 0 when scale == 0.
+ * codes_dev: uint32 [N][K/8]; sb_dev: sb_dtype [N][K/64][2].  K % 64 == 0, N >= 1.
+ * ------------------------------------------------------------------------------------------------- */
+moe_status q4_quantize(const float* w_dev, int32_t N, int32_t K, moe_dtype sb_dtype,
+                       uint32_t* codes_dev, void* sb_dev, void* stream);
+
+/* Encode one expert record from fp32 gate_up [2F][d] and down [d][F] weights (device) into record_dev
+ * (moe_record_bytes(d, F, sb_dtype) bytes, 256-byte aligned).  Padding bytes are left untouched. */
+moe_status q4_pack_expert(const float* w_gate_up_dev, const float* w_down_dev, int32_t d, int32_t F,
+                          moe_dtype sb_dtype, void* record_dev, void* stream);
+
+/* ---------------------------------------------------------------------------------------------------
+ * moe_rmsnorm — u[t] = x[t] / sqrt(mean(x[t]^2) + eps) * gamma, fp32 math, rounded to out_dtype (RNE).
+ * The pages list a normalisation (RMSNorm) kernel ([LEAF] "Du code sur-mesure sans dépendance externe";
+ * [DEVT] "Geen afhankelijkheden van llama.cpp en MLX"); it precedes each MoE block in the stacked decode.
+ * x_dev: x_dtype [T][d]; gamma_dev: fp32 [d]; out_dev: out_dtype [T][d].  d % 8 == 0, d <= 16384, T >= 1;
+ * x and gamma 16-byte aligned.
+ * ------------------------------------------------------------------------------------------------- */
+moe_status moe_rmsnorm(const void* x_dev, moe_dtype x_dtype, const float* gamma_dev, float eps,
+                       int32_t T, int32_t d, void* out_dev, moe_dtype out_dtype, void* stream);
+
+/* ---------------------------------------------------------------------------------------------------
+ * moe_router_topk — the 8-bit router and top-k selection ([G26] "Le pipeline de traitement": an 8-bit
+ * router picks the 8 experts a token needs; [DAILY] "L'atout caché des modèles MoE": 8 of 128 active).
+ *   logit[t][e] = row_scale[e] * sum_j w[e][j] * x[t][j]      (int8 x activation, fp32 accumulate)
+ *   ids[t]      = the k largest logits, descending; equal logits -> lower expert id first
+ *   weights[t]  = softmax of logit[t][ids[t][i]] over i < k   (sums to 1)
+ * With forced_ids_dev != NULL the selection is skipped: ids are copied from forced_ids_dev [T][k] (a routing
+ * trace) and weights are the softmax of the logits at those ids, in that order.
+ * x_dev: x_dtype [T][d]; w_dev: int8 [E][d] row-major; row_scale_dev: fp32 [E];
+ * ids_dev: int32 [T][k]; weights_dev: fp32 [T][k]; logits_dev: fp32 [T][E] or NULL.
+ * Limits: 1 <= k <= min(E, 32), E <= 1024, d % 16 == 0, d <= 8192.
+ * Workspace: moe_router_workspace_bytes(T, E) bytes of device memory that must be ZERO before its first
+ * use; every completed call leaves it zero again, so one workspace serves any number of calls ordered
+ * on one stream (and graph replays).  Calls that overlap in time need separate workspaces.
+ * ------------------------------------------------------------------------------------------------- */
+size_t moe_router_workspace_bytes(int32_t T, int32_t E);
+moe_status moe_router_topk(const void* x_dev, moe_dtype x_dtype, int32_t T, int32_t d,
+                           const int8_t* w_dev, const float* row_scale_dev, int32_t E, int32_t k,
+                           const int32_t* forced_ids_dev, int32_t* ids_dev, float* weights_dev,
+                           float* logits_dev, void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------------
+ * q4_expert_gemv — the selected experts' FFNs and the shared expert's FFN on 4-bit affine weights
+ * ([LEAF] "Du code sur-mesure sans dépendance externe": quantized matrix-vector kernels; [REMIO]
+ * "Mac Gemma 4 26B tient en mémoire...": one shared expert for every token besides the 8 routed ones).
+ * For each token t and each i < k with e = ids[t][i] (an index into `routed`):
+ *   y_routed[t][i] = W_down,e ( act(W_gate,e x[t]) * (W_up,e x[t]) )          fp32 [d]
+ * and, if shared != NULL (a pool whose record 0 is the shared expert, width shared->F):
+ *   y_shared[t]    = W_down,s ( act(W_gate,s x[t]) * (W_up,s x[t]) )          fp32 [d]
+ * Weights are dequantized on the fly; accumulation is fp32.  Both experts kinds run in the same launches.
+ * x_dev: x_dtype [T][d]; ids_dev: int32 [T][k] (device, e.g. straight from moe_router_topk or cache slot
+ * ids from expert_cache_stage); y_routed_dev: fp32 [T][k][d]; y_shared_dev: fp32 [T][d] (needed iff shared).
+ * T == 1 is the decode GEMV; T > 1 groups the (token, expert) pairs by expert so each selected expert's
+ * weights are read once per call (grouped small-M GEMM on the matrix cores).
+ * Limits: k <= 32; routed and shared share d; routed may be NULL (k == 0) to run only the shared expert.
+ * Workspace: q4_expert_gemv_workspace_bytes(...) bytes of device memory (contents need no initial value).
+ * An id outside [0, routed->n_records) makes that expert's y_routed row NaN.
+ * ------------------------------------------------------------------------------------------------- */
+size_t q4_expert_gemv_workspace_bytes(const moe_q4_pool* routed, int32_t k, const moe_q4_pool* shared, int32_t T);
+moe_status q4_expert_gemv(const moe_q4_pool* routed, const int32_t* ids_dev, int32_t k,
+                          const moe_q4_pool* shared, const void* x_dev, moe_dtype x_dtype, int32_t T,
+                          moe_act act, float* y_routed_dev, float* y_shared_dev,
+                          void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/* The two halves of q4_expert_gemv, for callers that schedule them separately (and for timing one
+ * launch).  q4_expert_gate_up computes h = act(W_gate x) * (W_up x) for the routed and shared experts
+ * into the workspace (fp32 [T][k][F] then [T][S]); q4_expert_down reads h from the same workspace and
+ * writes y_routed / y_shared.  Between the two calls the caller must pass the same pools, ids, k, T and
+ * workspace, in stream order.  Same limits and errors as q4_expert_gemv. */
+moe_status q4_expert_gate_up(const moe_q4_pool* routed, const int32_t* ids_dev, int32_t k, const moe_q4_pool* shared,
+                             const void* x_dev, moe_dtype x_dtype, int32_t T, moe_act act, void* workspace_dev,
+                             size_t workspace_bytes, void* stream);
+moe_status q4_expert_down(const moe_q4_pool* routed, const int32_t* ids_dev, int32_t k, const moe_q4_pool* shared,
+                          int32_t T, float* y_routed_dev, float* y_shared_dev, void* workspace_dev,
+                          size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------------
+ * moe_combine — merge the branches ([G26] "Concurrence pour masquer la latence": the shared-expert output
+ * and the routed outputs are combined once the routed experts are in; [REMIO] "L'affirmation des 2 Go...").
+ *   out[t] = round_out( sum_{i<k} weights[t][i] * y_routed[t][i] + y_shared[t] + residual[t] )
+ * summed in fp32 in the order i = 0..k-1, then shared, then residual; y_shared and residual may be NULL.
+ * y_routed_dev: fp32 [T][k][d]; weights_dev: fp32 [T][k]; y_shared_dev: fp32 [T][d]; residual_dev:
+ * residual_dtype [T][d]; out_dev: out_dtype [T][d] (may alias residual_dev when the dtypes match).
+ * ------------------------------------------------------------------------------------------------- */
+moe_status moe_combine(const float* y_routed_dev, const float* weights_dev, const float* y_shared_dev,
+                       const void* residual_dev, moe_dtype residual_dtype, int32_t T, int32_t k, int32_t d,
+                       void* out_dev, moe_dtype out_dtype, void* stream);
+
+/* ---------------------------------------------------------------------------------------------------
+ * Expert cache — 16-slot-per-layer least-frequently-used cache of expert records ([DAILY] "Cache
+ * d'experts"; [DEVT] "Wat is de belangrijkste architectuurtruuc"; [REMIO] "Mac Gemma 4 26B tient en
+ * mémoire..."), fed on demand from slower memory while the shared expert computes ([G26] "Concurrence
+ * pour masquer la latence").  Here the slow tier is pinned host memory and the fast tier is HBM; misses
+ * are copied with hipMemcpyAsync on a caller-provided copy stream.
+ *
+ * Policy (readings of "LFU"): in-cache LFU — a slot's use count starts at 1 on load and is forgotten on
+ * eviction; a request first marks every requested expert already resident (count += 1, last use = now)
+ * and pins it for the request; each miss, in request order, takes the lowest empty slot, else evicts the
+ * unpinned slot with the smallest (count, last use, slot index).  The cache starts empty.
+ *
+ * moe_expert_cache_create: n_layers x n_slots slots of record_bytes each.  host_pool_host[l] points to
+ * layer l's n_experts records in pinned host memory (hipHostMalloc); slot_pool_dev[l] points to layer l's
+ * n_slots slot records in device memory.  Both arrays of pointers are copied; the memory stays the
+ * caller's and must outlive the cache.  flags: 0, or MOE_CACHE_HOST_ONLY (slot pools and slot-id outputs
+ * are host memory, copies are memcpy, streams/events are ignored: the policy without a GPU).
+ * ------------------------------------------------------------------------------------------------- */
+typedef struct moe_expert_cache moe_expert_cache;
+#define MOE_CACHE_HOST_ONLY 1u
+
+moe_status moe_expert_cache_create(int32_t n_layers, int32_t n_experts, int32_t n_slots, size_t record_bytes,
+                                   const void* const* host_pool_host, void* const* slot_pool_dev,
+                                   uint32_t flags, moe_expert_cache** out);
+void moe_expert_cache_destroy(moe_expert_cache* cache);
+
+/* expert_cache_stage — make the n experts ids_host[0..n) of `layer` resident.
+ * Runs the policy on the host, enqueues one hipMemcpyAsync per miss (pinned host record -> HBM slot) on
+ * copy_stream after waiting on wait_event (if not NULL: the event recorded after the last kernel that read
+ * this layer's slots, so a slot is never overwritten while it is read), writes the slot index of each id
+ * to slot_ids_dev (int32 [n], copied on copy_stream), then records ready_event (if not NULL) on
+ * copy_stream.  Kernels that read the slots must wait on ready_event.
+ * Errors: duplicate ids or n > n_slots -> MOE_ERR_CACHE; id outside [0, n_experts) -> MOE_ERR_OUT_OF_RANGE;
+ * a failed copy -> MOE_ERR_HIP.  On any error the policy state is left as it was before the call
+ * (transactional) and the affected slots are marked empty if a copy may have been partially enqueued. */
+moe_status expert_cache_stage(moe_expert_cache* cache, int32_t layer, const int32_t* ids_host, int32_t n,
+                              int32_t* slot_ids_dev, void* copy_stream, void* wait_event, void* ready_event);
+
+/* Counters of one layer, or of all layers when layer == -1. Any output pointer may be NULL. */
+moe_status moe_expert_cache_stats(const moe_expert_cache* cache, int32_t layer, uint64_t* hits,
+                                  uint64_t* misses, uint64_t* bytes_copied);
+
+/* Expert held by each slot of a layer (-1 = empty): experts_host int32 [n_slots]. */
+moe_status moe_expert_cache_slots(const moe_expert_cache* cache, int32_t layer, int32_t* experts_host);
+
+/* Test hook: make the copy number `after_n_copies` (counted from this call, 0-based) fail with
+ * MOE_ERR_HIP without copying; -1 disables.  Used to force the failure path from the host. */
+moe_status moe_expert_cache_inject_copy_failure(moe_expert_cache* cache, int32_t after_n_copies);
+
+/* Thread-local message describing the last non-MOE_OK status returned on this thread. */
+const char* moe_last_error(void);
+
+/* Library version string. */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEQ4_H */

@@ -1,0 +1,63 @@
+"""Helpers shared by the GPU tests: device layers built from the seeded generator's device twin and the
+library's encoder, and the error measures of the parity bar."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import synth
+import synth.device as sdev
+from bit_quantized_expert_int8_amd import decoder, moeq4 as q
+
+
+def shape_of(cfg: synth.MoEConfig, act: int = q.MOE_ACT_GELU_TANH) -> decoder.Shape:
+    return decoder.Shape(d=cfg.d, n_experts=cfg.n_experts, k=cfg.k, F=cfg.F, S=cfg.S,
+                         sb_dtype=q.MOE_BF16 if cfg.sb_bf16 else q.MOE_F32,
+                         x_dtype=q.MOE_BF16 if cfg.x_bf16 else q.MOE_F32, act=act, rms_norm=cfg.rms_norm)
+
+
+def device_layer(cfg: synth.MoEConfig, layer: int, gamma_ones: bool = True) -> decoder.LayerWeights:
+    wc = cfg.weight_cfg
+
+    def fill_expert(e, wgu, wd):
+        sdev.weight_into(wgu, wc, layer, synth.TAG_GATE_UP, e)
+        sdev.weight_into(wd, wc, layer, synth.TAG_DOWN, e)
+
+    def fill_shared(wgu, wd):
+        sdev.weight_into(wgu, wc, layer, synth.TAG_SHARED_GATE_UP, 0)
+        sdev.weight_into(wd, wc, layer, synth.TAG_SHARED_DOWN, 0)
+
+    rw, rs = synth.router_int8(wc, layer, cfg.n_experts, cfg.d)
+    gamma = torch.from_numpy(synth.rms_gamma(wc, layer, cfg.d, ones=gamma_ones)) if cfg.rms_norm else None
+    return decoder.pack_layer(shape_of(cfg), fill_expert, fill_shared, torch.from_numpy(rw), torch.from_numpy(rs), gamma)
+
+
+def token_batch(cfg: synth.MoEConfig, tokens) -> torch.Tensor:
+    """Activations of the given tokens as a device tensor in the configuration's dtype."""
+    if cfg.x_bf16:
+        bits = np.stack([synth.activation(cfg.act_cfg, t, cfg.d, bf16=True) for t in tokens]).astype(np.int16)
+        return torch.from_numpy(bits).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.stack([synth.activation(cfg.act_cfg, t, cfg.d, bf16=False) for t in tokens])).cuda()
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def max_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """||got - ref||_inf / ||ref||_inf (the output parity measure)."""
+    return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+def topk_consistent(gpu_ids, ref_logits, k, gap=1e-3) -> bool:
+    """Exact ordered match when the oracle's k-th/k+1-th gap exceeds `gap`; otherwise the GPU's set must be
+    a valid top-k within `gap` (every chosen logit >= the k-th largest minus gap)."""
+    order = sorted(range(len(ref_logits)), key=lambda e: (-ref_logits[e], e))
+    if k == len(ref_logits) or ref_logits[order[k - 1]] - ref_logits[order[k]] > gap:
+        # ties among the kept ones within gap may also reorder; require the exact list otherwise
+        kept = [ref_logits[e] for e in order[:k]]
+        if all(kept[i] - kept[i + 1] > gap for i in range(k - 1)):
+            return list(gpu_ids) == order[:k]
+        return sorted(gpu_ids) == sorted(order[:k])
+    kth = ref_logits[order[k - 1]]
+    return len(set(gpu_ids)) == k and all(ref_logits[e] >= kth - gap for e in gpu_ids)
