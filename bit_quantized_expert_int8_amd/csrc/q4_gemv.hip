@@ -334,6 +334,12 @@ struct GemvArgs {
   int32_t nb_shared;       // blocks of the shared expert per token
   int32_t nb_routed;       // blocks per routed expert
   int32_t act;
+  // fused combine (down launch only): out[t] = round(sum_i w[t][i] y_routed[t][i] + y_shared[t] + residual[t])
+  const float* weights;    // [T][k]
+  const void* residual;    // [T][d] or NULL
+  int32_t res_bf16, out_bf16;
+  void* out;               // [T][d]
+  uint32_t* tile_counters; // [T][d/16], zero between calls
 };
 
 inline size_t lds_bytes(int K) { return (size_t)(K / 32) * (kHgStride * 4 + 16); }
@@ -391,7 +397,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gate_up_kernel(GemvArgs a) {
 // ------------------------------------------------------------------------------------------------
 // down: block = 16 consecutive output rows of one expert; input = that expert's h from gate_up
 // ------------------------------------------------------------------------------------------------
-template <int NBW, bool SB_BF16>
+template <int NBW, bool SB_BF16, bool COMBINE>
 __global__ __launch_bounds__(64 * kMaxWaves) void down_kernel(GemvArgs a) {
   extern __shared__ __align__(16) uint32_t lds[];
   const int d = a.d;
@@ -408,11 +414,48 @@ __global__ __launch_bounds__(64 * kMaxWaves) void down_kernel(GemvArgs a) {
   float yA, yB;
   rowpair_partial<NBW, float, SB_BF16>(rec + P.off_q + r * rowb, rec + P.off_q + (r + 8) * rowb, rec + P.off_sb + r * sbrow,
                                         rec + P.off_sb + (r + 8) * sbrow, h, K, st, sl.valid, yA, yB);
-  if (!block_sum(yA, yB)) return;
+  const bool total = block_sum(yA, yB);
   if (!sl.valid) yA = yB = __builtin_nanf("");
   float* y = sl.shared ? a.y_shared + (int64_t)t * d : a.y_routed + ((int64_t)t * a.k + sl.slot) * d;
-  y[r] = yA;
-  y[r + 8] = yB;
+  if (!COMBINE) {
+    if (total) {
+      y[r] = yA;
+      y[r + 8] = yB;
+    }
+    return;
+  }
+  // Fused combine: the k routed blocks and the shared block of a 16-row tile publish their rows with
+  // device-coherent stores and take a ticket; the last of them sums the tile in the fixed order
+  // i = 0..k-1, shared, residual (the order of moe_combine) and writes the rounded output.
+  __shared__ uint32_t last;
+  if (total) {
+    __hip_atomic_store(y + r, yA, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(y + r + 8, yB, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int ntiles = d / 16;
+  uint32_t* ctr = a.tile_counters + (int64_t)t * ntiles + sl.tile;
+  const uint32_t units = (uint32_t)a.k + (a.nb_shared ? 1u : 0u);
+  if (threadIdx.x == 0) last = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == units - 1;
+  __syncthreads();
+  if (!last || threadIdx.x >= 16) return;
+  const int row = sl.tile * 16 + threadIdx.x;
+  float acc = 0.f;
+  for (int i = 0; i < a.k; ++i)
+    acc = __builtin_fmaf(a.weights[(int64_t)t * a.k + i],
+                         __hip_atomic_load(a.y_routed + ((int64_t)t * a.k + i) * d + row, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT),
+                         acc);
+  if (a.nb_shared) acc += __hip_atomic_load(a.y_shared + (int64_t)t * d + row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (a.residual)
+    acc += a.res_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.residual)[(int64_t)t * d + row])
+                      : reinterpret_cast<const float*>(a.residual)[(int64_t)t * d + row];
+  if (a.out_bf16)
+    reinterpret_cast<uint16_t*>(a.out)[(int64_t)t * d + row] = (uint16_t)f32_to_bf16_bits(acc);
+  else
+    reinterpret_cast<float*>(a.out)[(int64_t)t * d + row] = acc;
+  if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -432,10 +475,15 @@ moe_status launch_gate_up(const GemvArgs& a, moe_dtype xdt, bool sb_bf16, dim3 g
 }
 
 template <int NBW>
-moe_status launch_down(const GemvArgs& a, bool sb_bf16, dim3 grid, int waves, size_t lds, hipStream_t s) {
+moe_status launch_down(const GemvArgs& a, bool sb_bf16, bool combine, dim3 grid, int waves, size_t lds, hipStream_t s) {
   const dim3 block(64 * waves);
-  if (sb_bf16) hipLaunchKernelGGL((down_kernel<NBW, true>), grid, block, lds, s, a);
-  else hipLaunchKernelGGL((down_kernel<NBW, false>), grid, block, lds, s, a);
+  if (combine) {
+    if (sb_bf16) hipLaunchKernelGGL((down_kernel<NBW, true, true>), grid, block, lds, s, a);
+    else hipLaunchKernelGGL((down_kernel<NBW, false, true>), grid, block, lds, s, a);
+  } else {
+    if (sb_bf16) hipLaunchKernelGGL((down_kernel<NBW, true, false>), grid, block, lds, s, a);
+    else hipLaunchKernelGGL((down_kernel<NBW, false, false>), grid, block, lds, s, a);
+  }
   return check_launch("q4_expert_gemv(down)");
 }
 
@@ -555,7 +603,8 @@ moe_status run_gate_up(GemvArgs a, const RecordOffsets& orr, const RecordOffsets
 }
 
 // down: 16 output rows per block; rows of K = F (routed) or S (shared)
-moe_status run_down(GemvArgs a, const RecordOffsets& orr, const RecordOffsets& osh, bool sb_bf16, int T, hipStream_t s) {
+moe_status run_down(GemvArgs a, const RecordOffsets& orr, const RecordOffsets& osh, bool sb_bf16, int T, hipStream_t s,
+                    bool combine = false) {
   a.routed.off_q = (int64_t)orr.down_q;
   a.routed.off_sb = (int64_t)orr.down_sb;
   a.shared.off_q = (int64_t)osh.down_q;
@@ -570,7 +619,7 @@ moe_status run_down(GemvArgs a, const RecordOffsets& orr, const RecordOffsets& o
   const int nbw = (nit_hi + waves - 1) / waves;
   dim3 grid(a.nb_shared + a.k * a.nb_routed, T);
   return dispatch_nbw(nbw, [&](auto nb) {
-    return launch_down<decltype(nb)::value>(a, sb_bf16, grid, waves, lds_bytes(nit_r > nit_s ? Fr : Fs), s);
+    return launch_down<decltype(nb)::value>(a, sb_bf16, combine, grid, waves, lds_bytes(nit_r > nit_s ? Fr : Fs), s);
   });
 }
 
@@ -616,4 +665,56 @@ extern "C" moe_status q4_expert_down(const moe_q4_pool* routed, const int32_t* i
                           y_shared_dev, workspace_dev, workspace_bytes, false, true, &a, &orr, &osh);
   if (st != MOE_OK) return st;
   return run_down(a, orr, osh, sb_is_bf16(routed, k, shared), T, as_stream(stream));
+}
+
+extern "C" size_t q4_expert_gemv_combine_workspace_bytes(const moe_q4_pool* routed, int32_t k, const moe_q4_pool* shared,
+                                                         int32_t T) {
+  if (T < 1 || (!shared && !(routed && k > 0))) return 0;
+  const int d = (routed && k > 0) ? routed->d : shared->d;
+  size_t b = q4_expert_gemv_workspace_bytes(routed, k, shared, T);
+  if (routed && k > 0) b += align256((size_t)T * k * d * 4);
+  if (shared) b += align256((size_t)T * d * 4);
+  return b + align256((size_t)T * (d / 16) * 4);
+}
+
+extern "C" moe_status q4_expert_gemv_combine(const moe_q4_pool* routed, const int32_t* ids_dev, int32_t k,
+                                             const moe_q4_pool* shared, const void* x_dev, moe_dtype x_dtype, int32_t T,
+                                             moe_act act, const float* weights_dev, const void* residual_dev,
+                                             moe_dtype residual_dtype, void* out_dev, moe_dtype out_dtype,
+                                             void* workspace_dev, size_t workspace_bytes, void* stream) {
+  const char* who = "q4_expert_gemv_combine";
+  const bool has_routed = routed && k > 0;
+  if (!out_dev) return fail(MOE_ERR_INVALID_ARG, "%s: out is NULL", who);
+  if (has_routed && !weights_dev) return fail(MOE_ERR_INVALID_ARG, "%s: weights is NULL", who);
+  if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "%s: bad out_dtype", who);
+  if (residual_dev && residual_dtype != MOE_F32 && residual_dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "%s: bad residual_dtype", who);
+  const size_t need = q4_expert_gemv_combine_workspace_bytes(routed, k, shared, T);
+  if (workspace_dev && workspace_bytes < need)
+    return fail(MOE_ERR_INVALID_ARG, "%s: workspace %zu bytes < %zu", who, workspace_bytes, need);
+  // y_routed / y_shared / tile counters live in the workspace after the hidden activations; prepare() checks
+  // the rest of the arguments with placeholder y pointers and fills in the hidden-activation layout
+  const size_t hb = q4_expert_gemv_workspace_bytes(routed, k, shared, T);
+  char* ws = static_cast<char*>(workspace_dev);
+  const int d = has_routed ? routed->d : (shared ? shared->d : 0);
+  float* y_r = has_routed && ws ? reinterpret_cast<float*>(ws + hb) : nullptr;
+  const size_t yrb = has_routed ? align256((size_t)T * k * d * 4) : 0;
+  float* y_s = shared && ws ? reinterpret_cast<float*>(ws + hb + yrb) : nullptr;
+  const size_t ysb = shared ? align256((size_t)T * d * 4) : 0;
+  GemvArgs a;
+  RecordOffsets orr{}, osh{};
+  moe_status st = prepare(who, routed, ids_dev, k, shared, x_dev, x_dtype, T, act, y_r, y_s, workspace_dev,
+                          workspace_bytes, true, true, &a, &orr, &osh);
+  if (st != MOE_OK) return st;
+  a.weights = weights_dev;
+  a.residual = residual_dev;
+  a.res_bf16 = residual_dtype == MOE_BF16;
+  a.out = out_dev;
+  a.out_bf16 = out_dtype == MOE_BF16;
+  a.tile_counters = reinterpret_cast<uint32_t*>(ws + hb + yrb + ysb);
+  const bool sb16 = sb_is_bf16(routed, k, shared);
+  hipStream_t s = as_stream(stream);
+  st = run_gate_up(a, orr, osh, x_dtype, sb16, T, s);
+  if (st != MOE_OK) return st;
+  return run_down(a, orr, osh, sb16, T, s, true);
 }

@@ -101,6 +101,9 @@ struct RouterArgs {
   float* weights;
   float* logits;         // [T][E]: caller's buffer or workspace
   uint32_t* counters;    // [T], zero between calls
+  const float* gamma;    // RMSNorm gain [d], or NULL: the router reads x as is
+  float eps;
+  void* u_out;           // [T][d] normalized activation (x dtype), written by block 0; NULL = not wanted
 };
 
 __device__ __forceinline__ bool better(float v, int i, float v2, int i2) { return v > v2 || (v == v2 && i < i2); }
@@ -122,25 +125,53 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
     const int c = lane + 64 * m;
     if (c < nch) q[m] = *reinterpret_cast<const int4*>(row + c * 16);
   }
-  // activation: 8 elements per thread and pass, all passes issued before any is used
-  {
-    constexpr int kPasses = 8192 / (8 * 256);
-    float v[kPasses][8];
+  // activation (and the norm gain): 8 elements per thread and pass, all issued before any is used
+  constexpr int kPasses = 8192 / (8 * 256);
+  float v[kPasses][8], g[kPasses][8];
 #pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-      const int j0 = (threadIdx.x + 256 * p) * 8;
-      if (j0 < a.d) load8(x + j0, v[p]);
+  for (int p = 0; p < kPasses; ++p) {
+    const int j0 = (threadIdx.x + 256 * p) * 8;
+    if (j0 < a.d) {
+      load8(x + j0, v[p]);
+      if (a.gamma) load8(a.gamma + j0, g[p]);
     }
+  }
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int j0 = (threadIdx.x + 256 * p) * 8;
+    if (j0 < a.d) {
+      *reinterpret_cast<float4*>(xs + j0) = make_float4(v[p][0], v[p][1], v[p][2], v[p][3]);
+      *reinterpret_cast<float4*>(xs + j0 + 4) = make_float4(v[p][4], v[p][5], v[p][6], v[p][7]);
+    }
+  }
+  __syncthreads();
+  if (a.gamma) {
+    // RMSNorm fused in: every block reduces x in the same fixed order (wave 0: lane p sums elements
+    // p, p+64, ... then a fixed xor tree), so all blocks obtain the same u bit for bit.
+    __shared__ float rinv;
+    if (wave == 0) {
+      float ss = 0.f;
+      for (int j = lane; j < a.d; j += 64) ss += xs[j] * xs[j];
+      ss = wave_sum(ss);
+      if (lane == 0) rinv = 1.0f / sqrtf(ss / (float)a.d + a.eps);
+    }
+    __syncthreads();
+    const float r = rinv;
+    constexpr bool bf16 = sizeof(XT) == 2;
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
       const int j0 = (threadIdx.x + 256 * p) * 8;
       if (j0 < a.d) {
-        *reinterpret_cast<float4*>(xs + j0) = make_float4(v[p][0], v[p][1], v[p][2], v[p][3]);
-        *reinterpret_cast<float4*>(xs + j0 + 4) = make_float4(v[p][4], v[p][5], v[p][6], v[p][7]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float u = (v[p][i] * r) * g[p][i];
+          xs[j0 + i] = bf16 ? bf16_bits_to_f32(f32_to_bf16_bits(u)) : u;   // the norm output's bf16 rounding point
+          if (a.u_out && blockIdx.x == 0) store_act(a.u_out, bf16, t * a.d + j0 + i, u);
+        }
       }
     }
+    __syncthreads();
   }
-  __syncthreads();
 
   if (e < a.E) {
     float acc = 0.f;
@@ -253,7 +284,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const float r = res ? load_act(res, t * d + j) : 0.f;
   float acc = 0.f;
 #pragma unroll
-  for (int i = 0; i < KT; ++i) acc += (i < k ? wv[i] : 0.f) * yv[i];
+  for (int i = 0; i < KT; ++i) acc = __builtin_fmaf(i < k ? wv[i] : 0.f, yv[i], acc);
   acc += s;
   acc += r;
   store_act(out, out_bf16, t * d + j, acc);
@@ -288,23 +319,50 @@ extern "C" size_t moe_router_workspace_bytes(int32_t T, int32_t E) {
   return counters + (size_t)T * E * 4;
 }
 
+namespace {
+moe_status router_launch(const char* who, const void* x_dev, moe_dtype x_dtype, int32_t T, int32_t d, const int8_t* w_dev,
+                         const float* row_scale_dev, int32_t E, int32_t k, const int32_t* forced_ids_dev, int32_t* ids_dev,
+                         float* weights_dev, float* logits_dev, void* workspace_dev, size_t workspace_bytes,
+                         const float* gamma_dev, float eps, void* u_dev, void* stream);
+}
+
 extern "C" moe_status moe_router_topk(const void* x_dev, moe_dtype x_dtype, int32_t T, int32_t d, const int8_t* w_dev,
                                       const float* row_scale_dev, int32_t E, int32_t k, const int32_t* forced_ids_dev,
                                       int32_t* ids_dev, float* weights_dev, float* logits_dev, void* workspace_dev,
                                       size_t workspace_bytes, void* stream) {
+  return router_launch("moe_router_topk", x_dev, x_dtype, T, d, w_dev, row_scale_dev, E, k, forced_ids_dev, ids_dev,
+                       weights_dev, logits_dev, workspace_dev, workspace_bytes, nullptr, 0.f, nullptr, stream);
+}
+
+extern "C" moe_status moe_norm_router_topk(const void* x_dev, moe_dtype x_dtype, const float* gamma_dev, float eps, int32_t T,
+                                           int32_t d, const int8_t* w_dev, const float* row_scale_dev, int32_t E, int32_t k,
+                                           const int32_t* forced_ids_dev, int32_t* ids_dev, float* weights_dev,
+                                           float* logits_dev, void* u_dev, void* workspace_dev, size_t workspace_bytes,
+                                           void* stream) {
+  if (!gamma_dev || !u_dev) return fail(MOE_ERR_INVALID_ARG, "moe_norm_router_topk: gamma or u is NULL");
+  if (!(eps >= 0.f)) return fail(MOE_ERR_INVALID_ARG, "moe_norm_router_topk: eps must be >= 0");
+  return router_launch("moe_norm_router_topk", x_dev, x_dtype, T, d, w_dev, row_scale_dev, E, k, forced_ids_dev, ids_dev,
+                       weights_dev, logits_dev, workspace_dev, workspace_bytes, gamma_dev, eps, u_dev, stream);
+}
+
+namespace {
+moe_status router_launch(const char* who, const void* x_dev, moe_dtype x_dtype, int32_t T, int32_t d, const int8_t* w_dev,
+                         const float* row_scale_dev, int32_t E, int32_t k, const int32_t* forced_ids_dev, int32_t* ids_dev,
+                         float* weights_dev, float* logits_dev, void* workspace_dev, size_t workspace_bytes,
+                         const float* gamma_dev, float eps, void* u_dev, void* stream) {
   if (!x_dev || !w_dev || !row_scale_dev || !ids_dev || !weights_dev || !workspace_dev)
-    return fail(MOE_ERR_INVALID_ARG, "moe_router_topk: NULL pointer");
-  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "moe_router_topk: bad x_dtype");
-  if (T < 1 || T > 65535) return fail(MOE_ERR_INVALID_ARG, "moe_router_topk: T=%d", T);
+    return fail(MOE_ERR_INVALID_ARG, "%s: NULL pointer", who);
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "%s: bad x_dtype", who);
+  if (T < 1 || T > 65535) return fail(MOE_ERR_INVALID_ARG, "%s: T=%d", who, T);
   if (E < 1 || E > kMaxExperts || k < 1 || k > E || k > kMaxK)
-    return fail(MOE_ERR_UNSUPPORTED, "moe_router_topk: E=%d k=%d (need 1 <= k <= min(E, 32), E <= 1024)", E, k);
-  if (d < 16 || d % 16 || d > 8192) return fail(MOE_ERR_UNSUPPORTED, "moe_router_topk: d=%d (multiple of 16, <= 8192)", d);
+    return fail(MOE_ERR_UNSUPPORTED, "%s: E=%d k=%d (need 1 <= k <= min(E, 32), E <= 1024)", who, E, k);
+  if (d < 16 || d % 16 || d > 8192) return fail(MOE_ERR_UNSUPPORTED, "%s: d=%d (multiple of 16, <= 8192)", who, d);
   if (!aligned(w_dev, 16) || !aligned(x_dev, 16))
-    return fail(MOE_ERR_INVALID_ARG, "moe_router_topk: router weights or x not 16-byte aligned");
+    return fail(MOE_ERR_INVALID_ARG, "%s: router weights or x not 16-byte aligned", who);
   const size_t need = moe_router_workspace_bytes(T, E);
   if (workspace_bytes < need)
-    return fail(MOE_ERR_INVALID_ARG, "moe_router_topk: workspace %zu bytes < %zu", workspace_bytes, need);
-  if (!aligned(workspace_dev, 256)) return fail(MOE_ERR_INVALID_ARG, "moe_router_topk: workspace not 256-byte aligned");
+    return fail(MOE_ERR_INVALID_ARG, "%s: workspace %zu bytes < %zu", who, workspace_bytes, need);
+  if (!aligned(workspace_dev, 256)) return fail(MOE_ERR_INVALID_ARG, "%s: workspace not 256-byte aligned", who);
   RouterArgs a;
   a.x = x_dev;
   a.d = d;
@@ -318,6 +376,10 @@ extern "C" moe_status moe_router_topk(const void* x_dev, moe_dtype x_dtype, int3
   a.counters = static_cast<uint32_t*>(workspace_dev);
   a.logits = logits_dev ? logits_dev
                         : reinterpret_cast<float*>(static_cast<char*>(workspace_dev) + ((size_t)T * 4 + 255) / 256 * 256);
+  a.gamma = gamma_dev;
+  a.eps = eps;
+  a.u_out = u_dev;
+  if (gamma_dev && !aligned(u_dev, 16)) return fail(MOE_ERR_INVALID_ARG, "%s: u not 16-byte aligned", who);
   dim3 grid((E + kRouterWaves - 1) / kRouterWaves, T);
   const size_t lds = (size_t)d * sizeof(float);
   hipStream_t s = as_stream(stream);
@@ -325,8 +387,9 @@ extern "C" moe_status moe_router_topk(const void* x_dev, moe_dtype x_dtype, int3
     hipLaunchKernelGGL(router_kernel<uint16_t>, grid, dim3(256), lds, s, a);
   else
     hipLaunchKernelGGL(router_kernel<float>, grid, dim3(256), lds, s, a);
-  return check_launch("moe_router_topk");
+  return check_launch(who);
 }
+}  // namespace
 
 extern "C" moe_status moe_combine(const float* y_routed_dev, const float* weights_dev, const float* y_shared_dev,
                                   const void* residual_dev, moe_dtype residual_dtype, int32_t T, int32_t k, int32_t d,

@@ -69,10 +69,15 @@ def pack_layer(shape: Shape, fill_expert: Callable, fill_shared: Optional[Callab
 
 
 class MoEDecoder:
-    """Runs T tokens through a stack of MoE layers (T = 1 is decode)."""
+    """Runs T tokens through a stack of MoE layers (T = 1 is decode).
 
-    def __init__(self, shape: Shape, layers: list, T: int = 1, device="cuda"):
-        self.shape, self.layers, self.T = shape, layers, T
+    fused=True (default) runs a layer as two library calls plus one: moe_norm_router_topk (RMSNorm inside
+    the router), then q4_expert_gemv_combine (expert GEMVs with the combine + residual in the down launch's
+    tail).  fused=False runs the five separate calls (moe_rmsnorm, moe_router_topk, q4_expert_gemv,
+    moe_combine); both give the same routing and, on the same normalized input, the same output bits."""
+
+    def __init__(self, shape: Shape, layers: list, T: int = 1, device="cuda", fused: bool = True):
+        self.shape, self.layers, self.T, self.fused = shape, layers, T, fused
         s = shape
         self.device = device
         self.routed_pools = [q.pool(L.pool, L.pool.shape[1], s.n_experts, s.d, s.F, s.sb_dtype) for L in layers]
@@ -93,12 +98,19 @@ class MoEDecoder:
         self.gemv_ws_bytes = max(q.q4_expert_gemv_workspace_bytes(rp, s.k, sp, T)
                                  for rp, sp in zip(self.routed_pools, self.shared_pools))
         self.gemv_ws = torch.empty(max(self.gemv_ws_bytes, 256), dtype=torch.uint8, device=device)
+        # the fused call's workspace ends in per-tile counters that must start at zero (calls leave them zero)
+        self.fused_ws_bytes = max(q.q4_expert_gemv_combine_workspace_bytes(rp, s.k, sp, T)
+                                  for rp, sp in zip(self.routed_pools, self.shared_pools))
+        self.fused_ws = torch.zeros(max(self.fused_ws_bytes, 256), dtype=torch.uint8, device=device)
         self.graph = None
 
     # one layer: x_in -> x_out (both [T][d] in the activation dtype)
     def layer(self, l: int, x_in: torch.Tensor, x_out: torch.Tensor, forced_ids: Optional[torch.Tensor] = None,
               routed_pool=None, ids: Optional[torch.Tensor] = None, stream=None) -> None:
         s, L, T = self.shape, self.layers[l], self.T
+        if self.fused:
+            self._layer_fused(l, x_in, x_out, forced_ids, routed_pool, ids, stream)
+            return
         if s.rms_norm:
             q.moe_rmsnorm(x_in, s.x_dtype, L.gamma, s.eps, T, s.d, self.u, s.x_dtype, stream)
             u = self.u
@@ -111,6 +123,21 @@ class MoEDecoder:
                          u, s.x_dtype, T, s.act, self.y_routed, self.y_shared, self.gemv_ws, self.gemv_ws_bytes, stream)
         q.moe_combine(self.y_routed, lw, self.y_shared if self.shared_pools[l] is not None else None,
                       x_in if s.rms_norm else None, s.x_dtype, T, s.k, s.d, x_out, s.x_dtype, stream)
+
+    def _layer_fused(self, l, x_in, x_out, forced_ids, routed_pool, ids, stream) -> None:
+        s, L, T = self.shape, self.layers[l], self.T
+        lid, lw, lg = self.ids_all[l], self.weights_all[l], self.logits_all[l]
+        if s.rms_norm:
+            q.moe_norm_router_topk(x_in, s.x_dtype, L.gamma, s.eps, T, s.d, L.router_w, L.router_s, s.n_experts, s.k,
+                                   forced_ids, lid, lw, lg, self.u, self.router_ws, self.router_ws_bytes, stream)
+            u = self.u
+        else:
+            q.moe_router_topk(x_in, s.x_dtype, T, s.d, L.router_w, L.router_s, s.n_experts, s.k, forced_ids, lid, lw,
+                              lg, self.router_ws, self.router_ws_bytes, stream)
+            u = x_in
+        q.q4_expert_gemv_combine(routed_pool or self.routed_pools[l], lid if ids is None else ids, s.k,
+                                 self.shared_pools[l], u, s.x_dtype, T, s.act, lw, x_in if s.rms_norm else None,
+                                 s.x_dtype, x_out, s.x_dtype, self.fused_ws, self.fused_ws_bytes, stream)
 
     def step(self, x: torch.Tensor, out: torch.Tensor, stream=None) -> None:
         """Run every layer: x -> out, ping-ponging between `out` and an internal buffer."""

@@ -61,6 +61,8 @@ _c = {
     "moe_router_workspace_bytes": _sig("moe_router_workspace_bytes", _sz, [_i32, _i32]),
     "moe_router_topk": _sig("moe_router_topk", _st, [_vp, ctypes.c_int, _i32, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp,
                                                      _vp, _vp, _sz, _vp]),
+    "moe_norm_router_topk": _sig("moe_norm_router_topk", _st, [_vp, ctypes.c_int, _vp, ctypes.c_float, _i32, _i32, _vp, _vp,
+                                                               _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "q4_expert_gemv_workspace_bytes": _sig("q4_expert_gemv_workspace_bytes", _sz,
                                            [ctypes.POINTER(moe_q4_pool), _i32, ctypes.POINTER(moe_q4_pool), _i32]),
     "q4_expert_gemv": _sig("q4_expert_gemv", _st, [ctypes.POINTER(moe_q4_pool), _vp, _i32, ctypes.POINTER(moe_q4_pool), _vp,
@@ -69,6 +71,11 @@ _c = {
                                                          _vp, ctypes.c_int, _i32, ctypes.c_int, _vp, _sz, _vp]),
     "q4_expert_down": _sig("q4_expert_down", _st, [ctypes.POINTER(moe_q4_pool), _vp, _i32, ctypes.POINTER(moe_q4_pool), _i32,
                                                    _vp, _vp, _vp, _sz, _vp]),
+    "q4_expert_gemv_combine_workspace_bytes": _sig("q4_expert_gemv_combine_workspace_bytes", _sz,
+                                                   [ctypes.POINTER(moe_q4_pool), _i32, ctypes.POINTER(moe_q4_pool), _i32]),
+    "q4_expert_gemv_combine": _sig("q4_expert_gemv_combine", _st,
+                                   [ctypes.POINTER(moe_q4_pool), _vp, _i32, ctypes.POINTER(moe_q4_pool), _vp, ctypes.c_int,
+                                    _i32, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _sz, _vp]),
     "moe_combine": _sig("moe_combine", _st, [_vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32, _vp, ctypes.c_int, _vp]),
     "moe_expert_cache_create": _sig("moe_expert_cache_create", _st, [_i32, _i32, _i32, _sz, ctypes.POINTER(_vp),
                                                                      ctypes.POINTER(_vp), _u32, ctypes.POINTER(_vp)]),
@@ -156,6 +163,13 @@ def moe_router_topk(x, x_dtype, T, d, w, row_scale, E, k, forced_ids, ids, weigh
                                  _p(logits), _p(workspace), workspace_bytes, _s(stream)), "moe_router_topk")
 
 
+def moe_norm_router_topk(x, x_dtype, gamma, eps, T, d, w, row_scale, E, k, forced_ids, ids, weights, logits, u,
+                         workspace, workspace_bytes, stream=None) -> None:
+    _check(_c["moe_norm_router_topk"](_p(x), x_dtype, _p(gamma), eps, T, d, _p(w), _p(row_scale), E, k, _p(forced_ids),
+                                      _p(ids), _p(weights), _p(logits), _p(u), _p(workspace), workspace_bytes,
+                                      _s(stream)), "moe_norm_router_topk")
+
+
 def _pp(p):
     return ctypes.byref(p) if p is not None else None
 
@@ -178,6 +192,17 @@ def q4_expert_gate_up(routed, ids, k, shared, x, x_dtype, T, act, workspace, wor
 def q4_expert_down(routed, ids, k, shared, T, y_routed, y_shared, workspace, workspace_bytes, stream=None) -> None:
     _check(_c["q4_expert_down"](_pp(routed), _p(ids), k, _pp(shared), T, _p(y_routed), _p(y_shared), _p(workspace),
                                 workspace_bytes, _s(stream)), "q4_expert_down")
+
+
+def q4_expert_gemv_combine_workspace_bytes(routed, k, shared, T) -> int:
+    return _c["q4_expert_gemv_combine_workspace_bytes"](_pp(routed), k, _pp(shared), T)
+
+
+def q4_expert_gemv_combine(routed, ids, k, shared, x, x_dtype, T, act, weights, residual, residual_dtype, out, out_dtype,
+                           workspace, workspace_bytes, stream=None) -> None:
+    _check(_c["q4_expert_gemv_combine"](_pp(routed), _p(ids), k, _pp(shared), _p(x), x_dtype, T, act, _p(weights),
+                                        _p(residual), residual_dtype, _p(out), out_dtype, _p(workspace), workspace_bytes,
+                                        _s(stream)), "q4_expert_gemv_combine")
 
 
 def moe_combine(y_routed, weights, y_shared, residual, residual_dtype, T, k, d, out, out_dtype, stream=None) -> None:

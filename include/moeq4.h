@@ -127,6 +127,20 @@ moe_status moe_router_topk(const void* x_dev, moe_dtype x_dtype, int32_t T, int3
                            const int32_t* forced_ids_dev, int32_t* ids_dev, float* weights_dev,
                            float* logits_dev, void* workspace_dev, size_t workspace_bytes, void* stream);
 
+/* moe_norm_router_topk — moe_rmsnorm fused into moe_router_topk for the stacked decode, where the norm
+ * output feeds both the router and the expert GEMVs ([LEAF] "Du code sur-mesure sans dépendance externe":
+ * the RMSNorm and router kernels of the engine).  Every router block normalizes x itself:
+ *   u[t] = round_x( x[t] / sqrt(mean(x[t]^2) + eps) * gamma )      (fp32 math, RNE to x_dtype)
+ * and routes u[t] exactly as moe_router_topk routes its x; block 0 also writes u to u_dev (x_dtype [T][d],
+ * 16-byte aligned) for the expert GEMVs.  The sum of squares is reduced in a fixed order that differs from
+ * moe_rmsnorm's, so u may differ from moe_rmsnorm's output in the last bit.  gamma_dev: fp32 [d], 16-byte
+ * aligned; eps >= 0.  Other arguments, limits and the workspace rule as moe_router_topk. */
+moe_status moe_norm_router_topk(const void* x_dev, moe_dtype x_dtype, const float* gamma_dev, float eps, int32_t T,
+                                int32_t d, const int8_t* w_dev, const float* row_scale_dev, int32_t E, int32_t k,
+                                const int32_t* forced_ids_dev, int32_t* ids_dev, float* weights_dev,
+                                float* logits_dev, void* u_dev, void* workspace_dev, size_t workspace_bytes,
+                                void* stream);
+
 /* ---------------------------------------------------------------------------------------------------
  * q4_expert_gemv — the selected experts' FFNs and the shared expert's FFN on 4-bit affine weights
  * ([LEAF] "Du code sur-mesure sans dépendance externe": quantized matrix-vector kernels; [REMIO]
@@ -173,6 +187,27 @@ moe_status q4_expert_down(const moe_q4_pool* routed, const int32_t* ids_dev, int
 moe_status moe_combine(const float* y_routed_dev, const float* weights_dev, const float* y_shared_dev,
                        const void* residual_dev, moe_dtype residual_dtype, int32_t T, int32_t k, int32_t d,
                        void* out_dev, moe_dtype out_dtype, void* stream);
+
+/* q4_expert_gemv_combine — q4_expert_gemv followed by moe_combine in two launches instead of three: the
+ * down GEMV's blocks publish their rows and the last block to finish a 16-row tile of token t applies the
+ * combine to it ([G26] "Concurrence pour masquer la latence": routed and shared outputs merged once all
+ * are in).  Computes, for every token t,
+ *   out[t] = round_out( sum_{i<k} weights[t][i] * y_routed[t][i] + y_shared[t] + residual[t] )
+ * with y_routed / y_shared as q4_expert_gemv defines them, summed in the same order as moe_combine; the
+ * result is bit-identical to q4_expert_gemv + moe_combine on the same inputs.  y_routed and y_shared stay
+ * internal (in the workspace).  weights_dev: fp32 [T][k] (e.g. from moe_router_topk; may be NULL iff
+ * k == 0); residual_dev: residual_dtype [T][d] or NULL; out_dev: out_dtype [T][d] (may alias residual_dev
+ * when the dtypes match).  Pools, ids, x, act, limits and errors as q4_expert_gemv.
+ * Workspace: q4_expert_gemv_combine_workspace_bytes(...) bytes of device memory, 256-byte aligned, that
+ * must be ZERO before its first use (its last T*d/16 words are per-tile counters that every completed
+ * call leaves zero again).  Calls that overlap in time need separate workspaces. */
+size_t q4_expert_gemv_combine_workspace_bytes(const moe_q4_pool* routed, int32_t k, const moe_q4_pool* shared,
+                                              int32_t T);
+moe_status q4_expert_gemv_combine(const moe_q4_pool* routed, const int32_t* ids_dev, int32_t k,
+                                  const moe_q4_pool* shared, const void* x_dev, moe_dtype x_dtype, int32_t T,
+                                  moe_act act, const float* weights_dev, const void* residual_dev,
+                                  moe_dtype residual_dtype, void* out_dev, moe_dtype out_dtype,
+                                  void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------------
  * Expert cache — 16-slot-per-layer least-frequently-used cache of expert records ([DAILY] "Cache

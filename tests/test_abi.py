@@ -70,6 +70,21 @@ def test_host_validation_errors():
     assert st(ctypes.byref(good), 256, 2, None, 256, 0, 1, 0, 256, None, 256, 16, None) == q.MOE_ERR_INVALID_ARG
     assert q.q4_expert_gemv_workspace_bytes(good, 2, None, 1) == 1024
     assert _status("moe_combine", None, None, None, None, 0, 1, 2, 64, 256, 0, None) == q.MOE_ERR_INVALID_ARG
+    # fused gemv + combine: hidden activations (1024) + y_routed (2*256*4) + one counter per 16 rows (16*4 -> 256)
+    assert q.q4_expert_gemv_combine_workspace_bytes(good, 2, None, 1) == 1024 + 2048 + 256
+    fc = q.raw("q4_expert_gemv_combine")
+    fargs = lambda w, out, ws: (ctypes.byref(good), 256, 2, None, 256, 1, 1, 0, w, None, 1, out, 1, 256, ws, None)
+    assert fc(*fargs(256, None, 1 << 20)) == q.MOE_ERR_INVALID_ARG                       # out NULL
+    assert fc(*fargs(None, 256, 1 << 20)) == q.MOE_ERR_INVALID_ARG                       # weights NULL with k > 0
+    assert fc(*fargs(256, 256, 3328 - 256)) == q.MOE_ERR_INVALID_ARG                     # no room for the counters
+    assert "workspace" in q.moe_last_error()
+    # fused norm + router: gamma and u are required, eps must be >= 0
+    nr = q.raw("moe_norm_router_topk")
+    nargs = lambda g, eps, u: (256, 1, g, ctypes.c_float(eps), 1, 64, 256, 256, 8, 2, None, 256, 256, None, u, 256,
+                               1 << 20, None)
+    assert nr(*nargs(None, 1e-6, 256)) == q.MOE_ERR_INVALID_ARG
+    assert nr(*nargs(256, 1e-6, None)) == q.MOE_ERR_INVALID_ARG
+    assert nr(*nargs(256, -1.0, 256)) == q.MOE_ERR_INVALID_ARG
     with pytest.raises(q.MoeError):
         q.q4_quantize(None, 4, 64, 1, 16, 16)
 
