@@ -1,0 +1,500 @@
+// Batched decode (T > 1 tokens per call): the T*k (token, slot) pairs are grouped by expert so that
+// each selected expert's rows are streamed from HBM once per call, for all of the tokens routed to it
+// ([G26] "Le pipeline de traitement" and [REMIO] "Mac Gemma 4 26B tient en mémoire...": a prompt's
+// tokens are processed together, sharing each expert's weights).
+//
+// 1. group_pairs_kernel (one block): counting sort of the pairs by expert id.  Counts per expert, an
+//    exclusive scan over experts, then a stable placement (pairs of one expert keep ascending pair
+//    order) into perm; non-empty experts are listed in `groups`.  Ids outside the routed pool form one
+//    extra group whose outputs are NaN, as in the single-token kernels.
+// 2. grouped gate_up / down: one block per (group, 16-row tile), and one block per tile of the shared
+//    expert with all T tokens.  The block loads its rows' codes and scale/bias into registers once, then
+//    walks its tokens kTM at a time: each wave stages the tokens' activation half-groups it consumes
+//    (the staging of the single-token kernel, repeated per token), computes the same dot2 chains, and
+//    the block adds the waves' partial sums in the same fixed order.  Each token's result is therefore
+//    bit-identical to the single-token kernel's; the arithmetic per code is shared by the tokens.
+// The problem is bound by HBM (about 12 flops per weight byte at 32 tokens), so the dot products stay on
+// the vector ALUs; see q4_device.h for the dequantization.
+#include "q4_device.h"
+
+namespace moeq4 {
+namespace {
+
+constexpr int kTM = 4;               // tokens staged per pass
+constexpr int kGroupThreads = 256;
+
+__device__ __forceinline__ int bucket_of(int32_t e, int n_valid) { return (unsigned)e < (unsigned)n_valid ? e : n_valid; }
+
+// Exclusive scan of two counters over the block (blockDim.x == kGroupThreads); *total gets the sums.
+__device__ __forceinline__ int2 block_exclusive_scan2(int2 v, int2* total) {
+  __shared__ int2 wsum[kGroupThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int2 inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int x = __shfl_up(inc.x, o, 64), y = __shfl_up(inc.y, o, 64);
+    if (lane >= o) {
+      inc.x += x;
+      inc.y += y;
+    }
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  int2 base = make_int2(0, 0), tot = make_int2(0, 0);
+#pragma unroll
+  for (int w = 0; w < kGroupThreads / 64; ++w) {
+    if (w < wave) {
+      base.x += wsum[w].x;
+      base.y += wsum[w].y;
+    }
+    tot.x += wsum[w].x;
+    tot.y += wsum[w].y;
+  }
+  *total = tot;
+  return make_int2(base.x + inc.x - v.x, base.y + inc.y - v.y);
+}
+
+__global__ __launch_bounds__(kGroupThreads) void group_pairs_kernel(const int32_t* __restrict__ ids, int P, int n_valid,
+                                                                    int32_t* __restrict__ n_groups, int4* __restrict__ groups,
+                                                                    int32_t* __restrict__ perm) {
+  __shared__ int cnt[kMaxGroupedRecords + 1];
+  __shared__ int cur[kMaxGroupedRecords + 1];
+  __shared__ int keys[kGroupThreads];
+  const int tid = threadIdx.x, nb = n_valid + 1;
+  for (int b = tid; b < nb; b += kGroupThreads) cnt[b] = 0;
+  __syncthreads();
+  for (int p = tid; p < P; p += kGroupThreads) atomicAdd(&cnt[bucket_of(ids[p], n_valid)], 1);   // integer counts
+  __syncthreads();
+  // buckets [b0, b1) per thread; scan of (pairs, non-empty buckets)
+  const int per = (nb + kGroupThreads - 1) / kGroupThreads;
+  const int b0 = min(nb, tid * per), b1 = min(nb, b0 + per);
+  int2 loc = make_int2(0, 0);
+  for (int b = b0; b < b1; ++b) {
+    loc.x += cnt[b];
+    loc.y += cnt[b] > 0;
+  }
+  int2 tot;
+  int2 base = block_exclusive_scan2(loc, &tot);
+  for (int b = b0; b < b1; ++b) {
+    cur[b] = base.x;
+    if (cnt[b] > 0) groups[base.y++] = make_int4(b, base.x, cnt[b], 0);
+    base.x += cnt[b];
+  }
+  if (tid == 0) *n_groups = tot.y;
+  __syncthreads();
+  // stable placement, kGroupThreads pairs per round: rank among the round's earlier pairs of the same expert
+  for (int p0 = 0; p0 < P; p0 += kGroupThreads) {
+    const int p = p0 + tid;
+    const int key = p < P ? bucket_of(ids[p], n_valid) : -1;
+    keys[tid] = key;
+    __syncthreads();
+    int r = 0;
+    bool last = true;
+    if (p < P) {
+      for (int u = 0; u < kGroupThreads; ++u) {
+        const bool same = keys[u] == key;
+        r += same && u < tid;
+        last = last && !(same && u > tid);
+      }
+      perm[cur[key] + r] = p;
+    }
+    __syncthreads();
+    if (p < P && last) cur[key] += r + 1;
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// grouped GEMV blocks
+// ------------------------------------------------------------------------------------------------
+struct GroupSlot {
+  bool shared, valid;
+  int tile, e, start, count;
+};
+
+// The block's matrix and token list; false for blocks past the last non-empty group.
+__device__ __forceinline__ bool group_slot(const GemvArgs& a, GroupSlot& s) {
+  int u = blockIdx.x;
+  s.shared = u < a.nb_shared;
+  s.valid = true;
+  s.e = 0;
+  s.start = 0;
+  if (s.shared) {
+    s.tile = u;
+    s.count = a.T;
+    return true;
+  }
+  u -= a.nb_shared;
+  const int j = u / a.nb_routed;
+  s.tile = u % a.nb_routed;
+  if (j >= *a.n_groups) return false;
+  const int4 g = a.groups[j];
+  s.valid = (unsigned)g.x < (unsigned)a.routed.n_records;
+  s.e = s.valid ? g.x : 0;
+  s.start = g.y;
+  s.count = g.z;
+  return true;
+}
+
+// pair index (t*k + i; the token itself for the shared expert) of entry c of the block's token list
+__device__ __forceinline__ int pair_of(const GemvArgs& a, const GroupSlot& s, int c) {
+  return s.shared ? c : a.perm[s.start + c];
+}
+
+template <int NBW, bool SB_BF16>
+struct RowPairRegs {
+  SbWord<SB_BF16> sa[NBW], sb[NBW];
+  u32x4 qa[NBW], qb[NBW];
+};
+
+// Steps 2-3 of the single-token row-pair routine: this lane's scale/bias words and code chunks.
+template <int NBW, bool SB_BF16>
+__device__ __forceinline__ void load_rowpair(const char* rowA, const char* rowB, const char* sbA, const char* sbB, int K,
+                                             bool valid, RowPairRegs<NBW, SB_BF16>& r) {
+  const int W = blockDim.x >> 6, wave = threadIdx.x >> 6, j = threadIdx.x & 7;
+  const int C = K / 32;
+  if (!valid) return;
+#pragma unroll
+  for (int m = 0; m < NBW; ++m) {
+    const int c = (wave + W * m) * kLanesPerRow + j;
+    if (c < C) {
+      r.sa[m] = load_sb<SB_BF16>(sbA, c >> 1);
+      r.sb[m] = load_sb<SB_BF16>(sbB, c >> 1);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < NBW; ++m) {
+    const int c = (wave + W * m) * kLanesPerRow + j;
+    if (c < C) {
+      r.qa[m] = load_nt(rowA + c * 16);
+      r.qb[m] = load_nt(rowB + c * 16);
+    }
+  }
+}
+
+// Steps 1 and 4: stage the first `nlive` of kTM activation vectors (this wave's half-groups of each).
+template <int NBW, typename XT>
+__device__ __forceinline__ void stage_tokens(const XT* const (&xs)[kTM], int nlive, int K, const Stage (&st)[kTM]) {
+  const int W = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int C = K / 32, nit = (C + kLanesPerRow - 1) / kLanesPerRow;
+  constexpr int kPasses = (NBW * 32 + 63) / 64;
+  XWord<XT> xw[kTM][kPasses];
+  int hgp[kPasses];
+  bool livep[kPasses];
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int s = lane + 64 * p, m = s >> 5, jj = (s >> 2) & 7;
+    const int it = wave + W * m;
+    hgp[p] = it * kLanesPerRow + jj;
+    livep[p] = m < NBW && it < nit && hgp[p] < C;
+  }
+#pragma unroll
+  for (int tk = 0; tk < kTM; ++tk)
+    if (tk < nlive) {
+#pragma unroll
+      for (int p = 0; p < kPasses; ++p)
+        if (livep[p]) load_word<XT>(xs[tk], hgp[p], (lane + 64 * p) & 3, xw[tk][p]);
+    }
+#pragma unroll
+  for (int tk = 0; tk < kTM; ++tk)
+    if (tk < nlive) {
+#pragma unroll
+      for (int p = 0; p < kPasses; ++p) {
+        float v[8];
+        if (livep[p]) word_to_f32<XT>(xw[tk][p], v);
+        else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = 0.f;
+        }
+        stage_word(v, livep[p], hgp[p], (lane + 64 * p) & 3, st[tk]);
+      }
+    }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Step 5 for each live token: the same dot2 chain as chunk_dot, with the codes dequantized once.
+template <int NBW, bool SB_BF16>
+__device__ __forceinline__ void rowpair_dots(const RowPairRegs<NBW, SB_BF16>& r, int K, const Stage (&st)[kTM], int nlive,
+                                             bool valid, float (&yA)[kTM], float (&yB)[kTM]) {
+  const int W = blockDim.x >> 6, wave = threadIdx.x >> 6, j = threadIdx.x & 7;
+  const int C = K / 32;
+#pragma unroll
+  for (int tk = 0; tk < kTM; ++tk) yA[tk] = yB[tk] = 0.f;
+  if (!valid) return;
+  const Dequant dq = make_dequant();
+#pragma unroll
+  for (int m = 0; m < NBW; ++m) {
+    const int c = (wave + W * m) * kLanesPerRow + j;
+    if (c >= C) continue;
+    uint32_t da[16], db[16];
+    const uint32_t wa[4] = {r.qa[m].x, r.qa[m].y, r.qa[m].z, r.qa[m].w};
+    const uint32_t wb[4] = {r.qb[m].x, r.qb[m].y, r.qb[m].z, r.qb[m].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t va = wa[i], ta = va >> 8, vb = wb[i], tb = vb >> 8;
+      da[4 * i + 0] = (va & dq.lo) | dq.magic;
+      da[4 * i + 1] = (va & dq.hi) | dq.magic;
+      da[4 * i + 2] = (ta & dq.lo) | dq.magic;
+      da[4 * i + 3] = (ta & dq.hi) | dq.magic;
+      db[4 * i + 0] = (vb & dq.lo) | dq.magic;
+      db[4 * i + 1] = (vb & dq.hi) | dq.magic;
+      db[4 * i + 2] = (tb & dq.lo) | dq.magic;
+      db[4 * i + 3] = (tb & dq.hi) | dq.magic;
+    }
+    float s0, b0, s1, b1;
+    sb_values<SB_BF16>(r.sa[m], s0, b0);
+    sb_values<SB_BF16>(r.sb[m], s1, b1);
+#pragma unroll
+    for (int tk = 0; tk < kTM; ++tk)
+      if (tk < nlive) {
+        const u32x4* xv = reinterpret_cast<const u32x4*>(st[tk].xw + c * kHgStride);
+        const u32x4 x4[4] = {xv[0], xv[1], xv[2], xv[3]};
+        const float4 h = st[tk].hg[c];
+        float accA = -h.y, accB = -h.y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          accA = dot2(da[4 * i + 0], x4[i].x, accA);
+          accA = dot2(da[4 * i + 1], x4[i].y, accA);
+          accA = dot2(da[4 * i + 2], x4[i].z, accA);
+          accA = dot2(da[4 * i + 3], x4[i].w, accA);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          accB = dot2(db[4 * i + 0], x4[i].x, accB);
+          accB = dot2(db[4 * i + 1], x4[i].y, accB);
+          accB = dot2(db[4 * i + 2], x4[i].z, accB);
+          accB = dot2(db[4 * i + 3], x4[i].w, accB);
+        }
+        yA[tk] = fmaf(h.x, fmaf(s0, accA, b0 * h.z), yA[tk]);
+        yB[tk] = fmaf(h.x, fmaf(s1, accB, b1 * h.z), yB[tk]);
+      }
+  }
+}
+
+// block_sum for kTM tokens (same order: 8 lanes, then waves 0..W-1).  The caller must pass a block
+// barrier before the next call (the LDS partials are reused).
+__device__ __forceinline__ bool block_sum_tokens(float (&yA)[kTM], float (&yB)[kTM], int nlive) {
+  __shared__ float red[kMaxWaves][kTM][16];
+  const int W = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63, ra = lane >> 3, j = lane & 7;
+#pragma unroll
+  for (int tk = 0; tk < kTM; ++tk)
+    if (tk < nlive) {
+      yA[tk] = reduce8(yA[tk]);
+      yB[tk] = reduce8(yB[tk]);
+    }
+  if (W == 1) return j == 0;
+  if (j == 0) {
+#pragma unroll
+    for (int tk = 0; tk < kTM; ++tk)
+      if (tk < nlive) {
+        red[wave][tk][ra] = yA[tk];
+        red[wave][tk][8 + ra] = yB[tk];
+      }
+  }
+  __syncthreads();
+  if (wave != 0 || j != 0) return false;
+#pragma unroll
+  for (int tk = 0; tk < kTM; ++tk)
+    if (tk < nlive) {
+      yA[tk] = red[0][tk][ra];
+      yB[tk] = red[0][tk][8 + ra];
+      for (int w = 1; w < W; ++w) {
+        yA[tk] += red[w][tk][ra];
+        yB[tk] += red[w][tk][8 + ra];
+      }
+    }
+  return true;
+}
+
+__device__ __forceinline__ void make_stages(uint32_t* lds, int nhg, Stage (&st)[kTM]) {
+  const int per_tok = nhg * (kHgStride + 4);
+#pragma unroll
+  for (int tk = 0; tk < kTM; ++tk)
+    st[tk] = Stage{lds + tk * per_tok, reinterpret_cast<float4*>(lds + tk * per_tok + nhg * kHgStride)};
+}
+
+template <int NBW, typename XT, bool SB_BF16>
+__global__ __launch_bounds__(64 * kMaxWaves) void gate_up_grouped_kernel(GemvArgs a) {
+  extern __shared__ __align__(16) uint32_t lds[];
+  GroupSlot sl;
+  if (!group_slot(a, sl)) return;
+  const Pool& P = sl.shared ? a.shared : a.routed;
+  const int K = a.d, nhg = K / 32;
+  const int ra = (threadIdx.x & 63) >> 3;
+  const int F = P.F, f = sl.tile * 8 + ra;
+  const char* rec = P.base + (int64_t)sl.e * P.record_bytes;
+  const int64_t rowb = K / 2, sbrow = (int64_t)(K / 64) * (SB_BF16 ? 4 : 8);
+  RowPairRegs<NBW, SB_BF16> w;
+  load_rowpair<NBW, SB_BF16>(rec + P.off_q + f * rowb, rec + P.off_q + (F + f) * rowb, rec + P.off_sb + f * sbrow,
+                             rec + P.off_sb + (F + f) * sbrow, K, sl.valid, w);
+  Stage st[kTM];
+  make_stages(lds, nhg, st);
+  const XT* x = reinterpret_cast<const XT*>(a.in);
+  float* hbase = sl.shared ? a.h_shared : a.h_routed;
+  for (int c0 = 0; c0 < sl.count; c0 += kTM) {
+    const int nlive = min(kTM, sl.count - c0);
+    int pair[kTM];
+    const XT* xs[kTM];
+#pragma unroll
+    for (int tk = 0; tk < kTM; ++tk) {
+      pair[tk] = tk < nlive ? pair_of(a, sl, c0 + tk) : 0;
+      xs[tk] = x + (int64_t)(sl.shared ? pair[tk] : pair[tk] / a.k) * K;
+    }
+    stage_tokens<NBW, XT>(xs, nlive, K, st);
+    float yA[kTM], yB[kTM];
+    rowpair_dots<NBW, SB_BF16>(w, K, st, nlive, sl.valid, yA, yB);
+    if (block_sum_tokens(yA, yB, nlive)) {
+#pragma unroll
+      for (int tk = 0; tk < kTM; ++tk)
+        if (tk < nlive)
+          hbase[(int64_t)pair[tk] * F + f] = sl.valid ? activation(yA[tk], a.act) * yB[tk] : __builtin_nanf("");
+    }
+    __syncthreads();
+  }
+}
+
+template <int NBW, bool SB_BF16, bool COMBINE>
+__global__ __launch_bounds__(64 * kMaxWaves) void down_grouped_kernel(GemvArgs a) {
+  extern __shared__ __align__(16) uint32_t lds[];
+  __shared__ uint32_t lastf[kTM];
+  GroupSlot sl;
+  if (!group_slot(a, sl)) return;
+  const Pool& P = sl.shared ? a.shared : a.routed;
+  const int d = a.d, K = P.F, nhg = K / 32;
+  const int ra = (threadIdx.x & 63) >> 3;
+  const int r = sl.tile * 16 + ra;
+  const char* rec = P.base + (int64_t)sl.e * P.record_bytes;
+  const int64_t rowb = K / 2, sbrow = (int64_t)(K / 64) * (SB_BF16 ? 4 : 8);
+  RowPairRegs<NBW, SB_BF16> w;
+  load_rowpair<NBW, SB_BF16>(rec + P.off_q + r * rowb, rec + P.off_q + (r + 8) * rowb, rec + P.off_sb + r * sbrow,
+                             rec + P.off_sb + (r + 8) * sbrow, K, sl.valid, w);
+  Stage st[kTM];
+  make_stages(lds, nhg, st);
+  const float* hbase = sl.shared ? a.h_shared : a.h_routed;
+  float* ybase = sl.shared ? a.y_shared : a.y_routed;
+  const uint32_t units = (uint32_t)a.k + (a.nb_shared ? 1u : 0u);
+  const int ntiles = d / 16;
+  for (int c0 = 0; c0 < sl.count; c0 += kTM) {
+    const int nlive = min(kTM, sl.count - c0);
+    int pair[kTM];
+    const float* xs[kTM];
+#pragma unroll
+    for (int tk = 0; tk < kTM; ++tk) {
+      pair[tk] = tk < nlive ? pair_of(a, sl, c0 + tk) : 0;
+      xs[tk] = hbase + (int64_t)pair[tk] * K;
+    }
+    stage_tokens<NBW, float>(xs, nlive, K, st);
+    float yA[kTM], yB[kTM];
+    rowpair_dots<NBW, SB_BF16>(w, K, st, nlive, sl.valid, yA, yB);
+    const bool total = block_sum_tokens(yA, yB, nlive);
+    if (!COMBINE) {
+      if (total) {
+#pragma unroll
+        for (int tk = 0; tk < kTM; ++tk)
+          if (tk < nlive) {
+            float* y = ybase + (int64_t)pair[tk] * d;
+            y[r] = sl.valid ? yA[tk] : __builtin_nanf("");
+            y[r + 8] = sl.valid ? yB[tk] : __builtin_nanf("");
+          }
+      }
+    } else {
+      // publish, take one ticket per token, and combine the tiles this block completed (see down_kernel)
+      if (total) {
+#pragma unroll
+        for (int tk = 0; tk < kTM; ++tk)
+          if (tk < nlive) {
+            float* y = ybase + (int64_t)pair[tk] * d;
+            __hip_atomic_store(y + r, sl.valid ? yA[tk] : __builtin_nanf(""), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(y + r + 8, sl.valid ? yB[tk] : __builtin_nanf(""), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+          }
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+#pragma unroll
+      for (int tk = 0; tk < kTM; ++tk)
+        if (tk < nlive && (int)threadIdx.x == tk) {
+          const int t = sl.shared ? pair[tk] : pair[tk] / a.k;
+          uint32_t* ctr = a.tile_counters + (int64_t)t * ntiles + sl.tile;
+          lastf[tk] = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == units - 1;
+        }
+      __syncthreads();
+#pragma unroll
+      for (int tk = 0; tk < kTM; ++tk)
+        if (tk < nlive && lastf[tk] && threadIdx.x < 16) {
+          const int t = sl.shared ? pair[tk] : pair[tk] / a.k;
+          combine_tile(a, t, sl.tile);
+          if (threadIdx.x == 0)
+            __hip_atomic_store(a.tile_counters + (int64_t)t * ntiles + sl.tile, 0u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+moe_status launch_group_pairs(const int32_t* ids, int P, int n_valid, int32_t* n_groups, int4* groups, int32_t* perm,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(group_pairs_kernel, dim3(1), dim3(kGroupThreads), 0, s, ids, P, n_valid, n_groups, groups, perm);
+  return check_launch("group_pairs");
+}
+
+moe_status launch_gate_up_grouped(const GemvArgs& a, moe_dtype x_dtype, bool sb_bf16, int nbw, int waves, dim3 grid,
+                                  hipStream_t s) {
+  const dim3 block(64 * waves);
+  const size_t lds = kTM * lds_bytes(a.d);
+  return dispatch_nbw(nbw, [&](auto nb) {
+    constexpr int N = decltype(nb)::value;
+    if (x_dtype == MOE_BF16) {
+      if (sb_bf16) hipLaunchKernelGGL((gate_up_grouped_kernel<N, uint16_t, true>), grid, block, lds, s, a);
+      else hipLaunchKernelGGL((gate_up_grouped_kernel<N, uint16_t, false>), grid, block, lds, s, a);
+    } else {
+      if (sb_bf16) hipLaunchKernelGGL((gate_up_grouped_kernel<N, float, true>), grid, block, lds, s, a);
+      else hipLaunchKernelGGL((gate_up_grouped_kernel<N, float, false>), grid, block, lds, s, a);
+    }
+    return check_launch("q4_expert_gemv(gate_up, grouped)");
+  });
+}
+
+moe_status launch_down_grouped(const GemvArgs& a, bool sb_bf16, bool combine, int nbw, int waves, dim3 grid, int K_lds,
+                               hipStream_t s) {
+  const dim3 block(64 * waves);
+  const size_t lds = kTM * lds_bytes(K_lds);
+  return dispatch_nbw(nbw, [&](auto nb) {
+    constexpr int N = decltype(nb)::value;
+    if (combine) {
+      if (sb_bf16) hipLaunchKernelGGL((down_grouped_kernel<N, true, true>), grid, block, lds, s, a);
+      else hipLaunchKernelGGL((down_grouped_kernel<N, false, true>), grid, block, lds, s, a);
+    } else {
+      if (sb_bf16) hipLaunchKernelGGL((down_grouped_kernel<N, true, false>), grid, block, lds, s, a);
+      else hipLaunchKernelGGL((down_grouped_kernel<N, false, false>), grid, block, lds, s, a);
+    }
+    return check_launch("q4_expert_gemv(down, grouped)");
+  });
+}
+
+}  // namespace moeq4
+
+using namespace moeq4;
+
+extern "C" int32_t moe_group_pairs_max_groups(int32_t T, int32_t k, int32_t n_valid) {
+  if (T < 1 || k < 1 || n_valid < 1) return 0;
+  const long long pairs = (long long)T * k, buckets = (long long)n_valid + 1;
+  return (int32_t)(pairs < buckets ? pairs : buckets);
+}
+
+extern "C" moe_status moe_group_pairs(const int32_t* ids_dev, int32_t T, int32_t k, int32_t n_valid, int32_t* n_groups_dev,
+                                      int32_t* groups_dev, int32_t* perm_dev, void* stream) {
+  if (!ids_dev || !n_groups_dev || !groups_dev || !perm_dev) return fail(MOE_ERR_INVALID_ARG, "moe_group_pairs: NULL pointer");
+  if (T < 1 || T > 65535 || k < 1 || k > 32)
+    return fail(MOE_ERR_INVALID_ARG, "moe_group_pairs: T=%d k=%d (1..65535, 1..32)", T, k);
+  if (n_valid < 1 || n_valid > kMaxGroupedRecords)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_group_pairs: n_valid=%d (1..%d)", n_valid, kMaxGroupedRecords);
+  if (!aligned(groups_dev, 16)) return fail(MOE_ERR_INVALID_ARG, "moe_group_pairs: groups not 16-byte aligned");
+  return launch_group_pairs(ids_dev, T * k, n_valid, n_groups_dev, reinterpret_cast<int4*>(groups_dev), perm_dev,
+                            as_stream(stream));
+}

@@ -63,6 +63,8 @@ _c = {
                                                      _vp, _vp, _sz, _vp]),
     "moe_norm_router_topk": _sig("moe_norm_router_topk", _st, [_vp, ctypes.c_int, _vp, ctypes.c_float, _i32, _i32, _vp, _vp,
                                                                _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_group_pairs_max_groups": _sig("moe_group_pairs_max_groups", _i32, [_i32, _i32, _i32]),
+    "moe_group_pairs": _sig("moe_group_pairs", _st, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "q4_expert_gemv_workspace_bytes": _sig("q4_expert_gemv_workspace_bytes", _sz,
                                            [ctypes.POINTER(moe_q4_pool), _i32, ctypes.POINTER(moe_q4_pool), _i32]),
     "q4_expert_gemv": _sig("q4_expert_gemv", _st, [ctypes.POINTER(moe_q4_pool), _vp, _i32, ctypes.POINTER(moe_q4_pool), _vp,
@@ -168,6 +170,15 @@ def moe_norm_router_topk(x, x_dtype, gamma, eps, T, d, w, row_scale, E, k, force
     _check(_c["moe_norm_router_topk"](_p(x), x_dtype, _p(gamma), eps, T, d, _p(w), _p(row_scale), E, k, _p(forced_ids),
                                       _p(ids), _p(weights), _p(logits), _p(u), _p(workspace), workspace_bytes,
                                       _s(stream)), "moe_norm_router_topk")
+
+
+def moe_group_pairs_max_groups(T: int, k: int, n_valid: int) -> int:
+    return _c["moe_group_pairs_max_groups"](T, k, n_valid)
+
+
+def moe_group_pairs(ids, T, k, n_valid, n_groups, groups, perm, stream=None) -> None:
+    _check(_c["moe_group_pairs"](_p(ids), T, k, n_valid, _p(n_groups), _p(groups), _p(perm), _s(stream)),
+           "moe_group_pairs")
 
 
 def _pp(p):

@@ -152,9 +152,11 @@ moe_status moe_norm_router_topk(const void* x_dev, moe_dtype x_dtype, const floa
  * Weights are dequantized on the fly; accumulation is fp32.  Both experts kinds run in the same launches.
  * x_dev: x_dtype [T][d]; ids_dev: int32 [T][k] (device, e.g. straight from moe_router_topk or cache slot
  * ids from expert_cache_stage); y_routed_dev: fp32 [T][k][d]; y_shared_dev: fp32 [T][d] (needed iff shared).
- * T == 1 is the decode GEMV; T > 1 groups the (token, expert) pairs by expert so each selected expert's
- * weights are read once per call (grouped small-M GEMM on the matrix cores).
- * Limits: k <= 32; routed and shared share d; routed may be NULL (k == 0) to run only the shared expert.
+ * T == 1 is the decode GEMV.  T > 1 first groups the T*k (token, slot) pairs by expert on the device
+ * (moe_group_pairs, below) and then streams each selected expert's rows once for all of its tokens, and
+ * the shared expert's rows once for all T tokens; every token's result is bit-identical to a T == 1 call.
+ * Limits: k <= 32; routed and shared share d; routed may be NULL (k == 0) to run only the shared expert;
+ * with T > 1 the routed pool has at most 4096 records (MOE_ERR_UNSUPPORTED otherwise).
  * Workspace: q4_expert_gemv_workspace_bytes(...) bytes of device memory (contents need no initial value).
  * An id outside [0, routed->n_records) makes that expert's y_routed row NaN.
  * ------------------------------------------------------------------------------------------------- */
@@ -163,6 +165,22 @@ moe_status q4_expert_gemv(const moe_q4_pool* routed, const int32_t* ids_dev, int
                           const moe_q4_pool* shared, const void* x_dev, moe_dtype x_dtype, int32_t T,
                           moe_act act, float* y_routed_dev, float* y_shared_dev,
                           void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------------
+ * moe_group_pairs — the batch's (token, slot) pairs grouped by expert, the first step of a T > 1
+ * q4_expert_gemv ([G26] "Le pipeline de traitement": a prompt's tokens processed together share each
+ * expert's weights).  Pair p = t*k + i carries expert ids[t][i]; ids outside [0, n_valid) form one bucket
+ * after all valid experts.  The pairs are sorted stably by bucket:
+ *   perm[0 .. T*k)      pair indices, bucket-ascending, pair-ascending within a bucket
+ *   groups[j] = (bucket, first index into perm, count, 0) for the non-empty buckets, bucket-ascending
+ *   *n_groups           number of non-empty buckets (<= moe_group_pairs_max_groups(T, k, n_valid))
+ * ids_dev: int32 [T][k]; n_groups_dev: int32 [1]; groups_dev: int32 [max_groups][4], 16-byte aligned;
+ * perm_dev: int32 [T*k] (all device).  Limits: 1 <= T <= 65535, 1 <= k <= 32, 1 <= n_valid <= 4096.
+ * One block; deterministic (integer work only).
+ * ------------------------------------------------------------------------------------------------- */
+int32_t moe_group_pairs_max_groups(int32_t T, int32_t k, int32_t n_valid);
+moe_status moe_group_pairs(const int32_t* ids_dev, int32_t T, int32_t k, int32_t n_valid, int32_t* n_groups_dev,
+                           int32_t* groups_dev, int32_t* perm_dev, void* stream);
 
 /* The two halves of q4_expert_gemv, for callers that schedule them separately (and for timing one
  * launch).  q4_expert_gate_up computes h = act(W_gate x) * (W_up x) for the routed and shared experts

@@ -427,6 +427,29 @@ def stack_layer_step(layer: OracleLayer, x_bf16_vals: np.ndarray, k: int, act: i
 
 
 # -------------------------------------------------------------------------------------------------
+# Grouping of a batch's (token, slot) pairs by expert (the batched decode)
+# -------------------------------------------------------------------------------------------------
+
+def group_pairs(ids: np.ndarray, n_valid: int):
+    """The batch of T tokens routed to k experts each, as groups of pairs that share an expert
+    ([G26] "Le pipeline de traitement": a prompt's tokens processed together share each expert's weights).
+
+    Pair p = t*k + i carries the expert ids[t][i].  Reading (the pages give no algorithm): a stable sort of
+    the pairs by expert, so pairs of one expert keep ascending pair order; ids outside [0, n_valid) all
+    count as one bucket, after every valid expert.  Returns (groups, perm) with perm the sorted pair
+    indices and groups the list of (bucket, first index into perm, count) of the non-empty buckets in
+    ascending bucket order."""
+    flat = np.asarray(ids, dtype=np.int64).reshape(-1)
+    bucket = np.where((flat >= 0) & (flat < n_valid), flat, n_valid)
+    perm = np.argsort(bucket, kind="stable")
+    groups = []
+    for b in np.unique(bucket):
+        members = np.nonzero(bucket[perm] == b)[0]
+        groups.append((int(b), int(members[0]), int(len(members))))
+    return groups, perm.astype(np.int64)
+
+
+# -------------------------------------------------------------------------------------------------
 # 16-slot LFU expert cache (policy simulation)
 # -------------------------------------------------------------------------------------------------
 

@@ -78,6 +78,16 @@ def test_host_validation_errors():
     assert fc(*fargs(None, 256, 1 << 20)) == q.MOE_ERR_INVALID_ARG                       # weights NULL with k > 0
     assert fc(*fargs(256, 256, 3328 - 256)) == q.MOE_ERR_INVALID_ARG                     # no room for the counters
     assert "workspace" in q.moe_last_error()
+    # batched (T = 3): hidden activations 3*2*128*4 = 3072, then the grouping tables: the group count (256),
+    # min(T*k, n_records + 1) = 6 groups of 16 bytes (-> 256) and T*k pair indices (-> 256)
+    assert q.q4_expert_gemv_workspace_bytes(good, 2, None, 3) == 3072 + 256 + 256 + 256
+    assert q.moe_group_pairs_max_groups(32, 8, 128) == 129 and q.moe_group_pairs_max_groups(1, 8, 128) == 8
+    gp = q.raw("moe_group_pairs")
+    assert gp(256, 4, 2, 5000, 256, 256, 256, None) == q.MOE_ERR_UNSUPPORTED          # pool too large to group
+    assert gp(256, 4, 2, 8, 256, 256 + 4, 256, None) == q.MOE_ERR_INVALID_ARG         # groups not 16-byte aligned
+    assert gp(256, 0, 2, 8, 256, 256, 256, None) == q.MOE_ERR_INVALID_ARG             # T = 0
+    big = q.pool(256, 61440, 5000, 256, 128, 0)
+    assert st(ctypes.byref(big), 256, 2, None, 256, 0, 2, 0, 256, None, 256, 1 << 24, None) == q.MOE_ERR_UNSUPPORTED
     # fused norm + router: gamma and u are required, eps must be >= 0
     nr = q.raw("moe_norm_router_topk")
     nargs = lambda g, eps, u: (256, 1, g, ctypes.c_float(eps), 1, 64, 256, 256, 8, 2, None, 256, 256, None, u, 256,

@@ -1,0 +1,150 @@
+"""GPU checks of the batched (T > 1) path on MI355X: the device grouping of (token, slot) pairs against the
+oracle's stable sort (bit-exact), and the grouped expert GEMVs against one-token calls (bit-exact) and the
+oracle."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import synth  # noqa: E402
+from oracle import moe  # noqa: E402
+from oracle import inputs as oin  # noqa: E402
+from bit_quantized_expert_int8_amd import moeq4 as q  # noqa: E402
+import gpu_helpers as H  # noqa: E402
+
+TOL = 1e-2   # max relative error of floating outputs (the parity bar)
+
+
+def _group_on_gpu(ids_np, n_valid):
+    T, k = ids_np.shape
+    gmax = q.moe_group_pairs_max_groups(T, k, n_valid)
+    ids = torch.from_numpy(ids_np.astype(np.int32)).cuda()
+    n = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    groups = torch.full((gmax, 4), -7, dtype=torch.int32, device="cuda")
+    perm = torch.full((T * k,), -7, dtype=torch.int32, device="cuda")
+    q.moe_group_pairs(ids, T, k, n_valid, n, groups, perm)
+    torch.cuda.synchronize()
+    ng = int(n.item())
+    return [tuple(r[:3]) for r in groups.cpu().numpy()[:ng].tolist()], perm.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,k,n_valid,kind", [(32, 8, 128, "router"), (32, 8, 128, "zipf"), (1, 8, 128, "router"),
+                                              (1000, 8, 128, "zipf"), (300, 3, 4096, "uniform"), (64, 2, 1, "invalid")])
+def test_group_pairs_bit_exact_vs_oracle(T, k, n_valid, kind):
+    """Routing of the batched configuration (top-8 of 128 per token), Zipf(1.1) routing with repeats across
+    tokens, batches large enough for several placement rounds, the largest pool, and out-of-pool ids."""
+    rng = np.random.default_rng(T * 31 + k)
+    if kind == "router":
+        ids = np.stack([rng.permutation(n_valid)[:k] for _ in range(T)])
+    elif kind == "zipf":
+        ids = synth.zipf_trace(9, T, 1, k, n_valid, 1.1)[:, 0, :]
+    elif kind == "uniform":
+        ids = rng.integers(0, n_valid, size=(T, k))
+    else:
+        ids = rng.integers(-3, 4, size=(T, k))
+    g_ref, p_ref = moe.group_pairs(ids, n_valid)
+    g, p = _group_on_gpu(ids, n_valid)
+    assert g == g_ref
+    assert np.array_equal(p, p_ref)
+
+
+def _tiny_pools(cfg, dev, shape):
+    rp = q.pool(dev.pool, dev.pool.shape[1], shape.n_experts, shape.d, shape.F, shape.sb_dtype)
+    sp = q.pool(dev.shared, dev.shared.shape[1], 1, shape.d, shape.S, shape.sb_dtype)
+    return rp, sp
+
+
+def _gemv(rp, sp, ids, k, x, x_dtype, T, act, d):
+    wb = q.q4_expert_gemv_workspace_bytes(rp, k, sp, T)
+    ws = torch.empty(max(wb, 256), dtype=torch.uint8, device="cuda")
+    yr = torch.full((T, max(k, 1), d), 7.0, dtype=torch.float32, device="cuda")
+    ys = torch.full((T, d), 7.0, dtype=torch.float32, device="cuda") if sp is not None else None
+    q.q4_expert_gemv(rp if k else None, ids, k, sp, x, x_dtype, T, act, yr if k else None, ys, ws, wb)
+    return yr, ys
+
+
+@pytest.mark.parametrize("cfg_name", ["tiny", "batched"])
+def test_grouped_gemv_equals_one_token_calls(cfg_name):
+    """Grouped T-token call vs T separate one-token calls, y_routed and y_shared bit for bit.  The ids carry
+    repeats across tokens, a duplicate within a token and (tiny) an id outside the pool, whose rows are NaN."""
+    cfg = synth.TINY if cfg_name == "tiny" else synth.BATCHED
+    dev = H.device_layer(cfg, 0)
+    shape = H.shape_of(cfg)
+    rp, sp = _tiny_pools(cfg, dev, shape)
+    T, k, E = (24, cfg.k, cfg.n_experts) if cfg_name == "tiny" else (cfg.n_tokens, cfg.k, cfg.n_experts)
+    rng = np.random.default_rng(11)
+    ids_np = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    ids_np[3, 1] = ids_np[3, 0]                      # duplicate expert within one token
+    if cfg_name == "tiny":
+        ids_np[5, 0] = E + 2                          # outside the pool
+    ids = torch.from_numpy(ids_np).cuda()
+    x = H.token_batch(cfg, range(T))
+    xdt = q.MOE_BF16 if cfg.x_bf16 else q.MOE_F32
+    yr, ys = _gemv(rp, sp, ids, k, x, xdt, T, shape.act, cfg.d)
+    check = range(T) if cfg_name == "tiny" else (0, 3, 17, 31)
+    for t in check:
+        yr1, ys1 = _gemv(rp, sp, ids[t:t + 1].contiguous(), k, x[t:t + 1].contiguous(), xdt, 1, shape.act, cfg.d)
+        torch.cuda.synchronize()
+        assert torch.equal(ys[t], ys1[0]), f"shared, token {t}"
+        for i in range(k):
+            if ids_np[t, i] >= E:
+                assert torch.isnan(yr[t, i]).all() and torch.isnan(yr1[0, i]).all()
+            else:
+                assert torch.equal(yr[t, i], yr1[0, i]), f"token {t} slot {i}"
+
+
+def test_grouped_gemv_tiny_vs_oracle():
+    """Tiny configuration (fp32 x and scale/bias), 24 tokens, every expert output against the oracle."""
+    cfg = synth.TINY
+    dev = H.device_layer(cfg, 0)
+    orc = oin.oracle_layer(cfg, 0)
+    shape = H.shape_of(cfg)
+    rp, sp = _tiny_pools(cfg, dev, shape)
+    T, k = 24, cfg.k
+    rng = np.random.default_rng(4)
+    ids_np = np.stack([rng.permutation(cfg.n_experts)[:k] for _ in range(T)]).astype(np.int32)
+    x = H.token_batch(cfg, range(T))
+    yr, ys = _gemv(rp, sp, torch.from_numpy(ids_np).cuda(), k, x, q.MOE_F32, T, shape.act, cfg.d)
+    torch.cuda.synchronize()
+    yr, ys = H.to_f64(yr), H.to_f64(ys)
+    worst = 0.0
+    for t in range(T):
+        u = oin.token_input(cfg, t)
+        for i in range(k):
+            ref = moe.expert_ffn(orc.decoded(int(ids_np[t, i])), u, moe.ACT_GELU_TANH)
+            worst = max(worst, H.max_rel_err(yr[t, i], ref))
+        worst = max(worst, H.max_rel_err(ys[t], moe.expert_ffn(orc.decoded_shared(), u, moe.ACT_GELU_TANH)))
+    print(f"tiny grouped expert gemv: max rel err {worst:.3e}")
+    assert worst <= TOL
+
+
+def test_grouped_fused_combine_equals_one_token_calls():
+    """q4_expert_gemv_combine with 32 tokens (grouped down with per-token tile tickets) equals 32 one-token
+    fused calls, twice in a row on one workspace."""
+    cfg = synth.STACK
+    dev = H.device_layer(cfg, 0)
+    shape = H.shape_of(cfg)
+    rp, sp = _tiny_pools(cfg, dev, shape)
+    T, k, E = 32, cfg.k, cfg.n_experts
+    ws_b = q.q4_expert_gemv_combine_workspace_bytes(rp, k, sp, T)
+    ws = torch.zeros(ws_b, dtype=torch.uint8, device="cuda")
+    ws1_b = q.q4_expert_gemv_combine_workspace_bytes(rp, k, sp, 1)
+    ws1 = torch.zeros(ws1_b, dtype=torch.uint8, device="cuda")
+    for call in range(2):
+        rng = np.random.default_rng(100 + call)
+        ids_np = synth.zipf_trace(20 + call, T, 1, k, E, 1.1)[:, 0, :].astype(np.int32)
+        ids = torch.from_numpy(ids_np).cuda()
+        w = torch.from_numpy(rng.dirichlet(np.ones(k), size=T).astype(np.float32)).cuda()
+        x = H.token_batch(cfg, range(50 * call, 50 * call + T))
+        res = H.token_batch(cfg, range(200, 200 + T))
+        out = torch.empty_like(x)
+        q.q4_expert_gemv_combine(rp, ids, k, sp, x, q.MOE_BF16, T, shape.act, w, res, q.MOE_BF16, out, q.MOE_BF16, ws,
+                                 ws_b)
+        for t in range(T):
+            o1 = torch.empty_like(x[t:t + 1])
+            q.q4_expert_gemv_combine(rp, ids[t:t + 1].contiguous(), k, sp, x[t:t + 1].contiguous(), q.MOE_BF16, 1,
+                                     shape.act, w[t:t + 1].contiguous(), res[t:t + 1].contiguous(), q.MOE_BF16, o1,
+                                     q.MOE_BF16, ws1, ws1_b)
+            torch.cuda.synchronize()
+            assert torch.equal(out[t], o1[0]), f"call {call} token {t}"

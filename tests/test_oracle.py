@@ -347,3 +347,39 @@ def test_lfu_relabel_invariant():
     s1, h1 = moe.lfu_simulate(tr, 16)
     s2, h2 = moe.lfu_simulate(perm[tr], 16)
     assert np.array_equal(s1, s2) and np.array_equal(h1, h2)
+
+
+# ---------------------------------------------------------------------------------------------
+# grouping of (token, slot) pairs by expert
+# ---------------------------------------------------------------------------------------------
+
+def test_group_pairs_hand_fixture(golden_dir):
+    rows = [r.split() for r in _read_fixture(golden_dir, "group_pairs_hand.txt")]
+    ids = np.array([[int(v) for v in r[1:]] for r in rows if r[0] == "ids"])
+    perm = [int(v) for r in rows if r[0] == "perm" for v in r[1:]]
+    groups = [tuple(int(v) for v in r[1:]) for r in rows if r[0] == "group"]
+    g, p = moe.group_pairs(ids, 4)
+    assert p.tolist() == perm
+    assert g == groups
+
+
+def test_group_pairs_brute_force_and_invariants():
+    """Against a bucket-by-bucket scan of the pairs (a different construction), plus the invariants:
+    perm is a permutation, buckets ascend along perm, pairs ascend within a bucket, counts = histogram."""
+    rng = np.random.default_rng(5)
+    for T, k, n in ((1, 8, 128), (5, 3, 8), (32, 8, 128), (7, 4, 3)):
+        ids = rng.integers(-2, n + 3, size=(T, k))
+        g, p = moe.group_pairs(ids, n)
+        flat = ids.reshape(-1)
+        bucket_of = [e if 0 <= e < n else n for e in flat.tolist()]
+        scan, ref_groups = [], []
+        for b in range(n + 1):
+            members = [q for q in range(T * k) if bucket_of[q] == b]
+            if members:
+                ref_groups.append((b, len(scan), len(members)))
+            scan += members
+        assert p.tolist() == scan and g == ref_groups
+        assert sorted(p.tolist()) == list(range(T * k))
+        bs = [bucket_of[q] for q in p.tolist()]
+        assert bs == sorted(bs)
+        assert np.array_equal(np.bincount(bs, minlength=n + 1), np.bincount(bucket_of, minlength=n + 1))
