@@ -10,6 +10,9 @@ already in HBM, rotated step by step.
 
 Prints one JSON line: decode tokens/s, plus the roofline of the dominant kernel (the expert gate/up
 GEMV launch, timed live with HIP events on its stream) and the CPU oracle's speed on a bounded sample.
+Alongside (not the headline value): per-launch times of the decode kernels, a 32-token batched step
+through the same stack, and the same stack served from pinned host memory through 16-slot LFU expert
+caches (hit rates, host-to-device rate against a plain pinned copy).
 """
 from __future__ import annotations
 
@@ -59,21 +62,14 @@ def gate_up_bytes(cfg) -> int:
     return (cfg.k * 2 * cfg.F + 2 * cfg.S) * row
 
 
-def time_gate_up(dec, cfg, reps):
-    """Average duration of the gate/up GEMV launch, from HIP events around a HIP graph of one launch per
-    layer (each with that layer's routing of the last decoded token), replayed `reps` times."""
+def time_graph(build, reps, stream):
+    """Average duration of one replay of the HIP graph that build() records, from HIP events on `stream`."""
     import torch
-    from bit_quantized_expert_int8_amd import moeq4 as q
 
-    s = dec.shape
-    stream = torch.cuda.Stream()
-    stream.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(stream):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            for l in range(len(dec.layers)):
-                q.q4_expert_gate_up(dec.routed_pools[l], dec.ids_all[l], s.k, dec.shared_pools[l], dec.u, s.x_dtype, 1,
-                                    s.act, dec.gemv_ws, dec.gemv_ws_bytes, torch.cuda.current_stream())
+            build()
         g.replay()
         stream.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -82,13 +78,175 @@ def time_gate_up(dec, cfg, reps):
             g.replay()
         e1.record(stream)
     e1.synchronize()
-    launches = reps * len(dec.layers)
-    return e0.elapsed_time(e1) * 1e-3 / launches, launches
+    return e0.elapsed_time(e1) * 1e-3 / reps
 
 
-def cpu_baseline(cfg, n_layers_sample, token=0):
+def time_decode_kernels(dec, xin, reps):
+    """Per-launch durations of the three launches of a decoded layer (RMSNorm + router + top-k; expert
+    gate/up; expert down + combine), each from a graph of one launch per layer with that layer's routing
+    of the last decoded token.  The down + combine time is the gate/up + down + combine call minus gate/up."""
+    import torch
+    from bit_quantized_expert_int8_amd import moeq4 as q
+
+    s, L = dec.shape, len(dec.layers)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    ids_keep = dec.ids_all.clone()
+    out = torch.empty_like(xin)
+    lg = torch.empty((1, s.n_experts), dtype=torch.float32, device="cuda")
+    ids_tmp = torch.empty((1, s.k), dtype=torch.int32, device="cuda")
+    w_tmp = torch.empty((1, s.k), dtype=torch.float32, device="cuda")
+    u_tmp = torch.empty_like(xin)
+
+    def routers():
+        for l, W in enumerate(dec.layers):
+            q.moe_norm_router_topk(xin, s.x_dtype, W.gamma, s.eps, 1, s.d, W.router_w, W.router_s, s.n_experts, s.k,
+                                   None, ids_tmp, w_tmp, lg, u_tmp, dec.router_ws, dec.router_ws_bytes, stream)
+
+    def gate_ups():
+        for l in range(L):
+            q.q4_expert_gate_up(dec.routed_pools[l], ids_keep[l], s.k, dec.shared_pools[l], dec.u, s.x_dtype, 1, s.act,
+                                dec.gemv_ws, dec.gemv_ws_bytes, stream)
+
+    def gemv_combines():
+        for l in range(L):
+            q.q4_expert_gemv_combine(dec.routed_pools[l], ids_keep[l], s.k, dec.shared_pools[l], dec.u, s.x_dtype, 1,
+                                     s.act, dec.weights_all[l], xin, s.x_dtype, out, s.x_dtype, dec.fused_ws,
+                                     dec.fused_ws_bytes, stream)
+
+    t_router = time_graph(routers, reps, stream) / L
+    t_gate_up = time_graph(gate_ups, reps, stream) / L
+    t_gemv_combine = time_graph(gemv_combines, reps, stream) / L
+    return {"norm_router_topk_us": t_router * 1e6, "gate_up_us": t_gate_up * 1e6,
+            "down_combine_us": (t_gemv_combine - t_gate_up) * 1e6}, t_gate_up, reps * L
+
+
+def distinct_expert_bytes(dec, cfg):
+    """HBM bytes of weights one step reads, from the routing of the last step: per layer the distinct routed
+    experts' records, the shared expert's record and the int8 router."""
+    from bit_quantized_expert_int8_amd import moeq4 as q
+
+    rb = q.moe_record_bytes(cfg.d, cfg.F, q.MOE_BF16)
+    srb = q.moe_record_bytes(cfg.d, cfg.S, q.MOE_BF16)
+    total, distinct = 0, []
+    for l in range(len(dec.layers)):
+        n = int(dec.ids_all[l].unique().numel())
+        distinct.append(n)
+        total += n * rb + srb + cfg.n_experts * cfg.d
+    return total, sum(distinct) / len(distinct)
+
+
+def measure_batched(shape, layers, cfg, tokens, steps, warmup):
+    """32 tokens decoded together through the stack (one grouped call per layer), graph-replayed with the
+    token batch rotated each step."""
+    import torch
+    from bit_quantized_expert_int8_amd import decoder
+
+    T = 32
+    dec = decoder.MoEDecoder(shape, layers, T=T)
+    n_batches = tokens.shape[0] // T
+    batches = tokens[: n_batches * T].reshape(n_batches, T, cfg.d)
+    xin = torch.empty((T, cfg.d), dtype=torch.bfloat16, device="cuda")
+    xout = torch.empty_like(xin)
+    xin.copy_(batches[0])
+    g = dec.capture(xin, xout)
+    for i in range(warmup):
+        xin.copy_(batches[i % n_batches])
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        xin.copy_(batches[i % n_batches])
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    step_s = e0.elapsed_time(e1) * 1e-3 / steps
+    nbytes, mean_distinct = distinct_expert_bytes(dec, cfg)
+    return {"tokens_per_step": T, "tok_s": round(T / step_s, 1), "ms_per_step": round(step_s * 1e3, 4),
+            "per_layer_us": round(step_s / len(layers) * 1e6, 2), "distinct_experts_per_layer": round(mean_distinct, 1),
+            "weight_bytes_per_step": nbytes, "achieved_GBps": round(nbytes / step_s / 1e9, 1)}
+
+
+def measure_streamed(shape, layers, cfg, dec, n_tokens):
+    """Experts served from pinned host memory through a 16-slot LFU cache per layer (routing forced by a
+    Zipf(1.1) trace): tokens/s over all tokens and over the second half (warm cache), hit rates, and the
+    host-to-device rate against a plain pinned 1 GiB copy measured in the same process."""
+    import numpy as np
+    import torch
+    import synth
+    from bit_quantized_expert_int8_amd import moeq4 as q
+
+    L, E, k, n_slots = len(layers), cfg.n_experts, cfg.k, 16
+    rb = layers[0].pool.shape[1]
+    # pinned-copy reference rate
+    ref_h = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+    ref_d = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    ref_d.copy_(ref_h, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        ref_d.copy_(ref_h, non_blocking=True)
+    e1.record()
+    e1.synchronize()
+    pinned_gbps = 3 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del ref_h, ref_d
+
+    host = [torch.empty((E, rb), dtype=torch.uint8, pin_memory=True) for _ in range(L)]
+    for h, lay in zip(host, layers):
+        h.copy_(lay.pool)
+    slots = [torch.empty((n_slots, rb), dtype=torch.uint8, device="cuda") for _ in range(L)]
+    cache = q.moe_expert_cache_create(L, E, n_slots, rb, [h.data_ptr() for h in host], [s_.data_ptr() for s_ in slots])
+    try:
+        trace = synth.zipf_trace(4, n_tokens, L, k, E, 1.1)
+        forced = torch.from_numpy(trace.astype(np.int32)).cuda()
+        slot_pools = [q.pool(s_, rb, n_slots, cfg.d, cfg.F, shape.sb_dtype) for s_ in slots]
+        slot_ids = torch.empty((L, 1, k), dtype=torch.int32, device="cuda")
+        copy_stream = torch.cuda.Stream()
+        compute = torch.cuda.current_stream()
+        ready = [torch.cuda.Event() for _ in range(L)]
+        freed = [torch.cuda.Event() for _ in range(L)]
+        for ev in ready + freed:
+            ev.record(copy_stream)
+        copy_stream.synchronize()
+        bits = np.stack([synth.activation(cfg.act_cfg, t % 64, cfg.d, bf16=True) for t in range(64)]).astype(np.int16)
+        toks = torch.from_numpy(bits).view(torch.bfloat16).cuda().reshape(64, 1, cfg.d)
+        bufs = [torch.empty((1, cfg.d), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+        half = n_tokens // 2
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(n_tokens):
+            if t == half:
+                torch.cuda.synchronize()
+                t_half = time.perf_counter()
+                hits_half = sum(q.moe_expert_cache_stats(cache, l)[0] for l in range(L))
+                bytes_half = q.moe_expert_cache_stats(cache, -1)[2]
+            x = toks[t % 64]
+            for l in range(L):
+                q.expert_cache_stage(cache, l, trace[t, l].tolist(), slot_ids[l], copy_stream, freed[l], ready[l])
+                compute.wait_event(ready[l])
+                out = bufs[l % 2]
+                dec.layer(l, x, out, forced_ids=forced[t, l].reshape(1, k), routed_pool=slot_pools[l], ids=slot_ids[l])
+                freed[l].record(compute)
+                x = out
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        hits, misses, nbytes = q.moe_expert_cache_stats(cache, -1)
+    finally:
+        q.moe_expert_cache_destroy(cache)
+    req = n_tokens * L * k
+    warm_req = (n_tokens - half) * L * k
+    return {"tokens": n_tokens, "layers": L, "slots_per_layer": n_slots, "trace": "Zipf(1.1) forced routing",
+            "tok_s_all": round(n_tokens / (t1 - t0), 2), "tok_s_warm": round((n_tokens - half) / (t1 - t_half), 2),
+            "hit_rate_all": round(hits / req, 4), "hit_rate_warm": round((hits - hits_half) / warm_req, 4),
+            "bytes_copied": int(nbytes), "h2d_GBps_effective_warm": round((nbytes - bytes_half) / (t1 - t_half) / 1e9, 2),
+            "pinned_copy_GBps": round(pinned_gbps, 2)}
+
+
+def cpu_baseline(cfg, n_layers_sample, repeats, token=0):
     """The CPU oracle (float64 numpy) on a bounded sample: one token through the first layers of the
-    stack, records of the experts it routes to prepared beforehand (untimed)."""
+    stack, repeated; the records of the experts it routes to are prepared beforehand (untimed)."""
     import numpy as np
     import synth
     from oracle import inputs as oin
@@ -106,14 +264,15 @@ def cpu_baseline(cfg, n_layers_sample, token=0):
     for L in layers:
         _, _, x = moe.stack_layer_step(L, x, cfg.k)
     t0 = time.perf_counter()
-    x = x0
-    for L in layers:
-        _, _, x = moe.stack_layer_step(L, x, cfg.k)
+    for _ in range(repeats):
+        x = x0
+        for L in layers:
+            _, _, x = moe.stack_layer_step(L, x, cfg.k)
     dt = time.perf_counter() - t0
-    per_layer = dt / n_layers_sample
+    per_layer = dt / (n_layers_sample * repeats)
     return {"value": 1.0 / (per_layer * cfg.n_layers), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"token {token} through {n_layers_sample} of {cfg.n_layers} layers "
-                      f"({dt:.2f} s), scaled to one 30-layer token"}
+            "sample": f"token {token} through layers 0-{n_layers_sample - 1} of {cfg.n_layers}, {repeats} times "
+                      f"({dt:.1f} s), scaled to one 30-layer token"}
 
 
 def main():
@@ -124,7 +283,10 @@ def main():
     ap.add_argument("--layers", type=int, default=30)
     ap.add_argument("--roofline-reps", type=int, default=20)
     ap.add_argument("--cpu-layers", type=int, default=2)
+    ap.add_argument("--cpu-repeats", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the batched and streamed measurements")
+    ap.add_argument("--stream-tokens", type=int, default=512)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -168,13 +330,14 @@ def main():
     gpu_s = e0.elapsed_time(e1) * 1e-3
     tok_s = args.steps / gpu_s
 
-    dur, launches = time_gate_up(dec, cfg, args.roofline_reps)
+    kernels, dur, launches = time_decode_kernels(dec, xin, args.roofline_reps)
     nbytes = gate_up_bytes(cfg)
     achieved = nbytes / dur / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                 "kernel": "gate_up_kernel (q4_expert_gate_up: 8 routed + shared expert, gate/up + GELU)",
                 "bytes_per_launch": nbytes, "avg_launch_us": round(dur * 1e6, 3), "launches_timed": launches}
+    step_bytes, _ = distinct_expert_bytes(dec, cfg)
 
     out = {"metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(gpu_s / args.steps * 1e3, 4), "higher_is_better": True,
@@ -184,9 +347,15 @@ def main():
                       "global_batch": 1, "layers": args.layers, "tokens_in_rotation": n_tok,
                       "expert_bytes_resident_gb": round(sum(L.pool.numel() + L.shared.numel() for L in layers) / 1e9, 3),
                       "parallelism": "single GPU"},
-           "roofline": roofline, "wall_s_timed_region": round(wall, 4), "build_s": round(t_build, 1)}
+           "roofline": roofline, "wall_s_timed_region": round(wall, 4), "build_s": round(t_build, 1),
+           "step_weight_bytes": step_bytes, "step_achieved_GBps": round(step_bytes / (gpu_s / args.steps) / 1e9, 1),
+           "per_layer_us": round(gpu_s / args.steps / args.layers * 1e6, 2),
+           "decode_kernels_us": {k_: round(v, 3) for k_, v in kernels.items()}}
+    if not args.no_extras:
+        out["batched"] = measure_batched(shape, layers, cfg, tokens.reshape(n_tok, cfg.d), 20, 3)
+        out["streamed"] = measure_streamed(shape, layers, cfg, dec, args.stream_tokens)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_layers)
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_layers, args.cpu_repeats)
     print(json.dumps(out), flush=True)
 
 
