@@ -5,12 +5,12 @@ top-8 of 128 -> 4-bit expert GEMVs (gate/up + GELU, down; 8 routed experts + the
 both in the same launches) -> routing-weighted combine + residual.  d=2816, F=704, shared width 2816,
 4-bit affine weights in groups of 64 with bf16 scale/bias, bf16 activations, fp32 accumulation.  All
 13.3 GB of expert records are resident in HBM; weights are seeded synthetic draws (no checkpoint).
-One step = one token through all 30 layers, replayed from a HIP graph; inputs are 256 seeded tokens
-already in HBM, rotated step by step.
+One step = one token through all 30 layers (one moe_decode_layer launch each), replayed from a HIP
+graph; inputs are 256 seeded tokens already in HBM, rotated step by step.
 
-Prints one JSON line: decode tokens/s, plus the roofline of the dominant kernel (the expert gate/up
-GEMV launch, timed live with HIP events on its stream) and the CPU oracle's speed on a bounded sample.
-Alongside (not the headline value): per-launch times of the decode kernels, a 32-token batched step
+Prints one JSON line: decode tokens/s, plus the roofline of the dominant kernel (the single-launch
+layer, timed live with HIP events on its stream) and the CPU oracle's speed on a bounded sample.
+Alongside (not the headline value): per-launch times of the layer split in three kernels, a 32-token batched step
 through the same stack, and the same stack served from pinned host memory through 16-slot LFU expert
 caches (hit rates, host-to-device rate against a plain pinned copy).
 """
@@ -55,11 +55,16 @@ def build_stack(cfg, n_layers):
     return shape, layers
 
 
-def gate_up_bytes(cfg) -> int:
-    """Algorithmic HBM bytes of one gate/up launch: k routed experts' and the shared expert's gate+up
-    codes (d/2 bytes per row) and bf16 scale/bias (d/64 * 4 bytes per row)."""
-    row = cfg.d // 2 + (cfg.d // 64) * 4
-    return (cfg.k * 2 * cfg.F + 2 * cfg.S) * row
+def record_data_bytes(d: int, F: int) -> int:
+    """Bytes of one expert's 4-bit codes and bf16 scale/bias (gate/up [2F][d] and down [d][F], groups of 64)."""
+    return 2 * F * (d // 2 + (d // 64) * 4) + d * (F // 2 + (F // 64) * 4)
+
+
+def layer_bytes(cfg) -> int:
+    """Algorithmic HBM bytes of one decoded layer: the int8 router and its row scales, the k selected experts'
+    records and the shared expert's record (activations, a few KB, not counted)."""
+    return cfg.n_experts * cfg.d + cfg.n_experts * 4 + cfg.k * record_data_bytes(cfg.d, cfg.F) + \
+        record_data_bytes(cfg.d, cfg.S)
 
 
 def time_graph(build, reps, stream):
@@ -81,10 +86,27 @@ def time_graph(build, reps, stream):
     return e0.elapsed_time(e1) * 1e-3 / reps
 
 
-def time_decode_kernels(dec, xin, reps):
-    """Per-launch durations of the three launches of a decoded layer (RMSNorm + router + top-k; expert
-    gate/up; expert down + combine), each from a graph of one launch per layer with that layer's routing
-    of the last decoded token.  The down + combine time is the gate/up + down + combine call minus gate/up."""
+def time_layer_kernel(dec, xin, reps):
+    """Average duration of the single-launch layer (moe_decode_layer) from HIP events around a graph of one
+    launch per layer of the stack, on the stream the launches are captured on."""
+    import torch
+
+    out = torch.empty_like(xin)
+    bufs = [xin, out]
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+
+    def layers():
+        for l in range(len(dec.layers)):
+            dec.layer(l, bufs[l % 2], bufs[(l + 1) % 2], stream=stream)
+
+    return time_graph(layers, reps, stream) / len(dec.layers), reps * len(dec.layers)
+
+
+def time_split_kernels(dec, xin, reps):
+    """Per-launch durations of the layer split in three launches (moe_norm_router_topk; q4_expert_gate_up;
+    down + combine = q4_expert_gemv_combine minus gate/up), each from a graph of one launch per layer with
+    that layer's routing of the last decoded token."""
     import torch
     from bit_quantized_expert_int8_amd import moeq4 as q
 
@@ -105,20 +127,20 @@ def time_decode_kernels(dec, xin, reps):
 
     def gate_ups():
         for l in range(L):
-            q.q4_expert_gate_up(dec.routed_pools[l], ids_keep[l], s.k, dec.shared_pools[l], dec.u, s.x_dtype, 1, s.act,
+            q.q4_expert_gate_up(dec.routed_pools[l], ids_keep[l], s.k, dec.shared_pools[l], u_tmp, s.x_dtype, 1, s.act,
                                 dec.gemv_ws, dec.gemv_ws_bytes, stream)
 
     def gemv_combines():
         for l in range(L):
-            q.q4_expert_gemv_combine(dec.routed_pools[l], ids_keep[l], s.k, dec.shared_pools[l], dec.u, s.x_dtype, 1,
+            q.q4_expert_gemv_combine(dec.routed_pools[l], ids_keep[l], s.k, dec.shared_pools[l], u_tmp, s.x_dtype, 1,
                                      s.act, dec.weights_all[l], xin, s.x_dtype, out, s.x_dtype, dec.fused_ws,
                                      dec.fused_ws_bytes, stream)
 
     t_router = time_graph(routers, reps, stream) / L
     t_gate_up = time_graph(gate_ups, reps, stream) / L
     t_gemv_combine = time_graph(gemv_combines, reps, stream) / L
-    return {"norm_router_topk_us": t_router * 1e6, "gate_up_us": t_gate_up * 1e6,
-            "down_combine_us": (t_gemv_combine - t_gate_up) * 1e6}, t_gate_up, reps * L
+    return {"norm_router_topk_us": round(t_router * 1e6, 3), "gate_up_us": round(t_gate_up * 1e6, 3),
+            "down_combine_us": round((t_gemv_combine - t_gate_up) * 1e6, 3)}
 
 
 def distinct_expert_bytes(dec, cfg):
@@ -330,13 +352,15 @@ def main():
     gpu_s = e0.elapsed_time(e1) * 1e-3
     tok_s = args.steps / gpu_s
 
-    kernels, dur, launches = time_decode_kernels(dec, xin, args.roofline_reps)
-    nbytes = gate_up_bytes(cfg)
+    dur, launches = time_layer_kernel(dec, xin, args.roofline_reps)
+    nbytes = layer_bytes(cfg)
     achieved = nbytes / dur / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "gate_up_kernel (q4_expert_gate_up: 8 routed + shared expert, gate/up + GELU)",
+                "kernel": "decode_layer_kernel (moe_decode_layer: RMSNorm, int8 router + top-8, 8 routed + shared "
+                          "4-bit expert FFNs, combine + residual, one launch per layer)",
                 "bytes_per_launch": nbytes, "avg_launch_us": round(dur * 1e6, 3), "launches_timed": launches}
+    split = time_split_kernels(dec, xin, args.roofline_reps)
     step_bytes, _ = distinct_expert_bytes(dec, cfg)
 
     out = {"metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -350,7 +374,7 @@ def main():
            "roofline": roofline, "wall_s_timed_region": round(wall, 4), "build_s": round(t_build, 1),
            "step_weight_bytes": step_bytes, "step_achieved_GBps": round(step_bytes / (gpu_s / args.steps) / 1e9, 1),
            "per_layer_us": round(gpu_s / args.steps / args.layers * 1e6, 2),
-           "decode_kernels_us": {k_: round(v, 3) for k_, v in kernels.items()}}
+           "decode_mode": dec.mode, "split_kernels_us": split}
     if not args.no_extras:
         out["batched"] = measure_batched(shape, layers, cfg, tokens.reshape(n_tok, cfg.d), 20, 3)
         out["streamed"] = measure_streamed(shape, layers, cfg, dec, args.stream_tokens)

@@ -68,16 +68,30 @@ def pack_layer(shape: Shape, fill_expert: Callable, fill_shared: Optional[Callab
                         None if gamma is None else gamma.to(device).contiguous())
 
 
+def layer_kernel_fits(shape: Shape, T: int) -> bool:
+    """Whether moe_decode_layer (batch 1) supports this shape."""
+    return (T == 1 and shape.d <= 4096 and shape.S <= 4096 and shape.F <= 1024 and shape.n_experts <= 256
+            and 1 <= shape.k <= min(32, shape.n_experts))
+
+
 class MoEDecoder:
     """Runs T tokens through a stack of MoE layers (T = 1 is decode).
 
-    fused=True (default) runs a layer as two library calls plus one: moe_norm_router_topk (RMSNorm inside
-    the router), then q4_expert_gemv_combine (expert GEMVs with the combine + residual in the down launch's
-    tail).  fused=False runs the five separate calls (moe_rmsnorm, moe_router_topk, q4_expert_gemv,
-    moe_combine); both give the same routing and, on the same normalized input, the same output bits."""
+    Three ways to run a layer, all through the library:
+      "layer"     one launch per layer (moe_decode_layer): norm, router, experts and combine together;
+                  the default for T = 1 when the shape is within that kernel's limits
+      "fused"     moe_norm_router_topk (RMSNorm inside the router) then q4_expert_gemv_combine (expert
+                  GEMVs with the combine + residual in the down launch's tail); the default otherwise
+      "separate"  moe_rmsnorm, moe_router_topk, q4_expert_gemv, moe_combine
+    "fused" and "separate" give the same routing and, on the same normalized input, the same output bits."""
 
-    def __init__(self, shape: Shape, layers: list, T: int = 1, device="cuda", fused: bool = True):
-        self.shape, self.layers, self.T, self.fused = shape, layers, T, fused
+    def __init__(self, shape: Shape, layers: list, T: int = 1, device="cuda", mode: Optional[str] = None):
+        self.shape, self.layers, self.T = shape, layers, T
+        if mode is None:
+            mode = "layer" if layer_kernel_fits(shape, T) else "fused"
+        if mode not in ("layer", "fused", "separate") or (mode == "layer" and not layer_kernel_fits(shape, T)):
+            raise ValueError(f"mode {mode!r} not available for this shape / batch")
+        self.mode = mode
         s = shape
         self.device = device
         self.routed_pools = [q.pool(L.pool, L.pool.shape[1], s.n_experts, s.d, s.F, s.sb_dtype) for L in layers]
@@ -102,13 +116,20 @@ class MoEDecoder:
         self.fused_ws_bytes = max(q.q4_expert_gemv_combine_workspace_bytes(rp, s.k, sp, T)
                                   for rp, sp in zip(self.routed_pools, self.shared_pools))
         self.fused_ws = torch.zeros(max(self.fused_ws_bytes, 256), dtype=torch.uint8, device=device)
+        # the single-launch layer's workspace: counters at the front start at zero and calls leave them zero
+        self.layer_ws_bytes = q.moe_decode_layer_workspace_bytes(s.d, s.n_experts, s.k, s.F,
+                                                                 s.S if layers and layers[0].shared is not None else 0)
+        self.layer_ws = torch.zeros(max(self.layer_ws_bytes, 256), dtype=torch.uint8, device=device)
         self.graph = None
 
     # one layer: x_in -> x_out (both [T][d] in the activation dtype)
     def layer(self, l: int, x_in: torch.Tensor, x_out: torch.Tensor, forced_ids: Optional[torch.Tensor] = None,
               routed_pool=None, ids: Optional[torch.Tensor] = None, stream=None) -> None:
         s, L, T = self.shape, self.layers[l], self.T
-        if self.fused:
+        if self.mode == "layer":
+            self._layer_single_launch(l, x_in, x_out, forced_ids, routed_pool, ids, stream)
+            return
+        if self.mode == "fused":
             self._layer_fused(l, x_in, x_out, forced_ids, routed_pool, ids, stream)
             return
         if s.rms_norm:
@@ -123,6 +144,13 @@ class MoEDecoder:
                          u, s.x_dtype, T, s.act, self.y_routed, self.y_shared, self.gemv_ws, self.gemv_ws_bytes, stream)
         q.moe_combine(self.y_routed, lw, self.y_shared if self.shared_pools[l] is not None else None,
                       x_in if s.rms_norm else None, s.x_dtype, T, s.k, s.d, x_out, s.x_dtype, stream)
+
+    def _layer_single_launch(self, l, x_in, x_out, forced_ids, routed_pool, ids, stream) -> None:
+        s, L = self.shape, self.layers[l]
+        q.moe_decode_layer(x_in, s.x_dtype, L.gamma if s.rms_norm else None, s.eps, s.rms_norm, L.router_w, L.router_s,
+                           s.n_experts, s.k, forced_ids, routed_pool or self.routed_pools[l], ids,
+                           self.shared_pools[l], s.act, self.ids_all[l], self.weights_all[l], self.logits_all[l], x_out,
+                           self.layer_ws, self.layer_ws_bytes, stream)
 
     def _layer_fused(self, l, x_in, x_out, forced_ids, routed_pool, ids, stream) -> None:
         s, L, T = self.shape, self.layers[l], self.T

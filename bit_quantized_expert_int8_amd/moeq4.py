@@ -78,6 +78,12 @@ _c = {
     "q4_expert_gemv_combine": _sig("q4_expert_gemv_combine", _st,
                                    [ctypes.POINTER(moe_q4_pool), _vp, _i32, ctypes.POINTER(moe_q4_pool), _vp, ctypes.c_int,
                                     _i32, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _sz, _vp]),
+    "moe_decode_layer_workspace_bytes": _sig("moe_decode_layer_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32]),
+    "moe_decode_layer_sync_bytes": _sig("moe_decode_layer_sync_bytes", _sz, [_i32, _i32]),
+    "moe_decode_layer": _sig("moe_decode_layer", _st,
+                             [_vp, ctypes.c_int, _vp, ctypes.c_float, _i32, _vp, _vp, _i32, _i32, _vp,
+                              ctypes.POINTER(moe_q4_pool), _vp, ctypes.POINTER(moe_q4_pool), ctypes.c_int, _vp, _vp,
+                              _vp, _vp, _vp, _sz, _vp]),
     "moe_combine": _sig("moe_combine", _st, [_vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32, _vp, ctypes.c_int, _vp]),
     "moe_expert_cache_create": _sig("moe_expert_cache_create", _st, [_i32, _i32, _i32, _sz, ctypes.POINTER(_vp),
                                                                      ctypes.POINTER(_vp), _u32, ctypes.POINTER(_vp)]),
@@ -214,6 +220,21 @@ def q4_expert_gemv_combine(routed, ids, k, shared, x, x_dtype, T, act, weights, 
     _check(_c["q4_expert_gemv_combine"](_pp(routed), _p(ids), k, _pp(shared), _p(x), x_dtype, T, act, _p(weights),
                                         _p(residual), residual_dtype, _p(out), out_dtype, _p(workspace), workspace_bytes,
                                         _s(stream)), "q4_expert_gemv_combine")
+
+
+def moe_decode_layer_workspace_bytes(d, E, k, F, S) -> int:
+    return _c["moe_decode_layer_workspace_bytes"](d, E, k, F, S)
+
+
+def moe_decode_layer_sync_bytes(d, k) -> int:
+    return _c["moe_decode_layer_sync_bytes"](d, k)
+
+
+def moe_decode_layer(x, x_dtype, gamma, eps, residual, router_w, router_scale, E, k, forced_ids, routed, gemv_ids,
+                     shared, act, ids, weights, logits, out, workspace, workspace_bytes, stream=None) -> None:
+    _check(_c["moe_decode_layer"](_p(x), x_dtype, _p(gamma), eps, int(residual), _p(router_w), _p(router_scale), E, k,
+                                  _p(forced_ids), _pp(routed), _p(gemv_ids), _pp(shared), act, _p(ids), _p(weights),
+                                  _p(logits), _p(out), _p(workspace), workspace_bytes, _s(stream)), "moe_decode_layer")
 
 
 def moe_combine(y_routed, weights, y_shared, residual, residual_dtype, T, k, d, out, out_dtype, stream=None) -> None:

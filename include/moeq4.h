@@ -228,6 +228,37 @@ moe_status q4_expert_gemv_combine(const moe_q4_pool* routed, const int32_t* ids_
                                   void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------------
+ * moe_decode_layer — one whole MoE layer of batch-1 decode in a single launch: RMSNorm, 8-bit router and
+ * top-k, the k selected experts and the shared expert, combine and residual ([G26] "Le pipeline de
+ * traitement"; [G26] "Concurrence pour masquer la latence": the shared expert runs without waiting for the
+ * routing, the branches are merged once the routed experts are in).  For the single token x:
+ *   u       = gamma ? round_x((x * gamma) * rsqrt(mean(x^2) + eps)) : x
+ *   logits  = row_scale[e] * (w[e] . u);  ids = top-k (or forced ids);  weights = softmax over ids
+ *   out     = round_x( sum_i weights[i] * FFN_{ids[i]}(u) + FFN_shared(u) + (residual ? x : 0) )
+ * with the selection, weights and expert arithmetic of moe_router_topk / q4_expert_gemv.  The norm's
+ * sum of squares uses its own fixed order, so u may differ from moe_rmsnorm's in the last bit.
+ * x_dev, out_dev: x_dtype [d] (16-byte aligned, must not alias); gamma_dev: fp32 [d] or NULL;
+ * router as moe_router_topk; forced_ids_dev: int32 [k] or NULL; routed: pool of experts, indexed by the
+ * selected ids, or by gemv_ids_dev[i] (int32 [k], e.g. cache slots from expert_cache_stage) when that is
+ * non-NULL; shared: pool whose record 0 is the shared expert, or NULL; ids_dev / weights_dev / logits_dev:
+ * optional outputs (int32 [k], fp32 [k], fp32 [E]).
+ * Limits: d <= 4096, shared width <= 4096, routed F <= 1024, E <= 256, 1 <= k <= min(E, 32).
+ * Workspace: moe_decode_layer_workspace_bytes(d, E, k, F, S) bytes (S = 0 without shared expert), 256-byte
+ * aligned, ZERO before its first use.  Its first moe_decode_layer_sync_bytes(d, k) bytes hold the counters
+ * and flags the blocks synchronise with; every completed call leaves them zero again, except 32-bit word 0:
+ * a sticky error flag, nonzero if a wait inside the kernel ran out (the results of that call are invalid;
+ * zero the workspace before reusing it).  Calls that overlap in time need separate workspaces.
+ * ------------------------------------------------------------------------------------------------- */
+size_t moe_decode_layer_workspace_bytes(int32_t d, int32_t E, int32_t k, int32_t F, int32_t S);
+size_t moe_decode_layer_sync_bytes(int32_t d, int32_t k);
+moe_status moe_decode_layer(const void* x_dev, moe_dtype x_dtype, const float* gamma_dev, float eps, int32_t residual,
+                            const int8_t* router_w_dev, const float* router_scale_dev, int32_t E, int32_t k,
+                            const int32_t* forced_ids_dev, const moe_q4_pool* routed, const int32_t* gemv_ids_dev,
+                            const moe_q4_pool* shared, moe_act act, int32_t* ids_dev, float* weights_dev,
+                            float* logits_dev, void* out_dev, void* workspace_dev, size_t workspace_bytes,
+                            void* stream);
+
+/* ---------------------------------------------------------------------------------------------------
  * Expert cache — 16-slot-per-layer least-frequently-used cache of expert records ([DAILY] "Cache
  * d'experts"; [DEVT] "Wat is de belangrijkste architectuurtruuc"; [REMIO] "Mac Gemma 4 26B tient en
  * mémoire..."), fed on demand from slower memory while the shared expert computes ([G26] "Concurrence

@@ -125,11 +125,12 @@ def test_expert_gemv_tiny_given_ids(tiny, act):
     assert worst <= TOL
 
 
-def test_layer_tiny_end_to_end(tiny):
+@pytest.mark.parametrize("mode", ["fused", "separate"])
+def test_layer_tiny_end_to_end(tiny, mode):
     cfg, dev, orc = tiny
     T = 16
     shape = H.shape_of(cfg)
-    dec = decoder.MoEDecoder(shape, [dev], T=T)
+    dec = decoder.MoEDecoder(shape, [dev], T=T, mode=mode)
     x = H.token_batch(cfg, range(T))
     out = torch.empty_like(x)
     dec.layer(0, x, out)
@@ -165,12 +166,13 @@ def full_layer():
     return cfg, H.device_layer(cfg, 0), oin.oracle_layer(cfg, 0, cache_experts=32)
 
 
-def test_full_size_layer_sampled_tokens(full_layer):
+@pytest.mark.parametrize("mode", ["fused", "separate"])
+def test_full_size_layer_sampled_tokens(full_layer, mode):
     """d=2816, 128 experts, top-8, F=704, shared 2816: four tokens, each checked against the oracle."""
     cfg, dev, orc = full_layer
     T = 4
     toks = [0, 1, 2, 3]
-    dec = decoder.MoEDecoder(H.shape_of(cfg), [dev], T=T)
+    dec = decoder.MoEDecoder(H.shape_of(cfg), [dev], T=T, mode=mode)
     x = H.token_batch(cfg, toks)
     out = torch.empty_like(x)
     dec.layer(0, x, out)

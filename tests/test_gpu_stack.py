@@ -54,8 +54,9 @@ def test_stack_teacher_forced_sampled_layers(stack):
         torch.cuda.synchronize()
         ids = dec.ids_all[l].cpu().numpy()[0]
         u_ref = moe.f64_round_to_bf16(moe.rms_norm(x_in, np.ones(cfg.d), 1e-6))
-        u_gpu = _bf16_to_f64(dec.u)[0]
-        assert H.max_rel_err(u_gpu, u_ref) <= 2 ** -7
+        if dec.mode != "layer":          # the single-launch layer keeps u internal
+            u_gpu = _bf16_to_f64(dec.u)[0]
+            assert H.max_rel_err(u_gpu, u_ref) <= 2 ** -7
         lg = moe.router_logits(orc.router_w, orc.router_s, u_ref)
         assert H.topk_consistent(ids.tolist(), lg, cfg.k), f"layer {l}"
         _, res, x_next = moe.stack_layer_step(orc, x_in, cfg.k, forced_ids=ids)
@@ -89,10 +90,13 @@ def test_graph_replays_match_eager(stack):
 
 
 def test_batched_tokens_match_single_token(stack):
-    """32 tokens in one call (the batched configuration) equal each token run alone, on layer 0."""
-    cfg, layers, dec1 = stack
+    """32 tokens in one call (the batched configuration, grouped by expert) equal each token run alone
+    through the same library calls (norm + router, then expert GEMVs with the combine), on layer 0."""
+    cfg, layers, _ = stack
     T = 32
     decT = decoder.MoEDecoder(H.shape_of(cfg), layers[:1], T=T)
+    dec1 = decoder.MoEDecoder(H.shape_of(cfg), layers[:1], T=1, mode="fused")
+    assert decT.mode == "fused"
     x = H.token_batch(cfg, range(T))
     out = torch.empty_like(x)
     decT.layer(0, x, out)
