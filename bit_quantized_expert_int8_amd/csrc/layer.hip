@@ -56,7 +56,8 @@ constexpr int kSharedSub = 16, kSharedFlags = 16;
 constexpr int kSlotSub = 1, kSlotFlags = 8;
 constexpr int kTilesSub = 1;
 // line 0: status word (sticky, bit 0 = a bounded wait ran out); then the sets route, shared, tiles, slots
-constexpr int kLinesFixed = 1 + (kRouteSub + 1 + kRouteFlags) + (kSharedSub + 1 + kSharedFlags) + (kTilesSub + 1);
+constexpr int kXFlags = 64;      // flags announcing a layer's output to the next layer of the launch
+constexpr int kLinesFixed = 1 + (kRouteSub + 1 + kRouteFlags) + (kSharedSub + 1 + kSharedFlags) + (kTilesSub + 1 + kXFlags);
 constexpr int kLinesPerSlot = kSlotSub + 1 + kSlotFlags;
 constexpr int kTileStride = 16;     // words between two tile tickets
 
@@ -83,11 +84,16 @@ struct LayerArgs {
   float* weights_out;
   float* logits_out;
   void* out;
+  int32_t x_f32, out_f32;  // activations held in the workspace as fp32 and exchanged coherently (the
+                           // layers between the first input and the last output of a launch)
   uint32_t* status;
-  SyncSet route, shared_h, tiles_done;
-  SyncSet slot_h[kLayerMaxK];
-  uint32_t* sync_base;  // all sync lines (reset by the block that combines the layer's last tile)
-  int32_t sync_lines;
+  SyncSet route, shared_h, tiles_done;   // tiles_done = this layer's output complete (flags: next layer)
+  SyncSet prev_x;                        // the previous layer's tiles_done, or base == NULL
+  uint32_t* slot_base;                   // per-slot sets, kLinesPerSlot lines apart
+  int32_t last_layer;                    // the block combining this layer's last tile resets every layer
+  uint32_t* sync_base;                   // sync lines of layer 0; layer l's are l * layer_words further
+  int64_t layer_words;
+  int32_t sync_lines, n_layers;
   uint32_t* tiles;     // [d/16] tickets, kTileStride words apart
   float* logits;       // [E]
   float* h_routed;     // [k][F]
@@ -95,7 +101,13 @@ struct LayerArgs {
   float* y_routed;     // [k][d]
   float* y_shared;     // [d]
   int32_t nR, nSG, nRG, nSD, nRD;
+  int32_t* route_ids_ws;   // [k] selected ids, published with route_w_ws before the route flags
+  float* route_w_ws;       // [k] their softmax weights
 };
+
+__device__ __forceinline__ SyncSet slot_set(const LayerArgs& a, int i) {
+  return SyncSet{a.slot_base + (int64_t)i * kLinesPerSlot * kLW, kSlotSub, kSlotFlags, (uint32_t)(a.routed.F / 8)};
+}
 
 __device__ __forceinline__ float ld_c(const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ __forceinline__ void st_c(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
@@ -109,7 +121,11 @@ __device__ __forceinline__ uint32_t add_cu(uint32_t* p, uint32_t v) {
 // One arrival (thread 0 of a block, after its published stores completed) out of `total` on set `s`;
 // `idx` in [0, total) picks the sub-counter.  True for the arrival that completed the set, which has then
 // raised every flag of the set.
-__device__ __forceinline__ bool arrive(const SyncSet& s, int idx, int total, uint32_t n = 1u) {
+__device__ __forceinline__ void raise_flags(const SyncSet& s) {
+  for (int f = 0; f < s.n_flags; ++f) st_cu(s.base + (s.n_sub + 1 + f) * kLW, 1u);
+}
+
+__device__ __forceinline__ bool arrive(const SyncSet& s, int idx, int total, uint32_t n = 1u, bool raise = true) {
   if (s.n_sub > 1) {
     const int sub = idx % s.n_sub;
     const uint32_t expect = (uint32_t)((total - sub + s.n_sub - 1) / s.n_sub);
@@ -119,7 +135,7 @@ __device__ __forceinline__ bool arrive(const SyncSet& s, int idx, int total, uin
   } else if (add_cu(s.base, n) + n != (uint32_t)total) {
     return false;
   }
-  for (int f = 0; f < s.n_flags; ++f) st_cu(s.base + (s.n_sub + 1 + f) * kLW, 1u);
+  if (raise) raise_flags(s);
   return true;
 }
 
@@ -166,7 +182,11 @@ __device__ __forceinline__ float norm_to_lds(const LayerArgs& a, float* xg, Norm
   float ss = 0.f;
   for (int j0 = threadIdx.x * 8; j0 < a.d; j0 += kThreads * 8) {
     float v[8];
-    if (sizeof(XT) == 2) {
+    if (a.x_f32) {
+      const float* xf = reinterpret_cast<const float*>(a.x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = ld_c(xf + j0 + i);
+    } else if (sizeof(XT) == 2) {
       const uint4 w = *reinterpret_cast<const uint4*>(x + j0);
       const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -220,61 +240,110 @@ __device__ __forceinline__ float u_of(float xg, float rinv, bool norm) {
 // routing inside a block
 // ------------------------------------------------------------------------------------------------
 struct RouteLds {
-  float lg[kLayerMaxE];
+  alignas(16) float lg[kLayerMaxE];
   float sel_v[kLayerMaxK];
   int sel_i[kLayerMaxK];
   float w[kLayerMaxK];
 };
 
-__device__ __forceinline__ void load_logits(const LayerArgs& a, RouteLds& r) {
-  wait_set(a.route, blockIdx.x, a.status);
+// The router block whose arrival completed the route ranks the published logits once (top-k: larger logit
+// first, equal logits -> lower id; or the forced ids), publishes ids and softmax weights, and only then
+// raises the route flags.  Every logit is published: each router block's stores completed before it
+// arrived.
+__device__ __forceinline__ void publish_route(const LayerArgs& a, RouteLds& r) {
   if ((int)threadIdx.x < a.E) r.lg[threadIdx.x] = ld_c(a.logits + threadIdx.x);
-  __syncthreads();
-}
-
-// sel_i[0..k) = the selected expert ids (top-k by rank: larger logit first, equal logits -> lower id),
-// or the forced ids (no wait on the router).  sel_v = their logits when with_logits.
-__device__ __forceinline__ void route_ids(const LayerArgs& a, RouteLds& r, bool with_logits) {
-  if (a.forced) {
-    if (with_logits) load_logits(a, r);
-    if ((int)threadIdx.x < a.k) {
-      const int i = a.forced[threadIdx.x];
-      r.sel_i[threadIdx.x] = i;
-      if (with_logits) r.sel_v[threadIdx.x] = (i >= 0 && i < a.E) ? r.lg[i] : __builtin_nanf("");
-    }
-    __syncthreads();
-    return;
-  }
-  load_logits(a, r);
   if ((int)threadIdx.x < kLayerMaxK) {
     r.sel_i[threadIdx.x] = -1;
     r.sel_v[threadIdx.x] = __builtin_nanf("");
   }
   __syncthreads();
-  const int c = threadIdx.x;
-  if (c < a.E) {
-    const float v = r.lg[c];
-    int rank = 0;
-    for (int e2 = 0; e2 < a.E; ++e2) {
-      const float u = r.lg[e2];
-      rank += (u > v) | ((u == v) & (e2 < c));
+  if (a.forced) {
+    if ((int)threadIdx.x < a.k) {
+      const int i = a.forced[threadIdx.x];
+      r.sel_i[threadIdx.x] = i;
+      r.sel_v[threadIdx.x] = (i >= 0 && i < a.E) ? r.lg[i] : __builtin_nanf("");
     }
-    if (rank < a.k) {
-      r.sel_i[rank] = c;
-      r.sel_v[rank] = v;
+  } else if (threadIdx.x < 64) {
+    // top-k by k rounds of a wavefront argmax over order-preserving keys (larger logit first; equal logits
+    // -> the lowest id, found with a ballot); a selected candidate's key is cleared
+    const int lane = threadIdx.x;
+    constexpr int kPer = kLayerMaxE / 64;
+    uint32_t key[kPer];
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+      const int idx = lane + 64 * m;
+      if (idx < a.E) {
+        const uint32_t u = __float_as_uint(r.lg[idx] + 0.0f);        // -0 -> +0: equal logits, equal keys
+        key[m] = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+        key[m] = key[m] ? key[m] : 1u;                                // 0 is reserved for "taken"
+      } else {
+        key[m] = 0u;
+      }
+    }
+    for (int rr = 0; rr < a.k; ++rr) {
+      uint32_t mx = key[0];
+#pragma unroll
+      for (int m = 1; m < kPer; ++m) mx = key[m] > mx ? key[m] : mx;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const uint32_t t = (uint32_t)__shfl_xor((int)mx, o, 64);
+        mx = t > mx ? t : mx;
+      }
+      int sel = -1;
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) {
+        const unsigned long long hit = __ballot(key[m] == mx && mx != 0u);
+        if (sel < 0 && hit) sel = 64 * m + (__ffsll((long long)hit) - 1);
+      }
+      if (sel >= 0) {
+#pragma unroll
+        for (int m = 0; m < kPer; ++m)
+          if (lane + 64 * m == sel) key[m] = 0u;
+      }
+      if (lane == 0) {
+        r.sel_i[rr] = sel;
+        r.sel_v[rr] = sel >= 0 ? r.lg[sel] : __builtin_nanf("");
+      }
     }
   }
   __syncthreads();
-}
-
-// w[0..k) = softmax of sel_v (after route_ids with logits); every thread sums the same terms in order
-__device__ __forceinline__ void route_weights(const LayerArgs& a, RouteLds& r) {
+  // softmax over the k kept logits: one exp per kept logit, the denominator summed in the order 0..k-1
+  float ex = 0.f;
   if ((int)threadIdx.x < a.k) {
     float mx = r.sel_v[0];
     for (int i = 1; i < a.k; ++i) mx = fmaxf(mx, r.sel_v[i]);
+    ex = expf(r.sel_v[threadIdx.x] - mx);
+    r.w[threadIdx.x] = ex;
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < a.k) {
     float den = 0.f;
-    for (int i = 0; i < a.k; ++i) den += expf(r.sel_v[i] - mx);
-    r.w[threadIdx.x] = expf(r.sel_v[threadIdx.x] - mx) / den;
+    for (int i = 0; i < a.k; ++i) den += r.w[i];
+    const float w = ex / den;
+    const int id = r.sel_i[threadIdx.x];
+    st_cu(reinterpret_cast<uint32_t*>(a.route_ids_ws) + threadIdx.x, (uint32_t)id);
+    st_c(a.route_w_ws + threadIdx.x, w);
+    if (a.ids_out) a.ids_out[threadIdx.x] = id;
+    if (a.weights_out) a.weights_out[threadIdx.x] = w;
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) raise_flags(a.route);
+}
+
+// sel_i[0..k) = the selected expert ids and, with need_weights, w[0..k) their weights.  With forced ids
+// and no weights needed there is nothing to wait for.
+__device__ __forceinline__ void get_route(const LayerArgs& a, RouteLds& r, bool need_weights) {
+  if (a.forced && !need_weights) {
+    if ((int)threadIdx.x < a.k) r.sel_i[threadIdx.x] = a.forced[threadIdx.x];
+    __syncthreads();
+    return;
+  }
+  wait_set(a.route, blockIdx.x, a.status);
+  if ((int)threadIdx.x < a.k) {
+    r.sel_i[threadIdx.x] = (int)__hip_atomic_load(reinterpret_cast<const uint32_t*>(a.route_ids_ws) + threadIdx.x,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    r.w[threadIdx.x] = ld_c(a.route_w_ws + threadIdx.x);
   }
   __syncthreads();
 }
@@ -293,6 +362,7 @@ __device__ __forceinline__ void router_block(const LayerArgs& a, int b, float* x
     const int c = lane + 64 * m;
     if (e < a.E && c < nch) q[m] = *reinterpret_cast<const int4*>(a.rw + (int64_t)e * a.d + c * 16);
   }
+  if (a.prev_x.base) wait_set(a.prev_x, blockIdx.x, a.status);
   const float rinv = norm_to_lds<XT>(a, xg, nl);
   // u in place (same rounding as the gate/up blocks)
   for (int j = threadIdx.x; j < a.d; j += kThreads) xg[j] = u_of<XT>(xg[j], rinv, a.gamma != nullptr);
@@ -321,7 +391,13 @@ __device__ __forceinline__ void router_block(const LayerArgs& a, int b, float* x
       if (a.logits_out) a.logits_out[e] = lgt;
     }
   }
-  publish(a.route, b, a.nR);
+  // publish this block's logits; the block that completes the set ranks them for everyone
+  __shared__ uint32_t last_s;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) last_s = arrive(a.route, b, a.nR, 1u, false) ? 1u : 0u;
+  __syncthreads();
+  if (last_s) publish_route(a, *reinterpret_cast<RouteLds*>(xg));   // LDS reuse: xg is no longer needed
 }
 
 // 8 features (gate rows f, up rows F + f) of one expert; the four waves split the row.  Split in a load
@@ -424,15 +500,29 @@ __device__ __forceinline__ void stage_published(const float* v, int K, Stage st)
 
 // Combine tile `tile` (threads 0..15) with the block's routing (r.sel_i, r.w)
 template <typename XT>
-__device__ __forceinline__ void combine_one(const LayerArgs& a, const RouteLds& r, int tile) {
-  const int row = tile * 16 + (int)threadIdx.x;
+__device__ __forceinline__ void combine_one(const LayerArgs& a, const RouteLds& r, int tile, int t16) {
+  const int row = tile * 16 + t16;
+  // all loads first (eight in flight), then the sum in the order i = 0..k-1, shared, residual
   float acc = 0.f;
-  for (int i = 0; i < a.k; ++i) acc = __builtin_fmaf(r.w[i], ld_c(a.y_routed + (int64_t)i * a.d + row), acc);
-  if (a.has_shared) acc += ld_c(a.y_shared + row);
+  const float ys = a.has_shared ? ld_c(a.y_shared + row) : 0.f;
+  for (int i0 = 0; i0 < a.k; i0 += 8) {
+    float yv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) yv[i] = i0 + i < a.k ? ld_c(a.y_routed + (int64_t)(i0 + i) * a.d + row) : 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i0 + i < a.k) acc = __builtin_fmaf(r.w[i0 + i], yv[i], acc);
+  }
+  if (a.has_shared) acc += ys;
   const XT* x = reinterpret_cast<const XT*>(a.x);
-  if (a.residual) acc += sizeof(XT) == 2 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(x)[row])
-                                         : reinterpret_cast<const float*>(x)[row];
-  if (sizeof(XT) == 2)
+  if (a.residual)
+    acc += a.x_f32 ? ld_c(reinterpret_cast<const float*>(a.x) + row)
+                   : sizeof(XT) == 2 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(x)[row])
+                                     : reinterpret_cast<const float*>(x)[row];
+  const float o = sizeof(XT) == 2 ? bf16_bits_to_f32(f32_to_bf16_bits(acc)) : acc;   // the layer output's rounding
+  if (a.out_f32)
+    st_c(reinterpret_cast<float*>(a.out) + row, o);
+  else if (sizeof(XT) == 2)
     reinterpret_cast<uint16_t*>(a.out)[row] = (uint16_t)f32_to_bf16_bits(acc);
   else
     reinterpret_cast<float*>(a.out)[row] = acc;
@@ -452,23 +542,23 @@ __device__ __forceinline__ void tile_epilogue(const LayerArgs& a, int tile0, int
   bool any = false;
   for (int t = 0; t < ntiles; ++t) any |= lastf[t] != 0;
   if (!any) return;
-  if (!have_weights) {
-    route_ids(a, r, true);
-    route_weights(a, r);
-  }
+  if (!have_weights) get_route(a, r, true);
   uint32_t n = 0;
-  for (int t = 0; t < ntiles; ++t) {
-    if (!lastf[t]) continue;
-    ++n;
-    if (threadIdx.x < 16) combine_one<XT>(a, r, tile0 + t);
-    if (threadIdx.x == 0) st_cu(a.tiles + (tile0 + t) * kTileStride, 0u);
-  }
+  for (int t = 0; t < ntiles; ++t) n += lastf[t] ? 1u : 0u;
+  // every completed tile at once: thread 16 t + i combines row i of tile t
+  if ((int)threadIdx.x < 16 * ntiles && lastf[threadIdx.x / 16]) combine_one<XT>(a, r, tile0 + threadIdx.x / 16, threadIdx.x % 16);
+  if ((int)threadIdx.x < ntiles && lastf[threadIdx.x]) st_cu(a.tiles + (tile0 + threadIdx.x) * kTileStride, 0u);
   __shared__ uint32_t final_s;
   if (threadIdx.x == 0) final_s = arrive(a.tiles_done, 0, a.d / 16, n) ? 1u : 0u;
   __syncthreads();
-  if (final_s) {
-    // every other block has passed all of its waits: clear the sync lines (not the status line)
-    for (int l = 1 + (int)threadIdx.x; l < a.sync_lines; l += kThreads) st_cu(a.sync_base + l * kLW, 0u);
+  if (final_s && a.last_layer) {
+    // every block of the launch has passed all of its waits: clear every layer's sync lines (not the
+    // status line, the first line of layer 0)
+    const int total = a.n_layers * a.sync_lines;
+    for (int t = 1 + (int)threadIdx.x; t < total; t += kThreads) {
+      const int l = t / a.sync_lines, line = t % a.sync_lines;
+      if (line > 0 || l > 0) st_cu(a.sync_base + l * a.layer_words + (int64_t)line * kLW, 0u);
+    }
   }
 }
 
@@ -479,7 +569,7 @@ __device__ __forceinline__ void shared_down_block(const LayerArgs& a, int tile, 
   const int K = P.F, lane = threadIdx.x & 63, wave = threadIdx.x >> 6, ra = lane >> 3, j = lane & 7;
   const int C = K / 32;
   const int row = tile * 16 + ra;
-  __builtin_amdgcn_s_sleep(40);     // about 1 us: let the router blocks' first loads go ahead
+  if (!a.prev_x.base) __builtin_amdgcn_s_sleep(40);   // about 1 us: let the router's first loads go ahead
   const char* rec = P.base;
   const int64_t rowb = K / 2, sbrow = (int64_t)(K / 64) * (SB_BF16 ? 4 : 8);
   SbWord<SB_BF16> sa[NBW], sb[NBW];
@@ -536,8 +626,7 @@ __device__ __forceinline__ void routed_down_block(const LayerArgs& a, int slot, 
   const int K = P.F, lane = threadIdx.x & 63, wave = threadIdx.x >> 6, ra = lane >> 3, j = lane & 7;
   const int C = K / 32;
   const int row = rb * 64 + wave * 16 + ra;
-  route_ids(a, r, true);      // with the weights: this block may combine tiles at the end
-  route_weights(a, r);
+  get_route(a, r, true);      // with the weights: this block may combine tiles at the end
   const int e = r.sel_i[slot];
   const int idx = a.gemv_ids ? a.gemv_ids[slot] : e;
   const bool valid = (unsigned)idx < (unsigned)P.n_records && (unsigned)e < (unsigned)a.E;
@@ -563,7 +652,7 @@ __device__ __forceinline__ void routed_down_block(const LayerArgs& a, int slot, 
       }
     }
   }
-  wait_set(a.slot_h[slot], blockIdx.x, a.status);
+  wait_set(slot_set(a, slot), blockIdx.x, a.status);
   stage_published(a.h_routed + (int64_t)slot * K, K, st);
   __syncthreads();
   float yA = 0.f, yB = 0.f;
@@ -596,55 +685,129 @@ __device__ __forceinline__ void routed_down_block(const LayerArgs& a, int slot, 
   tile_epilogue<XT>(a, rb * 4, 4, r, lastf, true);
 }
 
+// ------------------------------------------------------------------------------------------------
+// launch: the layers of one launch one after the other in the grid, each laid out as above
+// ------------------------------------------------------------------------------------------------
+constexpr int kMaxStackLayers = 32;
+
+struct StackLayer {           // what differs between the layers of a launch
+  const int8_t* rw;
+  const float* rs;
+  const float* gamma;
+  const char* routed_base;
+  const char* shared_base;
+  int32_t* ids_out;
+  float* weights_out;
+  float* logits_out;
+};
+
+struct WsLayout {
+  size_t tiles, logits, route, h_routed, h_shared, y_routed, y_shared, x_next, total;
+};
+
+struct StackArgs {
+  StackLayer layer[kMaxStackLayers];
+  LayerArgs base;             // fields common to all layers (per-layer ones are set by each block)
+  char* ws;                   // layer l's region at ws + l * w.total
+  WsLayout w;
+  const void* x_in;
+  void* out;
+  int32_t n_layers, per_layer_blocks;
+};
+
+__device__ __forceinline__ SyncSet layer_set(uint32_t* sync, int line, int n_sub, int n_flags, uint32_t total) {
+  return SyncSet{sync + line * kLW, n_sub, n_flags, total};
+}
+
 template <int NBW, typename XT, bool SB_BF16>
-__global__ __launch_bounds__(kThreads) void decode_layer_kernel(LayerArgs a) {
+__global__ __launch_bounds__(kThreads) void decode_stack_kernel(const StackArgs sa) {
   extern __shared__ __align__(16) uint32_t lds[];
   __shared__ NormLds nl;
   __shared__ RouteLds r;
   __shared__ uint32_t lastf[4];
+  const int l = blockIdx.x / sa.per_layer_blocks;
+  int b = blockIdx.x % sa.per_layer_blocks;
+  // this block's layer
+  LayerArgs a = sa.base;
+  const StackLayer& L = sa.layer[l];
+  a.rw = L.rw;
+  a.rs = L.rs;
+  a.gamma = L.gamma;
+  a.routed.base = L.routed_base;
+  a.shared.base = L.shared_base;
+  a.ids_out = L.ids_out;
+  a.weights_out = L.weights_out;
+  a.logits_out = L.logits_out;
+  char* ws = sa.ws + (int64_t)l * sa.w.total;
+  a.x = l == 0 ? sa.x_in : static_cast<const void*>(ws - sa.w.total + sa.w.x_next);
+  a.x_f32 = l > 0;
+  a.out = l == sa.n_layers - 1 ? sa.out : static_cast<void*>(ws + sa.w.x_next);
+  a.out_f32 = l < sa.n_layers - 1;
+  a.last_layer = l == sa.n_layers - 1;
+  a.status = reinterpret_cast<uint32_t*>(sa.ws);
+  a.sync_base = reinterpret_cast<uint32_t*>(sa.ws);
+  a.layer_words = (int64_t)(sa.w.total / 4);
+  a.n_layers = sa.n_layers;
+  uint32_t* sync = reinterpret_cast<uint32_t*>(ws);
+  int line = 1;
+  a.route = layer_set(sync, line, kRouteSub, kRouteFlags, (uint32_t)a.nR);
+  line += kRouteSub + 1 + kRouteFlags;
+  a.shared_h = layer_set(sync, line, kSharedSub, kSharedFlags, (uint32_t)a.nSG);
+  line += kSharedSub + 1 + kSharedFlags;
+  const int tiles_line = line;
+  a.tiles_done = layer_set(sync, line, kTilesSub, a.last_layer ? 0 : kXFlags, (uint32_t)(a.d / 16));
+  line += kTilesSub + 1 + kXFlags;
+  a.slot_base = sync + line * kLW;
+  a.prev_x = l > 0 ? layer_set(sync - a.layer_words, tiles_line, kTilesSub, kXFlags, (uint32_t)(a.d / 16))
+                   : SyncSet{nullptr, 1, 0, 0u};
+  a.tiles = reinterpret_cast<uint32_t*>(ws + sa.w.tiles);
+  a.logits = reinterpret_cast<float*>(ws + sa.w.logits);
+  a.route_ids_ws = reinterpret_cast<int32_t*>(ws + sa.w.route);
+  a.route_w_ws = reinterpret_cast<float*>(ws + sa.w.route) + kLayerMaxK;
+  a.h_routed = reinterpret_cast<float*>(ws + sa.w.h_routed);
+  a.h_shared = reinterpret_cast<float*>(ws + sa.w.h_shared);
+  a.y_routed = reinterpret_cast<float*>(ws + sa.w.y_routed);
+  a.y_shared = reinterpret_cast<float*>(ws + sa.w.y_shared);
   float* xg = reinterpret_cast<float*>(lds);                       // [d]
   uint32_t* stage_base = lds + a.d;                                 // staging area
-  int b = blockIdx.x;
   // staging area: [nhg][kHgStride] words then [nhg] float4; sized by the block's own K
   auto stage_for = [&](int K) {
     const int nhg = K / 32;
     return Stage{stage_base, reinterpret_cast<float4*>(stage_base + nhg * kHgStride)};
   };
+  // Issue priority between the wavefronts sharing a SIMD: the router and the routed experts are on the
+  // layer's critical path, the shared expert has slack (its result is needed only by the combine).
   if (b < a.nR) {
+    __builtin_amdgcn_s_setprio(3);
     router_block<XT>(a, b, xg, nl);
     return;
   }
   b -= a.nR;
   if (b < a.nSG) {
     // the shared expert needs only x: code words first, then the norm while they are in flight
-    __builtin_amdgcn_s_sleep(40);   // about 1 us: let the router blocks' first loads go ahead
+    if (!a.prev_x.base) __builtin_amdgcn_s_sleep(40);   // about 1 us: let the router's first loads go ahead
     GuRegs<NBW, SB_BF16> g;
     gu_load<NBW, SB_BF16>(a, a.shared, 0, true, b, g);
+    if (a.prev_x.base) wait_set(a.prev_x, blockIdx.x, a.status);
     const float rinv = norm_to_lds<XT>(a, xg, nl);
     gu_finish<NBW, XT, SB_BF16>(a, g, true, b, rinv, a.h_shared, a.shared_h, a.nSG, xg, stage_for(a.d));
     return;
   }
   b -= a.nSG;
   if (b < a.nRG) {
+    __builtin_amdgcn_s_setprio(2);
     const int per = a.routed.F / 8, slot = b / per, tile = b % per;
-    const bool designated = b == 0 && (a.ids_out || a.weights_out);
     // the norm needs only x: done while the router finishes
+    if (a.prev_x.base) wait_set(a.prev_x, blockIdx.x, a.status);
     const float rinv = norm_to_lds<XT>(a, xg, nl);
-    route_ids(a, r, designated);
-    if (designated) {
-      route_weights(a, r);
-      if ((int)threadIdx.x < a.k) {
-        if (a.ids_out) a.ids_out[threadIdx.x] = r.sel_i[threadIdx.x];
-        if (a.weights_out) a.weights_out[threadIdx.x] = r.w[threadIdx.x];
-      }
-    }
+    get_route(a, r, false);
     const int e = r.sel_i[slot];
     const int idx = a.gemv_ids ? a.gemv_ids[slot] : e;
     const bool valid = (unsigned)idx < (unsigned)a.routed.n_records && (unsigned)e < (unsigned)a.E;
     GuRegs<NBW, SB_BF16> g;
     gu_load<NBW, SB_BF16>(a, a.routed, idx, valid, tile, g);
     gu_finish<NBW, XT, SB_BF16>(a, g, valid, tile, rinv, a.h_routed + (int64_t)slot * a.routed.F,
-                                a.slot_h[slot], per, xg, stage_for(a.d));
+                                slot_set(a, slot), per, xg, stage_for(a.d));
     return;
   }
   b -= a.nRG;
@@ -653,25 +816,24 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(LayerArgs a) {
     return;
   }
   b -= a.nSD;
+  __builtin_amdgcn_s_setprio(2);
   const int per = a.d / 64, slot = b / per, rb = b % per;
   routed_down_block<NBW, XT, SB_BF16>(a, slot, rb, stage_for(a.routed.F), r, lastf);
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-struct WsLayout {
-  size_t tiles, logits, h_routed, h_shared, y_routed, y_shared, total;
-};
-
 WsLayout ws_layout(int d, int E, int k, int F, int S) {
   WsLayout w;
   size_t o = (size_t)(kLinesFixed + k * kLinesPerSlot) * kLW * 4;
   w.tiles = o;      o += align256((size_t)(d / 16) * kTileStride * 4);
   w.logits = o;     o += align256((size_t)E * 4);
+  w.route = o;      o += align256((size_t)kLayerMaxK * 8);
   w.h_routed = o;   o += align256((size_t)k * F * 4);
   w.h_shared = o;   o += align256((size_t)(S > 0 ? S : 1) * 4);
   w.y_routed = o;   o += align256((size_t)k * d * 4);
   w.y_shared = o;   o += align256((size_t)d * 4);
+  w.x_next = o;     o += align256((size_t)d * 4);
   w.total = o;
   return w;
 }
@@ -686,6 +848,89 @@ bool layer_pool(const moe_q4_pool* p, LayerPool* out, const char** why) {
   *out = LayerPool{static_cast<const char*>(p->base_dev), (int64_t)p->record_bytes, p->n_records, p->F,
                    (int64_t)o.gate_up_q, (int64_t)o.gate_up_sb, (int64_t)o.down_q, (int64_t)o.down_sb};
   return true;
+}
+
+// Checks shared by the one-layer and the stacked entry points; fills the common fields and the launch.
+moe_status prepare_launch(const char* who, const void* x_dev, moe_dtype x_dtype, float eps, bool any_gamma,
+                          int32_t residual, int32_t E, int32_t k, const moe_q4_pool* routed, const moe_q4_pool* shared,
+                          moe_act act, void* out_dev, void* workspace_dev, size_t workspace_bytes, int n_layers,
+                          StackArgs* sa, int* nbw, size_t* lds) {
+  if (!x_dev || !routed || !out_dev || !workspace_dev) return fail(MOE_ERR_INVALID_ARG, "%s: NULL pointer", who);
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "%s: bad x_dtype", who);
+  if (act != MOE_ACT_GELU_TANH && act != MOE_ACT_SILU) return fail(MOE_ERR_INVALID_ARG, "%s: bad act", who);
+  if (any_gamma && !(eps >= 0.f)) return fail(MOE_ERR_INVALID_ARG, "%s: eps must be >= 0", who);
+  const char* why = nullptr;
+  LayerArgs& a = sa->base;
+  a = LayerArgs{};
+  if (!layer_pool(routed, &a.routed, &why)) return fail(MOE_ERR_INVALID_ARG, "%s: routed %s", who, why);
+  const int d = routed->d;
+  if (shared) {
+    if (!layer_pool(shared, &a.shared, &why)) return fail(MOE_ERR_INVALID_ARG, "%s: shared %s", who, why);
+    if (shared->d != d) return fail(MOE_ERR_INVALID_ARG, "%s: routed d=%d != shared d=%d", who, d, shared->d);
+    if (shared->sb_dtype != routed->sb_dtype) return fail(MOE_ERR_UNSUPPORTED, "%s: scale/bias dtypes differ", who);
+  }
+  if (d > kLayerMaxD || routed->F > kLayerMaxF || (shared && shared->F > kLayerMaxD))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: d=%d F=%d S=%d (need d, S <= %d, F <= %d)", who, d, routed->F,
+                shared ? shared->F : 0, kLayerMaxD, kLayerMaxF);
+  if (E < 1 || E > kLayerMaxE || k < 1 || k > kLayerMaxK || k > E)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: E=%d k=%d (need 1 <= k <= min(E, 32), E <= %d)", who, E, k, kLayerMaxE);
+  if (!aligned(x_dev, 16)) return fail(MOE_ERR_INVALID_ARG, "%s: x must be 16-byte aligned", who);
+  const WsLayout w = ws_layout(d, E, k, routed->F, shared ? shared->F : 0);
+  if (workspace_bytes < w.total * n_layers)
+    return fail(MOE_ERR_INVALID_ARG, "%s: workspace %zu bytes < %zu", who, workspace_bytes, w.total * n_layers);
+  if (!aligned(workspace_dev, 256)) return fail(MOE_ERR_INVALID_ARG, "%s: workspace not 256-byte aligned", who);
+  a.eps = eps;
+  a.residual = residual != 0;
+  a.E = E;
+  a.k = k;
+  a.d = d;
+  a.act = act;
+  a.has_shared = shared != nullptr;
+  a.sync_lines = kLinesFixed + k * kLinesPerSlot;
+  a.nR = (E + 3) / 4;
+  a.nSG = shared ? shared->F / 8 : 0;
+  a.nRG = k * (routed->F / 8);
+  a.nSD = shared ? d / 16 : 0;
+  a.nRD = k * (d / 64);
+  sa->ws = static_cast<char*>(workspace_dev);
+  sa->w = w;
+  sa->x_in = x_dev;
+  sa->out = out_dev;
+  sa->n_layers = n_layers;
+  sa->per_layer_blocks = a.nR + a.nSG + a.nRG + a.nSD + a.nRD;
+  // chunk iterations per lane: gate/up rows (K = d) and shared down rows (K = S) split over 4 waves,
+  // routed down rows (K = F) whole per wave
+  const int it_gu = (iterations(d) + 3) / 4, it_sd = shared ? (iterations(shared->F) + 3) / 4 : 1;
+  const int it_rd = iterations(routed->F);
+  int n = it_gu > it_sd ? it_gu : it_sd;
+  n = n > it_rd ? n : it_rd;
+  if (n > 4) return fail(MOE_ERR_UNSUPPORTED, "%s: rows too long for the single-launch layer", who);
+  *nbw = n;
+  int kmax = d > routed->F ? d : routed->F;
+  if (shared && shared->F > kmax) kmax = shared->F;
+  *lds = (size_t)d * 4 + (size_t)(kmax / 32) * (kHgStride * 4 + 16);
+  return MOE_OK;
+}
+
+moe_status launch(const StackArgs& sa, moe_dtype x_dtype, bool sb16, int nbw, size_t lds, hipStream_t s,
+                  const char* who) {
+  const dim3 grid(sa.per_layer_blocks * sa.n_layers);
+  if (grid.x == 0) return MOE_OK;
+  return dispatch_nbw(nbw, [&](auto nb) {
+    constexpr int N = decltype(nb)::value;
+    if constexpr (N <= 4) {
+      if (x_dtype == MOE_BF16) {
+        if (sb16) hipLaunchKernelGGL((decode_stack_kernel<N, uint16_t, true>), grid, dim3(kThreads), lds, s, sa);
+        else hipLaunchKernelGGL((decode_stack_kernel<N, uint16_t, false>), grid, dim3(kThreads), lds, s, sa);
+      } else {
+        if (sb16) hipLaunchKernelGGL((decode_stack_kernel<N, float, true>), grid, dim3(kThreads), lds, s, sa);
+        else hipLaunchKernelGGL((decode_stack_kernel<N, float, false>), grid, dim3(kThreads), lds, s, sa);
+      }
+      return check_launch(who);
+    } else {
+      return fail(MOE_ERR_UNSUPPORTED, "%s: rows too long", who);
+    }
+  });
 }
 
 }  // namespace
@@ -703,6 +948,12 @@ extern "C" size_t moe_decode_layer_workspace_bytes(int32_t d, int32_t E, int32_t
   return ws_layout(d, E, k, F, S).total;
 }
 
+extern "C" size_t moe_decode_stack_workspace_bytes(int32_t n_layers, int32_t d, int32_t E, int32_t k, int32_t F,
+                                                   int32_t S) {
+  if (n_layers < 1 || n_layers > kMaxStackLayers) return 0;
+  return moe_decode_layer_workspace_bytes(d, E, k, F, S) * (size_t)n_layers;
+}
+
 extern "C" moe_status moe_decode_layer(const void* x_dev, moe_dtype x_dtype, const float* gamma_dev, float eps,
                                        int32_t residual, const int8_t* router_w_dev, const float* router_scale_dev,
                                        int32_t E, int32_t k, const int32_t* forced_ids_dev, const moe_q4_pool* routed,
@@ -710,100 +961,52 @@ extern "C" moe_status moe_decode_layer(const void* x_dev, moe_dtype x_dtype, con
                                        int32_t* ids_dev, float* weights_dev, float* logits_dev, void* out_dev,
                                        void* workspace_dev, size_t workspace_bytes, void* stream) {
   const char* who = "moe_decode_layer";
-  if (!x_dev || !router_w_dev || !router_scale_dev || !routed || !out_dev || !workspace_dev)
-    return fail(MOE_ERR_INVALID_ARG, "%s: NULL pointer", who);
-  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "%s: bad x_dtype", who);
-  if (act != MOE_ACT_GELU_TANH && act != MOE_ACT_SILU) return fail(MOE_ERR_INVALID_ARG, "%s: bad act", who);
-  if (gamma_dev && !(eps >= 0.f)) return fail(MOE_ERR_INVALID_ARG, "%s: eps must be >= 0", who);
-  const char* why = nullptr;
-  LayerArgs a{};
-  if (!layer_pool(routed, &a.routed, &why)) return fail(MOE_ERR_INVALID_ARG, "%s: routed %s", who, why);
-  const int d = routed->d;
-  if (shared) {
-    if (!layer_pool(shared, &a.shared, &why)) return fail(MOE_ERR_INVALID_ARG, "%s: shared %s", who, why);
-    if (shared->d != d) return fail(MOE_ERR_INVALID_ARG, "%s: routed d=%d != shared d=%d", who, d, shared->d);
-    if (shared->sb_dtype != routed->sb_dtype) return fail(MOE_ERR_UNSUPPORTED, "%s: scale/bias dtypes differ", who);
+  if (!router_w_dev || !router_scale_dev) return fail(MOE_ERR_INVALID_ARG, "%s: NULL pointer", who);
+  if (!aligned(router_w_dev, 16) || (gamma_dev && !aligned(gamma_dev, 16)))
+    return fail(MOE_ERR_INVALID_ARG, "%s: router weights and gamma must be 16-byte aligned", who);
+  StackArgs sa{};
+  int nbw = 0;
+  size_t lds = 0;
+  moe_status st = prepare_launch(who, x_dev, x_dtype, eps, gamma_dev != nullptr, residual, E, k, routed, shared, act,
+                                 out_dev, workspace_dev, workspace_bytes, 1, &sa, &nbw, &lds);
+  if (st != MOE_OK) return st;
+  sa.base.forced = forced_ids_dev;
+  sa.base.gemv_ids = gemv_ids_dev;
+  sa.layer[0] = StackLayer{router_w_dev, router_scale_dev, gamma_dev, static_cast<const char*>(routed->base_dev),
+                           shared ? static_cast<const char*>(shared->base_dev) : nullptr, ids_dev, weights_dev,
+                           logits_dev};
+  return launch(sa, x_dtype, routed->sb_dtype == MOE_BF16, nbw, lds, as_stream(stream), who);
+}
+
+extern "C" moe_status moe_decode_stack(const moe_stack_layer* layers_host, int32_t n_layers, const void* x_dev,
+                                       moe_dtype x_dtype, float eps, int32_t residual, int32_t E, int32_t k,
+                                       const moe_q4_pool* routed, const moe_q4_pool* shared, moe_act act,
+                                       void* out_dev, void* workspace_dev, size_t workspace_bytes, void* stream) {
+  const char* who = "moe_decode_stack";
+  if (!layers_host) return fail(MOE_ERR_INVALID_ARG, "%s: layers is NULL", who);
+  if (n_layers < 1 || n_layers > kMaxStackLayers)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: n_layers=%d (1..%d)", who, n_layers, kMaxStackLayers);
+  if (x_dev == out_dev) return fail(MOE_ERR_INVALID_ARG, "%s: out must not alias x", who);
+  bool any_gamma = false;
+  for (int l = 0; l < n_layers; ++l) {
+    const moe_stack_layer& L = layers_host[l];
+    if (!L.router_w_dev || !L.router_scale_dev || !L.routed_base_dev || (shared && !L.shared_base_dev))
+      return fail(MOE_ERR_INVALID_ARG, "%s: layer %d: NULL pointer", who, l);
+    if (!aligned(L.router_w_dev, 16) || (L.gamma_dev && !aligned(L.gamma_dev, 16)) || !aligned(L.routed_base_dev, 256) ||
+        (shared && !aligned(L.shared_base_dev, 256)))
+      return fail(MOE_ERR_INVALID_ARG, "%s: layer %d: misaligned pointer", who, l);
+    any_gamma |= L.gamma_dev != nullptr;
   }
-  if (d > kLayerMaxD || routed->F > kLayerMaxF || (shared && shared->F > kLayerMaxD))
-    return fail(MOE_ERR_UNSUPPORTED, "%s: d=%d F=%d S=%d (need d, S <= %d, F <= %d)", who, d, routed->F,
-                shared ? shared->F : 0, kLayerMaxD, kLayerMaxF);
-  if (E < 1 || E > kLayerMaxE || k < 1 || k > kLayerMaxK || k > E)
-    return fail(MOE_ERR_UNSUPPORTED, "%s: E=%d k=%d (need 1 <= k <= min(E, 32), E <= %d)", who, E, k, kLayerMaxE);
-  if (!aligned(x_dev, 16) || !aligned(router_w_dev, 16) || (gamma_dev && !aligned(gamma_dev, 16)))
-    return fail(MOE_ERR_INVALID_ARG, "%s: x, router weights and gamma must be 16-byte aligned", who);
-  const WsLayout w = ws_layout(d, E, k, routed->F, shared ? shared->F : 0);
-  if (workspace_bytes < w.total) return fail(MOE_ERR_INVALID_ARG, "%s: workspace %zu bytes < %zu", who, workspace_bytes, w.total);
-  if (!aligned(workspace_dev, 256)) return fail(MOE_ERR_INVALID_ARG, "%s: workspace not 256-byte aligned", who);
-  char* ws = static_cast<char*>(workspace_dev);
-  a.x = x_dev;
-  a.gamma = gamma_dev;
-  a.eps = eps;
-  a.residual = residual != 0;
-  a.rw = router_w_dev;
-  a.rs = router_scale_dev;
-  a.E = E;
-  a.k = k;
-  a.d = d;
-  a.act = act;
-  a.forced = forced_ids_dev;
-  a.gemv_ids = gemv_ids_dev;
-  a.has_shared = shared != nullptr;
-  a.ids_out = ids_dev;
-  a.weights_out = weights_dev;
-  a.logits_out = logits_dev;
-  a.out = out_dev;
-  uint32_t* sync = reinterpret_cast<uint32_t*>(ws);
-  a.status = sync;
-  a.sync_base = sync;
-  a.sync_lines = kLinesFixed + k * kLinesPerSlot;
-  int line = 1;
-  a.route = SyncSet{sync + line * kLW, kRouteSub, kRouteFlags, (uint32_t)((E + 3) / 4)};
-  line += kRouteSub + 1 + kRouteFlags;
-  a.shared_h = SyncSet{sync + line * kLW, kSharedSub, kSharedFlags, (uint32_t)(shared ? shared->F / 8 : 0)};
-  line += kSharedSub + 1 + kSharedFlags;
-  a.tiles_done = SyncSet{sync + line * kLW, kTilesSub, 0, (uint32_t)(d / 16)};
-  line += kTilesSub + 1;
-  for (int i = 0; i < k; ++i) {
-    a.slot_h[i] = SyncSet{sync + line * kLW, kSlotSub, kSlotFlags, (uint32_t)(routed->F / 8)};
-    line += kLinesPerSlot;
+  StackArgs sa{};
+  int nbw = 0;
+  size_t lds = 0;
+  moe_status st = prepare_launch(who, x_dev, x_dtype, eps, any_gamma, residual, E, k, routed, shared, act, out_dev,
+                                 workspace_dev, workspace_bytes, n_layers, &sa, &nbw, &lds);
+  if (st != MOE_OK) return st;
+  for (int l = 0; l < n_layers; ++l) {
+    const moe_stack_layer& L = layers_host[l];
+    sa.layer[l] = StackLayer{L.router_w_dev, L.router_scale_dev, L.gamma_dev, static_cast<const char*>(L.routed_base_dev),
+                             static_cast<const char*>(L.shared_base_dev), L.ids_dev, L.weights_dev, L.logits_dev};
   }
-  a.tiles = reinterpret_cast<uint32_t*>(ws + w.tiles);
-  a.logits = reinterpret_cast<float*>(ws + w.logits);
-  a.h_routed = reinterpret_cast<float*>(ws + w.h_routed);
-  a.h_shared = reinterpret_cast<float*>(ws + w.h_shared);
-  a.y_routed = reinterpret_cast<float*>(ws + w.y_routed);
-  a.y_shared = reinterpret_cast<float*>(ws + w.y_shared);
-  a.nR = (E + 3) / 4;
-  a.nSG = shared ? shared->F / 8 : 0;
-  a.nRG = k * (routed->F / 8);
-  a.nSD = shared ? d / 16 : 0;
-  a.nRD = k * (d / 64);
-  // chunk iterations per lane: gate/up rows (K = d) and shared down rows (K = S) split over 4 waves,
-  // routed down rows (K = F) whole per wave
-  const int it_gu = (iterations(d) + 3) / 4, it_sd = shared ? (iterations(shared->F) + 3) / 4 : 1;
-  const int it_rd = iterations(routed->F);
-  int nbw = it_gu > it_sd ? it_gu : it_sd;
-  nbw = nbw > it_rd ? nbw : it_rd;
-  if (nbw > 4) return fail(MOE_ERR_UNSUPPORTED, "%s: rows too long for the single-launch layer", who);
-  int kmax = d > routed->F ? d : routed->F;
-  if (shared && shared->F > kmax) kmax = shared->F;
-  const size_t lds = (size_t)d * 4 + (size_t)(kmax / 32) * (kHgStride * 4 + 16);
-  const dim3 grid(a.nR + a.nSG + a.nRG + a.nSD + a.nRD);
-  const bool sb16 = routed->sb_dtype == MOE_BF16;
-  hipStream_t s = as_stream(stream);
-  return dispatch_nbw(nbw, [&](auto nb) {
-    constexpr int N = decltype(nb)::value;
-    if constexpr (N <= 4) {
-      if (x_dtype == MOE_BF16) {
-        if (sb16) hipLaunchKernelGGL((decode_layer_kernel<N, uint16_t, true>), grid, dim3(kThreads), lds, s, a);
-        else hipLaunchKernelGGL((decode_layer_kernel<N, uint16_t, false>), grid, dim3(kThreads), lds, s, a);
-      } else {
-        if (sb16) hipLaunchKernelGGL((decode_layer_kernel<N, float, true>), grid, dim3(kThreads), lds, s, a);
-        else hipLaunchKernelGGL((decode_layer_kernel<N, float, false>), grid, dim3(kThreads), lds, s, a);
-      }
-      return check_launch("moe_decode_layer");
-    } else {
-      return fail(MOE_ERR_UNSUPPORTED, "moe_decode_layer: rows too long");
-    }
-  });
+  return launch(sa, x_dtype, routed->sb_dtype == MOE_BF16, nbw, lds, as_stream(stream), who);
 }

@@ -77,9 +77,10 @@ def layer_kernel_fits(shape: Shape, T: int) -> bool:
 class MoEDecoder:
     """Runs T tokens through a stack of MoE layers (T = 1 is decode).
 
-    Three ways to run a layer, all through the library:
-      "layer"     one launch per layer (moe_decode_layer): norm, router, experts and combine together;
-                  the default for T = 1 when the shape is within that kernel's limits
+    Four ways to run the layers, all through the library:
+      "layer"     moe_decode_layer per layer: two launches (router with the shared gate/up, then the routed
+                  experts, shared down and combine); the default for T = 1 within that kernel's limits
+      "stack"     one launch for the whole step (moe_decode_stack, <= 32 layers); layer() as "layer"
       "fused"     moe_norm_router_topk (RMSNorm inside the router) then q4_expert_gemv_combine (expert
                   GEMVs with the combine + residual in the down launch's tail); the default otherwise
       "separate"  moe_rmsnorm, moe_router_topk, q4_expert_gemv, moe_combine
@@ -89,7 +90,8 @@ class MoEDecoder:
         self.shape, self.layers, self.T = shape, layers, T
         if mode is None:
             mode = "layer" if layer_kernel_fits(shape, T) else "fused"
-        if mode not in ("layer", "fused", "separate") or (mode == "layer" and not layer_kernel_fits(shape, T)):
+        if mode not in ("stack", "layer", "fused", "separate") or \
+                (mode in ("stack", "layer") and not layer_kernel_fits(shape, T)) or (mode == "stack" and len(layers) > 32):
             raise ValueError(f"mode {mode!r} not available for this shape / batch")
         self.mode = mode
         s = shape
@@ -120,13 +122,22 @@ class MoEDecoder:
         self.layer_ws_bytes = q.moe_decode_layer_workspace_bytes(s.d, s.n_experts, s.k, s.F,
                                                                  s.S if layers and layers[0].shared is not None else 0)
         self.layer_ws = torch.zeros(max(self.layer_ws_bytes, 256), dtype=torch.uint8, device=device)
+        if mode == "stack":
+            S_ = s.S if layers and layers[0].shared is not None else 0
+            self.stack_ws_bytes = q.moe_decode_stack_workspace_bytes(L, s.d, s.n_experts, s.k, s.F, S_)
+            self.stack_ws = torch.zeros(self.stack_ws_bytes, dtype=torch.uint8, device=device)
+            self.stack_descs = q.stack_layers([
+                {"router_w_dev": W.router_w, "router_scale_dev": W.router_s,
+                 "gamma_dev": W.gamma if s.rms_norm else None, "routed_base_dev": W.pool, "shared_base_dev": W.shared,
+                 "ids_dev": self.ids_all[l], "weights_dev": self.weights_all[l], "logits_dev": self.logits_all[l]}
+                for l, W in enumerate(layers)])
         self.graph = None
 
     # one layer: x_in -> x_out (both [T][d] in the activation dtype)
     def layer(self, l: int, x_in: torch.Tensor, x_out: torch.Tensor, forced_ids: Optional[torch.Tensor] = None,
               routed_pool=None, ids: Optional[torch.Tensor] = None, stream=None) -> None:
         s, L, T = self.shape, self.layers[l], self.T
-        if self.mode == "layer":
+        if self.mode in ("stack", "layer"):
             self._layer_single_launch(l, x_in, x_out, forced_ids, routed_pool, ids, stream)
             return
         if self.mode == "fused":
@@ -168,8 +179,15 @@ class MoEDecoder:
                                  s.x_dtype, x_out, s.x_dtype, self.fused_ws, self.fused_ws_bytes, stream)
 
     def step(self, x: torch.Tensor, out: torch.Tensor, stream=None) -> None:
-        """Run every layer: x -> out, ping-ponging between `out` and an internal buffer."""
+        """Run every layer: x -> out (one launch in "stack" mode, else layer by layer through an internal
+        buffer)."""
         n = len(self.layers)
+        if self.mode == "stack":
+            s = self.shape
+            q.moe_decode_stack(self.stack_descs, n, x, s.x_dtype, s.eps, s.rms_norm, s.n_experts, s.k,
+                               self.routed_pools[0], self.shared_pools[0], s.act, out, self.stack_ws,
+                               self.stack_ws_bytes, stream)
+            return
         if not hasattr(self, "_tmp"):
             self._tmp = torch.empty_like(out)
         bufs = [self._tmp, out] if n % 2 == 0 else [out, self._tmp]

@@ -39,6 +39,11 @@ class moe_q4_pool(ctypes.Structure):
                 ("sb_dtype", ctypes.c_int)]
 
 
+class moe_stack_layer(ctypes.Structure):
+    _fields_ = [("router_w_dev", _vp), ("router_scale_dev", _vp), ("gamma_dev", _vp), ("routed_base_dev", _vp),
+                ("shared_base_dev", _vp), ("ids_dev", _vp), ("weights_dev", _vp), ("logits_dev", _vp)]
+
+
 class MoeError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -84,6 +89,12 @@ _c = {
                              [_vp, ctypes.c_int, _vp, ctypes.c_float, _i32, _vp, _vp, _i32, _i32, _vp,
                               ctypes.POINTER(moe_q4_pool), _vp, ctypes.POINTER(moe_q4_pool), ctypes.c_int, _vp, _vp,
                               _vp, _vp, _vp, _sz, _vp]),
+    "moe_decode_stack_workspace_bytes": _sig("moe_decode_stack_workspace_bytes", _sz,
+                                             [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "moe_decode_stack": _sig("moe_decode_stack", _st,
+                             [ctypes.POINTER(moe_stack_layer), _i32, _vp, ctypes.c_int, ctypes.c_float, _i32, _i32, _i32,
+                              ctypes.POINTER(moe_q4_pool), ctypes.POINTER(moe_q4_pool), ctypes.c_int, _vp, _vp, _sz,
+                              _vp]),
     "moe_combine": _sig("moe_combine", _st, [_vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32, _vp, ctypes.c_int, _vp]),
     "moe_expert_cache_create": _sig("moe_expert_cache_create", _st, [_i32, _i32, _i32, _sz, ctypes.POINTER(_vp),
                                                                      ctypes.POINTER(_vp), _u32, ctypes.POINTER(_vp)]),
@@ -235,6 +246,26 @@ def moe_decode_layer(x, x_dtype, gamma, eps, residual, router_w, router_scale, E
     _check(_c["moe_decode_layer"](_p(x), x_dtype, _p(gamma), eps, int(residual), _p(router_w), _p(router_scale), E, k,
                                   _p(forced_ids), _pp(routed), _p(gemv_ids), _pp(shared), act, _p(ids), _p(weights),
                                   _p(logits), _p(out), _p(workspace), workspace_bytes, _s(stream)), "moe_decode_layer")
+
+
+def moe_decode_stack_workspace_bytes(n_layers, d, E, k, F, S) -> int:
+    return _c["moe_decode_stack_workspace_bytes"](n_layers, d, E, k, F, S)
+
+
+def stack_layers(descs) -> ctypes.Array:
+    """ctypes array of moe_stack_layer from dicts with the field names (tensors or ints or None)."""
+    arr = (moe_stack_layer * len(descs))()
+    for i, d in enumerate(descs):
+        for name, _ in moe_stack_layer._fields_:
+            setattr(arr[i], name, _p(d.get(name)))
+    return arr
+
+
+def moe_decode_stack(layers, n_layers, x, x_dtype, eps, residual, E, k, routed, shared, act, out, workspace,
+                     workspace_bytes, stream=None) -> None:
+    """`layers`: a ctypes array from stack_layers()."""
+    _check(_c["moe_decode_stack"](layers, n_layers, _p(x), x_dtype, eps, int(residual), E, k, _pp(routed), _pp(shared),
+                                  act, _p(out), _p(workspace), workspace_bytes, _s(stream)), "moe_decode_stack")
 
 
 def moe_combine(y_routed, weights, y_shared, residual, residual_dtype, T, k, d, out, out_dtype, stream=None) -> None:

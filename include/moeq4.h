@@ -259,6 +259,40 @@ moe_status moe_decode_layer(const void* x_dev, moe_dtype x_dtype, const float* g
                             void* stream);
 
 /* ---------------------------------------------------------------------------------------------------
+ * moe_decode_stack — n_layers consecutive layers of moe_decode_layer for one token in a single launch
+ * (the stacked decode: RMSNorm and the MoE block per layer, residual stream between them).  Layer l + 1's
+ * blocks load their router rows and shared-expert weights while layer l finishes, then wait for layer l's
+ * output; intermediate activations stay in the workspace as fp32 holding values already rounded to
+ * x_dtype, so the result equals n_layers chained moe_decode_layer calls bit for bit.
+ * layers_host: host array of n_layers descriptors (copied into the launch; the device buffers they point to
+ * must stay valid until the work completes).  routed / shared: the pools' shape (d, F, record_bytes,
+ * n_records, sb_dtype; base_dev is ignored, every layer gives its own); shared may be NULL.
+ * x_dev: x_dtype [d] input of layer 0; out_dev: x_dtype [d] output of the last layer (must not alias x_dev).
+ * Per layer: router as moe_router_topk; gamma_dev fp32 [d] or NULL (no norm); ids/weights/logits optional
+ * outputs.  Limits as moe_decode_layer, and 1 <= n_layers <= 32.
+ * Workspace: moe_decode_stack_workspace_bytes(...) bytes, 256-byte aligned, ZERO before first use; the
+ * region of layer l is moe_decode_layer_workspace_bytes(d, E, k, F, S) bytes at offset l times that size,
+ * laid out as moe_decode_layer's (word 0 of the whole workspace is the sticky error flag); every completed
+ * call leaves the synchronisation bytes of every region zero again.
+ * ------------------------------------------------------------------------------------------------- */
+typedef struct {
+  const int8_t* router_w_dev;      /* int8 [E][d] */
+  const float* router_scale_dev;   /* fp32 [E] */
+  const float* gamma_dev;          /* fp32 [d] or NULL */
+  const void* routed_base_dev;     /* this layer's routed pool (n_records records) */
+  const void* shared_base_dev;     /* this layer's shared expert record, or NULL without shared pool */
+  int32_t* ids_dev;                /* int32 [k] or NULL */
+  float* weights_dev;              /* fp32 [k] or NULL */
+  float* logits_dev;               /* fp32 [E] or NULL */
+} moe_stack_layer;
+
+size_t moe_decode_stack_workspace_bytes(int32_t n_layers, int32_t d, int32_t E, int32_t k, int32_t F, int32_t S);
+moe_status moe_decode_stack(const moe_stack_layer* layers_host, int32_t n_layers, const void* x_dev,
+                            moe_dtype x_dtype, float eps, int32_t residual, int32_t E, int32_t k,
+                            const moe_q4_pool* routed, const moe_q4_pool* shared, moe_act act, void* out_dev,
+                            void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------------
  * Expert cache — 16-slot-per-layer least-frequently-used cache of expert records ([DAILY] "Cache
  * d'experts"; [DEVT] "Wat is de belangrijkste architectuurtruuc"; [REMIO] "Mac Gemma 4 26B tient en
  * mémoire..."), fed on demand from slower memory while the shared expert computes ([G26] "Concurrence

@@ -88,6 +88,16 @@ def test_host_validation_errors():
     assert gp(256, 0, 2, 8, 256, 256, 256, None) == q.MOE_ERR_INVALID_ARG             # T = 0
     big = q.pool(256, 61440, 5000, 256, 128, 0)
     assert st(ctypes.byref(big), 256, 2, None, 256, 0, 2, 0, 256, None, 256, 1 << 24, None) == q.MOE_ERR_UNSUPPORTED
+    # stacked layers: 1..32 layers, out must not alias x
+    stk = q.raw("moe_decode_stack")
+    one = q.stack_layers([{"router_w_dev": 256, "router_scale_dev": 256, "routed_base_dev": 256}])
+    assert stk(one, 0, 256, 1, ctypes.c_float(1e-6), 1, 8, 2, ctypes.byref(good), None, 0, 512, 256, 1 << 24,
+               None) == q.MOE_ERR_UNSUPPORTED
+    assert stk(one, 1, 256, 1, ctypes.c_float(1e-6), 1, 8, 2, ctypes.byref(good), None, 0, 256, 256, 1 << 24,
+               None) == q.MOE_ERR_INVALID_ARG
+    assert q.moe_decode_stack_workspace_bytes(33, 256, 8, 2, 128, 128) == 0
+    assert q.moe_decode_stack_workspace_bytes(3, 256, 8, 2, 128, 128) == 3 * q.moe_decode_layer_workspace_bytes(
+        256, 8, 2, 128, 128)
     # fused norm + router: gamma and u are required, eps must be >= 0
     nr = q.raw("moe_norm_router_topk")
     nargs = lambda g, eps, u: (256, 1, g, ctypes.c_float(eps), 1, 64, 256, 256, 8, 2, None, 256, 256, None, u, 256,

@@ -152,3 +152,43 @@ def test_decode_layer_tiny_no_norm_vs_oracle(shared):
         worst = max(worst, H.max_rel_err(H.to_f64(out), ref.out))
     print(f"tiny layer kernel (shared={shared}): max rel err {worst:.3e}")
     assert worst <= TOL
+
+
+def test_decode_stack_equals_chained_layers():
+    """Four d=2816 layers in one moe_decode_stack launch equal four chained moe_decode_layer calls bit for bit
+    (output, and every layer's ids, weights and logits), twice in a row on one workspace; every layer's
+    synchronisation region is back to zero and the error flag clear."""
+    cfg = synth.STACK
+    L = 4
+    devs = [H.device_layer(cfg, l) for l in range(L)]
+    shape = H.shape_of(cfg)
+    rp, sp = _pools(cfg, devs[0], shape)
+    E, k, d = cfg.n_experts, cfg.k, cfg.d
+    ids = torch.full((L, k), -1, dtype=torch.int32, device="cuda")
+    wts = torch.zeros((L, k), dtype=torch.float32, device="cuda")
+    lgs = torch.zeros((L, E), dtype=torch.float32, device="cuda")
+    descs = q.stack_layers([{"router_w_dev": W.router_w, "router_scale_dev": W.router_s, "gamma_dev": W.gamma,
+                             "routed_base_dev": W.pool, "shared_base_dev": W.shared, "ids_dev": ids[l],
+                             "weights_dev": wts[l], "logits_dev": lgs[l]} for l, W in enumerate(devs)])
+    sb = q.moe_decode_stack_workspace_bytes(L, d, E, k, cfg.F, cfg.S)
+    region = q.moe_decode_layer_workspace_bytes(d, E, k, cfg.F, cfg.S)
+    assert sb == L * region
+    ws = torch.zeros(sb, dtype=torch.uint8, device="cuda")
+    lws, lwb = _ws(cfg)
+    for tok in (11, 12):
+        x = H.token_batch(cfg, [tok])[0]
+        out = torch.empty_like(x)
+        q.moe_decode_stack(descs, L, x, q.MOE_BF16, 1e-6, 1, E, k, rp, sp, shape.act, out, ws, sb)
+        xs = x
+        for l, W in enumerate(devs):
+            i1, w1, g1, o1 = _run(cfg, W, shape, xs, lws, lwb, W.gamma, 1)
+            torch.cuda.synchronize()
+            assert torch.equal(i1, ids[l]) and torch.equal(w1, wts[l]) and torch.equal(g1, lgs[l]), f"layer {l}"
+            xs = o1
+        assert torch.equal(xs, out), f"token {tok}"
+        words = ws.view(torch.int32)
+        assert int(words[0].item()) == 0, "a wait inside the stack kernel ran out"
+        n = q.moe_decode_layer_sync_bytes(d, k) // 4
+        for l in range(L):
+            seg = words[l * region // 4: l * region // 4 + n]
+            assert int(seg.abs().sum().item()) == 0, f"layer {l} synchronisation words not reset"
