@@ -55,6 +55,24 @@ def build_stack(cfg, n_layers):
     return shape, layers
 
 
+# HBM traffic of one layer launch from FETCH_SIZE and WRITE_SIZE counter runs, each scaled by what the counter
+# reads for a plain 256 MiB device copy in the same run (profiles/decode_layer_kernel_stack30_decode.md).  It is
+# reported only while the kernel's sources are the ones the counters were taken on.
+LAYER_TRAFFIC_BYTES = 42329670
+LAYER_TRAFFIC_SOURCES = ("bit_quantized_expert_int8_amd/csrc/layer.hip", "bit_quantized_expert_int8_amd/csrc/q4_device.h",
+                         "bit_quantized_expert_int8_amd/csrc/common.h")
+LAYER_TRAFFIC_SHA = "70493af451ee74b6"
+
+
+def layer_traffic():
+    import hashlib
+    h = hashlib.sha256()
+    for p in LAYER_TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return LAYER_TRAFFIC_BYTES if h.hexdigest()[:16] == LAYER_TRAFFIC_SHA else None
+
+
 def record_data_bytes(d: int, F: int) -> int:
     """Bytes of one expert's 4-bit codes and bf16 scale/bias (gate/up [2F][d] and down [d][F], groups of 64)."""
     return 2 * F * (d // 2 + (d // 64) * 4) + d * (F // 2 + (F // 64) * 4)
@@ -309,6 +327,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the batched and streamed measurements")
     ap.add_argument("--stream-tokens", type=int, default=512)
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="also run one plain device-to-device copy of this many MiB (a reference for the HBM "
+                         "traffic counters of a profiled run)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -352,11 +373,17 @@ def main():
     gpu_s = e0.elapsed_time(e1) * 1e-3
     tok_s = args.steps / gpu_s
 
+    if args.calibration_copy_mib:
+        src = torch.empty(args.calibration_copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     dur, launches = time_layer_kernel(dec, xin, args.roofline_reps)
     nbytes = layer_bytes(cfg)
     achieved = nbytes / dur / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": layer_traffic(),
                 "kernel": "decode_layer_kernel (moe_decode_layer: RMSNorm, int8 router + top-8, 8 routed + shared "
                           "4-bit expert FFNs, combine + residual, one launch per layer)",
                 "bytes_per_launch": nbytes, "avg_launch_us": round(dur * 1e6, 3), "launches_timed": launches}

@@ -57,4 +57,55 @@ __device__ __forceinline__ float wave_min(float v) {
   return v;
 }
 
+// Maximum of an unsigned value over the 64 lanes of a wavefront, returned to every lane: row shifts
+// within each row of 16 lanes, then row broadcasts across rows, all in DPP (no LDS traffic).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+  v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true));   // row_shr:1
+  v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true));   // row_shr:2
+  v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true));   // row_shr:4
+  v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true));   // row_shr:8
+  v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Top-k of lg[0..E) by wavefront 0 of the calling block (threads 0..63; E <= 64 * PER): k rounds of an
+// argmax over order-preserving keys.  Larger logits first; equal logits (+0 and -0 are equal) -> the lower
+// id first.  Writes sel_i[0..k) and sel_v[0..k) (the logits); -1 / NaN when fewer than k candidates.
+template <int PER>
+__device__ __forceinline__ void topk_wave(const float* lg, int E, int k, int* sel_i, float* sel_v) {
+  const int lane = threadIdx.x;
+  uint32_t key[PER];
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {
+    const int idx = lane + 64 * m;
+    uint32_t u = idx < E ? __float_as_uint(lg[idx] + 0.0f) : 0u;
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    key[m] = idx < E ? (u ? u : 1u) : 0u;          // 0 marks "absent / taken"
+  }
+  const int nm = (E + 63) / 64;                    // key groups holding candidates (uniform)
+  for (int rr = 0; rr < k; ++rr) {
+    uint32_t mx = key[0];
+#pragma unroll
+    for (int m = 1; m < PER; ++m)
+      if (m < nm) mx = key[m] > mx ? key[m] : mx;
+    mx = wave_max_u32(mx);
+    int sel = -1;
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      if (m >= nm || sel >= 0) continue;
+      const unsigned long long hit = __ballot(key[m] == mx && mx != 0u);
+      if (hit) sel = 64 * m + (__ffsll((long long)hit) - 1);
+    }
+#pragma unroll
+    for (int m = 0; m < PER; ++m)
+      if (m < nm && lane + 64 * m == sel) key[m] = 0u;
+    if (lane == 0) {
+      sel_i[rr] = sel;
+      sel_v[rr] = sel >= 0 ? lg[sel] : __builtin_nanf("");
+    }
+  }
+}
+
 }  // namespace moeq4

@@ -264,47 +264,9 @@ __device__ __forceinline__ void publish_route(const LayerArgs& a, RouteLds& r) {
       r.sel_v[threadIdx.x] = (i >= 0 && i < a.E) ? r.lg[i] : __builtin_nanf("");
     }
   } else if (threadIdx.x < 64) {
-    // top-k by k rounds of a wavefront argmax over order-preserving keys (larger logit first; equal logits
-    // -> the lowest id, found with a ballot); a selected candidate's key is cleared
-    const int lane = threadIdx.x;
-    constexpr int kPer = kLayerMaxE / 64;
-    uint32_t key[kPer];
-#pragma unroll
-    for (int m = 0; m < kPer; ++m) {
-      const int idx = lane + 64 * m;
-      if (idx < a.E) {
-        const uint32_t u = __float_as_uint(r.lg[idx] + 0.0f);        // -0 -> +0: equal logits, equal keys
-        key[m] = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-        key[m] = key[m] ? key[m] : 1u;                                // 0 is reserved for "taken"
-      } else {
-        key[m] = 0u;
-      }
-    }
-    for (int rr = 0; rr < a.k; ++rr) {
-      uint32_t mx = key[0];
-#pragma unroll
-      for (int m = 1; m < kPer; ++m) mx = key[m] > mx ? key[m] : mx;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const uint32_t t = (uint32_t)__shfl_xor((int)mx, o, 64);
-        mx = t > mx ? t : mx;
-      }
-      int sel = -1;
-#pragma unroll
-      for (int m = 0; m < kPer; ++m) {
-        const unsigned long long hit = __ballot(key[m] == mx && mx != 0u);
-        if (sel < 0 && hit) sel = 64 * m + (__ffsll((long long)hit) - 1);
-      }
-      if (sel >= 0) {
-#pragma unroll
-        for (int m = 0; m < kPer; ++m)
-          if (lane + 64 * m == sel) key[m] = 0u;
-      }
-      if (lane == 0) {
-        r.sel_i[rr] = sel;
-        r.sel_v[rr] = sel >= 0 ? r.lg[sel] : __builtin_nanf("");
-      }
-    }
+    // the maximum of each round is a DPP reduction: a rank loop or shuffles would go through the LDS unit,
+    // which the co-resident blocks keep busy
+    topk_wave<kLayerMaxE / 64>(r.lg, a.E, a.k, r.sel_i, r.sel_v);
   }
   __syncthreads();
   // softmax over the k kept logits: one exp per kept logit, the denominator summed in the order 0..k-1

@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
   // The last block selects.  Top-k by rank: candidate e is kept iff fewer than k logits beat it
   // (larger value, or equal value and lower id), and its rank is its position in the output.  Every
   // comparison reads LDS by broadcast; there are no dependent cross-lane shuffle chains.
-  __shared__ __align__(16) float lgs[kMaxExperts];
+  __shared__ float lgs[kMaxExperts];
   __shared__ float sel_v[kMaxK];
   __shared__ int sel_i[kMaxK];
   const float* lg = a.logits + t * a.E;
@@ -230,26 +230,9 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
     for (int p = 0; p < kMaxExperts / 256; ++p) {
       const int c = threadIdx.x + 256 * p;
       if (c < a.E) {
-        // four logits per LDS read, eight reads in flight: the loop is not bound by LDS latency
         const float v = lgs[c];
         int rank = 0;
-        const float4* lg4 = reinterpret_cast<const float4*>(lgs);
-        const int n4 = a.E / 4;
-        int q = 0;
-        for (; q + 8 <= n4; q += 8) {
-          float4 u[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) u[i] = lg4[q + i];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int e2 = 4 * (q + i);
-            rank += (u[i].x > v) | ((u[i].x == v) & (e2 < c));
-            rank += (u[i].y > v) | ((u[i].y == v) & (e2 + 1 < c));
-            rank += (u[i].z > v) | ((u[i].z == v) & (e2 + 2 < c));
-            rank += (u[i].w > v) | ((u[i].w == v) & (e2 + 3 < c));
-          }
-        }
-        for (int e2 = 4 * q; e2 < a.E; ++e2) {
+        for (int e2 = 0; e2 < a.E; ++e2) {
           const float u = lgs[e2];
           rank += (u > v) | ((u == v) & (e2 < c));
         }
