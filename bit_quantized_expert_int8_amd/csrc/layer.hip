@@ -6,21 +6,33 @@
 //
 //   [router | shared gate/up | routed gate/up | shared down | routed down]
 //
-//   router            one expert per wavefront: RMSNorm of x, int8 dot product, logit published
+//   router            one expert per wavefront: RMSNorm of x, int8 dot product, logit published, then
+//                     that expert's rank among all logits (its routing entry if it is selected)
 //   shared gate/up    8 features of the shared expert (needs only x: starts at once)
-//   routed gate/up    8 features of the i-th selected expert: reads the published logits when all router
-//                     blocks are done and ranks them itself (or takes the forced ids: no wait at all)
+//   routed gate/up    8 features of the i-th selected expert: waits for its entry of the routing (or
+//                     takes the forced ids: no wait at all)
 //   shared down       16 rows of the shared expert, once all of its gate/up blocks are done
 //   routed down       64 rows of the i-th selected expert, once that expert's gate/up blocks are done;
 //                     its code words are loaded before the wait, so they stream while gate/up finishes
 //
 // Down blocks publish their rows and take a ticket per 16-row tile; the last of the k + 1 contributions to
-// a tile applies the routing-weighted combine and the residual, in the order of moe_combine.  Each block
-// only waits on blocks with smaller indices, which the dispatcher starts first, so every wait is on work
-// that is running or finished.  Waits are bounded: a wait that runs out sets the sticky status word of
-// the workspace instead of hanging (results are then invalid).  Values cross blocks by device-coherent
-// stores and loads and 32-bit relaxed device-scope counters; the block that combines the last tile resets
-// every counter, so the workspace is ready for the next call when the kernel ends.
+// a tile applies the routing-weighted combine and the residual, in the order of moe_combine.
+//
+// Apart from the router blocks (below), each block only waits on blocks with smaller indices, which the
+// dispatcher starts first, so every wait is on work that is running or finished.  Waits are bounded: a wait that runs out sets the sticky status
+// word of the workspace instead of hanging (results are then invalid).  Values cross blocks by
+// device-coherent stores and loads and 32-bit relaxed device-scope counters; the block that combines the
+// last tile resets every counter, so the workspace is ready for the next call when the kernel ends.
+//
+// The routing carries no counter.  Each logit is stored with the call's tag in the upper half of a 64-bit
+// word (one store, single-copy atomic), in 8 replicas.  Every router wavefront then waits until all E tags match and
+// counts the logits ranked before its own (larger, or equal with a smaller id); if that rank r is below
+// k, it stores (id, logit), tagged, as entry r of each of 16 route replicas.  A block that needs the
+// routing polls one replica until its k tags match and, if it needs the gate weights, takes the softmax
+// of the k logits itself (every block the same way, so all agree).  The tag is 1 + an epoch word of the
+// workspace that every block reads when it starts and the last block of the call increments.  The router
+// blocks are the first 32 of the grid, all resident at once: they are the only blocks that wait on blocks
+// with larger indices.
 //
 // The normalized activation is computed by every block that needs it with the same fixed-order
 // reduction, so all of them (and the router) see the same u:
@@ -51,15 +63,16 @@ struct SyncSet {
   uint32_t total;                   // arrivals that complete the set (waiters on a set without flag lines
                                     // poll its counter for this value)
 };
-constexpr int kRouteSub = 1, kRouteFlags = 64;
 constexpr int kSharedSub = 16, kSharedFlags = 16;
 constexpr int kSlotSub = 1, kSlotFlags = 8;
-constexpr int kTilesSub = 1;
-// line 0: status word (sticky, bit 0 = a bounded wait ran out); then the sets route, shared, tiles, slots
-constexpr int kXFlags = 64;      // flags announcing a layer's output to the next layer of the launch
-constexpr int kLinesFixed = 1 + (kRouteSub + 1 + kRouteFlags) + (kSharedSub + 1 + kSharedFlags) + (kTilesSub + 1 + kXFlags);
-constexpr int kLinesPerSlot = kSlotSub + 1 + kSlotFlags;
+constexpr int kDoneSub = 1;         // the layer-done set counts combined 16-row tiles
 constexpr int kTileStride = 16;     // words between two tile tickets
+// line 0: status word (sticky, bit 0 = a bounded wait ran out); then the sets shared, done, slots
+constexpr int kXFlags = 64;      // flags announcing a layer's output to the next layer of the launch
+constexpr int kLinesFixed = 1 + (kSharedSub + 1 + kSharedFlags) + (kDoneSub + 1 + kXFlags);
+constexpr int kRouteReplicas = 16;   // copies of the tagged routing (pollers spread over them)
+constexpr int kLgReplicas = 8;       // copies of the tagged logits (the router wavefronts poll them)
+constexpr int kLinesPerSlot = kSlotSub + 1 + kSlotFlags;
 
 struct LayerPool {
   const char* base;
@@ -87,22 +100,24 @@ struct LayerArgs {
   int32_t x_f32, out_f32;  // activations held in the workspace as fp32 and exchanged coherently (the
                            // layers between the first input and the last output of a launch)
   uint32_t* status;
-  SyncSet route, shared_h, tiles_done;   // tiles_done = this layer's output complete (flags: next layer)
-  SyncSet prev_x;                        // the previous layer's tiles_done, or base == NULL
+  uint32_t* epoch;                       // the call counter (one per launch, in layer 0's region)
+  uint32_t tag;                          // this call's tag: epoch + 1, read when the block starts
+  SyncSet shared_h, done;                // done = this layer's output complete: counts combined tiles
+                                         // (flags: the next layer of the launch)
+  SyncSet prev_x;                        // the previous layer's done, or base == NULL
   uint32_t* slot_base;                   // per-slot sets, kLinesPerSlot lines apart
   int32_t last_layer;                    // the block combining this layer's last tile resets every layer
   uint32_t* sync_base;                   // sync lines of layer 0; layer l's are l * layer_words further
   int64_t layer_words;
   int32_t sync_lines, n_layers;
-  uint32_t* tiles;     // [d/16] tickets, kTileStride words apart
-  float* logits;       // [E]
+  uint64_t* lg_tag;    // [kLgReplicas][E] (tag << 32) | logit bits
+  uint64_t* route;     // [kRouteReplicas][2][kLayerMaxK] (tag << 32) | id, (tag << 32) | weight bits
   float* h_routed;     // [k][F]
   float* h_shared;     // [S]
+  uint32_t* tiles;     // [d/16] tickets, kTileStride words apart
   float* y_routed;     // [k][d]
   float* y_shared;     // [d]
   int32_t nR, nSG, nRG, nSD, nRD;
-  int32_t* route_ids_ws;   // [k] selected ids, published with route_w_ws before the route flags
-  float* route_w_ws;       // [k] their softmax weights
 };
 
 __device__ __forceinline__ SyncSet slot_set(const LayerArgs& a, int i) {
@@ -114,29 +129,42 @@ __device__ __forceinline__ void st_c(float* p, float v) { __hip_atomic_store(p, 
 __device__ __forceinline__ void st_cu(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint32_t ld_cu(const uint32_t* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ void st_c64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_c64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ uint32_t add_cu(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One arrival (thread 0 of a block, after its published stores completed) out of `total` on set `s`;
-// `idx` in [0, total) picks the sub-counter.  True for the arrival that completed the set, which has then
-// raised every flag of the set.
+// Raise every flag of set `s`: called by a whole wavefront, lane f writes flag line f (n_flags <= 64).
 __device__ __forceinline__ void raise_flags(const SyncSet& s) {
-  for (int f = 0; f < s.n_flags; ++f) st_cu(s.base + (s.n_sub + 1 + f) * kLW, 1u);
+  const int lane = threadIdx.x & 63;
+  if (lane < s.n_flags) st_cu(s.base + (s.n_sub + 1 + lane) * kLW, 1u);
 }
 
+// One arrival (n units) out of `total` on set `s`, made by wavefront 0 of a block (all 64 lanes, after
+// the block's published stores completed); `idx` in [0, total) picks the sub-counter.  Lane 0 makes the
+// atomic round trips.  True, in every lane, for the arrival that completed the set; with `raise` the
+// wavefront has then raised every flag of the set.
 __device__ __forceinline__ bool arrive(const SyncSet& s, int idx, int total, uint32_t n = 1u, bool raise = true) {
-  if (s.n_sub > 1) {
-    const int sub = idx % s.n_sub;
-    const uint32_t expect = (uint32_t)((total - sub + s.n_sub - 1) / s.n_sub);
-    if (add_cu(s.base + sub * kLW, 1u) != expect - 1) return false;
-    const uint32_t subs_used = (uint32_t)(total < s.n_sub ? total : s.n_sub);
-    if (add_cu(s.base + s.n_sub * kLW, 1u) != subs_used - 1) return false;
-  } else if (add_cu(s.base, n) + n != (uint32_t)total) {
-    return false;
+  uint32_t done = 0u;
+  if ((threadIdx.x & 63) == 0) {
+    if (s.n_sub > 1) {
+      const int sub = idx % s.n_sub;
+      const uint32_t expect = (uint32_t)((total - sub + s.n_sub - 1) / s.n_sub);
+      const uint32_t subs_used = (uint32_t)(total < s.n_sub ? total : s.n_sub);
+      done = add_cu(s.base + sub * kLW, 1u) == expect - 1 && add_cu(s.base + s.n_sub * kLW, 1u) == subs_used - 1;
+    } else {
+      done = add_cu(s.base, n) + n == (uint32_t)total;
+    }
   }
-  if (raise) raise_flags(s);
-  return true;
+  done = __builtin_amdgcn_readfirstlane(done);
+  if (done && raise) raise_flags(s);
+  return done != 0u;
 }
 
 // Block-wide bounded wait for set `s` to complete: thread 0 polls flag line `who` mod n_flags, or the
@@ -158,11 +186,11 @@ __device__ __forceinline__ void wait_set(const SyncSet& s, int who, uint32_t* st
   __syncthreads();
 }
 
-// Publish: every thread's coherent stores have completed before thread 0 arrives on the set.
+// Publish: every thread's coherent stores have completed before wavefront 0 arrives on the set.
 __device__ __forceinline__ void publish(const SyncSet& s, int idx, int total) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) arrive(s, idx, total);
+  if (threadIdx.x < 64) arrive(s, idx, total);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -170,142 +198,187 @@ __device__ __forceinline__ void publish(const SyncSet& s, int idx, int total) {
 // ------------------------------------------------------------------------------------------------
 struct NormLds {
   float wsum[kThreads / 64];
-  float rinv;
 };
 
-// xg[j] = x[j] * gamma[j] (or x[j]) into LDS; returns rinv (1 without gamma).  Fixed reduction order:
-// per thread over its elements in index order, the wavefront xor tree, then the four waves in order.
+// u[j] from x[j] * gamma[j], rounded to the activation dtype (the norm output's rounding point)
 template <typename XT>
-__device__ __forceinline__ float norm_to_lds(const LayerArgs& a, float* xg, NormLds& nl) {
-  const XT* x = reinterpret_cast<const XT*>(a.x);
+__device__ __forceinline__ float u_of(float xg, float rinv) {
+  const float u = xg * rinv;
+  return sizeof(XT) == 2 ? bf16_bits_to_f32(f32_to_bf16_bits(u)) : u;
+}
+
+// u[0..d) into LDS: u[j] = round_x((x[j] * gamma[j]) * rinv), rinv = 1 / sqrt(sum_j x[j]^2 / d + eps), or
+// u = x without gamma.  Every load is issued before the first use.  Fixed reduction order: per thread
+// over its elements in index order, the wavefront sum, then the four waves in order (every thread adds
+// the four partial sums itself, the same way).
+template <typename XT>
+__device__ __forceinline__ void norm_to_lds(const LayerArgs& a, float* u, NormLds& nl) {
+  constexpr int kIt = kLayerMaxD / (kThreads * 8);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float ss = 0.f;
-  for (int j0 = threadIdx.x * 8; j0 < a.d; j0 += kThreads * 8) {
-    float v[8];
+  float v[kIt][8], g[kIt][8];
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    const int j0 = (threadIdx.x + it * kThreads) * 8;
+    if (j0 >= a.d) continue;
     if (a.x_f32) {
       const float* xf = reinterpret_cast<const float*>(a.x);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = ld_c(xf + j0 + i);
+      for (int i = 0; i < 8; ++i) v[it][i] = ld_c(xf + j0 + i);
     } else if (sizeof(XT) == 2) {
-      const uint4 w = *reinterpret_cast<const uint4*>(x + j0);
-      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+      const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const XT*>(a.x) + j0);
+      const uint32_t q[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        v[2 * m] = __uint_as_float(u[m] << 16);
-        v[2 * m + 1] = __uint_as_float(u[m] & 0xffff0000u);
+        v[it][2 * m] = __uint_as_float(q[m] << 16);
+        v[it][2 * m + 1] = __uint_as_float(q[m] & 0xffff0000u);
       }
     } else {
-      const float4 p0 = reinterpret_cast<const float4*>(x + j0)[0], p1 = reinterpret_cast<const float4*>(x + j0)[1];
-      v[0] = p0.x; v[1] = p0.y; v[2] = p0.z; v[3] = p0.w;
-      v[4] = p1.x; v[5] = p1.y; v[6] = p1.z; v[7] = p1.w;
+      const float4* xf = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + j0);
+      const float4 p0 = xf[0], p1 = xf[1];
+      v[it][0] = p0.x; v[it][1] = p0.y; v[it][2] = p0.z; v[it][3] = p0.w;
+      v[it][4] = p1.x; v[it][5] = p1.y; v[it][6] = p1.z; v[it][7] = p1.w;
     }
-    float g[8];
     if (a.gamma) {
       const float4 g0 = reinterpret_cast<const float4*>(a.gamma + j0)[0], g1 = reinterpret_cast<const float4*>(a.gamma + j0)[1];
-      g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w;
-      g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
+      g[it][0] = g0.x; g[it][1] = g0.y; g[it][2] = g0.z; g[it][3] = g0.w;
+      g[it][4] = g1.x; g[it][5] = g1.y; g[it][6] = g1.z; g[it][7] = g1.w;
     }
+  }
+  float rinv = 1.0f;
+  if (a.gamma) {
+    float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ss = fmaf(v[i], v[i], ss);
-      xg[j0 + i] = a.gamma ? v[i] * g[i] : v[i];
+    for (int it = 0; it < kIt; ++it) {
+      if ((int)(threadIdx.x + it * kThreads) * 8 >= a.d) continue;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss = fmaf(v[it][i], v[it][i], ss);
     }
-  }
-  if (!a.gamma) {
+    ss = wave_sum(ss);
+    if (lane == 0) nl.wsum[wave] = ss;
     __syncthreads();
-    return 1.0f;
-  }
-  ss = wave_sum(ss);
-  if (lane == 0) nl.wsum[wave] = ss;
-  __syncthreads();
-  if (threadIdx.x == 0) {
     float t = nl.wsum[0];
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) t += nl.wsum[w];
-    nl.rinv = 1.0f / sqrtf(t / (float)a.d + a.eps);
+    rinv = 1.0f / sqrtf(t / (float)a.d + a.eps);
+  }
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    const int j0 = (threadIdx.x + it * kThreads) * 8;
+    if (j0 >= a.d) continue;
+    float o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = a.gamma ? u_of<XT>(v[it][i] * g[it][i], rinv) : v[it][i];
+    reinterpret_cast<float4*>(u + j0)[0] = make_float4(o[0], o[1], o[2], o[3]);
+    reinterpret_cast<float4*>(u + j0)[1] = make_float4(o[4], o[5], o[6], o[7]);
   }
   __syncthreads();
-  return nl.rinv;
-}
-
-// u[j] from xg[j] (rounded to the activation dtype, the norm output's rounding point)
-template <typename XT>
-__device__ __forceinline__ float u_of(float xg, float rinv, bool norm) {
-  if (!norm) return xg;
-  const float u = xg * rinv;
-  return sizeof(XT) == 2 ? bf16_bits_to_f32(f32_to_bf16_bits(u)) : u;
 }
 
 // ------------------------------------------------------------------------------------------------
 // routing inside a block
 // ------------------------------------------------------------------------------------------------
 struct RouteLds {
-  alignas(16) float lg[kLayerMaxE];
-  float sel_v[kLayerMaxK];
   int sel_i[kLayerMaxK];
   float w[kLayerMaxK];
 };
 
-// The router block whose arrival completed the route ranks the published logits once (top-k: larger logit
-// first, equal logits -> lower id; or the forced ids), publishes ids and softmax weights, and only then
-// raises the route flags.  Every logit is published: each router block's stores completed before it
-// arrived.
-__device__ __forceinline__ void publish_route(const LayerArgs& a, RouteLds& r) {
-  if ((int)threadIdx.x < a.E) r.lg[threadIdx.x] = ld_c(a.logits + threadIdx.x);
-  if ((int)threadIdx.x < kLayerMaxK) {
-    r.sel_i[threadIdx.x] = -1;
-    r.sel_v[threadIdx.x] = __builtin_nanf("");
-  }
-  __syncthreads();
-  if (a.forced) {
-    if ((int)threadIdx.x < a.k) {
-      const int i = a.forced[threadIdx.x];
-      r.sel_i[threadIdx.x] = i;
-      r.sel_v[threadIdx.x] = (i >= 0 && i < a.E) ? r.lg[i] : __builtin_nanf("");
+// Router wavefront of expert e < E, after publishing logit lgt: wait for all E logits of this call, rank
+// lgt among them (larger logit first, equal logits -> lower id) and, if the rank is below k, publish
+// (e, lgt) as that entry of every route replica.  With forced ids nothing is ranked.  A wait that runs out
+// sets the status word and ranks whatever it read.
+template <int PER>
+__device__ __forceinline__ void rank_expert(const LayerArgs& a, int e, float lgt) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[PER];
+  for (int n = 0;; ++n) {
+    bool ok = true;
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      key[m] = 0u;
+      if (lane + 64 * m < a.E) {
+        const uint64_t t = ld_c64(a.lg_tag + (int64_t)(e % kLgReplicas) * a.E + lane + 64 * m);
+        ok = ok && (uint32_t)(t >> 32) == a.tag;
+        key[m] = order_key(__uint_as_float((uint32_t)t));
+      }
     }
-  } else if (threadIdx.x < 64) {
-    // the maximum of each round is a DPP reduction: a rank loop or shuffles would go through the LDS unit,
-    // which the co-resident blocks keep busy
-    topk_wave<kLayerMaxE / 64>(r.lg, a.E, a.k, r.sel_i, r.sel_v);
+    if (__ballot(!ok) == 0ull) break;
+    if (n >= kSpinLimit) {
+      if (lane == 0) __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
   }
-  __syncthreads();
-  // softmax over the k kept logits: one exp per kept logit, the denominator summed in the order 0..k-1
-  float ex = 0.f;
-  if ((int)threadIdx.x < a.k) {
-    float mx = r.sel_v[0];
-    for (int i = 1; i < a.k; ++i) mx = fmaxf(mx, r.sel_v[i]);
-    ex = expf(r.sel_v[threadIdx.x] - mx);
-    r.w[threadIdx.x] = ex;
+  const uint32_t ke = order_key(lgt);
+  int rank = 0;
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {
+    const int idx = lane + 64 * m;
+    const bool before = idx < a.E && (key[m] > ke || (key[m] == ke && idx < e));
+    rank += __popcll(__ballot(before));
   }
-  __syncthreads();
-  if ((int)threadIdx.x < a.k) {
-    float den = 0.f;
-    for (int i = 0; i < a.k; ++i) den += r.w[i];
-    const float w = ex / den;
-    const int id = r.sel_i[threadIdx.x];
-    st_cu(reinterpret_cast<uint32_t*>(a.route_ids_ws) + threadIdx.x, (uint32_t)id);
-    st_c(a.route_w_ws + threadIdx.x, w);
-    if (a.ids_out) a.ids_out[threadIdx.x] = id;
-    if (a.weights_out) a.weights_out[threadIdx.x] = w;
+  if (rank < a.k && lane < kRouteReplicas) {
+    uint64_t* rep_base = a.route + (int64_t)lane * 2 * kLayerMaxK;
+    const uint64_t tg = (uint64_t)a.tag << 32;
+    st_c64(rep_base + rank, tg | (uint32_t)e);
+    st_c64(rep_base + kLayerMaxK + rank, tg | __float_as_uint(lgt));
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) raise_flags(a.route);
 }
 
-// sel_i[0..k) = the selected expert ids and, with need_weights, w[0..k) their weights.  With forced ids
-// and no weights needed there is nothing to wait for.
-__device__ __forceinline__ void get_route(const LayerArgs& a, RouteLds& r, bool need_weights) {
-  if (a.forced && !need_weights) {
+// sel_i[0..k) = the selected expert ids and, with weights, w[0..k) their gate weights (softmax over the k
+// kept logits: one exp per kept logit, maximum and denominator taken in the order 0..k-1), in LDS for the
+// whole block; wavefront 0 polls route replica blockIdx mod kRouteReplicas (with forced ids: the forced
+// experts' logits).  With forced ids and no weights there is nothing to wait for.
+__device__ __forceinline__ void get_route(const LayerArgs& a, RouteLds& r, bool weights) {
+  if (a.forced && !weights) {
     if ((int)threadIdx.x < a.k) r.sel_i[threadIdx.x] = a.forced[threadIdx.x];
     __syncthreads();
     return;
   }
-  wait_set(a.route, blockIdx.x, a.status);
-  if ((int)threadIdx.x < a.k) {
-    r.sel_i[threadIdx.x] = (int)__hip_atomic_load(reinterpret_cast<const uint32_t*>(a.route_ids_ws) + threadIdx.x,
-                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    r.w[threadIdx.x] = ld_c(a.route_w_ws + threadIdx.x);
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const uint64_t* src = a.route + (int64_t)(blockIdx.x % kRouteReplicas) * 2 * kLayerMaxK;
+    int id = -1;
+    float v = __builtin_nanf("");
+    const int fid = a.forced && lane < a.k ? a.forced[lane] : -1;
+    const bool fvalid = fid >= 0 && fid < a.E;
+    for (int n = 0;; ++n) {
+      bool ok = true;
+      if (lane < a.k) {
+        if (a.forced) {
+          id = fid;
+          if (fvalid) {
+            const uint64_t t = ld_c64(a.lg_tag + (int64_t)(blockIdx.x % kLgReplicas) * a.E + fid);
+            ok = (uint32_t)(t >> 32) == a.tag;
+            v = __uint_as_float((uint32_t)t);
+          }
+        } else {
+          const uint64_t ti = ld_c64(src + lane), tv = ld_c64(src + kLayerMaxK + lane);
+          ok = (uint32_t)(ti >> 32) == a.tag && (uint32_t)(tv >> 32) == a.tag;
+          id = (int)(uint32_t)ti;
+          v = __uint_as_float((uint32_t)tv);
+        }
+      }
+      if (__ballot(!ok) == 0ull) break;
+      if (n >= kSpinLimit) {
+        if (lane == 0) __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    float w = 0.f;
+    if (weights) {
+      auto lane_f = [](float x, int i) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), i)); };
+      float mx = lane_f(v, 0);
+      for (int i = 1; i < a.k; ++i) mx = fmaxf(mx, lane_f(v, i));
+      const float ex = lane < a.k ? expf(v - mx) : 0.f;
+      float den = 0.f;
+      for (int i = 0; i < a.k; ++i) den += lane_f(ex, i);
+      w = ex / den;
+    }
+    if (lane < a.k) {
+      r.sel_i[lane] = id;
+      r.w[lane] = w;
+    }
   }
   __syncthreads();
 }
@@ -313,53 +386,58 @@ __device__ __forceinline__ void get_route(const LayerArgs& a, RouteLds& r, bool 
 // ------------------------------------------------------------------------------------------------
 // roles
 // ------------------------------------------------------------------------------------------------
+// Four experts per block, one per wavefront.  Lane l takes the 8-element pieces l, l + 64, ... of the row
+// (8 int8 weights: one 8-byte load each, issued before the norm), so the reads of u are conflict-free.
 template <typename XT>
-__device__ __forceinline__ void router_block(const LayerArgs& a, int b, float* xg, NormLds& nl) {
+__device__ __forceinline__ void router_block(const LayerArgs& a, int b, float* u, NormLds& nl) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int e = b * 4 + wave;
-  const int nch = a.d / 16;
-  int4 q[kLayerMaxD / 16 / 64];
+  const int np = a.d / 8;
+  constexpr int kM = kLayerMaxD / 8 / 64;
+  uint2 q[kM];
 #pragma unroll
-  for (int m = 0; m < kLayerMaxD / 16 / 64; ++m) {
-    const int c = lane + 64 * m;
-    if (e < a.E && c < nch) q[m] = *reinterpret_cast<const int4*>(a.rw + (int64_t)e * a.d + c * 16);
+  for (int m = 0; m < kM; ++m) {
+    const int p = lane + 64 * m;
+    if (e < a.E && p < np) q[m] = *reinterpret_cast<const uint2*>(a.rw + (int64_t)e * a.d + p * 8);
   }
   if (a.prev_x.base) wait_set(a.prev_x, blockIdx.x, a.status);
-  const float rinv = norm_to_lds<XT>(a, xg, nl);
-  // u in place (same rounding as the gate/up blocks)
-  for (int j = threadIdx.x; j < a.d; j += kThreads) xg[j] = u_of<XT>(xg[j], rinv, a.gamma != nullptr);
-  __syncthreads();
+  norm_to_lds<XT>(a, u, nl);
   if (e < a.E) {
     float acc = 0.f;
+    // three pieces at a time: their LDS reads are issued together
 #pragma unroll
-    for (int m = 0; m < kLayerMaxD / 16 / 64; ++m) {
-      const int c = lane + 64 * m;
-      if (c >= nch) break;
-      const float4* xv = reinterpret_cast<const float4*>(xg + c * 16);
-      const int qw[4] = {q[m].x, q[m].y, q[m].z, q[m].w};
+    for (int m0 = 0; m0 < kM; m0 += 3) {
+      if (m0 * 64 >= np) break;
+      float4 ub[3][2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 xx = xv[i];
-        acc += (float)(int8_t)(qw[i] & 0xff) * xx.x;
-        acc += (float)(int8_t)((qw[i] >> 8) & 0xff) * xx.y;
-        acc += (float)(int8_t)((qw[i] >> 16) & 0xff) * xx.z;
-        acc += (float)(int8_t)((qw[i] >> 24) & 0xff) * xx.w;
+      for (int mm = 0; mm < 3; ++mm) {
+        const int p = lane + 64 * (m0 + mm);
+        const int pc = (m0 + mm < kM && p < np) ? p : 0;
+        ub[mm][0] = reinterpret_cast<const float4*>(u + pc * 8)[0];
+        ub[mm][1] = reinterpret_cast<const float4*>(u + pc * 8)[1];
+      }
+#pragma unroll
+      for (int mm = 0; mm < 3; ++mm) {
+        const int p = lane + 64 * (m0 + mm);
+        if (m0 + mm >= kM || p >= np) continue;
+        const float us[8] = {ub[mm][0].x, ub[mm][0].y, ub[mm][0].z, ub[mm][0].w,
+                             ub[mm][1].x, ub[mm][1].y, ub[mm][1].z, ub[mm][1].w};
+        const uint32_t w[2] = {q[m0 + mm].x, q[m0 + mm].y};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc = fmaf((float)(int8_t)((w[i >> 2] >> (8 * (i & 3))) & 0xff), us[i], acc);
       }
     }
     acc = wave_sum(acc);
-    if (lane == 0) {
-      const float lgt = acc * a.rs[e];
-      st_c(a.logits + e, lgt);
-      if (a.logits_out) a.logits_out[e] = lgt;
+    const float lgt = acc * a.rs[e];
+    if (lane < kLgReplicas) st_c64(a.lg_tag + (int64_t)lane * a.E + e, ((uint64_t)a.tag << 32) | __float_as_uint(lgt));
+    if (lane == 0 && a.logits_out) a.logits_out[e] = lgt;
+    if (!a.forced) {
+      if (a.E <= 64) rank_expert<1>(a, e, lgt);
+      else if (a.E <= 128) rank_expert<2>(a, e, lgt);
+      else if (a.E <= 192) rank_expert<3>(a, e, lgt);
+      else rank_expert<4>(a, e, lgt);
     }
   }
-  // publish this block's logits; the block that completes the set ranks them for everyone
-  __shared__ uint32_t last_s;
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) last_s = arrive(a.route, b, a.nR, 1u, false) ? 1u : 0u;
-  __syncthreads();
-  if (last_s) publish_route(a, *reinterpret_cast<RouteLds*>(xg));   // LDS reuse: xg is no longer needed
 }
 
 // 8 features (gate rows f, up rows F + f) of one expert; the four waves split the row.  Split in a load
@@ -401,10 +479,9 @@ __device__ __forceinline__ void gu_load(const LayerArgs& a, const LayerPool& P, 
   }
 }
 
-template <int NBW, typename XT, bool SB_BF16>
+template <int NBW, bool SB_BF16>
 __device__ __forceinline__ void gu_finish(const LayerArgs& a, const GuRegs<NBW, SB_BF16>& g, bool valid, int tile,
-                                          float rinv, float* hout, const SyncSet& done, int done_total,
-                                          const float* xg, Stage st) {
+                                          float* hout, const SyncSet& done, int done_total, const float* u, Stage st) {
   const int K = a.d, lane = threadIdx.x & 63, wave = threadIdx.x >> 6, ra = lane >> 3, j = lane & 7;
   const int C = K / 32, nit = (C + kLanesPerRow - 1) / kLanesPerRow;
   const int f = tile * 8 + ra;
@@ -418,7 +495,7 @@ __device__ __forceinline__ void gu_finish(const LayerArgs& a, const GuRegs<NBW, 
     const bool live = m < NBW && it < nit && hg < C;
     float v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = live ? u_of<XT>(xg[hg * 32 + qd * 8 + i], rinv, a.gamma != nullptr) : 0.f;
+    for (int i = 0; i < 8; ++i) v[i] = live ? u[hg * 32 + qd * 8 + i] : 0.f;
     stage_word(v, live, hg, qd, st);
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -464,9 +541,16 @@ __device__ __forceinline__ void stage_published(const float* v, int K, Stage st)
 template <typename XT>
 __device__ __forceinline__ void combine_one(const LayerArgs& a, const RouteLds& r, int tile, int t16) {
   const int row = tile * 16 + t16;
-  // all loads first (eight in flight), then the sum in the order i = 0..k-1, shared, residual
+  // all loads first (shared, residual and eight routed rows in flight), then the sum in the order
+  // i = 0..k-1, shared, residual
   float acc = 0.f;
   const float ys = a.has_shared ? ld_c(a.y_shared + row) : 0.f;
+  const XT* x = reinterpret_cast<const XT*>(a.x);
+  float xr = 0.f;
+  if (a.residual)
+    xr = a.x_f32 ? ld_c(reinterpret_cast<const float*>(a.x) + row)
+                 : sizeof(XT) == 2 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(x)[row])
+                                   : reinterpret_cast<const float*>(x)[row];
   for (int i0 = 0; i0 < a.k; i0 += 8) {
     float yv[8];
 #pragma unroll
@@ -476,11 +560,7 @@ __device__ __forceinline__ void combine_one(const LayerArgs& a, const RouteLds& 
       if (i0 + i < a.k) acc = __builtin_fmaf(r.w[i0 + i], yv[i], acc);
   }
   if (a.has_shared) acc += ys;
-  const XT* x = reinterpret_cast<const XT*>(a.x);
-  if (a.residual)
-    acc += a.x_f32 ? ld_c(reinterpret_cast<const float*>(a.x) + row)
-                   : sizeof(XT) == 2 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(x)[row])
-                                     : reinterpret_cast<const float*>(x)[row];
+  if (a.residual) acc += xr;
   const float o = sizeof(XT) == 2 ? bf16_bits_to_f32(f32_to_bf16_bits(acc)) : acc;   // the layer output's rounding
   if (a.out_f32)
     st_c(reinterpret_cast<float*>(a.out) + row, o);
@@ -493,8 +573,8 @@ __device__ __forceinline__ void combine_one(const LayerArgs& a, const RouteLds& 
 // After a down block published its rows: one ticket per covered tile; combine the tiles this block
 // completed; the block that combines the last tile of the layer resets every counter.
 template <typename XT>
-__device__ __forceinline__ void tile_epilogue(const LayerArgs& a, int tile0, int ntiles, RouteLds& r, uint32_t* lastf,
-                                              bool have_weights) {
+__device__ __forceinline__ void tile_epilogue(const LayerArgs& a, int tile0, int ntiles, const RouteLds& r,
+                                              uint32_t* lastf) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const uint32_t units = (uint32_t)a.k + (a.has_shared ? 1u : 0u);
@@ -504,18 +584,21 @@ __device__ __forceinline__ void tile_epilogue(const LayerArgs& a, int tile0, int
   bool any = false;
   for (int t = 0; t < ntiles; ++t) any |= lastf[t] != 0;
   if (!any) return;
-  if (!have_weights) get_route(a, r, true);
   uint32_t n = 0;
   for (int t = 0; t < ntiles; ++t) n += lastf[t] ? 1u : 0u;
   // every completed tile at once: thread 16 t + i combines row i of tile t
   if ((int)threadIdx.x < 16 * ntiles && lastf[threadIdx.x / 16]) combine_one<XT>(a, r, tile0 + threadIdx.x / 16, threadIdx.x % 16);
   if ((int)threadIdx.x < ntiles && lastf[threadIdx.x]) st_cu(a.tiles + (tile0 + threadIdx.x) * kTileStride, 0u);
   __shared__ uint32_t final_s;
-  if (threadIdx.x == 0) final_s = arrive(a.tiles_done, 0, a.d / 16, n) ? 1u : 0u;
+  if (threadIdx.x < 64) {
+    const bool fin = arrive(a.done, 0, a.d / 16, n);
+    if (threadIdx.x == 0) final_s = fin ? 1u : 0u;
+  }
   __syncthreads();
   if (final_s && a.last_layer) {
     // every block of the launch has passed all of its waits: clear every layer's sync lines (not the
-    // status line, the first line of layer 0)
+    // status line, the first line of layer 0) and start the next call's epoch
+    if (threadIdx.x == 0) st_cu(a.epoch, a.tag);
     const int total = a.n_layers * a.sync_lines;
     for (int t = 1 + (int)threadIdx.x; t < total; t += kThreads) {
       const int l = t / a.sync_lines, line = t % a.sync_lines;
@@ -552,6 +635,8 @@ __device__ __forceinline__ void shared_down_block(const LayerArgs& a, int tile, 
       qb[m] = load_nt(rec + P.dn_q + (row + 8) * rowb + c * 16);
     }
   }
+  // the routing (this block may combine its tile): ready long before the shared h is
+  get_route(a, r, true);
   wait_set(a.shared_h, blockIdx.x, a.status);
   stage_published(a.h_shared, K, st);
   __syncthreads();
@@ -577,7 +662,7 @@ __device__ __forceinline__ void shared_down_block(const LayerArgs& a, int tile, 
     st_c(a.y_shared + row, yA);
     st_c(a.y_shared + row + 8, yB);
   }
-  tile_epilogue<XT>(a, tile, 1, r, lastf, false);
+  tile_epilogue<XT>(a, tile, 1, r, lastf);
 }
 
 // 64 rows of the i-th selected expert's down matrix: wave w takes rows 16w.. of the block, whole rows
@@ -589,6 +674,10 @@ __device__ __forceinline__ void routed_down_block(const LayerArgs& a, int slot, 
   const int C = K / 32;
   const int row = rb * 64 + wave * 16 + ra;
   get_route(a, r, true);      // with the weights: this block may combine tiles at the end
+  if (slot == 0 && rb == 0 && (int)threadIdx.x < a.k) {
+    if (a.ids_out) a.ids_out[threadIdx.x] = r.sel_i[threadIdx.x];
+    if (a.weights_out) a.weights_out[threadIdx.x] = r.w[threadIdx.x];
+  }
   const int e = r.sel_i[slot];
   const int idx = a.gemv_ids ? a.gemv_ids[slot] : e;
   const bool valid = (unsigned)idx < (unsigned)P.n_records && (unsigned)e < (unsigned)a.E;
@@ -644,7 +733,7 @@ __device__ __forceinline__ void routed_down_block(const LayerArgs& a, int slot, 
     st_c(y + row, valid ? yA : __builtin_nanf(""));
     st_c(y + row + 8, valid ? yB : __builtin_nanf(""));
   }
-  tile_epilogue<XT>(a, rb * 4, 4, r, lastf, true);
+  tile_epilogue<XT>(a, rb * 4, 4, r, lastf);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -664,7 +753,7 @@ struct StackLayer {           // what differs between the layers of a launch
 };
 
 struct WsLayout {
-  size_t tiles, logits, route, h_routed, h_shared, y_routed, y_shared, x_next, total;
+  size_t sync, tiles, epoch, lg_tag, route, h_routed, h_shared, y_routed, y_shared, x_next, total;
 };
 
 struct StackArgs {
@@ -712,25 +801,24 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(const StackArgs 
   a.n_layers = sa.n_layers;
   uint32_t* sync = reinterpret_cast<uint32_t*>(ws);
   int line = 1;
-  a.route = layer_set(sync, line, kRouteSub, kRouteFlags, (uint32_t)a.nR);
-  line += kRouteSub + 1 + kRouteFlags;
+  a.epoch = reinterpret_cast<uint32_t*>(sa.ws + sa.w.epoch);
+  a.tag = ld_cu(a.epoch) + 1u;
   a.shared_h = layer_set(sync, line, kSharedSub, kSharedFlags, (uint32_t)a.nSG);
   line += kSharedSub + 1 + kSharedFlags;
-  const int tiles_line = line;
-  a.tiles_done = layer_set(sync, line, kTilesSub, a.last_layer ? 0 : kXFlags, (uint32_t)(a.d / 16));
-  line += kTilesSub + 1 + kXFlags;
+  const int done_line = line;
+  a.done = layer_set(sync, line, kDoneSub, a.last_layer ? 0 : kXFlags, (uint32_t)(a.d / 16));
+  line += kDoneSub + 1 + kXFlags;
   a.slot_base = sync + line * kLW;
-  a.prev_x = l > 0 ? layer_set(sync - a.layer_words, tiles_line, kTilesSub, kXFlags, (uint32_t)(a.d / 16))
+  a.prev_x = l > 0 ? layer_set(sync - a.layer_words, done_line, kDoneSub, kXFlags, (uint32_t)(a.d / 16))
                    : SyncSet{nullptr, 1, 0, 0u};
-  a.tiles = reinterpret_cast<uint32_t*>(ws + sa.w.tiles);
-  a.logits = reinterpret_cast<float*>(ws + sa.w.logits);
-  a.route_ids_ws = reinterpret_cast<int32_t*>(ws + sa.w.route);
-  a.route_w_ws = reinterpret_cast<float*>(ws + sa.w.route) + kLayerMaxK;
+  a.lg_tag = reinterpret_cast<uint64_t*>(ws + sa.w.lg_tag);
+  a.route = reinterpret_cast<uint64_t*>(ws + sa.w.route);
   a.h_routed = reinterpret_cast<float*>(ws + sa.w.h_routed);
   a.h_shared = reinterpret_cast<float*>(ws + sa.w.h_shared);
+  a.tiles = reinterpret_cast<uint32_t*>(ws + sa.w.tiles);
   a.y_routed = reinterpret_cast<float*>(ws + sa.w.y_routed);
   a.y_shared = reinterpret_cast<float*>(ws + sa.w.y_shared);
-  float* xg = reinterpret_cast<float*>(lds);                       // [d]
+  float* u = reinterpret_cast<float*>(lds);                        // [d] the normalized activation
   uint32_t* stage_base = lds + a.d;                                 // staging area
   // staging area: [nhg][kHgStride] words then [nhg] float4; sized by the block's own K
   auto stage_for = [&](int K) {
@@ -741,18 +829,17 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(const StackArgs 
   // layer's critical path, the shared expert has slack (its result is needed only by the combine).
   if (b < a.nR) {
     __builtin_amdgcn_s_setprio(3);
-    router_block<XT>(a, b, xg, nl);
+    router_block<XT>(a, b, u, nl);
     return;
   }
   b -= a.nR;
   if (b < a.nSG) {
-    // the shared expert needs only x: code words first, then the norm while they are in flight
-    if (!a.prev_x.base) __builtin_amdgcn_s_sleep(40);   // about 1 us: let the router's first loads go ahead
+    // the shared expert needs only x: the norm (whose loads go out with the router's), then its code words
+    if (a.prev_x.base) wait_set(a.prev_x, blockIdx.x, a.status);
+    norm_to_lds<XT>(a, u, nl);
     GuRegs<NBW, SB_BF16> g;
     gu_load<NBW, SB_BF16>(a, a.shared, 0, true, b, g);
-    if (a.prev_x.base) wait_set(a.prev_x, blockIdx.x, a.status);
-    const float rinv = norm_to_lds<XT>(a, xg, nl);
-    gu_finish<NBW, XT, SB_BF16>(a, g, true, b, rinv, a.h_shared, a.shared_h, a.nSG, xg, stage_for(a.d));
+    gu_finish<NBW, SB_BF16>(a, g, true, b, a.h_shared, a.shared_h, a.nSG, u, stage_for(a.d));
     return;
   }
   b -= a.nSG;
@@ -761,15 +848,15 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(const StackArgs 
     const int per = a.routed.F / 8, slot = b / per, tile = b % per;
     // the norm needs only x: done while the router finishes
     if (a.prev_x.base) wait_set(a.prev_x, blockIdx.x, a.status);
-    const float rinv = norm_to_lds<XT>(a, xg, nl);
+    norm_to_lds<XT>(a, u, nl);
     get_route(a, r, false);
     const int e = r.sel_i[slot];
     const int idx = a.gemv_ids ? a.gemv_ids[slot] : e;
     const bool valid = (unsigned)idx < (unsigned)a.routed.n_records && (unsigned)e < (unsigned)a.E;
     GuRegs<NBW, SB_BF16> g;
     gu_load<NBW, SB_BF16>(a, a.routed, idx, valid, tile, g);
-    gu_finish<NBW, XT, SB_BF16>(a, g, valid, tile, rinv, a.h_routed + (int64_t)slot * a.routed.F,
-                                slot_set(a, slot), per, xg, stage_for(a.d));
+    gu_finish<NBW, SB_BF16>(a, g, valid, tile, a.h_routed + (int64_t)slot * a.routed.F, slot_set(a, slot), per, u,
+                            stage_for(a.d));
     return;
   }
   b -= a.nRG;
@@ -787,10 +874,12 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 WsLayout ws_layout(int d, int E, int k, int F, int S) {
   WsLayout w;
-  size_t o = (size_t)(kLinesFixed + k * kLinesPerSlot) * kLW * 4;
+  size_t o = 0;
+  w.sync = o;       o += (size_t)(kLinesFixed + k * kLinesPerSlot) * kLW * 4;
   w.tiles = o;      o += align256((size_t)(d / 16) * kTileStride * 4);
-  w.logits = o;     o += align256((size_t)E * 4);
-  w.route = o;      o += align256((size_t)kLayerMaxK * 8);
+  w.epoch = o;      o += 256;
+  w.lg_tag = o;     o += align256((size_t)kLgReplicas * E * 8);
+  w.route = o;      o += align256((size_t)kRouteReplicas * 2 * kLayerMaxK * 8);
   w.h_routed = o;   o += align256((size_t)k * F * 4);
   w.h_shared = o;   o += align256((size_t)(S > 0 ? S : 1) * 4);
   w.y_routed = o;   o += align256((size_t)k * d * 4);
@@ -835,7 +924,8 @@ moe_status prepare_launch(const char* who, const void* x_dev, moe_dtype x_dtype,
     return fail(MOE_ERR_UNSUPPORTED, "%s: d=%d F=%d S=%d (need d, S <= %d, F <= %d)", who, d, routed->F,
                 shared ? shared->F : 0, kLayerMaxD, kLayerMaxF);
   if (E < 1 || E > kLayerMaxE || k < 1 || k > kLayerMaxK || k > E)
-    return fail(MOE_ERR_UNSUPPORTED, "%s: E=%d k=%d (need 1 <= k <= min(E, 32), E <= %d)", who, E, k, kLayerMaxE);
+    return fail(MOE_ERR_UNSUPPORTED, "%s: E=%d k=%d (need 1 <= k <= min(E, %d), E <= %d)", who, E, k, kLayerMaxK,
+                kLayerMaxE);
   if (!aligned(x_dev, 16)) return fail(MOE_ERR_INVALID_ARG, "%s: x must be 16-byte aligned", who);
   const WsLayout w = ws_layout(d, E, k, routed->F, shared ? shared->F : 0);
   if (workspace_bytes < w.total * n_layers)
@@ -902,7 +992,7 @@ using namespace moeq4;
 
 extern "C" size_t moe_decode_layer_sync_bytes(int32_t d, int32_t k) {
   if (d < 64 || k < 1 || k > kLayerMaxK) return 0;
-  return ws_layout(d, 1, k, 64, 0).tiles + align256((size_t)(d / 16) * kTileStride * 4);
+  return ws_layout(d, 1, k, 64, 0).epoch;   // the sync lines and the tile tickets
 }
 
 extern "C" size_t moe_decode_layer_workspace_bytes(int32_t d, int32_t E, int32_t k, int32_t F, int32_t S) {

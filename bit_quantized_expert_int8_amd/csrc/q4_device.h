@@ -145,8 +145,8 @@ __device__ __forceinline__ void stage_word(const float v[8], bool live, int hg, 
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  amax = fmaxf(amax, dpp_f<kDppXor1>(amax));
+  amax = fmaxf(amax, dpp_f<kDppXor2>(amax));
   int e = 0;
   if (amax > 0.f && amax <= 3.0e38f) e = max(-100, min(100, ilogbf(amax) - 13));   // amax * 2^-e in [2^13, 2^14)
   const float inv = ldexpf(1.0f, -e);
@@ -158,10 +158,10 @@ __device__ __forceinline__ void stage_word(const float v[8], bool live, int hg, 
   const float sa = ((float)a0 + (float)a4) + ((float)a2 + (float)a6);
   const float sb = ((float)b1 + (float)b5) + ((float)b3 + (float)b7);
   float osum = sa + sb, ssum = sa + 16.0f * sb;
-  osum += __shfl_xor(osum, 1, 64);
-  ssum += __shfl_xor(ssum, 1, 64);
-  osum += __shfl_xor(osum, 2, 64);
-  ssum += __shfl_xor(ssum, 2, 64);
+  osum += dpp_f<kDppXor1>(osum);
+  ssum += dpp_f<kDppXor1>(ssum);
+  osum += dpp_f<kDppXor2>(osum);
+  ssum += dpp_f<kDppXor2>(ssum);
   if (live) {
     u32x4 qv;
     qv.x = pack_h2(a0, a4);
@@ -282,9 +282,9 @@ __device__ __forceinline__ void rowpair_partial(const char* rowA, const char* ro
 }
 
 __device__ __forceinline__ float reduce8(float v) {
-  v += __shfl_xor(v, 1, 64);
-  v += __shfl_xor(v, 2, 64);
-  v += __shfl_xor(v, 4, 64);
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += xor4_f(v);
   return v;
 }
 

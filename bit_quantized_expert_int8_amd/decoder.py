@@ -78,8 +78,8 @@ class MoEDecoder:
     """Runs T tokens through a stack of MoE layers (T = 1 is decode).
 
     Four ways to run the layers, all through the library:
-      "layer"     moe_decode_layer per layer: two launches (router with the shared gate/up, then the routed
-                  experts, shared down and combine); the default for T = 1 within that kernel's limits
+      "layer"     moe_decode_layer per layer: one launch each; the default for T = 1 within that kernel's
+                  limits
       "stack"     one launch for the whole step (moe_decode_stack, <= 32 layers); layer() as "layer"
       "fused"     moe_norm_router_topk (RMSNorm inside the router) then q4_expert_gemv_combine (expert
                   GEMVs with the combine + residual in the down launch's tail); the default otherwise

@@ -235,8 +235,9 @@ moe_status q4_expert_gemv_combine(const moe_q4_pool* routed, const int32_t* ids_
  *   u       = gamma ? round_x((x * gamma) * rsqrt(mean(x^2) + eps)) : x
  *   logits  = row_scale[e] * (w[e] . u);  ids = top-k (or forced ids);  weights = softmax over ids
  *   out     = round_x( sum_i weights[i] * FFN_{ids[i]}(u) + FFN_shared(u) + (residual ? x : 0) )
- * with the selection, weights and expert arithmetic of moe_router_topk / q4_expert_gemv.  The norm's
- * sum of squares uses its own fixed order, so u may differ from moe_rmsnorm's in the last bit.
+ * with the selection rule, weights and expert arithmetic of moe_router_topk / q4_expert_gemv.  The norm's
+ * sum of squares and the router's dot products use their own fixed orders, so u may differ from
+ * moe_rmsnorm's in the last bit and the logits from moe_router_topk's in the last bits.
  * x_dev, out_dev: x_dtype [d] (16-byte aligned, must not alias); gamma_dev: fp32 [d] or NULL;
  * router as moe_router_topk; forced_ids_dev: int32 [k] or NULL; routed: pool of experts, indexed by the
  * selected ids, or by gemv_ids_dev[i] (int32 [k], e.g. cache slots from expert_cache_stage) when that is
@@ -247,7 +248,9 @@ moe_status q4_expert_gemv_combine(const moe_q4_pool* routed, const int32_t* ids_
  * aligned, ZERO before its first use.  Its first moe_decode_layer_sync_bytes(d, k) bytes hold the counters
  * and flags the blocks synchronise with; every completed call leaves them zero again, except 32-bit word 0:
  * a sticky error flag, nonzero if a wait inside the kernel ran out (the results of that call are invalid;
- * zero the workspace before reusing it).  Calls that overlap in time need separate workspaces.
+ * zero the workspace before reusing it).  After them come a call counter, which every call advances by
+ * one (values published during a call carry it, so nothing else needs clearing), and the call's
+ * intermediate values.  Calls that overlap in time need separate workspaces.
  * ------------------------------------------------------------------------------------------------- */
 size_t moe_decode_layer_workspace_bytes(int32_t d, int32_t E, int32_t k, int32_t F, int32_t S);
 size_t moe_decode_layer_sync_bytes(int32_t d, int32_t k);
