@@ -362,5 +362,11 @@ extern "C" moe_status q4_expert_gemv_combine(const moe_q4_pool* routed, const in
   hipStream_t s = as_stream(stream);
   st = run_gate_up(a, orr, osh, x_dtype, sb16, T, s);
   if (st != MOE_OK) return st;
-  return run_down(a, orr, osh, sb16, T, s, true);
+  if (T == 1) return run_down(a, orr, osh, sb16, T, s, true);
+  // several tokens: per-tile tickets would cost T * d / 16 atomics per contribution, so the grouped down
+  // GEMV publishes its rows and the combine runs as its own launch
+  st = run_down(a, orr, osh, sb16, T, s, false);
+  if (st != MOE_OK) return st;
+  return moe_combine(y_r, weights_dev, y_s, residual_dev, residual_dtype, T, has_routed ? k : 0, d, out_dev, out_dtype,
+                     stream);
 }

@@ -12,7 +12,10 @@
 //    walks its tokens kTM at a time: each wave stages the tokens' activation half-groups it consumes
 //    (the staging of the single-token kernel, repeated per token), computes the same dot2 chains, and
 //    the block adds the waves' partial sums in the same fixed order.  Each token's result is therefore
-//    bit-identical to the single-token kernel's; the arithmetic per code is shared by the tokens.
+//    bit-identical to the single-token kernel's; the codes cross HBM once for all of the group's tokens.
+//    kTM = 1: staging several tokens at once made the compiler keep every token's LDS addresses live
+//    (193 VGPRs at 4 tokens: 2 blocks per CU); one token per pass keeps 4 blocks per CU resident, which
+//    measured faster at 32 tokens (354 -> 273 us per layer).
 // The problem is bound by HBM (about 12 flops per weight byte at 32 tokens), so the dot products stay on
 // the vector ALUs; see q4_device.h for the dequantization.
 #include "q4_device.h"
@@ -20,7 +23,7 @@
 namespace moeq4 {
 namespace {
 
-constexpr int kTM = 4;               // tokens staged per pass
+constexpr int kTM = 1;               // tokens staged per pass
 constexpr int kGroupThreads = 256;
 
 __device__ __forceinline__ int bucket_of(int32_t e, int n_valid) { return (unsigned)e < (unsigned)n_valid ? e : n_valid; }
@@ -214,7 +217,8 @@ __device__ __forceinline__ void stage_tokens(const XT* const (&xs)[kTM], int nli
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Step 5 for each live token: the same dot2 chain as chunk_dot, with the codes dequantized once.
+// Step 5 for each live token: chunk_dot on the staged activation (the codes are dequantized again per
+// token: a few extra VALU operations instead of 32 more live registers per chunk).
 template <int NBW, bool SB_BF16>
 __device__ __forceinline__ void rowpair_dots(const RowPairRegs<NBW, SB_BF16>& r, int K, const Stage (&st)[kTM], int nlive,
                                              bool valid, float (&yA)[kTM], float (&yB)[kTM]) {
@@ -228,21 +232,6 @@ __device__ __forceinline__ void rowpair_dots(const RowPairRegs<NBW, SB_BF16>& r,
   for (int m = 0; m < NBW; ++m) {
     const int c = (wave + W * m) * kLanesPerRow + j;
     if (c >= C) continue;
-    uint32_t da[16], db[16];
-    const uint32_t wa[4] = {r.qa[m].x, r.qa[m].y, r.qa[m].z, r.qa[m].w};
-    const uint32_t wb[4] = {r.qb[m].x, r.qb[m].y, r.qb[m].z, r.qb[m].w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t va = wa[i], ta = va >> 8, vb = wb[i], tb = vb >> 8;
-      da[4 * i + 0] = (va & dq.lo) | dq.magic;
-      da[4 * i + 1] = (va & dq.hi) | dq.magic;
-      da[4 * i + 2] = (ta & dq.lo) | dq.magic;
-      da[4 * i + 3] = (ta & dq.hi) | dq.magic;
-      db[4 * i + 0] = (vb & dq.lo) | dq.magic;
-      db[4 * i + 1] = (vb & dq.hi) | dq.magic;
-      db[4 * i + 2] = (tb & dq.lo) | dq.magic;
-      db[4 * i + 3] = (tb & dq.hi) | dq.magic;
-    }
     float s0, b0, s1, b1;
     sb_values<SB_BF16>(r.sa[m], s0, b0);
     sb_values<SB_BF16>(r.sb[m], s1, b1);
@@ -250,23 +239,10 @@ __device__ __forceinline__ void rowpair_dots(const RowPairRegs<NBW, SB_BF16>& r,
     for (int tk = 0; tk < kTM; ++tk)
       if (tk < nlive) {
         const u32x4* xv = reinterpret_cast<const u32x4*>(st[tk].xw + c * kHgStride);
-        const u32x4 x4[4] = {xv[0], xv[1], xv[2], xv[3]};
+        const u32x4 x0 = xv[0], x1 = xv[1], x2 = xv[2], x3 = xv[3];
         const float4 h = st[tk].hg[c];
-        float accA = -h.y, accB = -h.y;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          accA = dot2(da[4 * i + 0], x4[i].x, accA);
-          accA = dot2(da[4 * i + 1], x4[i].y, accA);
-          accA = dot2(da[4 * i + 2], x4[i].z, accA);
-          accA = dot2(da[4 * i + 3], x4[i].w, accA);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          accB = dot2(db[4 * i + 0], x4[i].x, accB);
-          accB = dot2(db[4 * i + 1], x4[i].y, accB);
-          accB = dot2(db[4 * i + 2], x4[i].z, accB);
-          accB = dot2(db[4 * i + 3], x4[i].w, accB);
-        }
+        const float accA = chunk_dot(r.qa[m], x0, x1, x2, x3, dq, -h.y);
+        const float accB = chunk_dot(r.qb[m], x0, x1, x2, x3, dq, -h.y);
         yA[tk] = fmaf(h.x, fmaf(s0, accA, b0 * h.z), yA[tk]);
         yB[tk] = fmaf(h.x, fmaf(s1, accB, b1 * h.z), yB[tk]);
       }

@@ -206,10 +206,11 @@ moe_status moe_combine(const float* y_routed_dev, const float* weights_dev, cons
                        const void* residual_dev, moe_dtype residual_dtype, int32_t T, int32_t k, int32_t d,
                        void* out_dev, moe_dtype out_dtype, void* stream);
 
-/* q4_expert_gemv_combine — q4_expert_gemv followed by moe_combine in two launches instead of three: the
- * down GEMV's blocks publish their rows and the last block to finish a 16-row tile of token t applies the
+/* q4_expert_gemv_combine — q4_expert_gemv followed by moe_combine.  With T == 1 in two launches instead of
+ * three: the down GEMV's blocks publish their rows and the last block to finish a 16-row tile applies the
  * combine to it ([G26] "Concurrence pour masquer la latence": routed and shared outputs merged once all
- * are in).  Computes, for every token t,
+ * are in); with T > 1 the grouped down GEMV and the combine are separate launches (per-tile tickets for
+ * every token would cost more than the launch they save).  Computes, for every token t,
  *   out[t] = round_out( sum_{i<k} weights[t][i] * y_routed[t][i] + y_shared[t] + residual[t] )
  * with y_routed / y_shared as q4_expert_gemv defines them, summed in the same order as moe_combine; the
  * result is bit-identical to q4_expert_gemv + moe_combine on the same inputs.  y_routed and y_shared stay
