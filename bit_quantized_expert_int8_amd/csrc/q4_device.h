@@ -77,6 +77,15 @@ __device__ __forceinline__ Dequant make_dequant() {
   return k;
 }
 
+// make_dequant as values the compiler cannot see through from one call to the next: called inside a loop
+// over tokens whose codes stay the same, it keeps the dequantized words from being hoisted out of the
+// loop (which would hold 16 more registers per code chunk live for the whole loop).
+__device__ __forceinline__ Dequant opaque_dequant() {
+  Dequant k{0x000F000Fu, 0x00F000F0u, kMagic};
+  asm volatile("" : "+v"(k.lo), "+v"(k.hi), "+v"(k.magic));
+  return k;
+}
+
 // Dot product of one 16-byte chunk (4 words, 32 codes) with its staged activation (16 dwords),
 // accumulated onto `acc` (the caller passes -O, so the result is sum_c code[c] * x_scaled[c]).
 __device__ __forceinline__ float chunk_dot(u32x4 q, const u32x4 x0, const u32x4 x1, const u32x4 x2, const u32x4 x3,
@@ -337,6 +346,7 @@ struct GemvArgs {
   float* y_shared;         // [T][d]
   int32_t nb_shared;       // blocks of the shared expert per token
   int32_t nb_routed;       // blocks per routed expert
+  int32_t down_waves;      // grouped down: the waves of the one-token down launch (its summation order)
   int32_t act;
   // fused combine (down launch only): out[t] = round(sum_i w[t][i] y_routed[t][i] + y_shared[t] + residual[t])
   const float* weights;    // [T][k]
@@ -376,12 +386,12 @@ __device__ __forceinline__ void combine_tile(const GemvArgs& a, int t, int tile)
 // a.ids by expert into a.groups / a.perm / a.n_groups; the grouped gate_up and down launches then run
 // one block per (group, tile) and stream each selected expert's rows once for all of its tokens.
 constexpr int kMaxGroupedRecords = 4096;   // routed pool records supported with T > 1
+constexpr int kSharedTokens = 8;           // tokens per shared-expert block of the grouped kernels
 moe_status launch_group_pairs(const int32_t* ids, int P, int n_valid, int32_t* n_groups, int4* groups, int32_t* perm,
                               hipStream_t s);
 moe_status launch_gate_up_grouped(const GemvArgs& a, moe_dtype x_dtype, bool sb_bf16, int nbw, int waves, dim3 grid,
                                   hipStream_t s);
-moe_status launch_down_grouped(const GemvArgs& a, bool sb_bf16, bool combine, int nbw, int waves, dim3 grid, int K_lds,
-                               hipStream_t s);
+moe_status launch_down_grouped(const GemvArgs& a, bool sb_bf16, int nbw, dim3 grid, int K_lds, hipStream_t s);
 
 inline size_t lds_bytes(int K) { return (size_t)(K / 32) * (kHgStride * 4 + 16); }
 

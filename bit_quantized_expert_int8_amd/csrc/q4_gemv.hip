@@ -235,7 +235,8 @@ moe_status run_gate_up(GemvArgs a, const RecordOffsets& orr, const RecordOffsets
       if (st != MOE_OK) return st;
     }
     const int gmax = a.k > 0 ? groups_max(a.routed.n_records, T, a.k) : 0;
-    return launch_gate_up_grouped(a, x_dtype, sb_bf16, nbw, waves, dim3(a.nb_shared + gmax * a.nb_routed), s);
+    const int shared_blocks = a.nb_shared * ((T + kSharedTokens - 1) / kSharedTokens);
+    return launch_gate_up_grouped(a, x_dtype, sb_bf16, nbw, waves, dim3(shared_blocks + gmax * a.nb_routed), s);
   }
   dim3 grid(a.nb_shared + a.k * a.nb_routed, T);
   return dispatch_nbw(nbw, [&](auto nb) {
@@ -259,9 +260,15 @@ moe_status run_down(GemvArgs a, const RecordOffsets& orr, const RecordOffsets& o
   const int waves = nit_lo < kMaxWaves ? nit_lo : kMaxWaves;
   const int nbw = (nit_hi + waves - 1) / waves;
   if (T > 1) {
-    const int gmax = a.k > 0 ? groups_max(a.routed.n_records, T, a.k) : 0;
-    return launch_down_grouped(a, sb_bf16, combine, nbw, waves, dim3(a.nb_shared + gmax * a.nb_routed),
-                               nit_r > nit_s ? Fr : Fs, s);
+    // grouped: 64 rows per routed block (whole rows per wave), 16 shared rows per block and token chunk
+    if (combine) return fail(MOE_ERR_UNSUPPORTED, "q4_expert_gemv: the combine of several tokens is its own launch");
+    const int gmax = has_routed ? groups_max(a.routed.n_records, T, a.k) : 0;
+    a.nb_routed = a.d / 64;
+    const int shared_blocks = a.nb_shared * ((T + kSharedTokens - 1) / kSharedTokens);
+    a.down_waves = waves;   // the split of the one-token launch, so every token's rows come out the same
+    const int nbw_s = has_shared ? (nit_s + waves - 1) / waves : 1;
+    const int nbw_g = nbw_s > nit_r ? nbw_s : nit_r;
+    return launch_down_grouped(a, sb_bf16, nbw_g, dim3(shared_blocks + gmax * a.nb_routed), Fr > Fs ? Fr : Fs, s);
   }
   dim3 grid(a.nb_shared + a.k * a.nb_routed, T);
   return dispatch_nbw(nbw, [&](auto nb) {

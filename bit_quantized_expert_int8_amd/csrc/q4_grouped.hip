@@ -7,15 +7,18 @@
 //    exclusive scan over experts, then a stable placement (pairs of one expert keep ascending pair
 //    order) into perm; non-empty experts are listed in `groups`.  Ids outside the routed pool form one
 //    extra group whose outputs are NaN, as in the single-token kernels.
-// 2. grouped gate_up / down: one block per (group, 16-row tile), and one block per tile of the shared
-//    expert with all T tokens.  The block loads its rows' codes and scale/bias into registers once, then
-//    walks its tokens kTM at a time: each wave stages the tokens' activation half-groups it consumes
-//    (the staging of the single-token kernel, repeated per token), computes the same dot2 chains, and
-//    the block adds the waves' partial sums in the same fixed order.  Each token's result is therefore
-//    bit-identical to the single-token kernel's; the codes cross HBM once for all of the group's tokens.
-//    kTM = 1: staging several tokens at once made the compiler keep every token's LDS addresses live
-//    (193 VGPRs at 4 tokens: 2 blocks per CU); one token per pass keeps 4 blocks per CU resident, which
-//    measured faster at 32 tokens (354 -> 273 us per layer).
+// 2. grouped gate_up: one block per (group, 8 features), and per (8 shared features, chunk of up to 8
+//    tokens).  The block loads its rows' codes and scale/bias into registers once, then walks its tokens:
+//    each wave stages the token's activation half-groups it consumes (the staging of the single-token
+//    kernel), computes the same dot2 chains, and the block adds the waves' partial sums in the same fixed
+//    order.  One token per pass: staging several at once made the compiler keep every token's LDS
+//    addresses live (193 VGPRs at 4 tokens, 2 blocks per CU, measured slower).
+// 3. grouped down: routed blocks take 64 output rows of a group's expert, wave w rows 16w.. whole (the
+//    mapping of the single-launch layer's down blocks): per token the block stages h once, each wave
+//    reduces its rows within itself, no block-wide sum.  Shared blocks take 16 rows of the shared expert
+//    (waves split the long row) for a chunk of up to 8 tokens.
+// Every token's result is bit-identical to the single-token kernels'; the codes cross HBM once for all of
+// the group's tokens (the shared expert's once per 8 tokens, the rest from the caches).
 // The problem is bound by HBM (about 12 flops per weight byte at 32 tokens), so the dot products stay on
 // the vector ALUs; see q4_device.h for the dequantization.
 #include "q4_device.h"
@@ -118,16 +121,18 @@ struct GroupSlot {
 // The block's matrix and token list; false for blocks past the last non-empty group.
 __device__ __forceinline__ bool group_slot(const GemvArgs& a, GroupSlot& s) {
   int u = blockIdx.x;
-  s.shared = u < a.nb_shared;
+  const int nsb = a.nb_shared * ((a.T + kSharedTokens - 1) / kSharedTokens);
+  s.shared = u < nsb;
   s.valid = true;
   s.e = 0;
   s.start = 0;
   if (s.shared) {
-    s.tile = u;
-    s.count = a.T;
+    s.tile = u % a.nb_shared;
+    s.start = (u / a.nb_shared) * kSharedTokens;
+    s.count = min(kSharedTokens, a.T - s.start);
     return true;
   }
-  u -= a.nb_shared;
+  u -= nsb;
   const int j = u / a.nb_routed;
   s.tile = u % a.nb_routed;
   if (j >= *a.n_groups) return false;
@@ -141,7 +146,7 @@ __device__ __forceinline__ bool group_slot(const GemvArgs& a, GroupSlot& s) {
 
 // pair index (t*k + i; the token itself for the shared expert) of entry c of the block's token list
 __device__ __forceinline__ int pair_of(const GemvArgs& a, const GroupSlot& s, int c) {
-  return s.shared ? c : a.perm[s.start + c];
+  return s.shared ? s.start + c : a.perm[s.start + c];
 }
 
 template <int NBW, bool SB_BF16>
@@ -153,8 +158,8 @@ struct RowPairRegs {
 // Steps 2-3 of the single-token row-pair routine: this lane's scale/bias words and code chunks.
 template <int NBW, bool SB_BF16>
 __device__ __forceinline__ void load_rowpair(const char* rowA, const char* rowB, const char* sbA, const char* sbB, int K,
-                                             bool valid, RowPairRegs<NBW, SB_BF16>& r) {
-  const int W = blockDim.x >> 6, wave = threadIdx.x >> 6, j = threadIdx.x & 7;
+                                             bool valid, RowPairRegs<NBW, SB_BF16>& r, int W) {
+  const int wave = threadIdx.x >> 6, j = threadIdx.x & 7;
   const int C = K / 32;
   if (!valid) return;
 #pragma unroll
@@ -177,8 +182,8 @@ __device__ __forceinline__ void load_rowpair(const char* rowA, const char* rowB,
 
 // Steps 1 and 4: stage the first `nlive` of kTM activation vectors (this wave's half-groups of each).
 template <int NBW, typename XT>
-__device__ __forceinline__ void stage_tokens(const XT* const (&xs)[kTM], int nlive, int K, const Stage (&st)[kTM]) {
-  const int W = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__device__ __forceinline__ void stage_tokens(const XT* const (&xs)[kTM], int nlive, int K, const Stage (&st)[kTM], int W) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int C = K / 32, nit = (C + kLanesPerRow - 1) / kLanesPerRow;
   constexpr int kPasses = (NBW * 32 + 63) / 64;
   XWord<XT> xw[kTM][kPasses];
@@ -221,13 +226,13 @@ __device__ __forceinline__ void stage_tokens(const XT* const (&xs)[kTM], int nli
 // token: a few extra VALU operations instead of 32 more live registers per chunk).
 template <int NBW, bool SB_BF16>
 __device__ __forceinline__ void rowpair_dots(const RowPairRegs<NBW, SB_BF16>& r, int K, const Stage (&st)[kTM], int nlive,
-                                             bool valid, float (&yA)[kTM], float (&yB)[kTM]) {
-  const int W = blockDim.x >> 6, wave = threadIdx.x >> 6, j = threadIdx.x & 7;
+                                             bool valid, float (&yA)[kTM], float (&yB)[kTM], int W) {
+  const int wave = threadIdx.x >> 6, j = threadIdx.x & 7;
   const int C = K / 32;
 #pragma unroll
   for (int tk = 0; tk < kTM; ++tk) yA[tk] = yB[tk] = 0.f;
   if (!valid) return;
-  const Dequant dq = make_dequant();
+  const Dequant dq = opaque_dequant();
 #pragma unroll
   for (int m = 0; m < NBW; ++m) {
     const int c = (wave + W * m) * kLanesPerRow + j;
@@ -251,17 +256,17 @@ __device__ __forceinline__ void rowpair_dots(const RowPairRegs<NBW, SB_BF16>& r,
 
 // block_sum for kTM tokens (same order: 8 lanes, then waves 0..W-1).  The caller must pass a block
 // barrier before the next call (the LDS partials are reused).
-__device__ __forceinline__ bool block_sum_tokens(float (&yA)[kTM], float (&yB)[kTM], int nlive) {
+__device__ __forceinline__ bool block_sum_tokens(float (&yA)[kTM], float (&yB)[kTM], int nlive, int W) {
   __shared__ float red[kMaxWaves][kTM][16];
-  const int W = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63, ra = lane >> 3, j = lane & 7;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, ra = lane >> 3, j = lane & 7;
 #pragma unroll
   for (int tk = 0; tk < kTM; ++tk)
     if (tk < nlive) {
       yA[tk] = reduce8(yA[tk]);
       yB[tk] = reduce8(yB[tk]);
     }
-  if (W == 1) return j == 0;
-  if (j == 0) {
+  if (W == 1 && blockDim.x == 64) return j == 0;
+  if (j == 0 && wave < W) {
 #pragma unroll
     for (int tk = 0; tk < kTM; ++tk)
       if (tk < nlive) {
@@ -304,7 +309,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gate_up_grouped_kernel(GemvArg
   const int64_t rowb = K / 2, sbrow = (int64_t)(K / 64) * (SB_BF16 ? 4 : 8);
   RowPairRegs<NBW, SB_BF16> w;
   load_rowpair<NBW, SB_BF16>(rec + P.off_q + f * rowb, rec + P.off_q + (F + f) * rowb, rec + P.off_sb + f * sbrow,
-                             rec + P.off_sb + (F + f) * sbrow, K, sl.valid, w);
+                             rec + P.off_sb + (F + f) * sbrow, K, sl.valid, w, blockDim.x >> 6);
   Stage st[kTM];
   make_stages(lds, nhg, st);
   const XT* x = reinterpret_cast<const XT*>(a.in);
@@ -318,10 +323,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gate_up_grouped_kernel(GemvArg
       pair[tk] = tk < nlive ? pair_of(a, sl, c0 + tk) : 0;
       xs[tk] = x + (int64_t)(sl.shared ? pair[tk] : pair[tk] / a.k) * K;
     }
-    stage_tokens<NBW, XT>(xs, nlive, K, st);
+    stage_tokens<NBW, XT>(xs, nlive, K, st, blockDim.x >> 6);
     float yA[kTM], yB[kTM];
-    rowpair_dots<NBW, SB_BF16>(w, K, st, nlive, sl.valid, yA, yB);
-    if (block_sum_tokens(yA, yB, nlive)) {
+    rowpair_dots<NBW, SB_BF16>(w, K, st, nlive, sl.valid, yA, yB, blockDim.x >> 6);
+    if (block_sum_tokens(yA, yB, nlive, blockDim.x >> 6)) {
 #pragma unroll
       for (int tk = 0; tk < kTM; ++tk)
         if (tk < nlive)
@@ -331,27 +336,117 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gate_up_grouped_kernel(GemvArg
   }
 }
 
-template <int NBW, bool SB_BF16, bool COMBINE>
+// The 64-row routed block: lane (ra, j) of wave w takes rows r = tile * 64 + 16 w + ra and r + 8, chunks
+// m * 8 + j of the whole row (NBW >= the row's chunk iterations).
+template <int NBW, bool SB_BF16>
+__device__ __forceinline__ void down_routed_rows(const GemvArgs& a, const GroupSlot& sl, uint32_t* lds) {
+  const Pool& P = a.routed;
+  const int W = a.down_waves;
+  const int d = a.d, K = P.F, nhg = K / 32, C = K / 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, ra = lane >> 3, j = lane & 7;
+  const int r = sl.tile * 64 + wave * 16 + ra;
+  const char* rec = P.base + (int64_t)sl.e * P.record_bytes;
+  const int64_t rowb = K / 2, sbrow = (int64_t)(K / 64) * (SB_BF16 ? 4 : 8);
+  SbWord<SB_BF16> sa[NBW], sb[NBW];
+  u32x4 qa[NBW], qb[NBW];
+  if (sl.valid) {
+#pragma unroll
+    for (int m = 0; m < NBW; ++m) {
+      const int c = m * kLanesPerRow + j;
+      if (c < C) {
+        sa[m] = load_sb<SB_BF16>(rec + P.off_sb + r * sbrow, c >> 1);
+        sb[m] = load_sb<SB_BF16>(rec + P.off_sb + (r + 8) * sbrow, c >> 1);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < NBW; ++m) {
+      const int c = m * kLanesPerRow + j;
+      if (c < C) {
+        qa[m] = load_nt(rec + P.off_q + r * rowb + c * 16);
+        qb[m] = load_nt(rec + P.off_q + (r + 8) * rowb + c * 16);
+      }
+    }
+  }
+  const Stage st{lds, reinterpret_cast<float4*>(lds + nhg * kHgStride)};
+  for (int c0 = 0; c0 < sl.count; ++c0) {
+    const int pair = pair_of(a, sl, c0);
+    const Dequant dq = opaque_dequant();
+    // the token's h, staged by the block (one (half-group, quarter) item per thread)
+    for (int t = threadIdx.x; t < nhg * 4; t += blockDim.x) {
+      const int hg = t >> 2, qd = t & 3;
+      const float4* hv = reinterpret_cast<const float4*>(a.h_routed + (int64_t)pair * K + hg * 32 + qd * 8);
+      const float4 h0 = hv[0], h1 = hv[1];
+      const float v[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+      stage_word(v, true, hg, qd, st);
+    }
+    __syncthreads();
+    // chunk iteration m belongs to wave m % W of the one-token launch: one partial per such wave, each
+    // summed over its 8 lanes, then added in wave order (that launch's association, bit for bit)
+    float pa[kMaxWaves], pb[kMaxWaves];
+#pragma unroll
+    for (int w = 0; w < kMaxWaves; ++w) pa[w] = pb[w] = 0.f;
+    if (sl.valid) {
+#pragma unroll
+      for (int m = 0; m < NBW; ++m) {
+        const int c = m * kLanesPerRow + j;
+        if (c < C) {
+          const u32x4* xv = reinterpret_cast<const u32x4*>(st.xw + c * kHgStride);
+          const u32x4 x0 = xv[0], x1 = xv[1], x2 = xv[2], x3 = xv[3];
+          const float4 h = st.hg[c];
+          const float accA = chunk_dot(qa[m], x0, x1, x2, x3, dq, -h.y);
+          const float accB = chunk_dot(qb[m], x0, x1, x2, x3, dq, -h.y);
+          float s0, b0, s1, b1;
+          sb_values<SB_BF16>(sa[m], s0, b0);
+          sb_values<SB_BF16>(sb[m], s1, b1);
+#pragma unroll
+          for (int w = 0; w < kMaxWaves; ++w)
+            if (m % W == w) {
+              pa[w] = fmaf(h.x, fmaf(s0, accA, b0 * h.z), pa[w]);
+              pb[w] = fmaf(h.x, fmaf(s1, accB, b1 * h.z), pb[w]);
+            }
+        }
+      }
+    }
+    float yA = reduce8(pa[0]), yB = reduce8(pb[0]);
+#pragma unroll
+    for (int w = 1; w < kMaxWaves; ++w)
+      if (w < W) {
+        yA += reduce8(pa[w]);
+        yB += reduce8(pb[w]);
+      }
+    if (j == 0) {
+      float* y = a.y_routed + (int64_t)pair * d;
+      y[r] = sl.valid ? yA : __builtin_nanf("");
+      y[r + 8] = sl.valid ? yB : __builtin_nanf("");
+    }
+    __syncthreads();   // the staging area is rewritten for the next token
+  }
+}
+
+template <int NBW, bool SB_BF16>
 __global__ __launch_bounds__(64 * kMaxWaves) void down_grouped_kernel(GemvArgs a) {
   extern __shared__ __align__(16) uint32_t lds[];
-  __shared__ uint32_t lastf[kTM];
   GroupSlot sl;
   if (!group_slot(a, sl)) return;
-  const Pool& P = sl.shared ? a.shared : a.routed;
+  if (!sl.shared) {
+    down_routed_rows<NBW, SB_BF16>(a, sl, lds);
+    return;
+  }
+  // 16 rows of the shared expert, the first down_waves waves split the row (K = S), as in the one-token
+  // launch; the others only take part in the block's barriers
+  const int W = a.down_waves;
+  const bool active = (int)(threadIdx.x >> 6) < W;
+  const Pool& P = a.shared;
   const int d = a.d, K = P.F, nhg = K / 32;
   const int ra = (threadIdx.x & 63) >> 3;
   const int r = sl.tile * 16 + ra;
-  const char* rec = P.base + (int64_t)sl.e * P.record_bytes;
+  const char* rec = P.base;
   const int64_t rowb = K / 2, sbrow = (int64_t)(K / 64) * (SB_BF16 ? 4 : 8);
   RowPairRegs<NBW, SB_BF16> w;
   load_rowpair<NBW, SB_BF16>(rec + P.off_q + r * rowb, rec + P.off_q + (r + 8) * rowb, rec + P.off_sb + r * sbrow,
-                             rec + P.off_sb + (r + 8) * sbrow, K, sl.valid, w);
+                             rec + P.off_sb + (r + 8) * sbrow, K, active, w, W);
   Stage st[kTM];
   make_stages(lds, nhg, st);
-  const float* hbase = sl.shared ? a.h_shared : a.h_routed;
-  float* ybase = sl.shared ? a.y_shared : a.y_routed;
-  const uint32_t units = (uint32_t)a.k + (a.nb_shared ? 1u : 0u);
-  const int ntiles = d / 16;
   for (int c0 = 0; c0 < sl.count; c0 += kTM) {
     const int nlive = min(kTM, sl.count - c0);
     int pair[kTM];
@@ -359,52 +454,18 @@ __global__ __launch_bounds__(64 * kMaxWaves) void down_grouped_kernel(GemvArgs a
 #pragma unroll
     for (int tk = 0; tk < kTM; ++tk) {
       pair[tk] = tk < nlive ? pair_of(a, sl, c0 + tk) : 0;
-      xs[tk] = hbase + (int64_t)pair[tk] * K;
+      xs[tk] = a.h_shared + (int64_t)pair[tk] * K;
     }
-    stage_tokens<NBW, float>(xs, nlive, K, st);
+    if (active) stage_tokens<NBW, float>(xs, nlive, K, st, W);
     float yA[kTM], yB[kTM];
-    rowpair_dots<NBW, SB_BF16>(w, K, st, nlive, sl.valid, yA, yB);
-    const bool total = block_sum_tokens(yA, yB, nlive);
-    if (!COMBINE) {
-      if (total) {
-#pragma unroll
-        for (int tk = 0; tk < kTM; ++tk)
-          if (tk < nlive) {
-            float* y = ybase + (int64_t)pair[tk] * d;
-            y[r] = sl.valid ? yA[tk] : __builtin_nanf("");
-            y[r + 8] = sl.valid ? yB[tk] : __builtin_nanf("");
-          }
-      }
-    } else {
-      // publish, take one ticket per token, and combine the tiles this block completed (see down_kernel)
-      if (total) {
-#pragma unroll
-        for (int tk = 0; tk < kTM; ++tk)
-          if (tk < nlive) {
-            float* y = ybase + (int64_t)pair[tk] * d;
-            __hip_atomic_store(y + r, sl.valid ? yA[tk] : __builtin_nanf(""), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(y + r + 8, sl.valid ? yB[tk] : __builtin_nanf(""), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-          }
-      }
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+    rowpair_dots<NBW, SB_BF16>(w, K, st, nlive, active, yA, yB, W);
+    if (block_sum_tokens(yA, yB, nlive, W)) {
 #pragma unroll
       for (int tk = 0; tk < kTM; ++tk)
-        if (tk < nlive && (int)threadIdx.x == tk) {
-          const int t = sl.shared ? pair[tk] : pair[tk] / a.k;
-          uint32_t* ctr = a.tile_counters + (int64_t)t * ntiles + sl.tile;
-          lastf[tk] = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == units - 1;
-        }
-      __syncthreads();
-#pragma unroll
-      for (int tk = 0; tk < kTM; ++tk)
-        if (tk < nlive && lastf[tk] && threadIdx.x < 16) {
-          const int t = sl.shared ? pair[tk] : pair[tk] / a.k;
-          combine_tile(a, t, sl.tile);
-          if (threadIdx.x == 0)
-            __hip_atomic_store(a.tile_counters + (int64_t)t * ntiles + sl.tile, 0u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+        if (tk < nlive) {
+          float* y = a.y_shared + (int64_t)pair[tk] * d;
+          y[r] = yA[tk];
+          y[r + 8] = yB[tk];
         }
     }
     __syncthreads();
@@ -436,19 +497,13 @@ moe_status launch_gate_up_grouped(const GemvArgs& a, moe_dtype x_dtype, bool sb_
   });
 }
 
-moe_status launch_down_grouped(const GemvArgs& a, bool sb_bf16, bool combine, int nbw, int waves, dim3 grid, int K_lds,
-                               hipStream_t s) {
-  const dim3 block(64 * waves);
+moe_status launch_down_grouped(const GemvArgs& a, bool sb_bf16, int nbw, dim3 grid, int K_lds, hipStream_t s) {
+  const dim3 block(64 * kMaxWaves);
   const size_t lds = kTM * lds_bytes(K_lds);
   return dispatch_nbw(nbw, [&](auto nb) {
     constexpr int N = decltype(nb)::value;
-    if (combine) {
-      if (sb_bf16) hipLaunchKernelGGL((down_grouped_kernel<N, true, true>), grid, block, lds, s, a);
-      else hipLaunchKernelGGL((down_grouped_kernel<N, false, true>), grid, block, lds, s, a);
-    } else {
-      if (sb_bf16) hipLaunchKernelGGL((down_grouped_kernel<N, true, false>), grid, block, lds, s, a);
-      else hipLaunchKernelGGL((down_grouped_kernel<N, false, false>), grid, block, lds, s, a);
-    }
+    if (sb_bf16) hipLaunchKernelGGL((down_grouped_kernel<N, true>), grid, block, lds, s, a);
+    else hipLaunchKernelGGL((down_grouped_kernel<N, false>), grid, block, lds, s, a);
     return check_launch("q4_expert_gemv(down, grouped)");
   });
 }
