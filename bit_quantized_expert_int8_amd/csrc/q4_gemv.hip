@@ -377,3 +377,73 @@ extern "C" moe_status q4_expert_gemv_combine(const moe_q4_pool* routed, const in
   return moe_combine(y_r, weights_dev, y_s, residual_dev, residual_dtype, T, has_routed ? k : 0, d, out_dev, out_dtype,
                      stream);
 }
+
+// ------------------------------------------------------------------------------------------------
+// q4_gemv: one 4-bit affine matrix [N][K] times T vectors, with the row-pair routine of the expert
+// kernels (same staging, dequantization and fixed-order wave sum), so its results are those of one
+// expert matrix inside q4_expert_gemv.  A block owns 16 rows; rows past N in a ragged last tile read row
+// N - 1 and are not stored.
+// ------------------------------------------------------------------------------------------------
+namespace moeq4 {
+namespace {
+
+struct MatArgs {
+  const void* x;      // x dtype [T][K]
+  const char* q;      // uint32 [N][K/8]
+  const char* sb;     // sb dtype [N][K/64][2]
+  float* y;           // [T][N]
+  int32_t N, K, sb_row_bytes;
+};
+
+template <int NBW, typename XT, bool SB_BF16>
+__global__ __launch_bounds__(64 * kMaxWaves) void matrix_gemv_kernel(MatArgs m) {
+  extern __shared__ __align__(16) uint32_t lds[];
+  const int C = m.K / 32, t = blockIdx.y, ra = (threadIdx.x & 63) >> 3;
+  const int rA = blockIdx.x * 16 + ra, rB = rA + 8;
+  const int lA = min(rA, m.N - 1), lB = min(rB, m.N - 1);
+  const Stage st{lds, reinterpret_cast<float4*>(lds + C * kHgStride)};
+  float yA, yB;
+  rowpair_partial<NBW, XT, SB_BF16>(m.q + (int64_t)lA * (m.K / 2), m.q + (int64_t)lB * (m.K / 2),
+                                    m.sb + (int64_t)lA * m.sb_row_bytes, m.sb + (int64_t)lB * m.sb_row_bytes,
+                                    reinterpret_cast<const XT*>(m.x) + (int64_t)t * m.K, m.K, st, true, yA, yB);
+  if (!block_sum(yA, yB)) return;
+  float* y = m.y + (int64_t)t * m.N;
+  if (rA < m.N) y[rA] = yA;
+  if (rB < m.N) y[rB] = yB;
+}
+
+}  // namespace
+}  // namespace moeq4
+
+extern "C" moe_status q4_gemv(const void* x_dev, moe_dtype x_dtype, int32_t T, const uint32_t* codes_dev,
+                              const void* sb_dev, moe_dtype sb_dtype, int32_t N, int32_t K, float* y_dev, void* stream) {
+  const char* who = "q4_gemv";
+  if (!x_dev || !codes_dev || !sb_dev || !y_dev) return fail(MOE_ERR_INVALID_ARG, "%s: NULL pointer", who);
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "%s: bad x_dtype", who);
+  if (sb_dtype != MOE_F32 && sb_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "%s: bad sb_dtype", who);
+  if (T < 1 || T > 65535 || N < 1 || K < 64 || K % 64 != 0 || K > kMaxK)
+    return fail(MOE_ERR_INVALID_ARG, "%s: T=%d N=%d K=%d (need 1 <= T <= 65535, N >= 1, K a multiple of 64, <= %d)",
+                who, T, N, K, kMaxK);
+  if (!aligned(x_dev, 16) || !aligned(codes_dev, 16) || !aligned(sb_dev, 8))
+    return fail(MOE_ERR_INVALID_ARG, "%s: x and codes must be 16-byte aligned, sb 8-byte aligned", who);
+  const int nit = iterations(K);
+  const int waves = nit < kMaxWaves ? nit : kMaxWaves;
+  const int nbw = (nit + waves - 1) / waves;
+  const int sb_elem = sb_dtype == MOE_BF16 ? 2 : 4;
+  const moeq4::MatArgs m{x_dev, reinterpret_cast<const char*>(codes_dev), reinterpret_cast<const char*>(sb_dev),
+                         y_dev, N, K, (K / 64) * 2 * sb_elem};
+  const dim3 grid((N + 15) / 16, T), block(64 * waves);
+  const size_t lds = lds_bytes(K);
+  hipStream_t s = as_stream(stream);
+  return dispatch_nbw(nbw, [&](auto nb) {
+    constexpr int NB = decltype(nb)::value;
+    if (x_dtype == MOE_BF16) {
+      if (sb_dtype == MOE_BF16) hipLaunchKernelGGL((moeq4::matrix_gemv_kernel<NB, uint16_t, true>), grid, block, lds, s, m);
+      else hipLaunchKernelGGL((moeq4::matrix_gemv_kernel<NB, uint16_t, false>), grid, block, lds, s, m);
+    } else {
+      if (sb_dtype == MOE_BF16) hipLaunchKernelGGL((moeq4::matrix_gemv_kernel<NB, float, true>), grid, block, lds, s, m);
+      else hipLaunchKernelGGL((moeq4::matrix_gemv_kernel<NB, float, false>), grid, block, lds, s, m);
+    }
+    return check_launch(who);
+  });
+}

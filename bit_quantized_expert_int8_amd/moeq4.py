@@ -62,6 +62,7 @@ _c = {
     "moe_record_layout": _sig("moe_record_layout", _st, [_i32, _i32, ctypes.c_int, ctypes.POINTER(_sz)]),
     "q4_quantize": _sig("q4_quantize", _st, [_vp, _i32, _i32, ctypes.c_int, _vp, _vp, _vp]),
     "q4_pack_expert": _sig("q4_pack_expert", _st, [_vp, _vp, _i32, _i32, ctypes.c_int, _vp, _vp]),
+    "q4_gemv": _sig("q4_gemv", _st, [_vp, ctypes.c_int, _i32, _vp, _vp, ctypes.c_int, _i32, _i32, _vp, _vp]),
     "moe_rmsnorm": _sig("moe_rmsnorm", _st, [_vp, ctypes.c_int, _vp, ctypes.c_float, _i32, _i32, _vp, ctypes.c_int, _vp]),
     "moe_router_workspace_bytes": _sig("moe_router_workspace_bytes", _sz, [_i32, _i32]),
     "moe_router_topk": _sig("moe_router_topk", _st, [_vp, ctypes.c_int, _i32, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp,
@@ -166,6 +167,10 @@ def q4_quantize(w, N, K, sb_dtype, codes, sb, stream=None) -> None:
 
 def q4_pack_expert(w_gate_up, w_down, d, F, sb_dtype, record, stream=None) -> None:
     _check(_c["q4_pack_expert"](_p(w_gate_up), _p(w_down), d, F, sb_dtype, _p(record), _s(stream)), "q4_pack_expert")
+
+
+def q4_gemv(x, x_dtype, T, codes, sb, sb_dtype, N, K, y, stream=None) -> None:
+    _check(_c["q4_gemv"](_p(x), x_dtype, T, _p(codes), _p(sb), sb_dtype, N, K, _p(y), _s(stream)), "q4_gemv")
 
 
 def moe_rmsnorm(x, x_dtype, gamma, eps, T, d, out, out_dtype, stream=None) -> None:

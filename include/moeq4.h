@@ -97,7 +97,24 @@ moe_status q4_pack_expert(const float* w_gate_up_dev, const float* w_down_dev, i
                           moe_dtype sb_dtype, void* record_dev, void* stream);
 
 /* ---------------------------------------------------------------------------------------------------
- * moe_rmsnorm — u[t] = x[t] / sqrt(mean(x[t]^2) + eps) * gamma, fp32 math, rounded to out_dtype (RNE).
+ * q4_gemv — one 4-bit affine matrix times T vectors, no activation ([LEAF] "Du code sur-mesure sans
+ * dépendance externe": fused dequantize + matrix-vector kernels; [REMIO] "L'affirmation des 2 Go fait de
+ * la bande passante SSD la nouvelle contrainte": MLX affine 4-bit weights):
+ *   y[t][r] = sum_c (scale[r][c/64] * code[r][c] + bias[r][c/64]) * x[t][c]        fp32
+ * Uses the row routine of q4_expert_gemv (same dequantization, accumulation and summation order), so a
+ * result equals that of the same matrix inside an expert record; with x = e_j it is column j of the
+ * dequantized matrix.
+ * x_dev: x_dtype [T][K] (fp32 or bf16), 16-byte aligned; codes_dev: uint32 [N][K/8], 16-byte aligned,
+ * code of column c in word c/8, bits 4*(c%8) (q4_quantize's output); sb_dev: sb_dtype [N][K/64][2]
+ * (scale, bias), 8-byte aligned; y_dev: fp32 [T][N].  All device memory owned by the caller.
+ * Limits: 1 <= T <= 65535, N >= 1, K a multiple of 64 with 64 <= K <= 8192 (MOE_ERR_INVALID_ARG otherwise;
+ * nothing is launched).  Asynchronous on `stream`.
+ * ------------------------------------------------------------------------------------------------- */
+moe_status q4_gemv(const void* x_dev, moe_dtype x_dtype, int32_t T, const uint32_t* codes_dev, const void* sb_dev,
+                   moe_dtype sb_dtype, int32_t N, int32_t K, float* y_dev, void* stream);
+
+/* ---------------------------------------------------------------------------------------------------
+ * moe_rmsnorm —u[t] = x[t] / sqrt(mean(x[t]^2) + eps) * gamma, fp32 math, rounded to out_dtype (RNE).
  * The pages list a normalisation (RMSNorm) kernel ([LEAF] "Du code sur-mesure sans dépendance externe";
  * [DEVT] "Geen afhankelijkheden van llama.cpp en MLX"); it precedes each MoE block in the stacked decode.
  * x_dev: x_dtype [T][d]; gamma_dev: fp32 [d]; out_dev: out_dtype [T][d].  d % 8 == 0, d <= 16384, T >= 1;

@@ -51,6 +51,15 @@ def test_host_validation_errors():
     assert _status("q4_quantize", None, 4, 64, 1, 16, 16, None) == q.MOE_ERR_INVALID_ARG
     assert _status("q4_quantize", 16, 4, 60, 1, 16, 16, None) == q.MOE_ERR_INVALID_ARG
     assert "multiple of 64" in q.moe_last_error()
+    # q4_gemv: K not a multiple of 64, K too large, N = 0, T = 0, NULL codes, misaligned x, bad dtype
+    g = lambda x, T, codes, N, K, sbt=1: _status("q4_gemv", x, 0, T, codes, 256, sbt, N, K, 256, None)
+    assert g(256, 1, 256, 16, 96) == q.MOE_ERR_INVALID_ARG and "multiple of 64" in q.moe_last_error()
+    assert g(256, 1, 256, 16, 8256) == q.MOE_ERR_INVALID_ARG
+    assert g(256, 1, 256, 0, 64) == q.MOE_ERR_INVALID_ARG
+    assert g(256, 0, 256, 16, 64) == q.MOE_ERR_INVALID_ARG
+    assert g(256, 1, None, 16, 64) == q.MOE_ERR_INVALID_ARG and "NULL" in q.moe_last_error()
+    assert g(256 + 4, 1, 256, 16, 64) == q.MOE_ERR_INVALID_ARG and "aligned" in q.moe_last_error()
+    assert g(256, 1, 256, 16, 64, sbt=7) == q.MOE_ERR_INVALID_ARG
     assert _status("moe_rmsnorm", 16, 1, 16, ctypes.c_float(1e-6), 0, 64, 16, 1, None) == q.MOE_ERR_INVALID_ARG
     # k > E, E too large, d not a multiple of 16
     args = lambda T, d, E, k, ws: (256, 1, T, d, 256, 256, E, k, None, 256, 256, None, 256, ws, None)
