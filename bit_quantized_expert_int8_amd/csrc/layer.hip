@@ -208,50 +208,67 @@ __device__ __forceinline__ float u_of(float xg, float rinv) {
 }
 
 // u[0..d) into LDS: u[j] = round_x((x[j] * gamma[j]) * rinv), rinv = 1 / sqrt(sum_j x[j]^2 / d + eps), or
-// u = x without gamma.  Every load is issued before the first use.  Fixed reduction order: per thread
-// over its elements in index order, the wavefront sum, then the four waves in order (every thread adds
-// the four partial sums itself, the same way).
-template <typename XT>
-__device__ __forceinline__ void norm_to_lds(const LayerArgs& a, float* u, NormLds& nl) {
+// u = x without gamma.  Fixed reduction order: per thread over its elements in index order, the wavefront
+// sum, then the four waves in order (every thread adds the four partial sums itself, the same way).
+// Every load of x and gamma is issued before the first use, without branches in between (an element
+// index past d reads element 0, which is discarded): a conversion or a branch between two loads makes the
+// compiler wait for the first before issuing the second.  The forms (x a previous layer's fp32 output read
+// with coherent loads; with or without gamma) are separate instantiations for the same reason.
+template <typename XT, bool XF32, bool GAMMA>
+__device__ __forceinline__ void norm_to_lds_impl(const LayerArgs& a, float* u, NormLds& nl) {
   constexpr int kIt = kLayerMaxD / (kThreads * 8);
+  constexpr int kXw = (XF32 || sizeof(XT) == 4) ? 2 : 1;   // 16-byte words per 8 elements
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float v[kIt][8], g[kIt][8];
+  bool live[kIt];
+  uint4 xw[kIt][kXw];
+  float4 gw[kIt][2];
 #pragma unroll
   for (int it = 0; it < kIt; ++it) {
-    const int j0 = (threadIdx.x + it * kThreads) * 8;
-    if (j0 >= a.d) continue;
-    if (a.x_f32) {
-      const float* xf = reinterpret_cast<const float*>(a.x);
+    const int j = (threadIdx.x + it * kThreads) * 8;
+    live[it] = j < a.d;
+    const int j0 = live[it] ? j : 0;
+    if (XF32) {
+      const float* xf = reinterpret_cast<const float*>(a.x) + j0;
+      xw[it][0] = make_uint4(__float_as_uint(ld_c(xf)), __float_as_uint(ld_c(xf + 1)), __float_as_uint(ld_c(xf + 2)),
+                             __float_as_uint(ld_c(xf + 3)));
+      xw[it][kXw - 1] = make_uint4(__float_as_uint(ld_c(xf + 4)), __float_as_uint(ld_c(xf + 5)),
+                                   __float_as_uint(ld_c(xf + 6)), __float_as_uint(ld_c(xf + 7)));
+    } else {
+      const uint4* xp = reinterpret_cast<const uint4*>(reinterpret_cast<const XT*>(a.x) + j0);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[it][i] = ld_c(xf + j0 + i);
-    } else if (sizeof(XT) == 2) {
-      const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const XT*>(a.x) + j0);
-      const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+      for (int w = 0; w < kXw; ++w) xw[it][w] = xp[w];
+    }
+    if (GAMMA) {
+      gw[it][0] = reinterpret_cast<const float4*>(a.gamma + j0)[0];
+      gw[it][1] = reinterpret_cast<const float4*>(a.gamma + j0)[1];
+    }
+  }
+  float v[kIt][8];
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    if (kXw == 1) {
+      const uint32_t q[4] = {xw[it][0].x, xw[it][0].y, xw[it][0].z, xw[it][0].w};
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         v[it][2 * m] = __uint_as_float(q[m] << 16);
         v[it][2 * m + 1] = __uint_as_float(q[m] & 0xffff0000u);
       }
     } else {
-      const float4* xf = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + j0);
-      const float4 p0 = xf[0], p1 = xf[1];
-      v[it][0] = p0.x; v[it][1] = p0.y; v[it][2] = p0.z; v[it][3] = p0.w;
-      v[it][4] = p1.x; v[it][5] = p1.y; v[it][6] = p1.z; v[it][7] = p1.w;
-    }
-    if (a.gamma) {
-      const float4 g0 = reinterpret_cast<const float4*>(a.gamma + j0)[0], g1 = reinterpret_cast<const float4*>(a.gamma + j0)[1];
-      g[it][0] = g0.x; g[it][1] = g0.y; g[it][2] = g0.z; g[it][3] = g0.w;
-      g[it][4] = g1.x; g[it][5] = g1.y; g[it][6] = g1.z; g[it][7] = g1.w;
+      const uint32_t q[8] = {xw[it][0].x, xw[it][0].y, xw[it][0].z, xw[it][0].w,
+                             xw[it][kXw - 1].x, xw[it][kXw - 1].y, xw[it][kXw - 1].z, xw[it][kXw - 1].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[it][i] = __uint_as_float(q[i]);
     }
   }
   float rinv = 1.0f;
-  if (a.gamma) {
+  if (GAMMA) {
     float ss = 0.f;
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
-      if ((int)(threadIdx.x + it * kThreads) * 8 >= a.d) continue;
+      float si = ss;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ss = fmaf(v[it][i], v[it][i], ss);
+      for (int i = 0; i < 8; ++i) si = fmaf(v[it][i], v[it][i], si);
+      ss = live[it] ? si : ss;
     }
     ss = wave_sum(ss);
     if (lane == 0) nl.wsum[wave] = ss;
@@ -263,15 +280,29 @@ __device__ __forceinline__ void norm_to_lds(const LayerArgs& a, float* u, NormLd
   }
 #pragma unroll
   for (int it = 0; it < kIt; ++it) {
+    if (!live[it]) continue;
     const int j0 = (threadIdx.x + it * kThreads) * 8;
-    if (j0 >= a.d) continue;
     float o[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = a.gamma ? u_of<XT>(v[it][i] * g[it][i], rinv) : v[it][i];
+    for (int i = 0; i < 8; ++i) {
+      const float gi = i < 4 ? (&gw[it][0].x)[i] : (&gw[it][1].x)[i - 4];
+      o[i] = GAMMA ? u_of<XT>(v[it][i] * gi, rinv) : v[it][i];
+    }
     reinterpret_cast<float4*>(u + j0)[0] = make_float4(o[0], o[1], o[2], o[3]);
     reinterpret_cast<float4*>(u + j0)[1] = make_float4(o[4], o[5], o[6], o[7]);
   }
   __syncthreads();
+}
+
+template <typename XT>
+__device__ __forceinline__ void norm_to_lds(const LayerArgs& a, float* u, NormLds& nl) {
+  if (a.x_f32) {
+    if (a.gamma) norm_to_lds_impl<XT, true, true>(a, u, nl);
+    else norm_to_lds_impl<XT, true, false>(a, u, nl);
+  } else {
+    if (a.gamma) norm_to_lds_impl<XT, false, true>(a, u, nl);
+    else norm_to_lds_impl<XT, false, false>(a, u, nl);
+  }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -770,14 +801,18 @@ __device__ __forceinline__ SyncSet layer_set(uint32_t* sync, int line, int n_sub
   return SyncSet{sync + line * kLW, n_sub, n_flags, total};
 }
 
-template <int NBW, typename XT, bool SB_BF16>
+// MULTI: the launch holds several layers.  A single-layer launch is its own instantiation, in which the
+// previous-layer wait and the coherent fp32 activations are absent at compile time (no run-time branches
+// around the first loads of a block).
+template <int NBW, typename XT, bool SB_BF16, bool MULTI>
 __global__ __launch_bounds__(kThreads) void decode_stack_kernel(const StackArgs sa) {
   extern __shared__ __align__(16) uint32_t lds[];
   __shared__ NormLds nl;
   __shared__ RouteLds r;
   __shared__ uint32_t lastf[4];
-  const int l = blockIdx.x / sa.per_layer_blocks;
-  int b = blockIdx.x % sa.per_layer_blocks;
+  const int l = MULTI ? (int)blockIdx.x / sa.per_layer_blocks : 0;
+  int b = MULTI ? (int)blockIdx.x % sa.per_layer_blocks : (int)blockIdx.x;
+  const bool last = !MULTI || l == sa.n_layers - 1;
   // this block's layer
   LayerArgs a = sa.base;
   const StackLayer& L = sa.layer[l];
@@ -792,9 +827,9 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(const StackArgs 
   char* ws = sa.ws + (int64_t)l * sa.w.total;
   a.x = l == 0 ? sa.x_in : static_cast<const void*>(ws - sa.w.total + sa.w.x_next);
   a.x_f32 = l > 0;
-  a.out = l == sa.n_layers - 1 ? sa.out : static_cast<void*>(ws + sa.w.x_next);
-  a.out_f32 = l < sa.n_layers - 1;
-  a.last_layer = l == sa.n_layers - 1;
+  a.out = last ? sa.out : static_cast<void*>(ws + sa.w.x_next);
+  a.out_f32 = !last;
+  a.last_layer = last;
   a.status = reinterpret_cast<uint32_t*>(sa.ws);
   a.sync_base = reinterpret_cast<uint32_t*>(sa.ws);
   a.layer_words = (int64_t)(sa.w.total / 4);
@@ -806,7 +841,7 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(const StackArgs 
   a.shared_h = layer_set(sync, line, kSharedSub, kSharedFlags, (uint32_t)a.nSG);
   line += kSharedSub + 1 + kSharedFlags;
   const int done_line = line;
-  a.done = layer_set(sync, line, kDoneSub, a.last_layer ? 0 : kXFlags, (uint32_t)(a.d / 16));
+  a.done = layer_set(sync, line, kDoneSub, last ? 0 : kXFlags, (uint32_t)(a.d / 16));
   line += kDoneSub + 1 + kXFlags;
   a.slot_base = sync + line * kLW;
   a.prev_x = l > 0 ? layer_set(sync - a.layer_words, done_line, kDoneSub, kXFlags, (uint32_t)(a.d / 16))
@@ -971,13 +1006,18 @@ moe_status launch(const StackArgs& sa, moe_dtype x_dtype, bool sb16, int nbw, si
   return dispatch_nbw(nbw, [&](auto nb) {
     constexpr int N = decltype(nb)::value;
     if constexpr (N <= 4) {
-      if (x_dtype == MOE_BF16) {
-        if (sb16) hipLaunchKernelGGL((decode_stack_kernel<N, uint16_t, true>), grid, dim3(kThreads), lds, s, sa);
-        else hipLaunchKernelGGL((decode_stack_kernel<N, uint16_t, false>), grid, dim3(kThreads), lds, s, sa);
-      } else {
-        if (sb16) hipLaunchKernelGGL((decode_stack_kernel<N, float, true>), grid, dim3(kThreads), lds, s, sa);
-        else hipLaunchKernelGGL((decode_stack_kernel<N, float, false>), grid, dim3(kThreads), lds, s, sa);
-      }
+      auto go = [&](auto multi) {
+        constexpr bool M = decltype(multi)::value;
+        if (x_dtype == MOE_BF16) {
+          if (sb16) hipLaunchKernelGGL((decode_stack_kernel<N, uint16_t, true, M>), grid, dim3(kThreads), lds, s, sa);
+          else hipLaunchKernelGGL((decode_stack_kernel<N, uint16_t, false, M>), grid, dim3(kThreads), lds, s, sa);
+        } else {
+          if (sb16) hipLaunchKernelGGL((decode_stack_kernel<N, float, true, M>), grid, dim3(kThreads), lds, s, sa);
+          else hipLaunchKernelGGL((decode_stack_kernel<N, float, false, M>), grid, dim3(kThreads), lds, s, sa);
+        }
+      };
+      if (sa.n_layers > 1) go(std::true_type());
+      else go(std::false_type());
       return check_launch(who);
     } else {
       return fail(MOE_ERR_UNSUPPORTED, "%s: rows too long", who);
