@@ -431,6 +431,10 @@ __device__ __forceinline__ void router_block(const LayerArgs& a, int b, float* u
     const int p = lane + 64 * m;
     if (e < a.E && p < np) q[m] = *reinterpret_cast<const uint2*>(a.rw + (int64_t)e * a.d + p * 8);
   }
+  // the row scale with the weights, not at its use after the dot product (the barriers of the norm keep
+  // the compiler from moving it up there, and the logit would wait a memory round trip for it); the
+  // expert is uniform over the wavefront, so it is a scalar load into a scalar register
+  const float rse = a.rs[__builtin_amdgcn_readfirstlane(e < a.E ? e : a.E - 1)];
   if (a.prev_x.base) wait_set(a.prev_x, blockIdx.x, a.status);
   norm_to_lds<XT>(a, u, nl);
   if (e < a.E) {
@@ -459,7 +463,7 @@ __device__ __forceinline__ void router_block(const LayerArgs& a, int b, float* u
       }
     }
     acc = wave_sum(acc);
-    const float lgt = acc * a.rs[e];
+    const float lgt = acc * rse;
     if (lane < kLgReplicas) st_c64(a.lg_tag + (int64_t)lane * a.E + e, ((uint64_t)a.tag << 32) | __float_as_uint(lgt));
     if (lane == 0 && a.logits_out) a.logits_out[e] = lgt;
     if (!a.forced) {
@@ -645,7 +649,6 @@ __device__ __forceinline__ void shared_down_block(const LayerArgs& a, int tile, 
   const int K = P.F, lane = threadIdx.x & 63, wave = threadIdx.x >> 6, ra = lane >> 3, j = lane & 7;
   const int C = K / 32;
   const int row = tile * 16 + ra;
-  if (!a.prev_x.base) __builtin_amdgcn_s_sleep(40);   // about 1 us: let the router's first loads go ahead
   const char* rec = P.base;
   const int64_t rowb = K / 2, sbrow = (int64_t)(K / 64) * (SB_BF16 ? 4 : 8);
   SbWord<SB_BF16> sa[NBW], sb[NBW];
@@ -860,13 +863,15 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(const StackArgs 
     const int nhg = K / 32;
     return Stage{stage_base, reinterpret_cast<float4*>(stage_base + nhg * kHgStride)};
   };
-  // Issue priority between the wavefronts sharing a SIMD: the router and the routed experts are on the
-  // layer's critical path, the shared expert has slack (its result is needed only by the combine).
+  // Issue priority between the wavefronts sharing a SIMD: the router above every other role (all of them
+  // wait for its routing or compete with it for the memory pipeline at the start); the other roles share
+  // one level (measured: the shared expert at a lower level becomes the last contributor to the tiles).
   if (b < a.nR) {
     __builtin_amdgcn_s_setprio(3);
     router_block<XT>(a, b, u, nl);
     return;
   }
+  __builtin_amdgcn_s_setprio(2);
   b -= a.nR;
   if (b < a.nSG) {
     // the shared expert needs only x: the norm (whose loads go out with the router's), then its code words
@@ -879,7 +884,6 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(const StackArgs 
   }
   b -= a.nSG;
   if (b < a.nRG) {
-    __builtin_amdgcn_s_setprio(2);
     const int per = a.routed.F / 8, slot = b / per, tile = b % per;
     // the norm needs only x: done while the router finishes
     if (a.prev_x.base) wait_set(a.prev_x, blockIdx.x, a.status);
@@ -900,7 +904,6 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(const StackArgs 
     return;
   }
   b -= a.nSD;
-  __builtin_amdgcn_s_setprio(2);
   const int per = a.d / 64, slot = b / per, rb = b % per;
   routed_down_block<NBW, XT, SB_BF16>(a, slot, rb, stage_for(a.routed.F), r, lastf);
 }
