@@ -19,18 +19,20 @@
 // a tile applies the routing-weighted combine and the residual, in the order of moe_combine.
 //
 // Apart from the router blocks (below), each block only waits on blocks with smaller indices, which the
-// dispatcher starts first, so every wait is on work that is running or finished.  Waits are bounded: a wait that runs out sets the sticky status
-// word of the workspace instead of hanging (results are then invalid).  Values cross blocks by
-// device-coherent stores and loads and 32-bit relaxed device-scope counters; the block that combines the
-// last tile resets every counter, so the workspace is ready for the next call when the kernel ends.
+// dispatcher starts first, so every wait is on work that is running or finished.  Waits are bounded: a
+// wait that runs out sets the sticky status word of the workspace instead of hanging (results are then
+// invalid).  Values cross blocks by device-coherent stores and loads and 32-bit relaxed device-scope
+// counters.  Nothing waits for the end of the call: each counter is zeroed by the arrival that completes
+// it, and flags and published values carry the call's tag, so the workspace is ready for the next call
+// when the last block exits.
 //
 // The routing carries no counter.  Each logit is stored with the call's tag in the upper half of a 64-bit
 // word (one store, single-copy atomic), in 8 replicas.  Every router wavefront then waits until all E tags match and
 // counts the logits ranked before its own (larger, or equal with a smaller id); if that rank r is below
 // k, it stores (id, logit), tagged, as entry r of each of 16 route replicas.  A block that needs the
 // routing polls one replica until its k tags match and, if it needs the gate weights, takes the softmax
-// of the k logits itself (every block the same way, so all agree).  The tag is 1 + an epoch word of the
-// workspace that every block reads when it starts and the last block of the call increments.  The router
+// of the k logits itself (every block the same way, so all agree).  The tag is the call number: each block
+// keeps a count of calls in a workspace word of its own, read and advanced when the block starts.  The router
 // blocks are the first 32 of the grid, all resident at once: they are the only blocks that wait on blocks
 // with larger indices.
 //
@@ -53,9 +55,11 @@ constexpr int kSpinLimit = 1 << 18;       // polls (about 0.1 s); a legitimate w
 
 // Synchronisation lives in 256-byte lines at the front of the workspace.  Many blocks polling one word
 // while others increment it serialize at the memory-side atomic unit, so waiting blocks poll flag lines
-// of their own: the arrival that completes a set writes a ready flag into each of its n_flags lines.  A
+// of their own: the arrival that completes a set writes the call's tag into each of its n_flags lines.  A
 // set with many arrivals counts them on n_sub sub-counters first (each on its own line); the last arrival
 // of a sub-counter bumps the top counter.  Small sets (n_sub = 1) save that second atomic round trip.
+// The arrival that completes a counter sets it back to zero (no other block touches it again in the call),
+// and flags hold the tag of the call that raised them, so nothing needs clearing between calls.
 constexpr int kLW = 64;             // 32-bit words per line
 struct SyncSet {
   uint32_t* base;                   // lines: [n_sub sub-counters][top][n_flags flags]
@@ -100,16 +104,12 @@ struct LayerArgs {
   int32_t x_f32, out_f32;  // activations held in the workspace as fp32 and exchanged coherently (the
                            // layers between the first input and the last output of a launch)
   uint32_t* status;
-  uint32_t* epoch;                       // the call counter (one per launch, in layer 0's region)
-  uint32_t tag;                          // this call's tag: epoch + 1, read when the block starts
+  uint32_t tag;                          // this call's tag: 1 + the calls counted in this block's word
   SyncSet shared_h, done;                // done = this layer's output complete: counts combined tiles
                                          // (flags: the next layer of the launch)
   SyncSet prev_x;                        // the previous layer's done, or base == NULL
   uint32_t* slot_base;                   // per-slot sets, kLinesPerSlot lines apart
-  int32_t last_layer;                    // the block combining this layer's last tile resets every layer
-  uint32_t* sync_base;                   // sync lines of layer 0; layer l's are l * layer_words further
-  int64_t layer_words;
-  int32_t sync_lines, n_layers;
+  int32_t last_layer;                    // no later layer of the launch waits for this one
   uint64_t* lg_tag;    // [kLgReplicas][E] (tag << 32) | logit bits
   uint64_t* route;     // [kRouteReplicas][2][kLayerMaxK] (tag << 32) | id, (tag << 32) | weight bits
   float* h_routed;     // [k][F]
@@ -140,57 +140,62 @@ __device__ __forceinline__ uint32_t add_cu(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Raise every flag of set `s`: called by a whole wavefront, lane f writes flag line f (n_flags <= 64).
-__device__ __forceinline__ void raise_flags(const SyncSet& s) {
+// Raise every flag of set `s` with this call's tag: called by a whole wavefront, lane f writes flag line f
+// (n_flags <= 64).
+__device__ __forceinline__ void raise_flags(const SyncSet& s, uint32_t tag) {
   const int lane = threadIdx.x & 63;
-  if (lane < s.n_flags) st_cu(s.base + (s.n_sub + 1 + lane) * kLW, 1u);
+  if (lane < s.n_flags) st_cu(s.base + (s.n_sub + 1 + lane) * kLW, tag);
 }
 
 // One arrival (n units) out of `total` on set `s`, made by wavefront 0 of a block (all 64 lanes, after
 // the block's published stores completed); `idx` in [0, total) picks the sub-counter.  Lane 0 makes the
-// atomic round trips.  True, in every lane, for the arrival that completed the set; with `raise` the
-// wavefront has then raised every flag of the set.
-__device__ __forceinline__ bool arrive(const SyncSet& s, int idx, int total, uint32_t n = 1u, bool raise = true) {
+// atomic round trips and zeroes each counter its arrival completed.  The arrival that completes the set
+// raises its flags with `tag`.
+__device__ __forceinline__ void arrive(const SyncSet& s, int idx, int total, uint32_t tag, uint32_t n = 1u) {
   uint32_t done = 0u;
   if ((threadIdx.x & 63) == 0) {
     if (s.n_sub > 1) {
       const int sub = idx % s.n_sub;
       const uint32_t expect = (uint32_t)((total - sub + s.n_sub - 1) / s.n_sub);
       const uint32_t subs_used = (uint32_t)(total < s.n_sub ? total : s.n_sub);
-      done = add_cu(s.base + sub * kLW, 1u) == expect - 1 && add_cu(s.base + s.n_sub * kLW, 1u) == subs_used - 1;
-    } else {
-      done = add_cu(s.base, n) + n == (uint32_t)total;
+      if (add_cu(s.base + sub * kLW, 1u) == expect - 1) {
+        st_cu(s.base + sub * kLW, 0u);
+        if (add_cu(s.base + s.n_sub * kLW, 1u) == subs_used - 1) {
+          st_cu(s.base + s.n_sub * kLW, 0u);
+          done = 1u;
+        }
+      }
+    } else if (add_cu(s.base, n) + n == (uint32_t)total) {
+      st_cu(s.base, 0u);
+      done = 1u;
     }
   }
   done = __builtin_amdgcn_readfirstlane(done);
-  if (done && raise) raise_flags(s);
-  return done != 0u;
+  if (done) raise_flags(s, tag);
 }
 
-// Block-wide bounded wait for set `s` to complete: thread 0 polls flag line `who` mod n_flags, or the
-// counter of a single-counter set without flag lines.  Ends with a block barrier.
-__device__ __forceinline__ void wait_set(const SyncSet& s, int who, uint32_t* status) {
+// Block-wide bounded wait for set `s` (n_flags > 0) to be completed by the call tagged `tag`: thread 0
+// polls flag line `who` mod n_flags.  Ends with a block barrier.
+__device__ __forceinline__ void wait_set(const SyncSet& s, int who, uint32_t tag, uint32_t* status) {
   if (threadIdx.x == 0) {
-    const bool flags = s.n_flags > 0;
-    uint32_t* f = flags ? s.base + (s.n_sub + 1 + who % s.n_flags) * kLW : s.base;
-    const uint32_t target = flags ? 1u : s.total;
+    uint32_t* f = s.base + (s.n_sub + 1 + who % s.n_flags) * kLW;
     uint32_t v = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int n = 0;
-    while (v < target && n < kSpinLimit) {
+    while (v != tag && n < kSpinLimit) {
       __builtin_amdgcn_s_sleep(1);
       v = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       ++n;
     }
-    if (v < target) __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (v != tag) __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
 }
 
 // Publish: every thread's coherent stores have completed before wavefront 0 arrives on the set.
-__device__ __forceinline__ void publish(const SyncSet& s, int idx, int total) {
+__device__ __forceinline__ void publish(const SyncSet& s, int idx, int total, uint32_t tag) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x < 64) arrive(s, idx, total);
+  if (threadIdx.x < 64) arrive(s, idx, total, tag);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -435,7 +440,7 @@ __device__ __forceinline__ void router_block(const LayerArgs& a, int b, float* u
   // the compiler from moving it up there, and the logit would wait a memory round trip for it); the
   // expert is uniform over the wavefront, so it is a scalar load into a scalar register
   const float rse = a.rs[__builtin_amdgcn_readfirstlane(e < a.E ? e : a.E - 1)];
-  if (a.prev_x.base) wait_set(a.prev_x, blockIdx.x, a.status);
+  if (a.prev_x.base) wait_set(a.prev_x, blockIdx.x, a.tag, a.status);
   norm_to_lds<XT>(a, u, nl);
   if (e < a.E) {
     float acc = 0.f;
@@ -557,7 +562,7 @@ __device__ __forceinline__ void gu_finish(const LayerArgs& a, const GuRegs<NBW, 
     }
   }
   if (block_sum(yA, yB)) st_c(hout + f, valid ? activation(yA, a.act) * yB : __builtin_nanf(""));
-  publish(done, tile, done_total);
+  publish(done, tile, done_total, a.tag);
 }
 
 // Stage all half-groups of a published vector v[0..K) (coherent loads) into `st`, block-cooperatively.
@@ -606,7 +611,8 @@ __device__ __forceinline__ void combine_one(const LayerArgs& a, const RouteLds& 
 }
 
 // After a down block published its rows: one ticket per covered tile; combine the tiles this block
-// completed; the block that combines the last tile of the layer resets every counter.
+// completed (and zero their tickets).  Within a launch of several layers, each layer but the last counts
+// its combined tiles, and the next layer waits for all of them.
 template <typename XT>
 __device__ __forceinline__ void tile_epilogue(const LayerArgs& a, int tile0, int ntiles, const RouteLds& r,
                                               uint32_t* lastf) {
@@ -624,21 +630,11 @@ __device__ __forceinline__ void tile_epilogue(const LayerArgs& a, int tile0, int
   // every completed tile at once: thread 16 t + i combines row i of tile t
   if ((int)threadIdx.x < 16 * ntiles && lastf[threadIdx.x / 16]) combine_one<XT>(a, r, tile0 + threadIdx.x / 16, threadIdx.x % 16);
   if ((int)threadIdx.x < ntiles && lastf[threadIdx.x]) st_cu(a.tiles + (tile0 + threadIdx.x) * kTileStride, 0u);
-  __shared__ uint32_t final_s;
-  if (threadIdx.x < 64) {
-    const bool fin = arrive(a.done, 0, a.d / 16, n);
-    if (threadIdx.x == 0) final_s = fin ? 1u : 0u;
-  }
-  __syncthreads();
-  if (final_s && a.last_layer) {
-    // every block of the launch has passed all of its waits: clear every layer's sync lines (not the
-    // status line, the first line of layer 0) and start the next call's epoch
-    if (threadIdx.x == 0) st_cu(a.epoch, a.tag);
-    const int total = a.n_layers * a.sync_lines;
-    for (int t = 1 + (int)threadIdx.x; t < total; t += kThreads) {
-      const int l = t / a.sync_lines, line = t % a.sync_lines;
-      if (line > 0 || l > 0) st_cu(a.sync_base + l * a.layer_words + (int64_t)line * kLW, 0u);
-    }
+  if (!a.last_layer) {
+    // the next layer reads these rows once the count is complete: they are stored before the arrival
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x < 64) arrive(a.done, 0, a.d / 16, a.tag, n);
   }
 }
 
@@ -671,7 +667,7 @@ __device__ __forceinline__ void shared_down_block(const LayerArgs& a, int tile, 
   }
   // the routing (this block may combine its tile): ready long before the shared h is
   get_route(a, r, true);
-  wait_set(a.shared_h, blockIdx.x, a.status);
+  wait_set(a.shared_h, blockIdx.x, a.tag, a.status);
   stage_published(a.h_shared, K, st);
   __syncthreads();
   float yA = 0.f, yB = 0.f;
@@ -737,7 +733,7 @@ __device__ __forceinline__ void routed_down_block(const LayerArgs& a, int slot, 
       }
     }
   }
-  wait_set(slot_set(a, slot), blockIdx.x, a.status);
+  wait_set(slot_set(a, slot), blockIdx.x, a.tag, a.status);
   stage_published(a.h_routed + (int64_t)slot * K, K, st);
   __syncthreads();
   float yA = 0.f, yB = 0.f;
@@ -787,7 +783,7 @@ struct StackLayer {           // what differs between the layers of a launch
 };
 
 struct WsLayout {
-  size_t sync, tiles, epoch, lg_tag, route, h_routed, h_shared, y_routed, y_shared, x_next, total;
+  size_t sync, tiles, calls, lg_tag, route, h_routed, h_shared, y_routed, y_shared, x_next, total;
 };
 
 struct StackArgs {
@@ -834,20 +830,24 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(const StackArgs 
   a.out_f32 = !last;
   a.last_layer = last;
   a.status = reinterpret_cast<uint32_t*>(sa.ws);
-  a.sync_base = reinterpret_cast<uint32_t*>(sa.ws);
-  a.layer_words = (int64_t)(sa.w.total / 4);
-  a.n_layers = sa.n_layers;
   uint32_t* sync = reinterpret_cast<uint32_t*>(ws);
   int line = 1;
-  a.epoch = reinterpret_cast<uint32_t*>(sa.ws + sa.w.epoch);
-  a.tag = ld_cu(a.epoch) + 1u;
+  // The call's tag, without a call-wide counter: every block counts the calls in a word of its own (no
+  // other block reads or writes it), so all words of a workspace hold the same count.  Every thread reads
+  // the word here; the block advances it when it ends.  Tag 0, the value of a zeroed workspace, is skipped
+  // when the count wraps.
+  uint32_t* const mine = reinterpret_cast<uint32_t*>(ws + sa.w.calls) + b;
+  {
+    const uint32_t t = ld_cu(mine) + 1u;
+    a.tag = t != 0u ? t : 1u;
+  }
   a.shared_h = layer_set(sync, line, kSharedSub, kSharedFlags, (uint32_t)a.nSG);
   line += kSharedSub + 1 + kSharedFlags;
   const int done_line = line;
   a.done = layer_set(sync, line, kDoneSub, last ? 0 : kXFlags, (uint32_t)(a.d / 16));
   line += kDoneSub + 1 + kXFlags;
   a.slot_base = sync + line * kLW;
-  a.prev_x = l > 0 ? layer_set(sync - a.layer_words, done_line, kDoneSub, kXFlags, (uint32_t)(a.d / 16))
+  a.prev_x = l > 0 ? layer_set(sync - sa.w.total / 4, done_line, kDoneSub, kXFlags, (uint32_t)(a.d / 16))
                    : SyncSet{nullptr, 1, 0, 0u};
   a.lg_tag = reinterpret_cast<uint64_t*>(ws + sa.w.lg_tag);
   a.route = reinterpret_cast<uint64_t*>(ws + sa.w.route);
@@ -869,53 +869,56 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(const StackArgs 
   if (b < a.nR) {
     __builtin_amdgcn_s_setprio(3);
     router_block<XT>(a, b, u, nl);
-    return;
+  } else {
+    __builtin_amdgcn_s_setprio(2);
+    b -= a.nR;
+    const int nG = a.nSG + a.nRG, nD = nG + a.nSD;
+    if (b < a.nSG) {
+      // the shared expert needs only x: the norm (whose loads go out with the router's), then its code words
+      if (a.prev_x.base) wait_set(a.prev_x, blockIdx.x, a.tag, a.status);
+      norm_to_lds<XT>(a, u, nl);
+      GuRegs<NBW, SB_BF16> g;
+      gu_load<NBW, SB_BF16>(a, a.shared, 0, true, b, g);
+      gu_finish<NBW, SB_BF16>(a, g, true, b, a.h_shared, a.shared_h, a.nSG, u, stage_for(a.d));
+    } else if (b < nG) {
+      const int per = a.routed.F / 8, slot = (b - a.nSG) / per, tile = (b - a.nSG) % per;
+      // the norm needs only x: done while the router finishes
+      if (a.prev_x.base) wait_set(a.prev_x, blockIdx.x, a.tag, a.status);
+      norm_to_lds<XT>(a, u, nl);
+      get_route(a, r, false);
+      const int e = r.sel_i[slot];
+      const int idx = a.gemv_ids ? a.gemv_ids[slot] : e;
+      const bool valid = (unsigned)idx < (unsigned)a.routed.n_records && (unsigned)e < (unsigned)a.E;
+      GuRegs<NBW, SB_BF16> g;
+      gu_load<NBW, SB_BF16>(a, a.routed, idx, valid, tile, g);
+      gu_finish<NBW, SB_BF16>(a, g, valid, tile, a.h_routed + (int64_t)slot * a.routed.F, slot_set(a, slot), per,
+                              u, stage_for(a.d));
+    } else if (b < nD) {
+      shared_down_block<NBW, XT, SB_BF16>(a, b - nG, stage_for(a.shared.F), r, lastf);
+    } else {
+      const int per = a.d / 64, slot = (b - nD) / per, rb = (b - nD) % per;
+      routed_down_block<NBW, XT, SB_BF16>(a, slot, rb, stage_for(a.routed.F), r, lastf);
+    }
   }
-  __builtin_amdgcn_s_setprio(2);
-  b -= a.nR;
-  if (b < a.nSG) {
-    // the shared expert needs only x: the norm (whose loads go out with the router's), then its code words
-    if (a.prev_x.base) wait_set(a.prev_x, blockIdx.x, a.status);
-    norm_to_lds<XT>(a, u, nl);
-    GuRegs<NBW, SB_BF16> g;
-    gu_load<NBW, SB_BF16>(a, a.shared, 0, true, b, g);
-    gu_finish<NBW, SB_BF16>(a, g, true, b, a.h_shared, a.shared_h, a.nSG, u, stage_for(a.d));
-    return;
-  }
-  b -= a.nSG;
-  if (b < a.nRG) {
-    const int per = a.routed.F / 8, slot = b / per, tile = b % per;
-    // the norm needs only x: done while the router finishes
-    if (a.prev_x.base) wait_set(a.prev_x, blockIdx.x, a.status);
-    norm_to_lds<XT>(a, u, nl);
-    get_route(a, r, false);
-    const int e = r.sel_i[slot];
-    const int idx = a.gemv_ids ? a.gemv_ids[slot] : e;
-    const bool valid = (unsigned)idx < (unsigned)a.routed.n_records && (unsigned)e < (unsigned)a.E;
-    GuRegs<NBW, SB_BF16> g;
-    gu_load<NBW, SB_BF16>(a, a.routed, idx, valid, tile, g);
-    gu_finish<NBW, SB_BF16>(a, g, valid, tile, a.h_routed + (int64_t)slot * a.routed.F, slot_set(a, slot), per, u,
-                            stage_for(a.d));
-    return;
-  }
-  b -= a.nRG;
-  if (b < a.nSD) {
-    shared_down_block<NBW, XT, SB_BF16>(a, b, stage_for(a.shared.F), r, lastf);
-    return;
-  }
-  b -= a.nSD;
-  const int per = a.d / 64, slot = b / per, rb = b % per;
-  routed_down_block<NBW, XT, SB_BF16>(a, slot, rb, stage_for(a.routed.F), r, lastf);
+  // count this call: every wavefront that uses the tag has read the word by now (a load still in flight
+  // belongs to a wavefront that never uses its value)
+  __syncthreads();
+  if (threadIdx.x == 0) st_cu(mine, a.tag);
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// blocks of one layer: router, shared gate/up, routed gate/up, shared down, routed down
+int layer_blocks(int d, int E, int k, int F, int S) {
+  return (E + 3) / 4 + S / 8 + k * (F / 8) + (S > 0 ? d / 16 : 0) + k * (d / 64);
+}
 
 WsLayout ws_layout(int d, int E, int k, int F, int S) {
   WsLayout w;
   size_t o = 0;
   w.sync = o;       o += (size_t)(kLinesFixed + k * kLinesPerSlot) * kLW * 4;
   w.tiles = o;      o += align256((size_t)(d / 16) * kTileStride * 4);
-  w.epoch = o;      o += 256;
+  w.calls = o;      o += align256((size_t)layer_blocks(d, E, k, F, S) * 4);
   w.lg_tag = o;     o += align256((size_t)kLgReplicas * E * 8);
   w.route = o;      o += align256((size_t)kRouteReplicas * 2 * kLayerMaxK * 8);
   w.h_routed = o;   o += align256((size_t)k * F * 4);
@@ -976,7 +979,6 @@ moe_status prepare_launch(const char* who, const void* x_dev, moe_dtype x_dtype,
   a.d = d;
   a.act = act;
   a.has_shared = shared != nullptr;
-  a.sync_lines = kLinesFixed + k * kLinesPerSlot;
   a.nR = (E + 3) / 4;
   a.nSG = shared ? shared->F / 8 : 0;
   a.nRG = k * (routed->F / 8);
@@ -988,6 +990,8 @@ moe_status prepare_launch(const char* who, const void* x_dev, moe_dtype x_dtype,
   sa->out = out_dev;
   sa->n_layers = n_layers;
   sa->per_layer_blocks = a.nR + a.nSG + a.nRG + a.nSD + a.nRD;
+  if (sa->per_layer_blocks != layer_blocks(d, E, k, routed->F, shared ? shared->F : 0))
+    return fail(MOE_ERR_INVALID_ARG, "%s: inconsistent block count", who);   // (the call words are per block)
   // chunk iterations per lane: gate/up rows (K = d) and shared down rows (K = S) split over 4 waves,
   // routed down rows (K = F) whole per wave
   const int it_gu = (iterations(d) + 3) / 4, it_sd = shared ? (iterations(shared->F) + 3) / 4 : 1;
@@ -1035,7 +1039,7 @@ using namespace moeq4;
 
 extern "C" size_t moe_decode_layer_sync_bytes(int32_t d, int32_t k) {
   if (d < 64 || k < 1 || k > kLayerMaxK) return 0;
-  return ws_layout(d, 1, k, 64, 0).epoch;   // the sync lines and the tile tickets
+  return ws_layout(d, 1, k, 64, 0).calls;   // the sync lines and the tile tickets
 }
 
 extern "C" size_t moe_decode_layer_workspace_bytes(int32_t d, int32_t E, int32_t k, int32_t F, int32_t S) {

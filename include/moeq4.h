@@ -114,7 +114,7 @@ moe_status q4_gemv(const void* x_dev, moe_dtype x_dtype, int32_t T, const uint32
                    moe_dtype sb_dtype, int32_t N, int32_t K, float* y_dev, void* stream);
 
 /* ---------------------------------------------------------------------------------------------------
- * moe_rmsnorm —u[t] = x[t] / sqrt(mean(x[t]^2) + eps) * gamma, fp32 math, rounded to out_dtype (RNE).
+ * moe_rmsnorm — u[t] = x[t] / sqrt(mean(x[t]^2) + eps) * gamma, fp32 math, rounded to out_dtype (RNE).
  * The pages list a normalisation (RMSNorm) kernel ([LEAF] "Du code sur-mesure sans dépendance externe";
  * [DEVT] "Geen afhankelijkheden van llama.cpp en MLX"); it precedes each MoE block in the stacked decode.
  * x_dev: x_dtype [T][d]; gamma_dev: fp32 [d]; out_dev: out_dtype [T][d].  d % 8 == 0, d <= 16384, T >= 1;
@@ -263,12 +263,14 @@ moe_status q4_expert_gemv_combine(const moe_q4_pool* routed, const int32_t* ids_
  * optional outputs (int32 [k], fp32 [k], fp32 [E]).
  * Limits: d <= 4096, shared width <= 4096, routed F <= 1024, E <= 256, 1 <= k <= min(E, 32).
  * Workspace: moe_decode_layer_workspace_bytes(d, E, k, F, S) bytes (S = 0 without shared expert), 256-byte
- * aligned, ZERO before its first use.  Its first moe_decode_layer_sync_bytes(d, k) bytes hold the counters
- * and flags the blocks synchronise with; every completed call leaves them zero again, except 32-bit word 0:
- * a sticky error flag, nonzero if a wait inside the kernel ran out (the results of that call are invalid;
- * zero the workspace before reusing it).  After them come a call counter, which every call advances by
- * one (values published during a call carry it, so nothing else needs clearing), and the call's
- * intermediate values.  Calls that overlap in time need separate workspaces.
+ * aligned, ZERO before its first use, and used with one shape (d, E, k, F, S and shared or not).  Its first
+ * moe_decode_layer_sync_bytes(d, k) bytes hold the counters and flags the blocks synchronise with: every
+ * completed call leaves each counter zero and each flag zero or at the number of calls made on the
+ * workspace; 32-bit word 0 is a sticky error flag, nonzero if a wait inside the kernel ran out (the results
+ * of that call are invalid; zero the workspace before reusing it).  After them come one call counter per
+ * block of the grid, each advanced by one per call (flags and the values published during a call carry
+ * the call number, so nothing needs clearing between calls), and the call's intermediate values.  Calls
+ * that overlap in time need separate workspaces.
  * ------------------------------------------------------------------------------------------------- */
 size_t moe_decode_layer_workspace_bytes(int32_t d, int32_t E, int32_t k, int32_t F, int32_t S);
 size_t moe_decode_layer_sync_bytes(int32_t d, int32_t k);
@@ -293,8 +295,8 @@ moe_status moe_decode_layer(const void* x_dev, moe_dtype x_dtype, const float* g
  * outputs.  Limits as moe_decode_layer, and 1 <= n_layers <= 32.
  * Workspace: moe_decode_stack_workspace_bytes(...) bytes, 256-byte aligned, ZERO before first use; the
  * region of layer l is moe_decode_layer_workspace_bytes(d, E, k, F, S) bytes at offset l times that size,
- * laid out as moe_decode_layer's (word 0 of the whole workspace is the sticky error flag); every completed
- * call leaves the synchronisation bytes of every region zero again.
+ * laid out as moe_decode_layer's (word 0 of the whole workspace is the sticky error flag), with the same
+ * state after every completed call: counters zero, flags zero or at the number of calls made.
  * ------------------------------------------------------------------------------------------------- */
 typedef struct {
   const int8_t* router_w_dev;      /* int8 [E][d] */

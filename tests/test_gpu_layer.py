@@ -45,16 +45,17 @@ def _run(cfg, dev, shape, x, ws, ws_b, gamma, residual, forced=None, routed=None
     return ids, w, lg, out
 
 
-def _check_clean(ws, cfg):
-    """Word 0 (sticky error flag) clear, and the synchronisation region (moe_decode_layer_sync_bytes) back
-    to zero."""
+def _check_clean(ws, cfg, calls):
+    """Word 0 (sticky error flag) clear; in the synchronisation region (moe_decode_layer_sync_bytes) every
+    counter back to zero and every flag zero or holding the number of calls made on the workspace."""
     torch.cuda.synchronize()
     n = q.moe_decode_layer_sync_bytes(cfg.d, cfg.k)
     assert 0 < n < ws.numel()
     words = ws[:n].view(torch.int32).cpu().numpy()
     assert words[0] == 0, "a wait inside the layer kernel ran out"
-    nz = np.nonzero(words)[0]
-    assert nz.size == 0, f"synchronisation words not reset: {nz[:8]}"
+    bad = np.nonzero((words != 0) & (words != calls))[0]
+    assert bad.size == 0, f"synchronisation words left at {words[bad[:8]]} (call {calls}) at {bad[:8]}"
+    assert (words == calls).any(), "no flag carries this call's number"
 
 
 @pytest.mark.parametrize("gamma_ones", [True, False])
@@ -68,10 +69,10 @@ def test_decode_layer_vs_oracle(stack_layer, gamma_ones):
     orc = oin.oracle_layer(cfg, 0, cache_experts=24)
     orc.gamma = gamma_np.astype(np.float64)
     ws, ws_b = _ws(cfg)
-    for tok in (0, 5, 77, 200):
+    for call, tok in enumerate((0, 5, 77, 200), 1):
         x = H.token_batch(cfg, [tok])[0]
         ids, w, lg, out = _run(cfg, dev, shape, x, ws, ws_b, gamma, 1)
-        _check_clean(ws, cfg)
+        _check_clean(ws, cfg, call)
         x64 = H.to_f64(x)
         u_ref = moe.f64_round_to_bf16(moe.rms_norm(x64, orc.gamma, 1e-6))
         ref_lg = moe.router_logits(orc.router_w, orc.router_s, u_ref)
@@ -93,13 +94,13 @@ def test_decode_layer_repeatable_on_one_workspace(stack_layer):
     cfg, dev, shape = stack_layer
     gamma = torch.ones(cfg.d, dtype=torch.float32, device="cuda")
     ws, ws_b = _ws(cfg)
-    for tok in (3, 4, 3, 9, 4):
+    for call, tok in enumerate((3, 4, 3, 9, 4), 1):
         x = H.token_batch(cfg, [tok])[0]
         ids, w, lg, out = _run(cfg, dev, shape, x, ws, ws_b, gamma, 1)
         fresh, fb = _ws(cfg)
         ids2, w2, lg2, out2 = _run(cfg, dev, shape, x, fresh, fb, gamma, 1)
-        _check_clean(ws, cfg)
-        _check_clean(fresh, cfg)
+        _check_clean(ws, cfg, call)
+        _check_clean(fresh, cfg, 1)
         assert torch.equal(ids, ids2) and torch.equal(w, w2) and torch.equal(lg, lg2) and torch.equal(out, out2)
 
 
@@ -123,7 +124,7 @@ def test_decode_layer_forced_and_slot_indirection(stack_layer):
         ids_a, w_a, _, out_a = _run(cfg, dev, shape, x, ws, ws_b, gamma, 1, forced=forced)
         ids_b, w_b, _, out_b = _run(cfg, dev, shape, x, ws, ws_b, gamma, 1, forced=forced, routed=slot_pool,
                                     gemv_ids=gemv_ids)
-        _check_clean(ws, cfg)
+        _check_clean(ws, cfg, 2)
         assert ids_a.cpu().numpy().tolist() == trace[t].tolist()
         assert torch.equal(ids_a, ids_b) and torch.equal(w_a, w_b) and torch.equal(out_a, out_b), f"token {t}"
 
@@ -143,7 +144,7 @@ def test_decode_layer_tiny_no_norm_vs_oracle(shared):
     for tok in range(16):
         x = H.token_batch(cfg, [tok])[0]
         ids, w, lg, out = _run(cfg, dev, shape, x, ws, ws_b, None, 0, shared=shared)
-        _check_clean(ws, cfg)
+        _check_clean(ws, cfg, tok + 1)
         u = oin.token_input(cfg, tok)
         ref_lg = moe.router_logits(orc.router_w, orc.router_s, u)
         assert np.abs(lg.cpu().numpy() - ref_lg).max() <= 1e-5 * max(1.0, np.abs(ref_lg).max())
@@ -156,8 +157,9 @@ def test_decode_layer_tiny_no_norm_vs_oracle(shared):
 
 def test_decode_stack_equals_chained_layers():
     """Four d=2816 layers in one moe_decode_stack launch equal four chained moe_decode_layer calls bit for bit
-    (output, and every layer's ids, weights and logits), twice in a row on one workspace; every layer's
-    synchronisation region is back to zero and the error flag clear."""
+    (output, and every layer's ids, weights and logits), twice in a row on one workspace; in every layer's
+    synchronisation region the counters are back to zero and the flags zero or at the call number, and the
+    error flag is clear."""
     cfg = synth.STACK
     L = 4
     devs = [H.device_layer(cfg, l) for l in range(L)]
@@ -175,7 +177,7 @@ def test_decode_stack_equals_chained_layers():
     assert sb == L * region
     ws = torch.zeros(sb, dtype=torch.uint8, device="cuda")
     lws, lwb = _ws(cfg)
-    for tok in (11, 12):
+    for call, tok in enumerate((11, 12), 1):
         x = H.token_batch(cfg, [tok])[0]
         out = torch.empty_like(x)
         q.moe_decode_stack(descs, L, x, q.MOE_BF16, 1e-6, 1, E, k, rp, sp, shape.act, out, ws, sb)
@@ -190,5 +192,6 @@ def test_decode_stack_equals_chained_layers():
         assert int(words[0].item()) == 0, "a wait inside the stack kernel ran out"
         n = q.moe_decode_layer_sync_bytes(d, k) // 4
         for l in range(L):
-            seg = words[l * region // 4: l * region // 4 + n]
-            assert int(seg.abs().sum().item()) == 0, f"layer {l} synchronisation words not reset"
+            seg = words[l * region // 4: l * region // 4 + n].cpu().numpy()
+            bad = np.nonzero((seg != 0) & (seg != call))[0]
+            assert bad.size == 0, f"layer {l}: synchronisation words left at {seg[bad[:8]]} (call {call})"
