@@ -15,8 +15,9 @@
 //   routed down       64 rows of the i-th selected expert, once that expert's gate/up blocks are done;
 //                     its code words are loaded before the wait, so they stream while gate/up finishes
 //
-// Down blocks publish their rows and take a ticket per 16-row tile; the last of the k + 1 contributions to
-// a tile applies the routing-weighted combine and the residual, in the order of moe_combine.
+// Down blocks publish their rows tagged with the call; the block of the last routed slot keeps its own rows,
+// polls the other k contributions to its 64 rows, and applies the routing-weighted combine and the
+// residual, in the order of moe_combine.
 //
 // Apart from the router blocks (below), each block only waits on blocks with smaller indices, which the
 // dispatcher starts first, so every wait is on work that is running or finished.  Waits are bounded: a
@@ -69,8 +70,7 @@ struct SyncSet {
 };
 constexpr int kSharedSub = 16, kSharedFlags = 16;
 constexpr int kSlotSub = 1, kSlotFlags = 8;
-constexpr int kDoneSub = 1;         // the layer-done set counts combined 16-row tiles
-constexpr int kTileStride = 16;     // words between two tile tickets
+constexpr int kDoneSub = 1;         // the layer-done set counts combined 64-row blocks
 // line 0: status word (sticky, bit 0 = a bounded wait ran out); then the sets shared, done, slots
 constexpr int kXFlags = 64;      // flags announcing a layer's output to the next layer of the launch
 constexpr int kLinesFixed = 1 + (kSharedSub + 1 + kSharedFlags) + (kDoneSub + 1 + kXFlags);
@@ -105,8 +105,8 @@ struct LayerArgs {
                            // layers between the first input and the last output of a launch)
   uint32_t* status;
   uint32_t tag;                          // this call's tag: 1 + the calls counted in this block's word
-  SyncSet shared_h, done;                // done = this layer's output complete: counts combined tiles
-                                         // (flags: the next layer of the launch)
+  SyncSet shared_h, done;                // done = this layer's output complete: counts combined 64-row
+                                         // blocks (flags: the next layer of the launch)
   SyncSet prev_x;                        // the previous layer's done, or base == NULL
   uint32_t* slot_base;                   // per-slot sets, kLinesPerSlot lines apart
   int32_t last_layer;                    // no later layer of the launch waits for this one
@@ -114,9 +114,8 @@ struct LayerArgs {
   uint64_t* route;     // [kRouteReplicas][2][kLayerMaxK] (tag << 32) | id, (tag << 32) | weight bits
   float* h_routed;     // [k][F]
   float* h_shared;     // [S]
-  uint32_t* tiles;     // [d/16] tickets, kTileStride words apart
-  float* y_routed;     // [k][d]
-  float* y_shared;     // [d]
+  uint64_t* y_routed;  // [k][d] (tag << 32) | row result bits
+  uint64_t* y_shared;  // [d]    (tag << 32) | row result bits
   int32_t nR, nSG, nRG, nSD, nRD;
 };
 
@@ -577,70 +576,71 @@ __device__ __forceinline__ void stage_published(const float* v, int K, Stage st)
   }
 }
 
-// Combine tile `tile` (threads 0..15) with the block's routing (r.sel_i, r.w)
+// The combine of rows [64 rb, 64 rb + 64), done by the block of the last routed slot for those rows once
+// its own rows are in comb[k - 1][*]: it polls the other contributions (routed slots 0..k-2 and the shared
+// expert, published tagged; all of one thread's loads in flight together) into comb, then thread t < 64
+// stores out[64 rb + t] = round_x(sum_i w_i y_i (i = 0..k-1) + y_shared + residual), in moe_combine's
+// order.  comb: LDS [k + 1][64] floats (index k: the shared expert).  Within a launch of several layers
+// each combine but the last layer's counts on the layer's done set.
 template <typename XT>
-__device__ __forceinline__ void combine_one(const LayerArgs& a, const RouteLds& r, int tile, int t16) {
-  const int row = tile * 16 + t16;
-  // all loads first (shared, residual and eight routed rows in flight), then the sum in the order
-  // i = 0..k-1, shared, residual
-  float acc = 0.f;
-  const float ys = a.has_shared ? ld_c(a.y_shared + row) : 0.f;
-  const XT* x = reinterpret_cast<const XT*>(a.x);
+__device__ __forceinline__ void combine_rows(const LayerArgs& a, const RouteLds& r, int rb, float* comb) {
+  constexpr int kPer = (kLayerMaxK + 1 + kThreads / 64 - 1) / (kThreads / 64);   // sources per thread, max
+  const int t = threadIdx.x, rl = t & 63, row = rb * 64 + rl;
+  const int nsrc = a.k - 1 + (a.has_shared ? 1 : 0);   // source s: routed slot s < k - 1, else shared
   float xr = 0.f;
-  if (a.residual)
+  if (a.residual && t < 64) {
+    const XT* x = reinterpret_cast<const XT*>(a.x);
     xr = a.x_f32 ? ld_c(reinterpret_cast<const float*>(a.x) + row)
                  : sizeof(XT) == 2 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(x)[row])
                                    : reinterpret_cast<const float*>(x)[row];
-  for (int i0 = 0; i0 < a.k; i0 += 8) {
-    float yv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) yv[i] = i0 + i < a.k ? ld_c(a.y_routed + (int64_t)(i0 + i) * a.d + row) : 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (i0 + i < a.k) acc = __builtin_fmaf(r.w[i0 + i], yv[i], acc);
   }
-  if (a.has_shared) acc += ys;
-  if (a.residual) acc += xr;
-  const float o = sizeof(XT) == 2 ? bf16_bits_to_f32(f32_to_bf16_bits(acc)) : acc;   // the layer output's rounding
-  if (a.out_f32)
-    st_c(reinterpret_cast<float*>(a.out) + row, o);
-  else if (sizeof(XT) == 2)
-    reinterpret_cast<uint16_t*>(a.out)[row] = (uint16_t)f32_to_bf16_bits(acc);
-  else
-    reinterpret_cast<float*>(a.out)[row] = acc;
-}
-
-// After a down block published its rows: one ticket per covered tile; combine the tiles this block
-// completed (and zero their tickets).  Within a launch of several layers, each layer but the last counts
-// its combined tiles, and the next layer waits for all of them.
-template <typename XT>
-__device__ __forceinline__ void tile_epilogue(const LayerArgs& a, int tile0, int ntiles, const RouteLds& r,
-                                              uint32_t* lastf) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  const uint32_t units = (uint32_t)a.k + (a.has_shared ? 1u : 0u);
-  if ((int)threadIdx.x < ntiles)
-    lastf[threadIdx.x] = add_cu(a.tiles + (tile0 + threadIdx.x) * kTileStride, 1u) == units - 1;
-  __syncthreads();
-  bool any = false;
-  for (int t = 0; t < ntiles; ++t) any |= lastf[t] != 0;
-  if (!any) return;
-  uint32_t n = 0;
-  for (int t = 0; t < ntiles; ++t) n += lastf[t] ? 1u : 0u;
-  // every completed tile at once: thread 16 t + i combines row i of tile t
-  if ((int)threadIdx.x < 16 * ntiles && lastf[threadIdx.x / 16]) combine_one<XT>(a, r, tile0 + threadIdx.x / 16, threadIdx.x % 16);
-  if ((int)threadIdx.x < ntiles && lastf[threadIdx.x]) st_cu(a.tiles + (tile0 + threadIdx.x) * kTileStride, 0u);
+  for (int n = 0;; ++n) {
+    uint64_t v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int sidx = (t >> 6) + i * (kThreads / 64);
+      if (sidx < nsrc) v[i] = ld_c64((sidx < a.k - 1 ? a.y_routed + (int64_t)sidx * a.d : a.y_shared) + row);
+    }
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int sidx = (t >> 6) + i * (kThreads / 64);
+      if (sidx < nsrc) {
+        ok = ok && (uint32_t)(v[i] >> 32) == a.tag;
+        comb[(sidx < a.k - 1 ? sidx : a.k) * 64 + rl] = __uint_as_float((uint32_t)v[i]);
+      }
+    }
+    if (!__syncthreads_or(!ok)) break;
+    if (n >= kSpinLimit) {
+      if (t == 0) __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (t < 64) {
+    float acc = 0.f;
+    for (int i = 0; i < a.k; ++i) acc = __builtin_fmaf(r.w[i], comb[i * 64 + rl], acc);
+    if (a.has_shared) acc += comb[a.k * 64 + rl];
+    if (a.residual) acc += xr;
+    const float o = sizeof(XT) == 2 ? bf16_bits_to_f32(f32_to_bf16_bits(acc)) : acc;   // the layer output's rounding
+    if (a.out_f32)
+      st_c(reinterpret_cast<float*>(a.out) + row, o);
+    else if (sizeof(XT) == 2)
+      reinterpret_cast<uint16_t*>(a.out)[row] = (uint16_t)f32_to_bf16_bits(acc);
+    else
+      reinterpret_cast<float*>(a.out)[row] = acc;
+  }
   if (!a.last_layer) {
     // the next layer reads these rows once the count is complete: they are stored before the arrival
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (threadIdx.x < 64) arrive(a.done, 0, a.d / 16, a.tag, n);
+    if (t < 64) arrive(a.done, 0, a.d / 64, a.tag);
   }
 }
 
 // 16 rows (r, r + 8 per lane group) of the shared expert's down matrix, waves split the row (K = S)
 template <int NBW, typename XT, bool SB_BF16>
-__device__ __forceinline__ void shared_down_block(const LayerArgs& a, int tile, Stage st, RouteLds& r, uint32_t* lastf) {
+__device__ __forceinline__ void shared_down_block(const LayerArgs& a, int tile, Stage st) {
   const LayerPool& P = a.shared;
   const int K = P.F, lane = threadIdx.x & 63, wave = threadIdx.x >> 6, ra = lane >> 3, j = lane & 7;
   const int C = K / 32;
@@ -665,8 +665,6 @@ __device__ __forceinline__ void shared_down_block(const LayerArgs& a, int tile, 
       qb[m] = load_nt(rec + P.dn_q + (row + 8) * rowb + c * 16);
     }
   }
-  // the routing (this block may combine its tile): ready long before the shared h is
-  get_route(a, r, true);
   wait_set(a.shared_h, blockIdx.x, a.tag, a.status);
   stage_published(a.h_shared, K, st);
   __syncthreads();
@@ -689,21 +687,22 @@ __device__ __forceinline__ void shared_down_block(const LayerArgs& a, int tile, 
     }
   }
   if (block_sum(yA, yB)) {
-    st_c(a.y_shared + row, yA);
-    st_c(a.y_shared + row + 8, yB);
+    const uint64_t tg = (uint64_t)a.tag << 32;
+    st_c64(a.y_shared + row, tg | __float_as_uint(yA));
+    st_c64(a.y_shared + row + 8, tg | __float_as_uint(yB));
   }
-  tile_epilogue<XT>(a, tile, 1, r, lastf);
 }
 
 // 64 rows of the i-th selected expert's down matrix: wave w takes rows 16w.. of the block, whole rows
 template <int NBW, typename XT, bool SB_BF16>
 __device__ __forceinline__ void routed_down_block(const LayerArgs& a, int slot, int rb, Stage st, RouteLds& r,
-                                                  uint32_t* lastf) {
+                                                  float* comb) {
   const LayerPool& P = a.routed;
   const int K = P.F, lane = threadIdx.x & 63, wave = threadIdx.x >> 6, ra = lane >> 3, j = lane & 7;
   const int C = K / 32;
   const int row = rb * 64 + wave * 16 + ra;
-  get_route(a, r, true);      // with the weights: this block may combine tiles at the end
+  const bool combiner = slot == a.k - 1;   // the last slot's block combines its 64 rows
+  get_route(a, r, combiner || (slot == 0 && rb == 0 && a.weights_out));
   if (slot == 0 && rb == 0 && (int)threadIdx.x < a.k) {
     if (a.ids_out) a.ids_out[threadIdx.x] = r.sel_i[threadIdx.x];
     if (a.weights_out) a.weights_out[threadIdx.x] = r.w[threadIdx.x];
@@ -758,12 +757,21 @@ __device__ __forceinline__ void routed_down_block(const LayerArgs& a, int slot, 
   }
   yA = reduce8(yA);
   yB = reduce8(yB);
-  if (j == 0) {
-    float* y = a.y_routed + (int64_t)slot * a.d;
-    st_c(y + row, valid ? yA : __builtin_nanf(""));
-    st_c(y + row + 8, valid ? yB : __builtin_nanf(""));
+  if (!valid) yA = yB = __builtin_nanf("");
+  if (!combiner) {
+    if (j == 0) {
+      const uint64_t tg = (uint64_t)a.tag << 32;
+      st_c64(a.y_routed + (int64_t)slot * a.d + row, tg | __float_as_uint(yA));
+      st_c64(a.y_routed + (int64_t)slot * a.d + row + 8, tg | __float_as_uint(yB));
+    }
+    return;
   }
-  tile_epilogue<XT>(a, rb * 4, 4, r, lastf);
+  __syncthreads();   // every wavefront is done with the staging area, which comb may overlay
+  if (j == 0) {      // (combine_rows makes these visible to the block before it reads them)
+    comb[(a.k - 1) * 64 + wave * 16 + ra] = yA;
+    comb[(a.k - 1) * 64 + wave * 16 + ra + 8] = yB;
+  }
+  combine_rows<XT>(a, r, rb, comb);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -783,7 +791,7 @@ struct StackLayer {           // what differs between the layers of a launch
 };
 
 struct WsLayout {
-  size_t sync, tiles, calls, lg_tag, route, h_routed, h_shared, y_routed, y_shared, x_next, total;
+  size_t sync, calls, lg_tag, route, h_routed, h_shared, y_routed, y_shared, x_next, total;
 };
 
 struct StackArgs {
@@ -808,7 +816,6 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(const StackArgs 
   extern __shared__ __align__(16) uint32_t lds[];
   __shared__ NormLds nl;
   __shared__ RouteLds r;
-  __shared__ uint32_t lastf[4];
   const int l = MULTI ? (int)blockIdx.x / sa.per_layer_blocks : 0;
   int b = MULTI ? (int)blockIdx.x % sa.per_layer_blocks : (int)blockIdx.x;
   const bool last = !MULTI || l == sa.n_layers - 1;
@@ -844,18 +851,17 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(const StackArgs 
   a.shared_h = layer_set(sync, line, kSharedSub, kSharedFlags, (uint32_t)a.nSG);
   line += kSharedSub + 1 + kSharedFlags;
   const int done_line = line;
-  a.done = layer_set(sync, line, kDoneSub, last ? 0 : kXFlags, (uint32_t)(a.d / 16));
+  a.done = layer_set(sync, line, kDoneSub, last ? 0 : kXFlags, (uint32_t)(a.d / 64));
   line += kDoneSub + 1 + kXFlags;
   a.slot_base = sync + line * kLW;
-  a.prev_x = l > 0 ? layer_set(sync - sa.w.total / 4, done_line, kDoneSub, kXFlags, (uint32_t)(a.d / 16))
+  a.prev_x = l > 0 ? layer_set(sync - sa.w.total / 4, done_line, kDoneSub, kXFlags, (uint32_t)(a.d / 64))
                    : SyncSet{nullptr, 1, 0, 0u};
   a.lg_tag = reinterpret_cast<uint64_t*>(ws + sa.w.lg_tag);
   a.route = reinterpret_cast<uint64_t*>(ws + sa.w.route);
   a.h_routed = reinterpret_cast<float*>(ws + sa.w.h_routed);
   a.h_shared = reinterpret_cast<float*>(ws + sa.w.h_shared);
-  a.tiles = reinterpret_cast<uint32_t*>(ws + sa.w.tiles);
-  a.y_routed = reinterpret_cast<float*>(ws + sa.w.y_routed);
-  a.y_shared = reinterpret_cast<float*>(ws + sa.w.y_shared);
+  a.y_routed = reinterpret_cast<uint64_t*>(ws + sa.w.y_routed);
+  a.y_shared = reinterpret_cast<uint64_t*>(ws + sa.w.y_shared);
   float* u = reinterpret_cast<float*>(lds);                        // [d] the normalized activation
   uint32_t* stage_base = lds + a.d;                                 // staging area
   // staging area: [nhg][kHgStride] words then [nhg] float4; sized by the block's own K
@@ -865,7 +871,7 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(const StackArgs 
   };
   // Issue priority between the wavefronts sharing a SIMD: the router above every other role (all of them
   // wait for its routing or compete with it for the memory pipeline at the start); the other roles share
-  // one level (measured: the shared expert at a lower level becomes the last contributor to the tiles).
+  // one level (measured: with the shared expert at a lower level the combine waited for its rows).
   if (b < a.nR) {
     __builtin_amdgcn_s_setprio(3);
     router_block<XT>(a, b, u, nl);
@@ -894,10 +900,11 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(const StackArgs 
       gu_finish<NBW, SB_BF16>(a, g, valid, tile, a.h_routed + (int64_t)slot * a.routed.F, slot_set(a, slot), per,
                               u, stage_for(a.d));
     } else if (b < nD) {
-      shared_down_block<NBW, XT, SB_BF16>(a, b - nG, stage_for(a.shared.F), r, lastf);
+      shared_down_block<NBW, XT, SB_BF16>(a, b - nG, stage_for(a.shared.F));
     } else {
       const int per = a.d / 64, slot = (b - nD) / per, rb = (b - nD) % per;
-      routed_down_block<NBW, XT, SB_BF16>(a, slot, rb, stage_for(a.routed.F), r, lastf);
+      // the combine buffer of the last slot's blocks overlays the (then finished) staging area
+      routed_down_block<NBW, XT, SB_BF16>(a, slot, rb, stage_for(a.routed.F), r, reinterpret_cast<float*>(lds));
     }
   }
   // count this call: every wavefront that uses the tag has read the word by now (a load still in flight
@@ -917,14 +924,13 @@ WsLayout ws_layout(int d, int E, int k, int F, int S) {
   WsLayout w;
   size_t o = 0;
   w.sync = o;       o += (size_t)(kLinesFixed + k * kLinesPerSlot) * kLW * 4;
-  w.tiles = o;      o += align256((size_t)(d / 16) * kTileStride * 4);
   w.calls = o;      o += align256((size_t)layer_blocks(d, E, k, F, S) * 4);
   w.lg_tag = o;     o += align256((size_t)kLgReplicas * E * 8);
   w.route = o;      o += align256((size_t)kRouteReplicas * 2 * kLayerMaxK * 8);
   w.h_routed = o;   o += align256((size_t)k * F * 4);
   w.h_shared = o;   o += align256((size_t)(S > 0 ? S : 1) * 4);
-  w.y_routed = o;   o += align256((size_t)k * d * 4);
-  w.y_shared = o;   o += align256((size_t)d * 4);
+  w.y_routed = o;   o += align256((size_t)k * d * 8);
+  w.y_shared = o;   o += align256((size_t)d * 8);
   w.x_next = o;     o += align256((size_t)d * 4);
   w.total = o;
   return w;
@@ -1003,6 +1009,7 @@ moe_status prepare_launch(const char* who, const void* x_dev, moe_dtype x_dtype,
   int kmax = d > routed->F ? d : routed->F;
   if (shared && shared->F > kmax) kmax = shared->F;
   *lds = (size_t)d * 4 + (size_t)(kmax / 32) * (kHgStride * 4 + 16);
+  if (*lds < (size_t)(k + 1) * 64 * 4) *lds = (size_t)(k + 1) * 64 * 4;   // the combine buffer
   return MOE_OK;
 }
 
@@ -1039,7 +1046,7 @@ using namespace moeq4;
 
 extern "C" size_t moe_decode_layer_sync_bytes(int32_t d, int32_t k) {
   if (d < 64 || k < 1 || k > kLayerMaxK) return 0;
-  return ws_layout(d, 1, k, 64, 0).calls;   // the sync lines and the tile tickets
+  return ws_layout(d, 1, k, 64, 0).calls;   // the sync lines
 }
 
 extern "C" size_t moe_decode_layer_workspace_bytes(int32_t d, int32_t E, int32_t k, int32_t F, int32_t S) {
