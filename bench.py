@@ -58,10 +58,10 @@ def build_stack(cfg, n_layers):
 # HBM traffic of one layer launch from FETCH_SIZE and WRITE_SIZE counter runs, each scaled by what the counter
 # reads for a plain 256 MiB device copy in the same run (profiles/decode_layer_kernel_stack30_decode.md).  It is
 # reported only while the kernel's sources are the ones the counters were taken on.
-LAYER_TRAFFIC_BYTES = 42343916
+LAYER_TRAFFIC_BYTES = 42567159
 LAYER_TRAFFIC_SOURCES = ("bit_quantized_expert_int8_amd/csrc/layer.hip", "bit_quantized_expert_int8_amd/csrc/q4_device.h",
                          "bit_quantized_expert_int8_amd/csrc/common.h")
-LAYER_TRAFFIC_SHA = "f011cd933a5fb9db"
+LAYER_TRAFFIC_SHA = "7bce2216c8a39d86"
 
 
 def layer_traffic():

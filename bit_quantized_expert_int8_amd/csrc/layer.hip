@@ -101,8 +101,9 @@ struct LayerArgs {
   float* weights_out;
   float* logits_out;
   void* out;
-  int32_t x_f32, out_f32;  // activations held in the workspace as fp32 and exchanged coherently (the
-                           // layers between the first input and the last output of a launch)
+  int32_t x_ws, out_ws;    // activations exchanged through the workspace, in the activation dtype and read
+                           // and written coherently (the layers between the first input and the last
+                           // output of a launch)
   uint32_t* status;
   uint32_t tag;                          // this call's tag: 1 + the calls counted in this block's word
   SyncSet shared_h, done;                // done = this layer's output complete: counts combined 64-row
@@ -134,6 +135,15 @@ __device__ __forceinline__ void st_c64(uint64_t* p, uint64_t v) {
 }
 __device__ __forceinline__ uint64_t ld_c64(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16 bytes at byte offset `off` of the buffer `r` describes, loaded coherently at device scope (sc1)
+__device__ __forceinline__ uint4 ld_c128(__amdgpu_buffer_rsrc_t r, int off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16 /* sc1 */);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+// A raw buffer over n bytes at p (out-of-range loads return zero)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* p, int n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, n, 0x00020000);
 }
 __device__ __forceinline__ uint32_t add_cu(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -216,12 +226,13 @@ __device__ __forceinline__ float u_of(float xg, float rinv) {
 // sum, then the four waves in order (every thread adds the four partial sums itself, the same way).
 // Every load of x and gamma is issued before the first use, without branches in between (an element
 // index past d reads element 0, which is discarded): a conversion or a branch between two loads makes the
-// compiler wait for the first before issuing the second.  The forms (x a previous layer's fp32 output read
-// with coherent loads; with or without gamma) are separate instantiations for the same reason.
-template <typename XT, bool XF32, bool GAMMA>
+// compiler wait for the first before issuing the second.  The forms (x a previous layer's output in the
+// workspace, read with coherent 16-byte loads; with or without gamma) are separate instantiations for the
+// same reason.
+template <typename XT, bool XWS, bool GAMMA>
 __device__ __forceinline__ void norm_to_lds_impl(const LayerArgs& a, float* u, NormLds& nl) {
   constexpr int kIt = kLayerMaxD / (kThreads * 8);
-  constexpr int kXw = (XF32 || sizeof(XT) == 4) ? 2 : 1;   // 16-byte words per 8 elements
+  constexpr int kXw = sizeof(XT) == 4 ? 2 : 1;   // 16-byte words per 8 elements
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   bool live[kIt];
   uint4 xw[kIt][kXw];
@@ -231,12 +242,10 @@ __device__ __forceinline__ void norm_to_lds_impl(const LayerArgs& a, float* u, N
     const int j = (threadIdx.x + it * kThreads) * 8;
     live[it] = j < a.d;
     const int j0 = live[it] ? j : 0;
-    if (XF32) {
-      const float* xf = reinterpret_cast<const float*>(a.x) + j0;
-      xw[it][0] = make_uint4(__float_as_uint(ld_c(xf)), __float_as_uint(ld_c(xf + 1)), __float_as_uint(ld_c(xf + 2)),
-                             __float_as_uint(ld_c(xf + 3)));
-      xw[it][kXw - 1] = make_uint4(__float_as_uint(ld_c(xf + 4)), __float_as_uint(ld_c(xf + 5)),
-                                   __float_as_uint(ld_c(xf + 6)), __float_as_uint(ld_c(xf + 7)));
+    if (XWS) {
+      const __amdgpu_buffer_rsrc_t xr = raw_buffer(a.x, a.d * (int)sizeof(XT));
+#pragma unroll
+      for (int w = 0; w < kXw; ++w) xw[it][w] = ld_c128(xr, (j0 * (int)sizeof(XT)) + 16 * w);
     } else {
       const uint4* xp = reinterpret_cast<const uint4*>(reinterpret_cast<const XT*>(a.x) + j0);
 #pragma unroll
@@ -300,7 +309,7 @@ __device__ __forceinline__ void norm_to_lds_impl(const LayerArgs& a, float* u, N
 
 template <typename XT>
 __device__ __forceinline__ void norm_to_lds(const LayerArgs& a, float* u, NormLds& nl) {
-  if (a.x_f32) {
+  if (a.x_ws) {
     if (a.gamma) norm_to_lds_impl<XT, true, true>(a, u, nl);
     else norm_to_lds_impl<XT, true, false>(a, u, nl);
   } else {
@@ -590,9 +599,14 @@ __device__ __forceinline__ void combine_rows(const LayerArgs& a, const RouteLds&
   float xr = 0.f;
   if (a.residual && t < 64) {
     const XT* x = reinterpret_cast<const XT*>(a.x);
-    xr = a.x_f32 ? ld_c(reinterpret_cast<const float*>(a.x) + row)
-                 : sizeof(XT) == 2 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(x)[row])
-                                   : reinterpret_cast<const float*>(x)[row];
+    if (!a.x_ws)
+      xr = sizeof(XT) == 2 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(x)[row])
+                           : reinterpret_cast<const float*>(x)[row];
+    else if (sizeof(XT) == 2)   // the bf16 pair holding the row, read coherently
+      xr = __uint_as_float((row & 1) ? ld_cu(reinterpret_cast<const uint32_t*>(x) + (row >> 1)) & 0xffff0000u
+                                     : ld_cu(reinterpret_cast<const uint32_t*>(x) + (row >> 1)) << 16);
+    else
+      xr = ld_c(reinterpret_cast<const float*>(x) + row);
   }
   for (int n = 0;; ++n) {
     uint64_t v[kPer];
@@ -622,13 +636,14 @@ __device__ __forceinline__ void combine_rows(const LayerArgs& a, const RouteLds&
     for (int i = 0; i < a.k; ++i) acc = __builtin_fmaf(r.w[i], comb[i * 64 + rl], acc);
     if (a.has_shared) acc += comb[a.k * 64 + rl];
     if (a.residual) acc += xr;
-    const float o = sizeof(XT) == 2 ? bf16_bits_to_f32(f32_to_bf16_bits(acc)) : acc;   // the layer output's rounding
-    if (a.out_f32)
-      st_c(reinterpret_cast<float*>(a.out) + row, o);
-    else if (sizeof(XT) == 2)
-      reinterpret_cast<uint16_t*>(a.out)[row] = (uint16_t)f32_to_bf16_bits(acc);
-    else
-      reinterpret_cast<float*>(a.out)[row] = acc;
+    if (sizeof(XT) == 2) {   // the layer output's rounding
+      const uint16_t o = (uint16_t)f32_to_bf16_bits(acc);
+      if (a.out_ws) __hip_atomic_store(reinterpret_cast<uint16_t*>(a.out) + row, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else reinterpret_cast<uint16_t*>(a.out)[row] = o;
+    } else {
+      if (a.out_ws) st_c(reinterpret_cast<float*>(a.out) + row, acc);
+      else reinterpret_cast<float*>(a.out)[row] = acc;
+    }
   }
   if (!a.last_layer) {
     // the next layer reads these rows once the count is complete: they are stored before the arrival
@@ -832,9 +847,9 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(const StackArgs 
   a.logits_out = L.logits_out;
   char* ws = sa.ws + (int64_t)l * sa.w.total;
   a.x = l == 0 ? sa.x_in : static_cast<const void*>(ws - sa.w.total + sa.w.x_next);
-  a.x_f32 = l > 0;
+  a.x_ws = l > 0;
   a.out = last ? sa.out : static_cast<void*>(ws + sa.w.x_next);
-  a.out_f32 = !last;
+  a.out_ws = !last;
   a.last_layer = last;
   a.status = reinterpret_cast<uint32_t*>(sa.ws);
   uint32_t* sync = reinterpret_cast<uint32_t*>(ws);
