@@ -12,7 +12,9 @@
 //    each wave stages the token's activation half-groups it consumes (the staging of the single-token
 //    kernel), computes the same dot2 chains, and the block adds the waves' partial sums in the same fixed
 //    order.  One token per pass: staging several at once made the compiler keep every token's LDS
-//    addresses live (193 VGPRs at 4 tokens, 2 blocks per CU, measured slower).
+//    addresses live (193 VGPRs at 4 tokens, 2 blocks per CU, measured slower).  The token loop is
+//    pipelined: the list's pair indices are read 64 at a time into a lane register, and the next token's
+//    activation words are loaded before the current token's dot products.
 // 3. grouped down: routed blocks take 64 output rows of a group's expert, wave w rows 16w.. whole (the
 //    mapping of the single-launch layer's down blocks): per token the block stages h once, each wave
 //    reduces its rows within itself, no block-wide sum.  Shared blocks take 16 rows of the shared expert
@@ -26,7 +28,6 @@
 namespace moeq4 {
 namespace {
 
-constexpr int kTM = 1;               // tokens staged per pass
 constexpr int kGroupThreads = 256;
 
 __device__ __forceinline__ int bucket_of(int32_t e, int n_valid) { return (unsigned)e < (unsigned)n_valid ? e : n_valid; }
@@ -144,11 +145,6 @@ __device__ __forceinline__ bool group_slot(const GemvArgs& a, GroupSlot& s) {
   return true;
 }
 
-// pair index (t*k + i; the token itself for the shared expert) of entry c of the block's token list
-__device__ __forceinline__ int pair_of(const GemvArgs& a, const GroupSlot& s, int c) {
-  return s.shared ? s.start + c : a.perm[s.start + c];
-}
-
 template <int NBW, bool SB_BF16>
 struct RowPairRegs {
   SbWord<SB_BF16> sa[NBW], sb[NBW];
@@ -180,57 +176,83 @@ __device__ __forceinline__ void load_rowpair(const char* rowA, const char* rowB,
   }
 }
 
-// Steps 1 and 4: stage the first `nlive` of kTM activation vectors (this wave's half-groups of each).
-template <int NBW, typename XT>
-__device__ __forceinline__ void stage_tokens(const XT* const (&xs)[kTM], int nlive, int K, const Stage (&st)[kTM], int W) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int C = K / 32, nit = (C + kLanesPerRow - 1) / kLanesPerRow;
-  constexpr int kPasses = (NBW * 32 + 63) / 64;
-  XWord<XT> xw[kTM][kPasses];
+// The block's token list: entry c is pair pair_at(c) (t*k + i; the token itself for the shared expert).
+// Routed lists are read from perm 64 entries at a time into a lane register, so a token's pair index is a
+// lane broadcast instead of a dependent load.
+struct TokenList {
+  const int32_t* perm;   // NULL for the shared expert
+  int start, count, base, lanes;
+  __device__ __forceinline__ int pair_at(int c) {
+    if (!perm) return start + c;
+    if (c - base >= 64 || c < base) {   // uniform over the block
+      base = c & ~63;
+      const int lane = threadIdx.x & 63;
+      lanes = base + lane < count ? perm[start + base + lane] : 0;
+    }
+    return __builtin_amdgcn_readlane(lanes, c - base);
+  }
+};
+
+__device__ __forceinline__ TokenList token_list(const GemvArgs& a, const GroupSlot& s) {
+  return TokenList{s.shared ? nullptr : a.perm, s.start, s.count, -64, 0};
+}
+
+// Step 1 of the single-token row-pair routine for one token: this wave's activation words (the slots are
+// the same for every token).
+template <int NBW>
+struct TokSlots {
+  static constexpr int kPasses = (NBW * 32 + 63) / 64;
   int hgp[kPasses];
   bool livep[kPasses];
+  __device__ __forceinline__ TokSlots(int K, int W) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int C = K / 32, nit = (C + kLanesPerRow - 1) / kLanesPerRow;
 #pragma unroll
-  for (int p = 0; p < kPasses; ++p) {
-    const int s = lane + 64 * p, m = s >> 5, jj = (s >> 2) & 7;
-    const int it = wave + W * m;
-    hgp[p] = it * kLanesPerRow + jj;
-    livep[p] = m < NBW && it < nit && hgp[p] < C;
+    for (int p = 0; p < kPasses; ++p) {
+      const int s = lane + 64 * p, m = s >> 5, jj = (s >> 2) & 7;
+      const int it = wave + W * m;
+      hgp[p] = it * kLanesPerRow + jj;
+      livep[p] = m < NBW && it < nit && hgp[p] < C;
+    }
   }
+};
+
+template <int NBW, typename XT>
+__device__ __forceinline__ void load_token(const XT* x, const TokSlots<NBW>& ts, XWord<XT> (&xw)[TokSlots<NBW>::kPasses]) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int tk = 0; tk < kTM; ++tk)
-    if (tk < nlive) {
+  for (int p = 0; p < TokSlots<NBW>::kPasses; ++p)
+    if (ts.livep[p]) load_word<XT>(x, ts.hgp[p], (lane + 64 * p) & 3, xw[p]);
+}
+
+// Step 4: stage this wave's half-groups of the loaded token (wave-local).
+template <int NBW, typename XT>
+__device__ __forceinline__ void stage_token(const XWord<XT> (&xw)[TokSlots<NBW>::kPasses], const TokSlots<NBW>& ts,
+                                            Stage st) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-      for (int p = 0; p < kPasses; ++p)
-        if (livep[p]) load_word<XT>(xs[tk], hgp[p], (lane + 64 * p) & 3, xw[tk][p]);
+  for (int p = 0; p < TokSlots<NBW>::kPasses; ++p) {
+    float v[8];
+    if (ts.livep[p]) word_to_f32<XT>(xw[p], v);
+    else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.f;
     }
-#pragma unroll
-  for (int tk = 0; tk < kTM; ++tk)
-    if (tk < nlive) {
-#pragma unroll
-      for (int p = 0; p < kPasses; ++p) {
-        float v[8];
-        if (livep[p]) word_to_f32<XT>(xw[tk][p], v);
-        else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) v[i] = 0.f;
-        }
-        stage_word(v, livep[p], hgp[p], (lane + 64 * p) & 3, st[tk]);
-      }
-    }
+    stage_word(v, ts.livep[p], ts.hgp[p], (lane + 64 * p) & 3, st);
+  }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Step 5 for each live token: chunk_dot on the staged activation (the codes are dequantized again per
-// token: a few extra VALU operations instead of 32 more live registers per chunk).
+// Step 5: chunk_dot on the staged activation (the codes are dequantized again per token: a few extra VALU
+// operations instead of 32 more live registers per chunk).
 template <int NBW, bool SB_BF16>
-__device__ __forceinline__ void rowpair_dots(const RowPairRegs<NBW, SB_BF16>& r, int K, const Stage (&st)[kTM], int nlive,
-                                             bool valid, float (&yA)[kTM], float (&yB)[kTM], int W) {
+__device__ __forceinline__ void rowpair_dots(const RowPairRegs<NBW, SB_BF16>& r, int K, Stage st, bool valid, float& yA,
+                                             float& yB, int W) {
   const int wave = threadIdx.x >> 6, j = threadIdx.x & 7;
   const int C = K / 32;
-#pragma unroll
-  for (int tk = 0; tk < kTM; ++tk) yA[tk] = yB[tk] = 0.f;
+  yA = yB = 0.f;
   if (!valid) return;
   const Dequant dq = opaque_dequant();
 #pragma unroll
@@ -240,60 +262,61 @@ __device__ __forceinline__ void rowpair_dots(const RowPairRegs<NBW, SB_BF16>& r,
     float s0, b0, s1, b1;
     sb_values<SB_BF16>(r.sa[m], s0, b0);
     sb_values<SB_BF16>(r.sb[m], s1, b1);
-#pragma unroll
-    for (int tk = 0; tk < kTM; ++tk)
-      if (tk < nlive) {
-        const u32x4* xv = reinterpret_cast<const u32x4*>(st[tk].xw + c * kHgStride);
-        const u32x4 x0 = xv[0], x1 = xv[1], x2 = xv[2], x3 = xv[3];
-        const float4 h = st[tk].hg[c];
-        const float accA = chunk_dot(r.qa[m], x0, x1, x2, x3, dq, -h.y);
-        const float accB = chunk_dot(r.qb[m], x0, x1, x2, x3, dq, -h.y);
-        yA[tk] = fmaf(h.x, fmaf(s0, accA, b0 * h.z), yA[tk]);
-        yB[tk] = fmaf(h.x, fmaf(s1, accB, b1 * h.z), yB[tk]);
-      }
+    const u32x4* xv = reinterpret_cast<const u32x4*>(st.xw + c * kHgStride);
+    const u32x4 x0 = xv[0], x1 = xv[1], x2 = xv[2], x3 = xv[3];
+    const float4 h = st.hg[c];
+    const float accA = chunk_dot(r.qa[m], x0, x1, x2, x3, dq, -h.y);
+    const float accB = chunk_dot(r.qb[m], x0, x1, x2, x3, dq, -h.y);
+    yA = fmaf(h.x, fmaf(s0, accA, b0 * h.z), yA);
+    yB = fmaf(h.x, fmaf(s1, accB, b1 * h.z), yB);
   }
 }
 
-// block_sum for kTM tokens (same order: 8 lanes, then waves 0..W-1).  The caller must pass a block
+// block_sum over the first W waves (same order: 8 lanes, then waves 0..W-1).  The caller must pass a block
 // barrier before the next call (the LDS partials are reused).
-__device__ __forceinline__ bool block_sum_tokens(float (&yA)[kTM], float (&yB)[kTM], int nlive, int W) {
-  __shared__ float red[kMaxWaves][kTM][16];
+__device__ __forceinline__ bool block_sum_waves(float& yA, float& yB, int W) {
+  __shared__ float red[kMaxWaves][16];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, ra = lane >> 3, j = lane & 7;
-#pragma unroll
-  for (int tk = 0; tk < kTM; ++tk)
-    if (tk < nlive) {
-      yA[tk] = reduce8(yA[tk]);
-      yB[tk] = reduce8(yB[tk]);
-    }
+  yA = reduce8(yA);
+  yB = reduce8(yB);
   if (W == 1 && blockDim.x == 64) return j == 0;
   if (j == 0 && wave < W) {
-#pragma unroll
-    for (int tk = 0; tk < kTM; ++tk)
-      if (tk < nlive) {
-        red[wave][tk][ra] = yA[tk];
-        red[wave][tk][8 + ra] = yB[tk];
-      }
+    red[wave][ra] = yA;
+    red[wave][8 + ra] = yB;
   }
   __syncthreads();
   if (wave != 0 || j != 0) return false;
-#pragma unroll
-  for (int tk = 0; tk < kTM; ++tk)
-    if (tk < nlive) {
-      yA[tk] = red[0][tk][ra];
-      yB[tk] = red[0][tk][8 + ra];
-      for (int w = 1; w < W; ++w) {
-        yA[tk] += red[w][tk][ra];
-        yB[tk] += red[w][tk][8 + ra];
-      }
-    }
+  yA = red[0][ra];
+  yB = red[0][8 + ra];
+  for (int w = 1; w < W; ++w) {
+    yA += red[w][ra];
+    yB += red[w][8 + ra];
+  }
   return true;
 }
 
-__device__ __forceinline__ void make_stages(uint32_t* lds, int nhg, Stage (&st)[kTM]) {
-  const int per_tok = nhg * (kHgStride + 4);
+// The token loop of the row-pair blocks (gate_up, shared down): rows in registers, each token staged by
+// the waves that use it; the next token's words are loaded before the current token's dot products.
+// emit(pair, yA, yB) runs on the lanes holding the totals.
+template <int NBW, typename XT, bool SB_BF16, typename Row, typename Emit>
+__device__ __forceinline__ void rowpair_token_loop(const RowPairRegs<NBW, SB_BF16>& w, TokenList tl, int K, Stage st,
+                                                   bool valid, bool active, int W, Row row_of, Emit emit) {
+  const TokSlots<NBW> ts(K, W);
+  XWord<XT> cur[TokSlots<NBW>::kPasses], nxt[TokSlots<NBW>::kPasses];
+  int pair = tl.count > 0 ? tl.pair_at(0) : 0;
+  if (active && tl.count > 0) load_token<NBW, XT>(row_of(pair), ts, cur);
+  for (int c = 0; c < tl.count; ++c) {
+    if (active) stage_token<NBW, XT>(cur, ts, st);
+    const int next = c + 1 < tl.count ? tl.pair_at(c + 1) : 0;
+    if (active && c + 1 < tl.count) load_token<NBW, XT>(row_of(next), ts, nxt);
+    float yA, yB;
+    rowpair_dots<NBW, SB_BF16>(w, K, st, valid && active, yA, yB, W);
+    if (block_sum_waves(yA, yB, W)) emit(pair, yA, yB);
+    __syncthreads();   // the staging area and the partials are rewritten for the next token
 #pragma unroll
-  for (int tk = 0; tk < kTM; ++tk)
-    st[tk] = Stage{lds + tk * per_tok, reinterpret_cast<float4*>(lds + tk * per_tok + nhg * kHgStride)};
+    for (int p = 0; p < TokSlots<NBW>::kPasses; ++p) cur[p] = nxt[p];
+    pair = next;
+  }
 }
 
 template <int NBW, typename XT, bool SB_BF16>
@@ -302,38 +325,25 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gate_up_grouped_kernel(GemvArg
   GroupSlot sl;
   if (!group_slot(a, sl)) return;
   const Pool& P = sl.shared ? a.shared : a.routed;
-  const int K = a.d, nhg = K / 32;
+  const int K = a.d, nhg = K / 32, W = blockDim.x >> 6;
   const int ra = (threadIdx.x & 63) >> 3;
   const int F = P.F, f = sl.tile * 8 + ra;
   const char* rec = P.base + (int64_t)sl.e * P.record_bytes;
   const int64_t rowb = K / 2, sbrow = (int64_t)(K / 64) * (SB_BF16 ? 4 : 8);
   RowPairRegs<NBW, SB_BF16> w;
   load_rowpair<NBW, SB_BF16>(rec + P.off_q + f * rowb, rec + P.off_q + (F + f) * rowb, rec + P.off_sb + f * sbrow,
-                             rec + P.off_sb + (F + f) * sbrow, K, sl.valid, w, blockDim.x >> 6);
-  Stage st[kTM];
-  make_stages(lds, nhg, st);
+                             rec + P.off_sb + (F + f) * sbrow, K, sl.valid, w, W);
+  const Stage st{lds, reinterpret_cast<float4*>(lds + nhg * kHgStride)};
   const XT* x = reinterpret_cast<const XT*>(a.in);
   float* hbase = sl.shared ? a.h_shared : a.h_routed;
-  for (int c0 = 0; c0 < sl.count; c0 += kTM) {
-    const int nlive = min(kTM, sl.count - c0);
-    int pair[kTM];
-    const XT* xs[kTM];
-#pragma unroll
-    for (int tk = 0; tk < kTM; ++tk) {
-      pair[tk] = tk < nlive ? pair_of(a, sl, c0 + tk) : 0;
-      xs[tk] = x + (int64_t)(sl.shared ? pair[tk] : pair[tk] / a.k) * K;
-    }
-    stage_tokens<NBW, XT>(xs, nlive, K, st, blockDim.x >> 6);
-    float yA[kTM], yB[kTM];
-    rowpair_dots<NBW, SB_BF16>(w, K, st, nlive, sl.valid, yA, yB, blockDim.x >> 6);
-    if (block_sum_tokens(yA, yB, nlive, blockDim.x >> 6)) {
-#pragma unroll
-      for (int tk = 0; tk < kTM; ++tk)
-        if (tk < nlive)
-          hbase[(int64_t)pair[tk] * F + f] = sl.valid ? activation(yA[tk], a.act) * yB[tk] : __builtin_nanf("");
-    }
-    __syncthreads();
-  }
+  const bool shared = sl.shared, valid = sl.valid;
+  const int k = a.k, act = a.act;
+  rowpair_token_loop<NBW, XT, SB_BF16>(
+      w, token_list(a, sl), K, st, valid, true, W,
+      [=](int pair) { return x + (int64_t)(shared ? pair : pair / k) * K; },
+      [=](int pair, float yA, float yB) {
+        hbase[(int64_t)pair * F + f] = valid ? activation(yA, act) * yB : __builtin_nanf("");
+      });
 }
 
 // The 64-row routed block: lane (ra, j) of wave w takes rows r = tile * 64 + 16 w + ra and r + 8, chunks
@@ -368,16 +378,29 @@ __device__ __forceinline__ void down_routed_rows(const GemvArgs& a, const GroupS
     }
   }
   const Stage st{lds, reinterpret_cast<float4*>(lds + nhg * kHgStride)};
-  for (int c0 = 0; c0 < sl.count; ++c0) {
-    const int pair = pair_of(a, sl, c0);
+  // the token's h is staged by the block, one (half-group, quarter) item per thread (K <= 1024 with 256
+  // threads: one item each); the next token's h is loaded before the current token's dot products
+  TokenList tl = token_list(a, sl);
+  const int item = threadIdx.x, hg_i = item >> 2, qd_i = item & 3;
+  const bool has_item = item < nhg * 4;
+  float4 hc0 = make_float4(0.f, 0.f, 0.f, 0.f), hc1 = hc0, hn0 = hc0, hn1 = hc0;
+  int pair = tl.count > 0 ? tl.pair_at(0) : 0;
+  if (has_item && tl.count > 0) {
+    const float4* hv = reinterpret_cast<const float4*>(a.h_routed + (int64_t)pair * K + hg_i * 32 + qd_i * 8);
+    hc0 = hv[0];
+    hc1 = hv[1];
+  }
+  for (int c0 = 0; c0 < tl.count; ++c0) {
     const Dequant dq = opaque_dequant();
-    // the token's h, staged by the block (one (half-group, quarter) item per thread)
-    for (int t = threadIdx.x; t < nhg * 4; t += blockDim.x) {
-      const int hg = t >> 2, qd = t & 3;
-      const float4* hv = reinterpret_cast<const float4*>(a.h_routed + (int64_t)pair * K + hg * 32 + qd * 8);
-      const float4 h0 = hv[0], h1 = hv[1];
-      const float v[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-      stage_word(v, true, hg, qd, st);
+    {
+      const float v[8] = {hc0.x, hc0.y, hc0.z, hc0.w, hc1.x, hc1.y, hc1.z, hc1.w};
+      stage_word(v, has_item, hg_i, qd_i, st);
+    }
+    const int next = c0 + 1 < tl.count ? tl.pair_at(c0 + 1) : 0;
+    if (has_item && c0 + 1 < tl.count) {
+      const float4* hv = reinterpret_cast<const float4*>(a.h_routed + (int64_t)next * K + hg_i * 32 + qd_i * 8);
+      hn0 = hv[0];
+      hn1 = hv[1];
     }
     __syncthreads();
     // chunk iteration m belongs to wave m % W of the one-token launch: one partial per such wave, each
@@ -420,6 +443,9 @@ __device__ __forceinline__ void down_routed_rows(const GemvArgs& a, const GroupS
       y[r + 8] = sl.valid ? yB : __builtin_nanf("");
     }
     __syncthreads();   // the staging area is rewritten for the next token
+    hc0 = hn0;
+    hc1 = hn1;
+    pair = next;
   }
 }
 
@@ -445,31 +471,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void down_grouped_kernel(GemvArgs a
   RowPairRegs<NBW, SB_BF16> w;
   load_rowpair<NBW, SB_BF16>(rec + P.off_q + r * rowb, rec + P.off_q + (r + 8) * rowb, rec + P.off_sb + r * sbrow,
                              rec + P.off_sb + (r + 8) * sbrow, K, active, w, W);
-  Stage st[kTM];
-  make_stages(lds, nhg, st);
-  for (int c0 = 0; c0 < sl.count; c0 += kTM) {
-    const int nlive = min(kTM, sl.count - c0);
-    int pair[kTM];
-    const float* xs[kTM];
-#pragma unroll
-    for (int tk = 0; tk < kTM; ++tk) {
-      pair[tk] = tk < nlive ? pair_of(a, sl, c0 + tk) : 0;
-      xs[tk] = a.h_shared + (int64_t)pair[tk] * K;
-    }
-    if (active) stage_tokens<NBW, float>(xs, nlive, K, st, W);
-    float yA[kTM], yB[kTM];
-    rowpair_dots<NBW, SB_BF16>(w, K, st, nlive, active, yA, yB, W);
-    if (block_sum_tokens(yA, yB, nlive, W)) {
-#pragma unroll
-      for (int tk = 0; tk < kTM; ++tk)
-        if (tk < nlive) {
-          float* y = a.y_shared + (int64_t)pair[tk] * d;
-          y[r] = yA[tk];
-          y[r + 8] = yB[tk];
-        }
-    }
-    __syncthreads();
-  }
+  const Stage st{lds, reinterpret_cast<float4*>(lds + nhg * kHgStride)};
+  const float* hs = a.h_shared;
+  float* ys = a.y_shared;
+  rowpair_token_loop<NBW, float, SB_BF16>(
+      w, token_list(a, sl), K, st, true, active, W, [=](int pair) { return hs + (int64_t)pair * K; },
+      [=](int pair, float yA, float yB) {
+        ys[(int64_t)pair * d + r] = yA;
+        ys[(int64_t)pair * d + r + 8] = yB;
+      });
 }
 
 }  // namespace
@@ -483,7 +493,7 @@ moe_status launch_group_pairs(const int32_t* ids, int P, int n_valid, int32_t* n
 moe_status launch_gate_up_grouped(const GemvArgs& a, moe_dtype x_dtype, bool sb_bf16, int nbw, int waves, dim3 grid,
                                   hipStream_t s) {
   const dim3 block(64 * waves);
-  const size_t lds = kTM * lds_bytes(a.d);
+  const size_t lds = lds_bytes(a.d);
   return dispatch_nbw(nbw, [&](auto nb) {
     constexpr int N = decltype(nb)::value;
     if (x_dtype == MOE_BF16) {
@@ -499,7 +509,7 @@ moe_status launch_gate_up_grouped(const GemvArgs& a, moe_dtype x_dtype, bool sb_
 
 moe_status launch_down_grouped(const GemvArgs& a, bool sb_bf16, int nbw, dim3 grid, int K_lds, hipStream_t s) {
   const dim3 block(64 * kMaxWaves);
-  const size_t lds = kTM * lds_bytes(K_lds);
+  const size_t lds = lds_bytes(K_lds);
   return dispatch_nbw(nbw, [&](auto nb) {
     constexpr int N = decltype(nb)::value;
     if (sb_bf16) hipLaunchKernelGGL((down_grouped_kernel<N, true>), grid, block, lds, s, a);
