@@ -346,7 +346,6 @@ struct GemvArgs {
   float* y_shared;         // [T][d]
   int32_t nb_shared;       // blocks of the shared expert per token
   int32_t nb_routed;       // blocks per routed expert
-  int32_t down_waves;      // grouped down: the waves of the one-token down launch (its summation order)
   int32_t act;
   // fused combine (down launch only): out[t] = round(sum_i w[t][i] y_routed[t][i] + y_shared[t] + residual[t])
   const float* weights;    // [T][k]
@@ -359,6 +358,7 @@ struct GemvArgs {
   int32_t* n_groups;       // [1] non-empty groups (written by the grouping kernel)
   int4* groups;            // [groups_max] (expert or n_records for invalid ids, first index into perm, count, 0)
   int32_t* perm;           // [T*k] pair indices, grouped by expert, ascending within a group
+  char* stage;             // activations staged for the matrix cores (StagedRows), T > 1
 };
 
 // The combine of one 16-row tile of token t, summed in the order i = 0..k-1, shared, residual (the
@@ -382,18 +382,57 @@ __device__ __forceinline__ void combine_tile(const GemvArgs& a, int t, int tile)
     reinterpret_cast<float*>(a.out)[(int64_t)t * d + row] = acc;
 }
 
-// Launchers of the grouped kernels (q4_grouped.hip).  The grouping kernel sorts the T*k pairs of
-// a.ids by expert into a.groups / a.perm / a.n_groups; the grouped gate_up and down launches then run
-// one block per (group, tile) and stream each selected expert's rows once for all of its tokens.
+// The grouping of a batch's T*k (token, slot) pairs by expert (q4_grouped.hip): a.ids sorted into
+// a.groups / a.perm / a.n_groups, so that the grouped products (q4_mfma.hip) stream each selected expert's
+// rows once for all of its tokens.
 constexpr int kMaxGroupedRecords = 4096;   // routed pool records supported with T > 1
-constexpr int kSharedTokens = 8;           // tokens per shared-expert block of the grouped kernels
 moe_status launch_group_pairs(const int32_t* ids, int P, int n_valid, int32_t* n_groups, int4* groups, int32_t* perm,
                               hipStream_t s);
-moe_status launch_gate_up_grouped(const GemvArgs& a, moe_dtype x_dtype, bool sb_bf16, int nbw, int waves, dim3 grid,
-                                  hipStream_t s);
-moe_status launch_down_grouped(const GemvArgs& a, bool sb_bf16, int nbw, dim3 grid, int K_lds, hipStream_t s);
 
 inline size_t lds_bytes(int K) { return (size_t)(K / 32) * (kHgStride * 4 + 16); }
+
+// Matrix-core path for T > 1 (q4_mfma.hip).  Activation rows are staged once per call in the fp16 form the
+// MFMA kernel multiplies (one power-of-two scale per row, per-64-group sums); then one block per 16 weight
+// rows and (group or shared matrix) multiplies them with up to 16 tokens at a time.
+struct StagedRows {
+  _Float16* xq;   // [rows][K]
+  float2* os;     // [rows][K/64]: (1024 * sum of the group's staged values, sum of its values / 2^e)
+  float* ef;      // [rows] 2^e
+};
+inline size_t staged_rows_bytes(int64_t rows, int K) {
+  auto a256 = [](size_t x) { return (x + 255) / 256 * 256; };
+  return a256((size_t)rows * K * 2) + a256((size_t)rows * (K / 64) * 8) + a256((size_t)rows * 4);
+}
+inline StagedRows staged_rows_at(char* base, int64_t rows, int K) {
+  auto a256 = [](size_t x) { return (x + 255) / 256 * 256; };
+  StagedRows r;
+  r.xq = reinterpret_cast<_Float16*>(base);
+  r.os = reinterpret_cast<float2*>(base + a256((size_t)rows * K * 2));
+  r.ef = reinterpret_cast<float*>(base + a256((size_t)rows * K * 2) + a256((size_t)rows * (K / 64) * 8));
+  return r;
+}
+moe_status launch_stage_rows(const void* x, bool x_bf16, int rows, int K, const StagedRows& out, hipStream_t s);
+// The grouped products of T > 1 tokens on the matrix cores.  Shared blocks come first, then n_routed_blocks
+// per group of (token, slot) pairs; a block's 4 waves hold 4 / wk tiles of 16 weight rows (gate_up: 8
+// gate and the 8 matching up rows), the wk waves of a tile splitting its K.
+struct MfmaArgs {
+  Pool routed, shared;          // off_q / off_sb select the matrix
+  int32_t K_routed, K_shared;   // row lengths
+  int32_t wk_routed, wk_shared; // waves per tile: 1, 2 or 4
+  int32_t gate_up;              // 1: out = act(gate) * up per feature; 0: out = the 16 rows' products
+  int32_t act;
+  int32_t T, k;
+  int32_t n_shared_blocks, n_routed_blocks;
+  const int32_t* n_groups;
+  const int4* groups;
+  const int32_t* perm;
+  StagedRows xs_routed, xs_shared;   // routed rows are tokens (gate_up) or pairs (down); shared rows are tokens
+  float* out_routed;            // gate_up: h [pairs][F]; down: y [pairs][d]
+  float* out_shared;            // gate_up: h [T][S];     down: y [T][d]
+  int32_t out_len_routed, out_len_shared;
+};
+int mfma_waves_per_tile(int K);
+moe_status launch_grouped_mfma(const MfmaArgs& a, int gmax, bool sb_bf16, hipStream_t s);
 
 struct Slot {
   bool shared, valid;

@@ -140,12 +140,23 @@ size_t group_table_bytes(int n_records, int T, int k) {
 
 using namespace moeq4;
 
+// T > 1: the activations staged for the matrix cores, the tokens' (gate_up) or the hidden vectors (down)
+size_t stage_region_bytes(const moe_q4_pool* routed, int32_t k, const moe_q4_pool* shared, int32_t T) {
+  const bool has_routed = routed && k > 0;
+  const int d = has_routed ? routed->d : shared->d;
+  const size_t gu = moeq4::staged_rows_bytes(T, d);
+  const size_t dn = (has_routed ? moeq4::staged_rows_bytes((int64_t)T * k, routed->F) : 0) +
+                    (shared ? moeq4::staged_rows_bytes(T, shared->F) : 0);
+  return gu > dn ? gu : dn;
+}
+
 extern "C" size_t q4_expert_gemv_workspace_bytes(const moe_q4_pool* routed, int32_t k, const moe_q4_pool* shared, int32_t T) {
   if (T < 1) return 0;
   size_t b = 0;
   if (routed && k > 0) b += align256((size_t)T * k * routed->F * 4);
   if (shared) b += align256((size_t)T * shared->F * 4);
   if (routed && k > 0 && T > 1) b += group_table_bytes(routed->n_records, T, k);
+  if (T > 1 && ((routed && k > 0) || shared)) b += stage_region_bytes(routed, k, shared, T);
   return b;
 }
 
@@ -207,12 +218,14 @@ moe_status prepare(const char* who, const moe_q4_pool* routed, const int32_t* id
   a->y_shared = y_shared_dev;
   a->act = act;
   a->T = T;
+  char* g = ws + (has_routed ? align256((size_t)T * k * Fr * 4) : 0) + (shared ? align256((size_t)T * Fs * 4) : 0);
   if (has_routed && T > 1) {
-    char* g = ws + align256((size_t)T * k * Fr * 4) + (shared ? align256((size_t)T * Fs * 4) : 0);
     a->n_groups = reinterpret_cast<int32_t*>(g);
     a->groups = reinterpret_cast<int4*>(g + 256);
     a->perm = reinterpret_cast<int32_t*>(g + 256 + align256((size_t)groups_max(routed->n_records, T, k) * 16));
+    g += group_table_bytes(routed->n_records, T, k);
   }
+  a->stage = T > 1 ? g : nullptr;
   return MOE_OK;
 }
 
@@ -229,14 +242,35 @@ moe_status run_gate_up(GemvArgs a, const RecordOffsets& orr, const RecordOffsets
   const int waves = nit < kMaxWaves ? nit : kMaxWaves;
   const int nbw = (nit + waves - 1) / waves;
   if (T > 1) {
-    // grouped: sort the pairs by expert, then one block per (group, 8 features) and per shared tile
+    // grouped on the matrix cores: sort the pairs by expert, stage the T tokens once, then one block per
+    // (group, 8 features) and per 8 shared features, each with all of its tokens
     if (a.k > 0) {
       const moe_status st = launch_group_pairs(a.ids, T * a.k, a.routed.n_records, a.n_groups, a.groups, a.perm, s);
       if (st != MOE_OK) return st;
     }
-    const int gmax = a.k > 0 ? groups_max(a.routed.n_records, T, a.k) : 0;
-    const int shared_blocks = a.nb_shared * ((T + kSharedTokens - 1) / kSharedTokens);
-    return launch_gate_up_grouped(a, x_dtype, sb_bf16, nbw, waves, dim3(shared_blocks + gmax * a.nb_routed), s);
+    const StagedRows xs = staged_rows_at(a.stage, T, a.d);
+    moe_status st = launch_stage_rows(a.in, x_dtype == MOE_BF16, T, a.d, xs, s);
+    if (st != MOE_OK) return st;
+    MfmaArgs m{};
+    m.routed = a.routed;
+    m.shared = a.shared;
+    m.K_routed = m.K_shared = a.d;
+    m.wk_routed = m.wk_shared = mfma_waves_per_tile(a.d);
+    m.gate_up = 1;
+    m.act = a.act;
+    m.T = T;
+    m.k = a.k;
+    m.n_shared_blocks = a.nb_shared * m.wk_shared / 4;     // 8 features a tile, 4 / wk tiles a block
+    m.n_routed_blocks = a.nb_routed * m.wk_routed / 4;
+    m.n_groups = a.n_groups;
+    m.groups = a.groups;
+    m.perm = a.perm;
+    m.xs_routed = m.xs_shared = xs;
+    m.out_routed = a.h_routed;
+    m.out_shared = a.h_shared;
+    m.out_len_routed = a.routed.F;
+    m.out_len_shared = a.shared.F;
+    return launch_grouped_mfma(m, a.k > 0 ? groups_max(a.routed.n_records, T, a.k) : 0, sb_bf16, s);
   }
   dim3 grid(a.nb_shared + a.k * a.nb_routed, T);
   return dispatch_nbw(nbw, [&](auto nb) {
@@ -260,15 +294,45 @@ moe_status run_down(GemvArgs a, const RecordOffsets& orr, const RecordOffsets& o
   const int waves = nit_lo < kMaxWaves ? nit_lo : kMaxWaves;
   const int nbw = (nit_hi + waves - 1) / waves;
   if (T > 1) {
-    // grouped: 64 rows per routed block (whole rows per wave), 16 shared rows per block and token chunk
+    // grouped on the matrix cores: stage the hidden vectors (one row per pair, one per token for the shared
+    // expert), then one launch for both matrices: tiles of 16 rows of d with all of a group's pairs (routed,
+    // row length F) or all T tokens (shared, row length S)
     if (combine) return fail(MOE_ERR_UNSUPPORTED, "q4_expert_gemv: the combine of several tokens is its own launch");
-    const int gmax = has_routed ? groups_max(a.routed.n_records, T, a.k) : 0;
-    a.nb_routed = a.d / 64;
-    const int shared_blocks = a.nb_shared * ((T + kSharedTokens - 1) / kSharedTokens);
-    a.down_waves = waves;   // the split of the one-token launch, so every token's rows come out the same
-    const int nbw_s = has_shared ? (nit_s + waves - 1) / waves : 1;
-    const int nbw_g = nbw_s > nit_r ? nbw_s : nit_r;
-    return launch_down_grouped(a, sb_bf16, nbw_g, dim3(shared_blocks + gmax * a.nb_routed), Fr > Fs ? Fr : Fs, s);
+    const int P = T * a.k;
+    char* base = a.stage;
+    StagedRows xr{}, xsh{};
+    moe_status st = MOE_OK;
+    if (has_routed) {
+      xr = staged_rows_at(base, P, Fr);
+      base += staged_rows_bytes(P, Fr);
+      st = launch_stage_rows(a.h_routed, false, P, Fr, xr, s);
+      if (st != MOE_OK) return st;
+    }
+    if (has_shared) {
+      xsh = staged_rows_at(base, T, Fs);
+      st = launch_stage_rows(a.h_shared, false, T, Fs, xsh, s);
+      if (st != MOE_OK) return st;
+    }
+    MfmaArgs m{};
+    m.routed = a.routed;
+    m.shared = a.shared;
+    m.K_routed = Fr;
+    m.K_shared = Fs;
+    m.wk_routed = has_routed ? mfma_waves_per_tile(Fr) : 1;
+    m.wk_shared = has_shared ? mfma_waves_per_tile(Fs) : 1;
+    m.T = T;
+    m.k = a.k;
+    m.n_shared_blocks = has_shared ? a.d / 16 * m.wk_shared / 4 : 0;   // 16 rows a tile, 4 / wk tiles a block
+    m.n_routed_blocks = has_routed ? a.d / 16 * m.wk_routed / 4 : 0;
+    m.n_groups = a.n_groups;
+    m.groups = a.groups;
+    m.perm = a.perm;
+    m.xs_routed = xr;
+    m.xs_shared = xsh;
+    m.out_routed = a.y_routed;
+    m.out_shared = a.y_shared;
+    m.out_len_routed = m.out_len_shared = a.d;
+    return launch_grouped_mfma(m, has_routed ? groups_max(a.routed.n_records, T, a.k) : 0, sb_bf16, s);
   }
   dim3 grid(a.nb_shared + a.k * a.nb_routed, T);
   return dispatch_nbw(nbw, [&](auto nb) {

@@ -169,9 +169,12 @@ moe_status moe_norm_router_topk(const void* x_dev, moe_dtype x_dtype, const floa
  * Weights are dequantized on the fly; accumulation is fp32.  Both experts kinds run in the same launches.
  * x_dev: x_dtype [T][d]; ids_dev: int32 [T][k] (device, e.g. straight from moe_router_topk or cache slot
  * ids from expert_cache_stage); y_routed_dev: fp32 [T][k][d]; y_shared_dev: fp32 [T][d] (needed iff shared).
- * T == 1 is the decode GEMV.  T > 1 first groups the T*k (token, slot) pairs by expert on the device
- * (moe_group_pairs, below) and then streams each selected expert's rows once for all of its tokens, and
- * the shared expert's rows once for all T tokens; every token's result is bit-identical to a T == 1 call.
+ * T == 1 is the decode GEMV (vector ALUs, dot2).  T > 1 first groups the T*k (token, slot) pairs by
+ * expert on the device (moe_group_pairs, below), then streams each selected expert's rows once for all of
+ * its tokens, and the shared expert's rows once for all T tokens, as small dense products on the matrix
+ * cores (fp16 inputs: codes exactly, activations scaled by a power of two per token row; fp32 sums).
+ * The two paths round differently: a token's T > 1 result matches its T == 1 result within the fp32/fp16
+ * rounding of the activations (tested to max relative error 1e-2 with the oracle), not bit for bit.
  * Limits: k <= 32; routed and shared share d; routed may be NULL (k == 0) to run only the shared expert;
  * with T > 1 the routed pool has at most 4096 records (MOE_ERR_UNSUPPORTED otherwise).
  * Workspace: q4_expert_gemv_workspace_bytes(...) bytes of device memory (contents need no initial value).
@@ -226,8 +229,8 @@ moe_status moe_combine(const float* y_routed_dev, const float* weights_dev, cons
 /* q4_expert_gemv_combine — q4_expert_gemv followed by moe_combine.  With T == 1 in two launches instead of
  * three: the down GEMV's blocks publish their rows and the last block to finish a 16-row tile applies the
  * combine to it ([G26] "Concurrence pour masquer la latence": routed and shared outputs merged once all
- * are in); with T > 1 the grouped down GEMV and the combine are separate launches (per-tile tickets for
- * every token would cost more than the launch they save).  Computes, for every token t,
+ * are in); with T > 1 the grouped down products and the combine are separate launches (per-tile tickets
+ * for every token would cost more than the launch they save).  Computes, for every token t,
  *   out[t] = round_out( sum_{i<k} weights[t][i] * y_routed[t][i] + y_shared[t] + residual[t] )
  * with y_routed / y_shared as q4_expert_gemv defines them, summed in the same order as moe_combine; the
  * result is bit-identical to q4_expert_gemv + moe_combine on the same inputs.  y_routed and y_shared stay

@@ -1,6 +1,7 @@
 """GPU checks of the batched (T > 1) path on MI355X: the device grouping of (token, slot) pairs against the
-oracle's stable sort (bit-exact), and the grouped expert GEMVs against one-token calls (bit-exact) and the
-oracle."""
+oracle's stable sort (bit-exact), and the grouped expert GEMVs, which run on the matrix cores, against the
+oracle and against one-token calls (within the parity bar: the two paths scale and sum the activations
+differently, so their roundings differ)."""
 import numpy as np
 import pytest
 
@@ -64,10 +65,15 @@ def _gemv(rp, sp, ids, k, x, x_dtype, T, act, d):
     return yr, ys
 
 
+def _oracle_act(shape):
+    return moe.ACT_GELU_TANH if shape.act == q.MOE_ACT_GELU_TANH else moe.ACT_SILU
+
+
 @pytest.mark.parametrize("cfg_name", ["tiny", "batched"])
-def test_grouped_gemv_equals_one_token_calls(cfg_name):
-    """Grouped T-token call vs T separate one-token calls, y_routed and y_shared bit for bit.  The ids carry
-    repeats across tokens, a duplicate within a token and (tiny) an id outside the pool, whose rows are NaN."""
+def test_grouped_gemv_matches_one_token_calls(cfg_name):
+    """Grouped T-token call vs T separate one-token calls, y_routed and y_shared within the parity bar, and
+    (batched) sampled expert outputs against the oracle.  The ids carry repeats across tokens, a duplicate
+    within a token and (tiny) an id outside the pool, whose rows are NaN on both paths."""
     cfg = synth.TINY if cfg_name == "tiny" else synth.BATCHED
     dev = H.device_layer(cfg, 0)
     shape = H.shape_of(cfg)
@@ -83,15 +89,31 @@ def test_grouped_gemv_equals_one_token_calls(cfg_name):
     xdt = q.MOE_BF16 if cfg.x_bf16 else q.MOE_F32
     yr, ys = _gemv(rp, sp, ids, k, x, xdt, T, shape.act, cfg.d)
     check = range(T) if cfg_name == "tiny" else (0, 3, 17, 31)
+    worst = 0.0
     for t in check:
         yr1, ys1 = _gemv(rp, sp, ids[t:t + 1].contiguous(), k, x[t:t + 1].contiguous(), xdt, 1, shape.act, cfg.d)
         torch.cuda.synchronize()
-        assert torch.equal(ys[t], ys1[0]), f"shared, token {t}"
+        worst = max(worst, H.max_rel_err(H.to_f64(ys[t]), H.to_f64(ys1[0])))
         for i in range(k):
             if ids_np[t, i] >= E:
                 assert torch.isnan(yr[t, i]).all() and torch.isnan(yr1[0, i]).all()
             else:
-                assert torch.equal(yr[t, i], yr1[0, i]), f"token {t} slot {i}"
+                assert torch.isfinite(yr[t, i]).all(), f"token {t} slot {i}"
+                worst = max(worst, H.max_rel_err(H.to_f64(yr[t, i]), H.to_f64(yr1[0, i])))
+    print(f"{cfg_name}: grouped vs one-token calls, max rel difference {worst:.3e}")
+    assert worst <= TOL
+    if cfg_name == "batched":
+        orc = oin.oracle_layer(cfg, 0)
+        act = _oracle_act(shape)
+        yr64, ys64 = H.to_f64(yr), H.to_f64(ys)
+        err = 0.0
+        for t in (0, 3, 31):
+            u = H.to_f64(x[t])
+            err = max(err, H.max_rel_err(ys64[t], moe.expert_ffn(orc.decoded_shared(), u, act)))
+            for i in range(k):
+                err = max(err, H.max_rel_err(yr64[t, i], moe.expert_ffn(orc.decoded(int(ids_np[t, i])), u, act)))
+        print(f"batched grouped expert gemv vs oracle: max rel err {err:.3e}")
+        assert err <= TOL
 
 
 def test_grouped_gemv_tiny_vs_oracle():
@@ -119,9 +141,9 @@ def test_grouped_gemv_tiny_vs_oracle():
     assert worst <= TOL
 
 
-def test_grouped_fused_combine_equals_one_token_calls():
-    """q4_expert_gemv_combine with 32 tokens (grouped down with per-token tile tickets) equals 32 one-token
-    fused calls, twice in a row on one workspace."""
+def test_grouped_fused_combine_matches_one_token_calls():
+    """q4_expert_gemv_combine with 32 tokens (grouped on the matrix cores, then the combine) matches 32
+    one-token fused calls within the parity bar, twice in a row on one workspace."""
     cfg = synth.STACK
     dev = H.device_layer(cfg, 0)
     shape = H.shape_of(cfg)
@@ -147,4 +169,5 @@ def test_grouped_fused_combine_equals_one_token_calls():
                                      shape.act, w[t:t + 1].contiguous(), res[t:t + 1].contiguous(), q.MOE_BF16, o1,
                                      q.MOE_BF16, ws1, ws1_b)
             torch.cuda.synchronize()
-            assert torch.equal(out[t], o1[0]), f"call {call} token {t}"
+            err = H.max_rel_err(H.to_f64(out[t]), H.to_f64(o1[0]))
+            assert err <= TOL, f"call {call} token {t}: {err:.3e}"

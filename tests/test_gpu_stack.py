@@ -90,8 +90,9 @@ def test_graph_replays_match_eager(stack):
 
 
 def test_batched_tokens_match_single_token(stack):
-    """32 tokens in one call (the batched configuration, grouped by expert) equal each token run alone
-    through the same library calls (norm + router, then expert GEMVs with the combine), on layer 0."""
+    """32 tokens in one call (the batched configuration, grouped by expert on the matrix cores) match each
+    token run alone through the same library calls (norm + router, then expert GEMVs with the combine), on
+    layer 0, within the parity bar (max relative error 1e-2)."""
     cfg, layers, _ = stack
     T = 32
     decT = decoder.MoEDecoder(H.shape_of(cfg), layers[:1], T=T)
@@ -105,7 +106,8 @@ def test_batched_tokens_match_single_token(stack):
         o1 = torch.empty_like(x[t:t + 1])
         dec1.layer(0, x[t:t + 1].contiguous(), o1)
         torch.cuda.synchronize()
-        assert torch.equal(o1[0], out[t]), f"token {t}"
+        err = H.max_rel_err(H.to_f64(out[t]), H.to_f64(o1[0]))
+        assert err <= 1e-2, f"token {t}: {err:.3e}"
 
 
 def test_batched_layer_vs_oracle():
