@@ -412,17 +412,18 @@ inline StagedRows staged_rows_at(char* base, int64_t rows, int K) {
   return r;
 }
 moe_status launch_stage_rows(const void* x, bool x_bf16, int rows, int K, const StagedRows& out, hipStream_t s);
-// The grouped products of T > 1 tokens on the matrix cores.  Shared blocks come first, then n_routed_blocks
-// per group of (token, slot) pairs; a block's 4 waves hold 4 / wk tiles of 16 weight rows (gate_up: 8
-// gate and the 8 matching up rows), the wk waves of a tile splitting its K.
+// The grouped products of T > 1 tokens on the matrix cores (q4_mfma.hip).  A tile is 16 weight rows
+// (gate_up: 8 gate rows and the matching 8 up rows); wk waves of a block split a tile's K, so a block
+// of 8 waves works on 8 / wk tiles at a time (one step).  Fill the per-matrix fields; the launcher sets
+// the step counts and the block split.
 struct MfmaArgs {
   Pool routed, shared;          // off_q / off_sb select the matrix
   int32_t K_routed, K_shared;   // row lengths
-  int32_t wk_routed, wk_shared; // waves per tile: 1, 2 or 4
+  int32_t wk_routed, wk_shared; // waves per tile: 1, 2, 4 or 8 (mfma_waves_per_tile)
+  int32_t tiles_routed, tiles_shared;
   int32_t gate_up;              // 1: out = act(gate) * up per feature; 0: out = the 16 rows' products
   int32_t act;
   int32_t T, k;
-  int32_t n_shared_blocks, n_routed_blocks;
   const int32_t* n_groups;
   const int4* groups;
   const int32_t* perm;
@@ -430,9 +431,11 @@ struct MfmaArgs {
   float* out_routed;            // gate_up: h [pairs][F]; down: y [pairs][d]
   float* out_shared;            // gate_up: h [T][S];     down: y [T][d]
   int32_t out_len_routed, out_len_shared;
+  // set by launch_grouped_mfma
+  int32_t steps_routed, steps_shared;   // steps of a matrix (0: no such matrix)
 };
 int mfma_waves_per_tile(int K);
-moe_status launch_grouped_mfma(const MfmaArgs& a, int gmax, bool sb_bf16, hipStream_t s);
+moe_status launch_grouped_mfma(MfmaArgs a, bool has_shared, bool has_routed, bool sb_bf16, hipStream_t s);
 
 struct Slot {
   bool shared, valid;

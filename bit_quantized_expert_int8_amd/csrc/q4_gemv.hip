@@ -260,8 +260,8 @@ moe_status run_gate_up(GemvArgs a, const RecordOffsets& orr, const RecordOffsets
     m.act = a.act;
     m.T = T;
     m.k = a.k;
-    m.n_shared_blocks = a.nb_shared * m.wk_shared / 4;     // 8 features a tile, 4 / wk tiles a block
-    m.n_routed_blocks = a.nb_routed * m.wk_routed / 4;
+    m.tiles_shared = a.nb_shared;   // 8 features a tile
+    m.tiles_routed = a.nb_routed;
     m.n_groups = a.n_groups;
     m.groups = a.groups;
     m.perm = a.perm;
@@ -270,7 +270,7 @@ moe_status run_gate_up(GemvArgs a, const RecordOffsets& orr, const RecordOffsets
     m.out_shared = a.h_shared;
     m.out_len_routed = a.routed.F;
     m.out_len_shared = a.shared.F;
-    return launch_grouped_mfma(m, a.k > 0 ? groups_max(a.routed.n_records, T, a.k) : 0, sb_bf16, s);
+    return launch_grouped_mfma(m, a.nb_shared > 0, a.k > 0, sb_bf16, s);
   }
   dim3 grid(a.nb_shared + a.k * a.nb_routed, T);
   return dispatch_nbw(nbw, [&](auto nb) {
@@ -322,8 +322,7 @@ moe_status run_down(GemvArgs a, const RecordOffsets& orr, const RecordOffsets& o
     m.wk_shared = has_shared ? mfma_waves_per_tile(Fs) : 1;
     m.T = T;
     m.k = a.k;
-    m.n_shared_blocks = has_shared ? a.d / 16 * m.wk_shared / 4 : 0;   // 16 rows a tile, 4 / wk tiles a block
-    m.n_routed_blocks = has_routed ? a.d / 16 * m.wk_routed / 4 : 0;
+    m.tiles_shared = m.tiles_routed = a.d / 16;   // 16 rows a tile
     m.n_groups = a.n_groups;
     m.groups = a.groups;
     m.perm = a.perm;
@@ -332,7 +331,7 @@ moe_status run_down(GemvArgs a, const RecordOffsets& orr, const RecordOffsets& o
     m.out_routed = a.y_routed;
     m.out_shared = a.y_shared;
     m.out_len_routed = m.out_len_shared = a.d;
-    return launch_grouped_mfma(m, has_routed ? groups_max(a.routed.n_records, T, a.k) : 0, sb_bf16, s);
+    return launch_grouped_mfma(m, has_shared, has_routed, sb_bf16, s);
   }
   dim3 grid(a.nb_shared + a.k * a.nb_routed, T);
   return dispatch_nbw(nbw, [&](auto nb) {

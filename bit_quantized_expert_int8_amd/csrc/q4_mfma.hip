@@ -33,7 +33,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreadsM = 256;
+constexpr int kThreadsM = 256;                     // staging block
 constexpr int kStageIt = kMaxK / 8 / kThreadsM;   // 8-value blocks per thread of a staged row (K <= 8192)
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -105,10 +105,13 @@ __global__ __launch_bounds__(kThreadsM) void stage_rows_kernel(const XT* __restr
   if (t == 0) out.ef[row] = ldexpf(1.0f, e);
 }
 
-// Dynamic LDS of a block: red [4][16][16] fp32, os [G][16] float2, ef [16], rows [16] (stage and output rows)
-inline size_t mfma_lds_bytes(int K) { return (size_t)4 * 256 * 4 + (size_t)(K / 64) * 16 * 8 + 16 * 4 + 16 * 4 * 2; }
+constexpr int kWavesG = 4;                 // wavefronts of a grouped-product block
+constexpr int kThreadsG = 64 * kWavesG;
 
-constexpr int kAhead = 3;   // groups of A in flight per wave
+// Dynamic LDS of a block: red [4][16][16] fp32, os [G][16] float2, ef [16], rows [16] (stage and output rows)
+inline size_t mfma_lds_bytes(int K) {
+  return (size_t)kWavesG * 256 * 4 + (size_t)(K / 64) * 16 * 8 + 16 * 4 + 16 * 4 * 2;
+}
 
 template <bool SB_BF16>
 __device__ __forceinline__ void opaque_sb(SbWord<SB_BF16>& w);
@@ -119,67 +122,46 @@ __device__ __forceinline__ void opaque_sb<true>(SbWord<true>& w) {
 template <>
 __device__ __forceinline__ void opaque_sb<false>(SbWord<false>&) {}
 
-// A block's 4 waves take 4 / wk tiles of 16 weight rows; the wk waves of a tile split its groups.  Blocks
-// [0, n_shared_blocks) hold the shared matrix's tiles with all T tokens; the rest, n_routed_blocks per
-// group, the tiles of a routed group with that group's pairs.  Tokens go through in chunks of 16.
+// One block's work: steps [s0, s1) of one matrix (a step = 8 / wk tiles of 16 rows, one per group of wk
+// waves) for a list of tokens, 16 at a time.  Per chunk of tokens each wave loads its A operands (its
+// groups' staged activations) once; per step it streams the code words and scale/bias of its rows, the
+// next step's words requested as soon as the current step's are unpacked, so a step's weights are in
+// flight while the previous step is multiplied, reduced and stored.
 template <int NG, bool SB_BF16>
-__global__ __launch_bounds__(kThreadsM) void grouped_mfma_kernel(MfmaArgs a) {
-  extern __shared__ __align__(16) uint32_t lds[];
-  float* red = reinterpret_cast<float*>(lds);                       // [4 waves][16 tokens][16 rows]
-
-  int u = blockIdx.x;
-  const bool shared = u < a.n_shared_blocks;
-  int e = 0, start = 0, count = a.T;
-  bool valid = true;
-  if (!shared) {
-    u -= a.n_shared_blocks;
-    const int j = u / a.n_routed_blocks;
-    u -= j * a.n_routed_blocks;
-    if (j >= *a.n_groups) return;
-    const int4 g = a.groups[j];
-    valid = (unsigned)g.x < (unsigned)a.routed.n_records;
-    e = valid ? g.x : 0;
-    start = g.y;
-    count = g.z;
-  }
-  const Pool P = shared ? a.shared : a.routed;                 // copies: held in SGPRs, not re-read
+__device__ __forceinline__ void mfma_item(const MfmaArgs& a, bool shared, int e, bool valid, int start, int count,
+                                          int s0, int s1, uint32_t* lds) {
+  float* red = reinterpret_cast<float*>(lds);                      // [4 waves][16 tokens][16 rows]
+  const Pool P = shared ? a.shared : a.routed;                      // copies: held in SGPRs, not re-read
   const StagedRows xs = shared ? a.xs_shared : a.xs_routed;
   const int K = shared ? a.K_shared : a.K_routed, wk = shared ? a.wk_shared : a.wk_routed;
-  const int G = K / 64;
-  float2* os_l = reinterpret_cast<float2*>(lds + 4 * 256);            // [G][16]
-  float* ef_l = reinterpret_cast<float*>(lds + 4 * 256 + G * 32);      // [16]
-  int* srow_l = reinterpret_cast<int*>(ef_l + 16);                     // [16] staged row of token m
-  int* orow_l = srow_l + 16;                                           // [16] output row of token m
+  const int n_tiles = shared ? a.tiles_shared : a.tiles_routed;
+  float* const out = shared ? a.out_shared : a.out_routed;
+  const int out_len = shared ? a.out_len_shared : a.out_len_routed;
+  const int G = K / 64, tps = kWavesG / wk;
+  float2* os_l = reinterpret_cast<float2*>(lds + kWavesG * 256);    // [G][16]
+  float* ef_l = reinterpret_cast<float*>(lds + kWavesG * 256 + G * 32);
+  int* srow_l = reinterpret_cast<int*>(ef_l + 16);
+  int* orow_l = srow_l + 16;
 
   // the wave index through readfirstlane, so that the compiler sees the group range as wave-uniform
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, n = lane & 15,
             kb = lane >> 4;
-  const int tpb = 4 / wk, part = wave % wk;
-  const int tile = u * tpb + wave / wk;
-  // this lane's weight row
-  const int row = a.gate_up ? (n < 8 ? tile * 8 + n : P.F + tile * 8 + (n - 8)) : tile * 16 + n;
-  const char* rec = P.base + (int64_t)e * P.record_bytes;
-  const uint32_t* qrow = reinterpret_cast<const uint32_t*>(rec + P.off_q + (int64_t)row * (K / 2));
-  const char* sbrow = rec + P.off_sb + (int64_t)row * (G * (SB_BF16 ? 4 : 8));
-  // this wave's groups [g0, g0 + nw)
+  const int part = wave % wk, wt = wave / wk;
   const int g0 = (part * G) / wk, nw = ((part + 1) * G) / wk - g0;
-  // all NG loads issued unconditionally (no branch, so no wait between them): slots past the wave's range
-  // read the row's last group again, an invalid expert reads record 0; neither value is used
-  u32x2 q[NG];
-  SbWord<SB_BF16> sbw[NG];
-#pragma unroll
-  for (int i = 0; i < NG; ++i) sbw[i] = load_sb<SB_BF16>(sbrow, min(g0 + i, G - 1));
-#pragma unroll
-  for (int i = 0; i < NG; ++i)
-    q[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(qrow + min(g0 + i, G - 1) * 8 + 2 * kb));
+  const char* rec = P.base + (int64_t)e * P.record_bytes;
+  const uint32_t* qmat = reinterpret_cast<const uint32_t*>(rec + P.off_q);
+  const char* sbmat = rec + P.off_sb;
+  const int sb_row = G * (SB_BF16 ? 4 : 8);
+  // this lane's row in tile t (tiles past the matrix read its last tile; their results are not stored)
+  auto row_of = [&](int t) {
+    t = min(t, n_tiles - 1);
+    return a.gate_up ? (n < 8 ? t * 8 + n : P.F + t * 8 + (n - 8)) : t * 16 + n;
+  };
 
   for (int c0 = 0; c0 < count; c0 += 16) {
-    const Dequant dq = opaque_dequant();   // the dequantized words stay inside the chunk loop
-    uint32_t sh8 = 8;                      // and so do the shifted code words
-    asm volatile("" : "+v"(sh8));
     const int nlive = min(16, count - c0);
-    // the chunk's tokens: staged row, output row, 2^e, and the groups' (1024 O, Sx).  Slots past the last
-    // token repeat the first token's staged row, so their A loads fall on lines the wave reads anyway.
+    // the chunk's tokens: staged row, output row, 2^e.  Slots past the last token repeat the first token's
+    // staged row, so their A loads fall on lines the wave reads anyway; their results are not stored.
     if ((int)threadIdx.x < 16) {
       const int m = threadIdx.x;
       const int mm = m < nlive ? m : 0;
@@ -191,11 +173,9 @@ __global__ __launch_bounds__(kThreadsM) void grouped_mfma_kernel(MfmaArgs a) {
     }
     __syncthreads();
     {
-      // thread i stages (group i / 16 + 16 r, token i % 16) for every r: one token row per thread, the loads
-      // issued together with the group clamped into the row (slots past the last token read the first
-      // token's row; those values are never used)
-      constexpr int kRep = (NG + 3) / 4;   // G <= 4 NG (a wave has at most NG groups, wk <= 4), so G * 16 <= kRep * 256
-      const int nrep = (G * 16 + kThreadsM - 1) / kThreadsM;
+      // (1024 O, Sx) of every (group, token): thread i stages group i / 16 + 16 r of token i % 16
+      constexpr int kRep = (NG * kWavesG + 15) / 16;   // G <= 4 NG, so G * 16 <= kRep * 256
+      const int nrep = (G * 16 + kThreadsG - 1) / kThreadsG;
       const float2* orow = xs.os + (int64_t)srow_l[threadIdx.x & 15] * G;
       const int gq = threadIdx.x >> 4;
       float2 ov[kRep];
@@ -204,31 +184,48 @@ __global__ __launch_bounds__(kThreadsM) void grouped_mfma_kernel(MfmaArgs a) {
         if (r < nrep) ov[r] = orow[min(gq + 16 * r, G - 1)];
 #pragma unroll
       for (int r = 0; r < kRep; ++r)
-        if (r < nrep && gq + 16 * r < G) os_l[threadIdx.x + r * kThreadsM] = ov[r];
+        if (r < nrep && gq + 16 * r < G) os_l[threadIdx.x + r * kThreadsG] = ov[r];
     }
-    const _Float16* arow = xs.xq + (int64_t)srow_l[n] * K + 16 * kb;   // token n's 32 bytes per group
-    __syncthreads();
-    f32x4 y = {0.f, 0.f, 0.f, 0.f};
-    if (valid) {
-      // A for the next kAhead groups in flight; group indexes past the wave's range are clamped to the
-      // row's last group (loads that stay in the row; their values are not used)
-      half8 ar[kAhead][2];
+    // A of this wave's groups for the whole chunk: token n's 32 bytes of each group (index clamped into
+    // the row for slots past the wave's range)
+    const _Float16* arow = xs.xq + (int64_t)srow_l[n] * K + 16 * kb;
+    half8 A0[NG], A1[NG];
 #pragma unroll
-      for (int p = 0; p < kAhead; ++p) {
-        const u32x4* ap = reinterpret_cast<const u32x4*>(arow + min(g0 + p, G - 1) * 64);
-        ar[p][0] = __builtin_bit_cast(half8, ap[0]);
-        ar[p][1] = __builtin_bit_cast(half8, ap[1]);
-      }
+    for (int i = 0; i < NG; ++i) {
+      const u32x4* ap = reinterpret_cast<const u32x4*>(arow + min(g0 + i, G - 1) * 64);
+      A0[i] = __builtin_bit_cast(half8, ap[0]);
+      A1[i] = __builtin_bit_cast(half8, ap[1]);
+    }
+    // the first step's code words and scale/bias (record 0 for an invalid expert: never used).  Plain
+    // loads, not streaming ones: a lane reads 8 bytes of a 128-byte line whose other bytes the row's next
+    // groups read soon after, so the line should stay in L2 (streaming loads measured 17% slower).
+    u32x2 q[NG];
+    SbWord<SB_BF16> sbw[NG];
+    {
+      const int r = row_of(s0 * tps + wt);
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
-        const half8 a0 = ar[i % kAhead][0], a1 = ar[i % kAhead][1];
-        if (i + kAhead < NG) {
-          const u32x4* ap = reinterpret_cast<const u32x4*>(arow + min(g0 + i + kAhead, G - 1) * 64);
-          ar[i % kAhead][0] = __builtin_bit_cast(half8, ap[0]);
-          ar[i % kAhead][1] = __builtin_bit_cast(half8, ap[1]);
-        }
-        if (i >= nw) continue;   // wave-uniform; a break would keep the loop from unrolling
-        const int g = g0 + i;
+        const int gi = min(g0 + i, G - 1);
+        q[i] = *reinterpret_cast<const u32x2*>(qmat + (int64_t)r * (K / 8) + gi * 8 + 2 * kb);
+        sbw[i] = load_sb<SB_BF16>(sbmat + (int64_t)r * sb_row, gi);
+      }
+    }
+    __syncthreads();   // os, ef and the token rows are in LDS
+
+    for (int s = s0; s < s1; ++s) {
+      const Dequant dq = opaque_dequant();   // the dequantized words stay inside the step loop
+      uint32_t sh8 = 8;
+      asm volatile("" : "+v"(sh8));
+      // the groups' (1024 O, Sx) are read from LDS in every step, not held in registers across steps
+      int os_off = 4 * kb;
+      asm volatile("" : "+v"(os_off));
+      // the next step's rows (the last step reads its own again: cache hits, no branch)
+      const int rn = row_of(min(s + 1, s1 - 1) * tps + wt);
+      const uint32_t* qn = qmat + (int64_t)rn * (K / 8) + 2 * kb;
+      const char* sbn = sbmat + (int64_t)rn * sb_row;
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
         const uint32_t w0 = q[i].x, w1 = q[i].y, t0 = w0 >> sh8, t1 = w1 >> sh8;
         u32x4 b0, b1;
         b0.x = (w0 & dq.lo) | dq.magic;
@@ -239,50 +236,97 @@ __global__ __launch_bounds__(kThreadsM) void grouped_mfma_kernel(MfmaArgs a) {
         b1.y = (w1 & dq.hi) | dq.magic;
         b1.z = (t1 & dq.lo) | dq.magic;
         b1.w = (t1 & dq.hi) | dq.magic;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, __builtin_bit_cast(half8, b0), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, __builtin_bit_cast(half8, b1), acc, 0, 0, 0);
         SbWord<SB_BF16> sw = sbw[i];
-        opaque_sb(sw);   // decoded here, not once above the chunk loop (two registers a group instead of one)
-        float s, b;
-        sb_values<SB_BF16>(sw, s, b);
-        const float4* osp = reinterpret_cast<const float4*>(os_l + g * 16 + 4 * kb);
-        const float4 o01 = osp[0], o23 = osp[1];   // (1024 O, Sx) of tokens 4 kb .. 4 kb + 3
-        y[0] = fmaf(s, acc[0] - o01.x, fmaf(b, o01.y, y[0]));
-        y[1] = fmaf(s, acc[1] - o01.z, fmaf(b, o01.w, y[1]));
-        y[2] = fmaf(s, acc[2] - o23.x, fmaf(b, o23.y, y[2]));
-        y[3] = fmaf(s, acc[3] - o23.z, fmaf(b, o23.w, y[3]));
-        __builtin_amdgcn_sched_barrier(0);   // one group at a time: the next group's B is made after this one
-      }
-    }
-    // the waves' partial sums, added in wave order; thread (m, nn) finishes token m, row nn of each tile
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red[wave * 256 + (4 * kb + i) * 16 + n] = y[i];
-    __syncthreads();
-    {
-      const int m = threadIdx.x >> 4, nn = threadIdx.x & 15;
-      float* out = shared ? a.out_shared : a.out_routed;
-      const int out_len = shared ? a.out_len_shared : a.out_len_routed;
-      if (m < nlive) {
-        const float sc = ef_l[m];
-        for (int tt = 0; tt < tpb; ++tt) {
-          auto total = [&](int col) {
-            float acc = red[(tt * wk) * 256 + m * 16 + col];
-            for (int w = 1; w < wk; ++w) acc += red[(tt * wk + w) * 256 + m * 16 + col];
-            return acc;
-          };
-          const int t_out = u * tpb + tt;
-          if (a.gate_up) {
-            if (nn < 8)
-              out[(int64_t)orow_l[m] * out_len + t_out * 8 + nn] =
-                  valid ? activation(sc * total(nn), a.act) * (sc * total(nn + 8)) : __builtin_nanf("");
-          } else {
-            out[(int64_t)orow_l[m] * out_len + t_out * 16 + nn] = valid ? sc * total(nn) : __builtin_nanf("");
-          }
+        opaque_sb(sw);
+        float sc, bi;
+        sb_values<SB_BF16>(sw, sc, bi);
+        // slots past the wave's groups multiply the row's last group again, with weight zero: no branch, so
+        // the unpacking above cannot sink below the reload
+        if (i >= nw) sc = bi = 0.f;
+        // group i's registers are free: request the next step's into them (the barrier keeps the unpacking
+        // above the load, so the new words reuse the old words' registers instead of being copied back)
+        __builtin_amdgcn_sched_barrier(0);
+        const int gi = min(g0 + i, G - 1);
+        q[i] = *reinterpret_cast<const u32x2*>(qn + gi * 8);
+        sbw[i] = load_sb<SB_BF16>(sbn, gi);
+        {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0[i], __builtin_bit_cast(half8, b0), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1[i], __builtin_bit_cast(half8, b1), acc, 0, 0, 0);
+          const float4* osp = reinterpret_cast<const float4*>(os_l + gi * 16 + os_off);
+          const float4 o01 = osp[0], o23 = osp[1];   // (1024 O, Sx) of tokens 4 kb .. 4 kb + 3
+          y[0] = fmaf(sc, acc[0] - o01.x, fmaf(bi, o01.y, y[0]));
+          y[1] = fmaf(sc, acc[1] - o01.z, fmaf(bi, o01.w, y[1]));
+          y[2] = fmaf(sc, acc[2] - o23.x, fmaf(bi, o23.y, y[2]));
+          y[3] = fmaf(sc, acc[3] - o23.z, fmaf(bi, o23.w, y[3]));
         }
+        __builtin_amdgcn_sched_barrier(0);   // one group at a time
       }
+      // the waves' partial tiles, added in wave order
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave * 256 + (4 * kb + i) * 16 + n] = y[i];
+      __syncthreads();
+      for (int idx = threadIdx.x; idx < tps * 256; idx += kThreadsG) {
+        const int tt = idx >> 8, m = (idx >> 4) & 15, nn = idx & 15;
+        const int tile = s * tps + tt;
+        if (m >= nlive || tile >= n_tiles || (a.gate_up && nn >= 8)) continue;
+        auto total = [&](int col) {
+          float v = red[(tt * wk) * 256 + m * 16 + col];
+          for (int w = 1; w < wk; ++w) v += red[(tt * wk + w) * 256 + m * 16 + col];
+          return v;
+        };
+        const float sc = ef_l[m];
+        float v;
+        if (!valid) v = __builtin_nanf("");
+        else if (a.gate_up) v = activation(sc * total(nn), a.act) * (sc * total(nn + 8));
+        else v = sc * total(nn);
+        out[(int64_t)orow_l[m] * out_len + tile * (a.gate_up ? 8 : 16) + nn] = v;
+      }
+      __syncthreads();   // red is rewritten by the next step
     }
-    __syncthreads();   // red, os and the token rows are rewritten by the next chunk
+  }
+}
+
+// The grid is one wave of resident blocks.  Each block reads the number of routed groups g and splits the
+// work the same way: the shared matrix gets blocks in proportion to its steps (times its token chunks)
+// against the routed steps of g groups, and splits its steps evenly over them; with R blocks left, block
+// b takes part b / g of group b % g when g < R (each group's steps split as evenly as the blocks allow),
+// else groups b, b + R, ... whole.
+template <int NG, bool SB_BF16>
+__global__ __launch_bounds__(kThreadsG) void grouped_mfma_kernel(MfmaArgs a) {
+  extern __shared__ __align__(16) uint32_t lds[];
+  const int b = blockIdx.x, nb = gridDim.x;
+  const int ng = a.steps_routed > 0 ? *a.n_groups : 0;
+  int nsb = 0;
+  if (a.steps_shared > 0) {
+    if (ng <= 0) {
+      nsb = nb;
+    } else {
+      const int64_t us = (int64_t)a.steps_shared * ((a.T + 15) / 16), ur = (int64_t)a.steps_routed * ng;
+      nsb = (int)((nb * us + (us + ur) / 2) / (us + ur));
+      nsb = max(1, min(nsb, min(a.steps_shared, nb - 1)));
+    }
+  }
+  if (b < nsb) {
+    const int spb = (a.steps_shared + nsb - 1) / nsb;
+    const int s0 = b * spb, s1 = min(s0 + spb, a.steps_shared);
+    if (s0 < s1) mfma_item<NG, SB_BF16>(a, true, 0, true, 0, a.T, s0, s1, lds);
+    return;
+  }
+  if (ng <= 0) return;
+  const int rb = b - nsb, R = nb - nsb;
+  const int steps = a.steps_routed;
+  for (int j = rb % ng, part = rb / ng; j < ng; j += R) {
+    int s0 = 0, s1 = steps;
+    if (ng < R) {
+      const int parts = (R - 1 - j) / ng + 1;   // blocks given to group j
+      s0 = (int)((int64_t)part * steps / parts);
+      s1 = (int)((int64_t)(part + 1) * steps / parts);
+    }
+    const int4 g = a.groups[j];
+    const bool valid = (unsigned)g.x < (unsigned)a.routed.n_records;
+    if (s0 < s1) mfma_item<NG, SB_BF16>(a, false, valid ? g.x : 0, valid, g.y, g.z, s0, s1, lds);
+    if (ng < R) break;
   }
 }
 
@@ -298,35 +342,56 @@ moe_status launch_stage_rows(const void* x, bool x_bf16, int rows, int K, const 
 }
 
 int mfma_waves_per_tile(int K) {
+  // a wave holds its groups' A operands and code words in registers: at most 11 groups where possible
   const int G = K / 64;
-  return G <= 12 ? 1 : G <= 24 ? 2 : 4;
+  int wk = 1;
+  while (wk < kWavesG && (G + wk - 1) / wk > 11) wk *= 2;
+  return wk;
 }
 
-moe_status launch_grouped_mfma(const MfmaArgs& a, int gmax, bool sb_bf16, hipStream_t s) {
-  const int n_routed = a.n_routed_blocks > 0 ? gmax * a.n_routed_blocks : 0;
-  const dim3 grid(a.n_shared_blocks + n_routed);
-  if (grid.x == 0) return MOE_OK;
+int mfma_device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+  }
+  return cus[dev];
+}
+
+moe_status launch_grouped_mfma(MfmaArgs a, bool has_shared, bool has_routed, bool sb_bf16, hipStream_t s) {
+  // steps per matrix (a step: one tile per group of wk waves)
+  auto steps_of = [](int tiles, int wk) { const int tps = kWavesG / wk; return (tiles + tps - 1) / tps; };
+  a.steps_shared = has_shared ? steps_of(a.tiles_shared, a.wk_shared) : 0;
+  a.steps_routed = has_routed ? steps_of(a.tiles_routed, a.wk_routed) : 0;
   int per_wave = 0, kmax = 0;
-  if (a.n_shared_blocks > 0) {
+  if (has_shared) {
     per_wave = (a.K_shared / 64 + a.wk_shared - 1) / a.wk_shared;
     kmax = a.K_shared;
   }
-  if (n_routed > 0) {
+  if (has_routed) {
     per_wave = max(per_wave, (a.K_routed / 64 + a.wk_routed - 1) / a.wk_routed);
     kmax = max(kmax, a.K_routed);
   }
   const size_t lds = mfma_lds_bytes(kmax);
   auto go = [&](auto ng) {
     constexpr int NG = decltype(ng)::value;
-    if (sb_bf16) hipLaunchKernelGGL((grouped_mfma_kernel<NG, true>), grid, dim3(kThreadsM), lds, s, a);
-    else hipLaunchKernelGGL((grouped_mfma_kernel<NG, false>), grid, dim3(kThreadsM), lds, s, a);
+    auto kern = sb_bf16 ? grouped_mfma_kernel<NG, true> : grouped_mfma_kernel<NG, false>;
+    // as many blocks as are resident at once
+    static int per_cu_cached[2] = {0, 0};   // per kernel instantiation (and scale/bias type)
+    int& per_cu = per_cu_cached[sb_bf16 ? 1 : 0];
+    if (per_cu == 0 && (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreadsG, lds) != hipSuccess ||
+                        per_cu < 1))
+      per_cu = 1;
+    const dim3 grid(max(2, per_cu * mfma_device_cus()));   // one wave of resident blocks (at least one per role)
+    hipLaunchKernelGGL(kern, grid, dim3(kThreadsG), lds, s, a);
     return check_launch("grouped_mfma_kernel");
   };
   if (per_wave <= 4) return go(std::integral_constant<int, 4>());
   if (per_wave <= 8) return go(std::integral_constant<int, 8>());
-  if (per_wave <= 12) return go(std::integral_constant<int, 12>());
+  if (per_wave <= 11) return go(std::integral_constant<int, 11>());
   if (per_wave <= 16) return go(std::integral_constant<int, 16>());
-  if (per_wave <= 24) return go(std::integral_constant<int, 24>());
   return go(std::integral_constant<int, 32>());
 }
 
