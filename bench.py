@@ -176,13 +176,13 @@ def distinct_expert_bytes(dec, cfg):
     return total, sum(distinct) / len(distinct)
 
 
-def measure_batched(shape, layers, cfg, tokens, steps, warmup):
-    """32 tokens decoded together through the stack (one grouped call per layer), graph-replayed with the
-    token batch rotated each step."""
+def measure_batched(shape, layers, cfg, tokens, steps, warmup, T=32):
+    """T tokens decoded together through the stack (one grouped call per layer, the expert products on the
+    matrix cores), graph-replayed with the token batch rotated each step: 32 (the batched decode
+    configuration) or 128 (a prefill chunk)."""
     import torch
     from bit_quantized_expert_int8_amd import decoder
 
-    T = 32
     dec = decoder.MoEDecoder(shape, layers, T=T)
     n_batches = tokens.shape[0] // T
     batches = tokens[: n_batches * T].reshape(n_batches, T, cfg.d)
@@ -404,6 +404,7 @@ def main():
            "decode_mode": dec.mode, "split_kernels_us": split}
     if not args.no_extras:
         out["batched"] = measure_batched(shape, layers, cfg, tokens.reshape(n_tok, cfg.d), 20, 3)
+        out["prefill_chunk_128"] = measure_batched(shape, layers, cfg, tokens.reshape(n_tok, cfg.d), 8, 2, T=128)
         out["streamed"] = measure_streamed(shape, layers, cfg, dec, args.stream_tokens)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_layers, args.cpu_repeats)

@@ -358,6 +358,8 @@ struct GemvArgs {
   int32_t* n_groups;       // [1] non-empty groups (written by the grouping kernel)
   int4* groups;            // [groups_max] (expert or n_records for invalid ids, first index into perm, count, 0)
   int32_t* perm;           // [T*k] pair indices, grouped by expert, ascending within a group
+  int32_t* n_chunks;       // [1] the groups' runs of at most 16 pairs (written by the grouping kernel)
+  int4* chunks;            // [chunks_max] (expert or n_records, first index into perm, count <= 16, 0)
   char* stage;             // activations staged for the matrix cores (StagedRows), T > 1
 };
 
@@ -386,8 +388,11 @@ __device__ __forceinline__ void combine_tile(const GemvArgs& a, int t, int tile)
 // a.groups / a.perm / a.n_groups, so that the grouped products (q4_mfma.hip) stream each selected expert's
 // rows once for all of its tokens.
 constexpr int kMaxGroupedRecords = 4096;   // routed pool records supported with T > 1
+constexpr int kChunkPairs = 16;            // pairs per chunk (the tokens of one matrix-core pass)
+// n_chunks / chunks (optional): each group split into runs of at most kChunkPairs pairs, in group order,
+// (expert, first index into perm, count, 0); at most groups + P / kChunkPairs entries
 moe_status launch_group_pairs(const int32_t* ids, int P, int n_valid, int32_t* n_groups, int4* groups, int32_t* perm,
-                              hipStream_t s);
+                              hipStream_t s, int32_t* n_chunks = nullptr, int4* chunks = nullptr);
 
 inline size_t lds_bytes(int K) { return (size_t)(K / 32) * (kHgStride * 4 + 16); }
 
@@ -424,8 +429,8 @@ struct MfmaArgs {
   int32_t gate_up;              // 1: out = act(gate) * up per feature; 0: out = the 16 rows' products
   int32_t act;
   int32_t T, k;
-  const int32_t* n_groups;
-  const int4* groups;
+  const int32_t* n_chunks;      // routed work: runs of at most 16 pairs of one expert (device count)
+  const int4* chunks;           // (expert or n_records, first index into perm, count, 0)
   const int32_t* perm;
   StagedRows xs_routed, xs_shared;   // routed rows are tokens (gate_up) or pairs (down); shared rows are tokens
   float* out_routed;            // gate_up: h [pairs][F]; down: y [pairs][d]

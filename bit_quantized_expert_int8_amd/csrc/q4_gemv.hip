@@ -131,8 +131,11 @@ int groups_max(int n_records, int T, int k) {
 }
 
 // Bytes of the grouping tables of a grouped call: group count, groups, pair permutation.
+int chunks_max(int n_records, int T, int k) { return groups_max(n_records, T, k) + T * k / kChunkPairs; }
+// the group count and chunk count (one 256-byte slot), groups, chunks, perm
 size_t group_table_bytes(int n_records, int T, int k) {
-  return 256 + align256((size_t)groups_max(n_records, T, k) * 16) + align256((size_t)T * k * 4);
+  return 256 + align256((size_t)groups_max(n_records, T, k) * 16) + align256((size_t)chunks_max(n_records, T, k) * 16) +
+         align256((size_t)T * k * 4);
 }
 
 }  // namespace
@@ -220,9 +223,13 @@ moe_status prepare(const char* who, const moe_q4_pool* routed, const int32_t* id
   a->T = T;
   char* g = ws + (has_routed ? align256((size_t)T * k * Fr * 4) : 0) + (shared ? align256((size_t)T * Fs * 4) : 0);
   if (has_routed && T > 1) {
+    const size_t gb = align256((size_t)groups_max(routed->n_records, T, k) * 16);
+    const size_t cb = align256((size_t)chunks_max(routed->n_records, T, k) * 16);
     a->n_groups = reinterpret_cast<int32_t*>(g);
+    a->n_chunks = reinterpret_cast<int32_t*>(g) + 1;
     a->groups = reinterpret_cast<int4*>(g + 256);
-    a->perm = reinterpret_cast<int32_t*>(g + 256 + align256((size_t)groups_max(routed->n_records, T, k) * 16));
+    a->chunks = reinterpret_cast<int4*>(g + 256 + gb);
+    a->perm = reinterpret_cast<int32_t*>(g + 256 + gb + cb);
     g += group_table_bytes(routed->n_records, T, k);
   }
   a->stage = T > 1 ? g : nullptr;
@@ -245,7 +252,8 @@ moe_status run_gate_up(GemvArgs a, const RecordOffsets& orr, const RecordOffsets
     // grouped on the matrix cores: sort the pairs by expert, stage the T tokens once, then one block per
     // (group, 8 features) and per 8 shared features, each with all of its tokens
     if (a.k > 0) {
-      const moe_status st = launch_group_pairs(a.ids, T * a.k, a.routed.n_records, a.n_groups, a.groups, a.perm, s);
+      const moe_status st =
+          launch_group_pairs(a.ids, T * a.k, a.routed.n_records, a.n_groups, a.groups, a.perm, s, a.n_chunks, a.chunks);
       if (st != MOE_OK) return st;
     }
     const StagedRows xs = staged_rows_at(a.stage, T, a.d);
@@ -262,8 +270,8 @@ moe_status run_gate_up(GemvArgs a, const RecordOffsets& orr, const RecordOffsets
     m.k = a.k;
     m.tiles_shared = a.nb_shared;   // 8 features a tile
     m.tiles_routed = a.nb_routed;
-    m.n_groups = a.n_groups;
-    m.groups = a.groups;
+    m.n_chunks = a.n_chunks;
+    m.chunks = a.chunks;
     m.perm = a.perm;
     m.xs_routed = m.xs_shared = xs;
     m.out_routed = a.h_routed;
@@ -323,8 +331,8 @@ moe_status run_down(GemvArgs a, const RecordOffsets& orr, const RecordOffsets& o
     m.T = T;
     m.k = a.k;
     m.tiles_shared = m.tiles_routed = a.d / 16;   // 16 rows a tile
-    m.n_groups = a.n_groups;
-    m.groups = a.groups;
+    m.n_chunks = a.n_chunks;
+    m.chunks = a.chunks;
     m.perm = a.perm;
     m.xs_routed = xr;
     m.xs_shared = xsh;

@@ -287,16 +287,17 @@ __device__ __forceinline__ void mfma_item(const MfmaArgs& a, bool shared, int e,
   }
 }
 
-// The grid is one wave of resident blocks.  Each block reads the number of routed groups g and splits the
+// The grid is one wave of resident blocks.  Routed work comes as chunks (runs of at most 16 pairs of one
+// expert, so a chunk is one pass of the token loop).  Each block reads the chunk count c and splits the
 // work the same way: the shared matrix gets blocks in proportion to its steps (times its token chunks)
-// against the routed steps of g groups, and splits its steps evenly over them; with R blocks left, block
-// b takes part b / g of group b % g when g < R (each group's steps split as evenly as the blocks allow),
-// else groups b, b + R, ... whole.
+// against the routed steps of the c chunks, and splits its steps evenly over them; with R blocks left,
+// block b takes part b / c of chunk b % c when c < R (each chunk's steps split as evenly as the blocks
+// allow), else chunks b, b + R, ... whole.
 template <int NG, bool SB_BF16>
 __global__ __launch_bounds__(kThreadsG) void grouped_mfma_kernel(MfmaArgs a) {
   extern __shared__ __align__(16) uint32_t lds[];
   const int b = blockIdx.x, nb = gridDim.x;
-  const int ng = a.steps_routed > 0 ? *a.n_groups : 0;
+  const int ng = a.steps_routed > 0 ? *a.n_chunks : 0;
   int nsb = 0;
   if (a.steps_shared > 0) {
     if (ng <= 0) {
@@ -319,11 +320,11 @@ __global__ __launch_bounds__(kThreadsG) void grouped_mfma_kernel(MfmaArgs a) {
   for (int j = rb % ng, part = rb / ng; j < ng; j += R) {
     int s0 = 0, s1 = steps;
     if (ng < R) {
-      const int parts = (R - 1 - j) / ng + 1;   // blocks given to group j
+      const int parts = (R - 1 - j) / ng + 1;   // blocks given to chunk j
       s0 = (int)((int64_t)part * steps / parts);
       s1 = (int)((int64_t)(part + 1) * steps / parts);
     }
-    const int4 g = a.groups[j];
+    const int4 g = a.chunks[j];
     const bool valid = (unsigned)g.x < (unsigned)a.routed.n_records;
     if (s0 < s1) mfma_item<NG, SB_BF16>(a, false, valid ? g.x : 0, valid, g.y, g.z, s0, s1, lds);
     if (ng < R) break;

@@ -87,11 +87,12 @@ def test_host_validation_errors():
     assert fc(*fargs(None, 256, 1 << 20)) == q.MOE_ERR_INVALID_ARG                       # weights NULL with k > 0
     assert fc(*fargs(256, 256, 3328 - 256)) == q.MOE_ERR_INVALID_ARG                     # no room for the counters
     assert "workspace" in q.moe_last_error()
-    # batched (T = 3): hidden activations 3*2*128*4 = 3072, then the grouping tables: the group count (256),
-    # min(T*k, n_records + 1) = 6 groups of 16 bytes (-> 256) and T*k pair indices (-> 256); then the rows
-    # staged for the matrix cores, the larger of the tokens (3 x 256 fp16 = 1536, 3 x 4 groups x 8 bytes ->
-    # 256, 3 row scales -> 256) and the hidden vectors (6 x 128 fp16 = 1536, 6 x 2 x 8 -> 256, 6 -> 256)
-    assert q.q4_expert_gemv_workspace_bytes(good, 2, None, 3) == 3072 + 256 + 256 + 256 + 2048
+    # batched (T = 3): hidden activations 3*2*128*4 = 3072, then the grouping tables: the group and chunk
+    # counts (256), min(T*k, n_records + 1) = 6 groups of 16 bytes (-> 256), at most 6 + T*k/16 = 6 chunks
+    # of 16 pairs (-> 256) and T*k pair indices (-> 256); then the rows staged for the matrix cores, the
+    # larger of the tokens (3 x 256 fp16 = 1536, 3 x 4 groups x 8 bytes -> 256, 3 row scales -> 256) and the
+    # hidden vectors (6 x 128 fp16 = 1536, 6 x 2 x 8 -> 256, 6 -> 256)
+    assert q.q4_expert_gemv_workspace_bytes(good, 2, None, 3) == 3072 + 256 + 256 + 256 + 256 + 2048
     assert q.moe_group_pairs_max_groups(32, 8, 128) == 129 and q.moe_group_pairs_max_groups(1, 8, 128) == 8
     gp = q.raw("moe_group_pairs")
     assert gp(256, 4, 2, 5000, 256, 256, 256, None) == q.MOE_ERR_UNSUPPORTED          # pool too large to group

@@ -171,3 +171,34 @@ def test_grouped_fused_combine_matches_one_token_calls():
             torch.cuda.synchronize()
             err = H.max_rel_err(H.to_f64(out[t]), H.to_f64(o1[0]))
             assert err <= TOL, f"call {call} token {t}: {err:.3e}"
+
+
+def test_prefill_chunk_128_tokens_vs_oracle():
+    """A 128-token chunk (the pages' prefill processes a prompt's tokens together) through the full-size
+    experts: about 8 tokens per expert, several experts with more than 16 (more than one token chunk of the
+    matrix-core kernel), 8 chunks of the shared expert.  Sampled expert outputs against the oracle; every
+    output finite."""
+    cfg = synth.BATCHED
+    dev = H.device_layer(cfg, 0)
+    shape = H.shape_of(cfg)
+    rp, sp = _tiny_pools(cfg, dev, shape)
+    T, k, E = 128, cfg.k, cfg.n_experts
+    ids_np = synth.zipf_trace(31, T, 1, k, E, 1.1)[:, 0, :].astype(np.int32)
+    counts = np.bincount(ids_np.ravel(), minlength=E)
+    assert counts.max() > 16   # the multi-chunk path is exercised
+    x = H.token_batch(cfg, range(300, 300 + T))
+    yr, ys = _gemv(rp, sp, torch.from_numpy(ids_np).cuda(), k, x, q.MOE_BF16, T, shape.act, cfg.d)
+    torch.cuda.synchronize()
+    assert torch.isfinite(yr).all() and torch.isfinite(ys).all()
+    orc = oin.oracle_layer(cfg, 0)
+    act = _oracle_act(shape)
+    yr64, ys64 = H.to_f64(yr), H.to_f64(ys)
+    busiest = int(np.argmax(counts))
+    err = 0.0
+    for t in sorted({0, 17, 77, 127, *np.nonzero((ids_np == busiest).any(1))[0][-2:].tolist()}):
+        u = H.to_f64(x[t])
+        err = max(err, H.max_rel_err(ys64[t], moe.expert_ffn(orc.decoded_shared(), u, act)))
+        for i in range(k):
+            err = max(err, H.max_rel_err(yr64[t, i], moe.expert_ffn(orc.decoded(int(ids_np[t, i])), u, act)))
+    print(f"128-token chunk: max rel err {err:.3e} (busiest expert {busiest}: {counts[busiest]} tokens)")
+    assert err <= TOL
