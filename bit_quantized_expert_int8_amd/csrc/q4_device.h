@@ -400,6 +400,7 @@ inline size_t lds_bytes(int K) { return (size_t)(K / 32) * (kHgStride * 4 + 16);
 // MFMA kernel multiplies (one power-of-two scale per row, per-64-group sums); then one block per 16 weight
 // rows and (group or shared matrix) multiplies them with up to 16 tokens at a time.
 struct StagedRows {
+  int32_t rows;
   _Float16* xq;   // [rows][K]
   float2* os;     // [rows][K/64]: (1024 * sum of the group's staged values, sum of its values / 2^e)
   float* ef;      // [rows] 2^e
@@ -411,6 +412,7 @@ inline size_t staged_rows_bytes(int64_t rows, int K) {
 inline StagedRows staged_rows_at(char* base, int64_t rows, int K) {
   auto a256 = [](size_t x) { return (x + 255) / 256 * 256; };
   StagedRows r;
+  r.rows = (int32_t)rows;
   r.xq = reinterpret_cast<_Float16*>(base);
   r.os = reinterpret_cast<float2*>(base + a256((size_t)rows * K * 2));
   r.ef = reinterpret_cast<float*>(base + a256((size_t)rows * K * 2) + a256((size_t)rows * (K / 64) * 8));

@@ -122,7 +122,26 @@ __device__ __forceinline__ void opaque_sb<true>(SbWord<true>& w) {
 template <>
 __device__ __forceinline__ void opaque_sb<false>(SbWord<false>&) {}
 
-// One block's work: steps [s0, s1) of one matrix (a step = 8 / wk tiles of 16 rows, one per group of wk
+// Buffer loads: a uniform base (the resource, in SGPRs) + a per-lane 32-bit offset + a uniform offset, so
+// that per-group loads need no 64-bit address registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+// Scale/bias of 16 bytes per load: 4 groups (bf16 pairs) or 2 (fp32 pairs) of a row; word i of a load.
+template <bool SB_BF16>
+__device__ __forceinline__ SbWord<SB_BF16> sb_word(const u32x4& v, int i) {
+  SbWord<SB_BF16> w;
+  if constexpr (SB_BF16) {
+    w.s = v[i];
+    w.b = 0;
+  } else {
+    w.s = v[2 * i];
+    w.b = v[2 * i + 1];
+  }
+  return w;
+}
+
+// One block's work: steps [s0, s1) of one matrix (a step = 4 / wk tiles of 16 rows, one per group of wk
 // waves) for a list of tokens, 16 at a time.  Per chunk of tokens each wave loads its A operands (its
 // groups' staged activations) once; per step it streams the code words and scale/bias of its rows, the
 // next step's words requested as soon as the current step's are unpacked, so a step's weights are in
@@ -149,9 +168,11 @@ __device__ __forceinline__ void mfma_item(const MfmaArgs& a, bool shared, int e,
   const int part = wave % wk, wt = wave / wk;
   const int g0 = (part * G) / wk, nw = ((part + 1) * G) / wk - g0;
   const char* rec = P.base + (int64_t)e * P.record_bytes;
-  const uint32_t* qmat = reinterpret_cast<const uint32_t*>(rec + P.off_q);
-  const char* sbmat = rec + P.off_sb;
   const int sb_row = G * (SB_BF16 ? 4 : 8);
+  const int mat_rows = a.gate_up ? 2 * P.F : n_tiles * 16;
+  const __amdgpu_buffer_rsrc_t qr = buf_rsrc(rec + P.off_q, (uint32_t)mat_rows * (K / 2));
+  const __amdgpu_buffer_rsrc_t sr = buf_rsrc(rec + P.off_sb, (uint32_t)mat_rows * sb_row);
+  const __amdgpu_buffer_rsrc_t ar = buf_rsrc(xs.xq, (uint32_t)xs.rows * K * 2);
   // this lane's row in tile t (tiles past the matrix read its last tile; their results are not stored)
   auto row_of = [&](int t) {
     t = min(t, n_tiles - 1);
@@ -188,26 +209,31 @@ __device__ __forceinline__ void mfma_item(const MfmaArgs& a, bool shared, int e,
     }
     // A of this wave's groups for the whole chunk: token n's 32 bytes of each group (index clamped into
     // the row for slots past the wave's range)
-    const _Float16* arow = xs.xq + (int64_t)srow_l[n] * K + 16 * kb;
+    const int a_off = (srow_l[n] * K + 16 * kb) * 2;
     half8 A0[NG], A1[NG];
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
-      const u32x4* ap = reinterpret_cast<const u32x4*>(arow + min(g0 + i, G - 1) * 64);
-      A0[i] = __builtin_bit_cast(half8, ap[0]);
-      A1[i] = __builtin_bit_cast(half8, ap[1]);
+      const int gi = min(g0 + i, G - 1);
+      A0[i] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(ar, a_off, gi * 128, 0));
+      A1[i] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(ar, a_off + 16, gi * 128, 0));
     }
     // the first step's code words and scale/bias (record 0 for an invalid expert: never used).  Plain
     // loads, not streaming ones: a lane reads 8 bytes of a 128-byte line whose other bytes the row's next
     // groups read soon after, so the line should stay in L2 (streaming loads measured 17% slower).
+    // scale/bias: the 4 lanes of a row read the same 16 bytes (one request), a load per SPL groups; bytes
+    // past the row's groups belong to slots that carry weight zero (or lie outside the buffer: zeros)
+    constexpr int SPL = SB_BF16 ? 4 : 2, NS = (NG + SPL - 1) / SPL, SB_BYTES = SB_BF16 ? 4 : 8;
     u32x2 q[NG];
-    SbWord<SB_BF16> sbw[NG];
+    u32x4 sbv[NS];
     {
       const int r = row_of(s0 * tps + wt);
+      const int q_off = r * (K / 2) + 8 * kb, s_off = r * sb_row;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) sbv[j] = __builtin_amdgcn_raw_buffer_load_b128(sr, s_off, (g0 + j * SPL) * SB_BYTES, 0);
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
         const int gi = min(g0 + i, G - 1);
-        q[i] = *reinterpret_cast<const u32x2*>(qmat + (int64_t)r * (K / 8) + gi * 8 + 2 * kb);
-        sbw[i] = load_sb<SB_BF16>(sbmat + (int64_t)r * sb_row, gi);
+        q[i] = __builtin_amdgcn_raw_buffer_load_b64(qr, q_off, gi * 32, 0);
       }
     }
     __syncthreads();   // os, ef and the token rows are in LDS
@@ -221,8 +247,7 @@ __device__ __forceinline__ void mfma_item(const MfmaArgs& a, bool shared, int e,
       asm volatile("" : "+v"(os_off));
       // the next step's rows (the last step reads its own again: cache hits, no branch)
       const int rn = row_of(min(s + 1, s1 - 1) * tps + wt);
-      const uint32_t* qn = qmat + (int64_t)rn * (K / 8) + 2 * kb;
-      const char* sbn = sbmat + (int64_t)rn * sb_row;
+      const int qn_off = rn * (K / 2) + 8 * kb, sn_off = rn * sb_row;
       f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
@@ -236,7 +261,7 @@ __device__ __forceinline__ void mfma_item(const MfmaArgs& a, bool shared, int e,
         b1.y = (w1 & dq.hi) | dq.magic;
         b1.z = (t1 & dq.lo) | dq.magic;
         b1.w = (t1 & dq.hi) | dq.magic;
-        SbWord<SB_BF16> sw = sbw[i];
+        SbWord<SB_BF16> sw = sb_word<SB_BF16>(sbv[i / SPL], i % SPL);
         opaque_sb(sw);
         float sc, bi;
         sb_values<SB_BF16>(sw, sc, bi);
@@ -247,8 +272,9 @@ __device__ __forceinline__ void mfma_item(const MfmaArgs& a, bool shared, int e,
         // above the load, so the new words reuse the old words' registers instead of being copied back)
         __builtin_amdgcn_sched_barrier(0);
         const int gi = min(g0 + i, G - 1);
-        q[i] = *reinterpret_cast<const u32x2*>(qn + gi * 8);
-        sbw[i] = load_sb<SB_BF16>(sbn, gi);
+        q[i] = __builtin_amdgcn_raw_buffer_load_b64(qr, qn_off, gi * 32, 0);
+        if (i % SPL == SPL - 1 || i == NG - 1)
+          sbv[i / SPL] = __builtin_amdgcn_raw_buffer_load_b128(sr, sn_off, (g0 + (i / SPL) * SPL) * SB_BYTES, 0);
         {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
           acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0[i], __builtin_bit_cast(half8, b0), acc, 0, 0, 0);
