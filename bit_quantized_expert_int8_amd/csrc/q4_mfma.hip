@@ -108,9 +108,15 @@ __global__ __launch_bounds__(kThreadsM) void stage_rows_kernel(const XT* __restr
 constexpr int kWavesG = 4;                 // wavefronts of a grouped-product block
 constexpr int kThreadsG = 64 * kWavesG;
 
-// Dynamic LDS of a block: red [4][16][16] fp32, os [G][16] float2, ef [16], rows [16] (stage and output rows)
-inline size_t mfma_lds_bytes(int K) {
-  return (size_t)kWavesG * 256 * 4 + (size_t)(K / 64) * 16 * 8 + 16 * 4 + 16 * 4 * 2;
+// A wave's code words of one step, staged in LDS: 16 rows of NG groups (32 bytes each), rows padded by 16
+// bytes so that the 16 rows of an MFMA operand read fall on different banks.
+constexpr int slice_stride(int ng) { return ng * 32 + 16; }
+
+// Dynamic LDS of a block: red [4][16][16] fp32, the waves' code-word slices [4][16][stride], os [G][16]
+// float2, ef [16], rows [16] (stage and output rows)
+inline size_t mfma_lds_bytes(int K, int ng) {
+  return (size_t)kWavesG * 256 * 4 + (size_t)kWavesG * 16 * slice_stride(ng) + (size_t)(K / 64) * 16 * 8 + 16 * 4 +
+         16 * 4 * 2;
 }
 
 template <bool SB_BF16>
@@ -157,8 +163,10 @@ __device__ __forceinline__ void mfma_item(const MfmaArgs& a, bool shared, int e,
   float* const out = shared ? a.out_shared : a.out_routed;
   const int out_len = shared ? a.out_len_shared : a.out_len_routed;
   const int G = K / 64, tps = kWavesG / wk;
-  float2* os_l = reinterpret_cast<float2*>(lds + kWavesG * 256);    // [G][16]
-  float* ef_l = reinterpret_cast<float*>(lds + kWavesG * 256 + G * 32);
+  constexpr int kStride = slice_stride(NG);                         // bytes
+  char* slice = reinterpret_cast<char*>(lds) + kWavesG * 256 * 4;   // [4 waves][16 rows][kStride]
+  float2* os_l = reinterpret_cast<float2*>(slice + kWavesG * 16 * kStride);   // [G][16]
+  float* ef_l = reinterpret_cast<float*>(os_l + G * 16);
   int* srow_l = reinterpret_cast<int*>(ef_l + 16);
   int* orow_l = srow_l + 16;
 
@@ -223,18 +231,29 @@ __device__ __forceinline__ void mfma_item(const MfmaArgs& a, bool shared, int e,
     // scale/bias: the 4 lanes of a row read the same 16 bytes (one request), a load per SPL groups; bytes
     // past the row's groups belong to slots that carry weight zero (or lie outside the buffer: zeros)
     constexpr int SPL = SB_BF16 ? 4 : 2, NS = (NG + SPL - 1) / SPL, SB_BYTES = SB_BF16 ? 4 : 8;
-    u32x2 q[NG];
+    // code words: each wave streams its 16 rows x NG groups as whole 16-byte pieces of the rows (22 lanes
+    // cover a row's 352 bytes at 11 groups, so a load instruction reads whole 128-byte lines), writes them
+    // to its LDS slice and reads them back in the MFMA operand layout
+    constexpr int CPR = 2 * NG, NCH = (16 * CPR + 63) / 64;   // 16-byte pieces per row; loads per lane
+    char* my_slice = slice + wave * 16 * kStride;
+    // piece j of a lane: row (lane + 64 j) / CPR of the tile, column (lane + 64 j) % CPR (lanes past the
+    // last piece repeat it and do not store it); recomputed where used rather than held in registers
+    auto piece_c = [&](int j) { return min(lane + 64 * j, 16 * CPR - 1); };
+    auto piece_off = [&](int t, int j) {   // byte offset of piece j of tile t in the matrix (group g0 first)
+      t = min(t, n_tiles - 1);
+      const int c = piece_c(j), rt = c / CPR;
+      const int row = a.gate_up ? (rt < 8 ? t * 8 + rt : P.F + t * 8 + (rt - 8)) : t * 16 + rt;
+      return row * (K / 2) + (c % CPR) * 16;
+    };
+    u32x4 wq[NCH];
     u32x4 sbv[NS];
     {
       const int r = row_of(s0 * tps + wt);
-      const int q_off = r * (K / 2) + 8 * kb, s_off = r * sb_row;
+      const int s_off = r * sb_row;
 #pragma unroll
       for (int j = 0; j < NS; ++j) sbv[j] = __builtin_amdgcn_raw_buffer_load_b128(sr, s_off, (g0 + j * SPL) * SB_BYTES, 0);
 #pragma unroll
-      for (int i = 0; i < NG; ++i) {
-        const int gi = min(g0 + i, G - 1);
-        q[i] = __builtin_amdgcn_raw_buffer_load_b64(qr, q_off, gi * 32, 0);
-      }
+      for (int j = 0; j < NCH; ++j) wq[j] = __builtin_amdgcn_raw_buffer_load_b128(qr, piece_off(s0 * tps + wt, j), g0 * 32, 0);
     }
     __syncthreads();   // os, ef and the token rows are in LDS
 
@@ -246,12 +265,30 @@ __device__ __forceinline__ void mfma_item(const MfmaArgs& a, bool shared, int e,
       int os_off = 4 * kb;
       asm volatile("" : "+v"(os_off));
       // the next step's rows (the last step reads its own again: cache hits, no branch)
-      const int rn = row_of(min(s + 1, s1 - 1) * tps + wt);
-      const int qn_off = rn * (K / 2) + 8 * kb, sn_off = rn * sb_row;
+      const int tn = min(s + 1, s1 - 1) * tps + wt;
+      const int rn = row_of(tn), sn_off = rn * sb_row;
+      // this step's pieces into the slice, then the next step's requested into the same registers (the
+      // pieces past a row's groups, or past the matrix, read zeros or other rows: never multiplied)
+#pragma unroll
+      for (int j = 0; j < NCH; ++j)
+        if (lane + 64 * j < 16 * CPR) {
+          const int c = lane + 64 * j;
+          *reinterpret_cast<u32x4*>(my_slice + (c / CPR) * kStride + (c % CPR) * 16) = wq[j];
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) wq[j] = __builtin_amdgcn_raw_buffer_load_b128(qr, piece_off(tn, j), g0 * 32, 0);
+      // the MFMA operand words: row n, group i, words 2 kb and 2 kb + 1, read two groups ahead
+      const char* opnd = my_slice + n * kStride + kb * 8;
+      u32x2 qr3[3];
+      qr3[0] = *reinterpret_cast<const u32x2*>(opnd);
+      if (NG > 1) qr3[1] = *reinterpret_cast<const u32x2*>(opnd + 32);
       f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
-        const uint32_t w0 = q[i].x, w1 = q[i].y, t0 = w0 >> sh8, t1 = w1 >> sh8;
+        if (i + 2 < NG) qr3[(i + 2) % 3] = *reinterpret_cast<const u32x2*>(opnd + (i + 2) * 32);
+        const u32x2 qi = qr3[i % 3];
+        const uint32_t w0 = qi.x, w1 = qi.y, t0 = w0 >> sh8, t1 = w1 >> sh8;
         u32x4 b0, b1;
         b0.x = (w0 & dq.lo) | dq.magic;
         b0.y = (w0 & dq.hi) | dq.magic;
@@ -268,11 +305,10 @@ __device__ __forceinline__ void mfma_item(const MfmaArgs& a, bool shared, int e,
         // slots past the wave's groups multiply the row's last group again, with weight zero: no branch, so
         // the unpacking above cannot sink below the reload
         if (i >= nw) sc = bi = 0.f;
-        // group i's registers are free: request the next step's into them (the barrier keeps the unpacking
-        // above the load, so the new words reuse the old words' registers instead of being copied back)
+        // the barrier keeps the unpacking above the reload, so the new scale/bias words reuse the old ones'
+        // registers instead of being copied back
         __builtin_amdgcn_sched_barrier(0);
         const int gi = min(g0 + i, G - 1);
-        q[i] = __builtin_amdgcn_raw_buffer_load_b64(qr, qn_off, gi * 32, 0);
         if (i % SPL == SPL - 1 || i == NG - 1)
           sbv[i / SPL] = __builtin_amdgcn_raw_buffer_load_b128(sr, sn_off, (g0 + (i / SPL) * SPL) * SB_BYTES, 0);
         {
@@ -401,9 +437,9 @@ moe_status launch_grouped_mfma(MfmaArgs a, bool has_shared, bool has_routed, boo
     per_wave = max(per_wave, (a.K_routed / 64 + a.wk_routed - 1) / a.wk_routed);
     kmax = max(kmax, a.K_routed);
   }
-  const size_t lds = mfma_lds_bytes(kmax);
   auto go = [&](auto ng) {
     constexpr int NG = decltype(ng)::value;
+    const size_t lds = mfma_lds_bytes(kmax, NG);
     auto kern = sb_bf16 ? grouped_mfma_kernel<NG, true> : grouped_mfma_kernel<NG, false>;
     // as many blocks as are resident at once
     static int per_cu_cached[2] = {0, 0};   // per kernel instantiation (and scale/bias type)
