@@ -3,8 +3,8 @@
 // la bande passante SSD la nouvelle contrainte": 4-bit affine MLX weights).
 //
 // With several tokens per expert the one-token kernels' dot2 chains become the bottleneck (every token
-// repeats the dequantization and 36 VALU operations per 32 codes).  Here a block holds 16 weight rows in
-// registers and multiplies them with up to 16 tokens at a time by v_mfma_f32_16x16x32_f16:
+// repeats the dequantization and 36 VALU operations per 32 codes).  Here 16 weight rows are multiplied with
+// up to 16 tokens at a time by v_mfma_f32_16x16x32_f16:
 //
 //   A (16 tokens x 32 k, fp16)   lane l: token l % 16, k block l / 16 (8 values)
 //   B (32 k x 16 rows)           lane l: row l % 16, the same 8 k = one 32-bit word of 8 codes
@@ -20,10 +20,10 @@
 // and finally y *= 2^e.  Products of an 11-bit and an 11-bit significand are exact in fp32.
 //
 // Each pair of MFMA steps covers one group: lane (row, k block kb) takes the two code words 8 g + 2 kb
-// and 8 g + 2 kb + 1 of its row (one 8-byte load), and the A lanes read the matching 32 staged bytes of
-// their token (k order within a group is a permutation shared by A and B).  The block's 4 waves split the
-// row's groups; their 16 x 16 partial results are added in LDS in wave order.  Results match the
-// one-token kernels within rounding (the activation is scaled per token, not per half-group).
+// and 8 g + 2 kb + 1 of its row, and the A lanes hold the matching 32 staged bytes of their token (k order
+// within a group is a permutation shared by A and B).  The waves of a tile split the row's groups; their
+// 16 x 16 partial results are added in LDS in wave order.  Results match the one-token kernels within
+// rounding (the activation is scaled per token row, not per 32 values).
 #include "q4_device.h"
 
 namespace moeq4 {
@@ -149,9 +149,9 @@ __device__ __forceinline__ SbWord<SB_BF16> sb_word(const u32x4& v, int i) {
 
 // One block's work: steps [s0, s1) of one matrix (a step = 4 / wk tiles of 16 rows, one per group of wk
 // waves) for a list of tokens, 16 at a time.  Per chunk of tokens each wave loads its A operands (its
-// groups' staged activations) once; per step it streams the code words and scale/bias of its rows, the
-// next step's words requested as soon as the current step's are unpacked, so a step's weights are in
-// flight while the previous step is multiplied, reduced and stored.
+// groups' staged activations) once; per step it stages the step's code words in its LDS slice and at once
+// requests the next step's (and the scale/bias words as soon as they are unpacked), so a step's weights are
+// in flight while the previous step is multiplied, reduced and stored.
 template <int NG, bool SB_BF16>
 __device__ __forceinline__ void mfma_item(const MfmaArgs& a, bool shared, int e, bool valid, int start, int count,
                                           int s0, int s1, uint32_t* lds) {
