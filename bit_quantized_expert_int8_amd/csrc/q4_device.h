@@ -419,6 +419,9 @@ inline StagedRows staged_rows_at(char* base, int64_t rows, int K) {
   return r;
 }
 moe_status launch_stage_rows(const void* x, bool x_bf16, int rows, int K, const StagedRows& out, hipStream_t s);
+// two fp32 row sets staged in one launch (rows0 of x0, then rows1 of x1)
+moe_status launch_stage_rows2(const float* x0, int rows0, int K0, const StagedRows& out0, const float* x1, int rows1,
+                              int K1, const StagedRows& out1, hipStream_t s);
 // The grouped products of T > 1 tokens on the matrix cores (q4_mfma.hip).  A tile is 16 weight rows
 // (gate_up: 8 gate rows and the matching 8 up rows); wk waves of a block split a tile's K, so a block
 // of 8 waves works on 8 / wk tiles at a time (one step).  Fill the per-matrix fields; the launcher sets

@@ -309,18 +309,14 @@ moe_status run_down(GemvArgs a, const RecordOffsets& orr, const RecordOffsets& o
     const int P = T * a.k;
     char* base = a.stage;
     StagedRows xr{}, xsh{};
-    moe_status st = MOE_OK;
     if (has_routed) {
       xr = staged_rows_at(base, P, Fr);
       base += staged_rows_bytes(P, Fr);
-      st = launch_stage_rows(a.h_routed, false, P, Fr, xr, s);
-      if (st != MOE_OK) return st;
     }
-    if (has_shared) {
-      xsh = staged_rows_at(base, T, Fs);
-      st = launch_stage_rows(a.h_shared, false, T, Fs, xsh, s);
-      if (st != MOE_OK) return st;
-    }
+    if (has_shared) xsh = staged_rows_at(base, T, Fs);
+    const moe_status st =
+        launch_stage_rows2(a.h_routed, has_routed ? P : 0, Fr, xr, a.h_shared, has_shared ? T : 0, Fs, xsh, s);
+    if (st != MOE_OK) return st;
     MfmaArgs m{};
     m.routed = a.routed;
     m.shared = a.shared;

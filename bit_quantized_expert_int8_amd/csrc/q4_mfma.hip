@@ -48,10 +48,23 @@ __device__ __forceinline__ float wave_max(float v) {
 // One block per row: xq[row] (fp16, the MFMA order above), os[row][g] = (1024 O_g, Sx_g), ef[row] = 2^e.
 // Fixed summation order: per 8 values ((a0 + a4) + (a2 + a6)) and ((b1 + b5) + (b3 + b7)), then the 8
 // blocks of a group by an xor butterfly.
+// Blocks [0, rows0) stage the rows of j0, the rest those of j1 (the down launch stages the routed and the
+// shared hidden vectors together).
 template <typename XT>
-__global__ __launch_bounds__(kThreadsM) void stage_rows_kernel(const XT* __restrict__ x, int K, StagedRows out) {
+struct StageJob {
+  const XT* x;
+  int K;
+  StagedRows out;
+};
+
+template <typename XT>
+__global__ __launch_bounds__(kThreadsM) void stage_rows_kernel(StageJob<XT> j0, StageJob<XT> j1, int rows0) {
   __shared__ float wmax[kThreadsM / 64];
-  const int row = blockIdx.x, t = threadIdx.x;
+  const bool second = (int)blockIdx.x >= rows0;
+  const XT* __restrict__ x = second ? j1.x : j0.x;
+  const int K = second ? j1.K : j0.K;
+  const StagedRows out = second ? j1.out : j0.out;
+  const int row = second ? (int)blockIdx.x - rows0 : (int)blockIdx.x, t = threadIdx.x;
   const int nb = K / 8;
   const XT* xr = x + (int64_t)row * K;
   float v[kStageIt][8];
@@ -397,10 +410,21 @@ __global__ __launch_bounds__(kThreadsG) void grouped_mfma_kernel(MfmaArgs a) {
 
 moe_status launch_stage_rows(const void* x, bool x_bf16, int rows, int K, const StagedRows& out, hipStream_t s) {
   if (rows <= 0) return MOE_OK;
-  if (x_bf16) hipLaunchKernelGGL((stage_rows_kernel<uint16_t>), dim3(rows), dim3(kThreadsM), 0, s,
-                                 static_cast<const uint16_t*>(x), K, out);
-  else hipLaunchKernelGGL((stage_rows_kernel<float>), dim3(rows), dim3(kThreadsM), 0, s, static_cast<const float*>(x), K,
-                          out);
+  if (x_bf16) {
+    const StageJob<uint16_t> j{static_cast<const uint16_t*>(x), K, out};
+    hipLaunchKernelGGL((stage_rows_kernel<uint16_t>), dim3(rows), dim3(kThreadsM), 0, s, j, j, rows);
+  } else {
+    const StageJob<float> j{static_cast<const float*>(x), K, out};
+    hipLaunchKernelGGL((stage_rows_kernel<float>), dim3(rows), dim3(kThreadsM), 0, s, j, j, rows);
+  }
+  return check_launch("stage_rows_kernel");
+}
+
+moe_status launch_stage_rows2(const float* x0, int rows0, int K0, const StagedRows& out0, const float* x1, int rows1,
+                              int K1, const StagedRows& out1, hipStream_t s) {
+  if (rows0 + rows1 <= 0) return MOE_OK;
+  const StageJob<float> j0{x0, K0, out0}, j1{x1, K1, out1};
+  hipLaunchKernelGGL((stage_rows_kernel<float>), dim3(rows0 + rows1), dim3(kThreadsM), 0, s, j0, j1, rows0);
   return check_launch("stage_rows_kernel");
 }
 
