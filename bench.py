@@ -11,8 +11,9 @@ graph; inputs are 256 seeded tokens already in HBM, rotated step by step.
 Prints one JSON line: decode tokens/s, plus the roofline of the dominant kernel (the single-launch
 layer, timed live with HIP events on its stream) and the CPU oracle's speed on a bounded sample.
 Alongside (not the headline value): per-launch times of the layer split in three kernels, a 32-token batched step
-through the same stack, and the same stack served from pinned host memory through 16-slot LFU expert
-caches (hit rates, host-to-device rate against a plain pinned copy).
+and a 128-token prefill chunk through the same stack (grouped products on the matrix cores), and the same
+stack served from pinned host memory through 16-slot LFU expert caches (hit rates, host-to-device rate
+against a plain pinned copy).
 """
 from __future__ import annotations
 
@@ -58,10 +59,10 @@ def build_stack(cfg, n_layers):
 # HBM traffic of one layer launch from FETCH_SIZE and WRITE_SIZE counter runs, each scaled by what the counter
 # reads for a plain 256 MiB device copy in the same run (profiles/decode_layer_kernel_stack30_decode.md).  It is
 # reported only while the kernel's sources are the ones the counters were taken on.
-LAYER_TRAFFIC_BYTES = 42567159
+LAYER_TRAFFIC_BYTES = 42566437
 LAYER_TRAFFIC_SOURCES = ("bit_quantized_expert_int8_amd/csrc/layer.hip", "bit_quantized_expert_int8_amd/csrc/q4_device.h",
                          "bit_quantized_expert_int8_amd/csrc/common.h")
-LAYER_TRAFFIC_SHA = "7bce2216c8a39d86"
+LAYER_TRAFFIC_SHA = "e2f0e1972e8c6818"
 
 
 def layer_traffic():
