@@ -56,9 +56,10 @@ def build_stack(cfg, n_layers):
     return shape, layers
 
 
-# HBM traffic of one layer launch from FETCH_SIZE and WRITE_SIZE counter runs, each scaled by what the counter
-# reads for a plain 256 MiB device copy in the same run (profiles/decode_layer_kernel_stack30_decode.md).  It is
-# reported only while the kernel's sources are the ones the counters were taken on.
+# HBM traffic of one layer launch from rocprofv3 FETCH_SIZE and WRITE_SIZE counter runs of this script (2 steps,
+# --calibration-copy-mib 256), each scaled by what the counter reads for the plain 256 MiB device copy in the
+# same run (FETCH_SIZE x 1.9997, WRITE_SIZE x 1.0).  It is reported only while the kernel's sources are the
+# ones the counters were taken on.
 LAYER_TRAFFIC_BYTES = 42566437
 LAYER_TRAFFIC_SOURCES = ("bit_quantized_expert_int8_amd/csrc/layer.hip", "bit_quantized_expert_int8_amd/csrc/q4_device.h",
                          "bit_quantized_expert_int8_amd/csrc/common.h")
@@ -333,7 +334,7 @@ def main():
                          "traffic counters of a profiled run)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
 
