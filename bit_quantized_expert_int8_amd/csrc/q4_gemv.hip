@@ -193,6 +193,14 @@ moe_status prepare(const char* who, const moe_q4_pool* routed, const int32_t* id
     if (need_y && !y_shared_dev) return fail(MOE_ERR_INVALID_ARG, "%s: y_shared is NULL", who);
   }
   const int d = has_routed ? routed->d : shared->d;
+  if (T > 1) {
+    // the matrix-core kernels address staged rows with 32-bit byte offsets
+    const int64_t rows = has_routed ? (int64_t)T * k : T;
+    const int64_t kmax = std::max<int64_t>(d, std::max<int64_t>(has_routed ? routed->F : 0, shared ? shared->F : 0));
+    if (rows * kmax * 2 >= (int64_t(1) << 31))
+      return fail(MOE_ERR_UNSUPPORTED, "%s: T=%d: %lld staged rows of %lld values exceed 2 GiB", who, T, (long long)rows,
+                  (long long)kmax);
+  }
   if (has_routed && shared) {
     if (shared->d != d) return fail(MOE_ERR_INVALID_ARG, "%s: routed d=%d != shared d=%d", who, d, shared->d);
     if (shared->sb_dtype != routed->sb_dtype)

@@ -176,7 +176,8 @@ moe_status moe_norm_router_topk(const void* x_dev, moe_dtype x_dtype, const floa
  * The two paths round differently: a token's T > 1 result matches its T == 1 result within the fp32/fp16
  * rounding of the activations (tested to max relative error 1e-2 with the oracle), not bit for bit.
  * Limits: k <= 32; routed and shared share d; routed may be NULL (k == 0) to run only the shared expert;
- * with T > 1 the routed pool has at most 4096 records (MOE_ERR_UNSUPPORTED otherwise).
+ * with T > 1 the routed pool has at most 4096 records, and T*k rows (T without routed experts) of the longest
+ * row length among d, F and S take less than 2 GiB in fp16 (MOE_ERR_UNSUPPORTED otherwise).
  * Workspace: q4_expert_gemv_workspace_bytes(...) bytes of device memory (contents need no initial value).
  * An id outside [0, routed->n_records) makes that expert's y_routed row NaN.
  * ------------------------------------------------------------------------------------------------- */

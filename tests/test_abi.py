@@ -100,6 +100,10 @@ def test_host_validation_errors():
     assert gp(256, 0, 2, 8, 256, 256, 256, None) == q.MOE_ERR_INVALID_ARG             # T = 0
     big = q.pool(256, 61440, 5000, 256, 128, 0)
     assert st(ctypes.byref(big), 256, 2, None, 256, 0, 2, 0, 256, None, 256, 1 << 24, None) == q.MOE_ERR_UNSUPPORTED
+    # a batch whose staged rows (T*k rows of the longest row, fp16) would pass 2 GiB: 65535 * 32 * 1024 * 2
+    wide = q.pool(256, q.moe_record_bytes(1024, 512, 0), 8, 1024, 512, 0)
+    assert st(ctypes.byref(wide), 256, 32, None, 256, 0, 65535, 0, 256, None, 256, 1 << 40, None) == q.MOE_ERR_UNSUPPORTED
+    assert "2 GiB" in q.moe_last_error()
     # stacked layers: 1..32 layers, out must not alias x
     stk = q.raw("moe_decode_stack")
     one = q.stack_layers([{"router_w_dev": 256, "router_scale_dev": 256, "routed_base_dev": 256}])
