@@ -202,3 +202,37 @@ def test_prefill_chunk_128_tokens_vs_oracle():
             err = max(err, H.max_rel_err(yr64[t, i], moe.expert_ffn(orc.decoded(int(ids_np[t, i])), u, act)))
     print(f"128-token chunk: max rel err {err:.3e} (busiest expert {busiest}: {counts[busiest]} tokens)")
     assert err <= TOL
+
+
+def test_grouped_gemv_longest_rows_vs_oracle():
+    """Rows of the largest supported length (d = 8192: 32 groups per wavefront in the gate/up products, the
+    widest register and LDS configuration of the matrix-core kernel), fp32 scale/bias and activations,
+    5 tokens, every expert output and the shared expert's against the oracle."""
+    d, F, S, E, k, T = 8192, 128, 192, 3, 2, 5
+    rng = np.random.default_rng(8192)
+    recs, decoded = [], []
+    for _ in range(E + 1):
+        wgu = (rng.standard_normal((2 * F, d)) * 0.02).astype(np.float32)
+        wd = (rng.standard_normal((d, F)) * 0.02).astype(np.float32)
+        recs.append(moe.encode_record(wgu, wd, False))
+        decoded.append(moe.decode_record(recs[-1], d, F, False))
+    wgu = (rng.standard_normal((2 * S, d)) * 0.02).astype(np.float32)
+    wd = (rng.standard_normal((d, S)) * 0.02).astype(np.float32)
+    srec = moe.encode_record(wgu, wd, False)
+    sdec = moe.decode_record(srec, d, S, False)
+    pool = torch.from_numpy(np.stack(recs[:E])).cuda()
+    shared = torch.from_numpy(srec[None, :].copy()).cuda()
+    rp = q.pool(pool, pool.shape[1], E, d, F, q.MOE_F32)
+    sp = q.pool(shared, shared.shape[1], 1, d, S, q.MOE_F32)
+    ids_np = np.array([[0, 2], [1, 0], [2, 1], [0, 1], [2, 0]], dtype=np.int32)
+    x = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).cuda()
+    yr, ys = _gemv(rp, sp, torch.from_numpy(ids_np).cuda(), k, x, q.MOE_F32, T, q.MOE_ACT_GELU_TANH, d)
+    torch.cuda.synchronize()
+    yr, ys, u = H.to_f64(yr), H.to_f64(ys), H.to_f64(x)
+    err = 0.0
+    for t in range(T):
+        err = max(err, H.max_rel_err(ys[t], moe.expert_ffn(sdec, u[t], moe.ACT_GELU_TANH)))
+        for i in range(k):
+            err = max(err, H.max_rel_err(yr[t, i], moe.expert_ffn(decoded[ids_np[t, i]], u[t], moe.ACT_GELU_TANH)))
+    print(f"d=8192 grouped expert gemv: max rel err {err:.3e}")
+    assert err <= TOL
