@@ -12,6 +12,9 @@ namespace moeq4 {
 namespace {
 
 constexpr int kRouterWaves = 4;
+// One ticket counter per token, 256 bytes apart: a token's E / 4 blocks take their tickets at once, and
+// with the counters of all tokens in one line every ticket of a batch would queue on one L2 channel.
+constexpr int kCounterStride = 64;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxK = 32;
 constexpr int kRouterChunks = 8;    // 16-byte chunks per lane: rows of up to 8192 int8
@@ -100,7 +103,7 @@ struct RouterArgs {
   int32_t* ids;
   float* weights;
   float* logits;         // [T][E]: caller's buffer or workspace
-  uint32_t* counters;    // [T], zero between calls
+  uint32_t* counters;    // [T] at a stride of kCounterStride words, zero between calls
   const float* gamma;    // RMSNorm gain [d], or NULL: the router reads x as is
   float eps;
   void* u_out;           // [T][d] normalized activation (x dtype), written by block 0; NULL = not wanted
@@ -200,7 +203,7 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t ticket = __hip_atomic_fetch_add(a.counters + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t ticket = __hip_atomic_fetch_add(a.counters + t * kCounterStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     last_flag = (ticket == gridDim.x - 1) ? 1u : 0u;
   }
   __syncthreads();
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
     a.ids[t * a.k + threadIdx.x] = sel_i[threadIdx.x];
     a.weights[t * a.k + threadIdx.x] = expf(sel_v[threadIdx.x] - mx) / den;
   }
-  if (threadIdx.x == 0) __hip_atomic_store(a.counters + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) __hip_atomic_store(a.counters + t * kCounterStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -315,7 +318,7 @@ extern "C" moe_status moe_rmsnorm(const void* x_dev, moe_dtype x_dtype, const fl
 
 extern "C" size_t moe_router_workspace_bytes(int32_t T, int32_t E) {
   if (T < 1 || E < 1) return 0;
-  const size_t counters = ((size_t)T * 4 + 255) / 256 * 256;
+  const size_t counters = (size_t)T * kCounterStride * 4;
   return counters + (size_t)T * E * 4;
 }
 
@@ -375,7 +378,7 @@ moe_status router_launch(const char* who, const void* x_dev, moe_dtype x_dtype, 
   a.weights = weights_dev;
   a.counters = static_cast<uint32_t*>(workspace_dev);
   a.logits = logits_dev ? logits_dev
-                        : reinterpret_cast<float*>(static_cast<char*>(workspace_dev) + ((size_t)T * 4 + 255) / 256 * 256);
+                        : reinterpret_cast<float*>(static_cast<char*>(workspace_dev) + (size_t)T * kCounterStride * 4);
   a.gamma = gamma_dev;
   a.eps = eps;
   a.u_out = u_dev;
