@@ -1,7 +1,7 @@
 // q4_expert_gemv and its halves: the single-token (decode) kernels and the C entry points.  The
 // arithmetic, the work mapping and the dequantization are described in q4_device.h; batches of more
 // than one token go through the grouped kernels of q4_grouped.hip.
-#include "q4_device.h"
+#include "q4_grouping.h"
 
 namespace moeq4 {
 namespace {
@@ -257,15 +257,13 @@ moe_status run_gate_up(GemvArgs a, const RecordOffsets& orr, const RecordOffsets
   const int waves = nit < kMaxWaves ? nit : kMaxWaves;
   const int nbw = (nit + waves - 1) / waves;
   if (T > 1) {
-    // grouped on the matrix cores: sort the pairs by expert, stage the T tokens once, then one block per
-    // (group, 8 features) and per 8 shared features, each with all of its tokens
-    if (a.k > 0) {
-      const moe_status st =
-          launch_group_pairs(a.ids, T * a.k, a.routed.n_records, a.n_groups, a.groups, a.perm, s, a.n_chunks, a.chunks);
-      if (st != MOE_OK) return st;
-    }
+    // grouped on the matrix cores: sort the pairs by expert and stage the T tokens (one launch), then the
+    // products, every selected expert's and the shared expert's rows streamed once per chunk of tokens
     const StagedRows xs = staged_rows_at(a.stage, T, a.d);
-    moe_status st = launch_stage_rows(a.in, x_dtype == MOE_BF16, T, a.d, xs, s);
+    const moe_status st =
+        a.k > 0 ? launch_group_and_stage(a.ids, T * a.k, a.routed.n_records, a.n_groups, a.groups, a.perm, a.n_chunks,
+                                         a.chunks, a.in, x_dtype == MOE_BF16, T, a.d, xs, s)
+                : launch_stage_rows(a.in, x_dtype == MOE_BF16, T, a.d, xs, s);
     if (st != MOE_OK) return st;
     MfmaArgs m{};
     m.routed = a.routed;

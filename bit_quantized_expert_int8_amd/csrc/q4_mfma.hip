@@ -24,7 +24,7 @@
 // within a group is a permutation shared by A and B).  The waves of a tile split the row's groups; their
 // 16 x 16 partial results are added in LDS in wave order.  Results match the one-token kernels within
 // rounding (the activation is scaled per token row, not per 32 values).
-#include "q4_device.h"
+#include "q4_grouping.h"
 
 namespace moeq4 {
 namespace {
@@ -58,13 +58,12 @@ struct StageJob {
 };
 
 template <typename XT>
-__global__ __launch_bounds__(kThreadsM) void stage_rows_kernel(StageJob<XT> j0, StageJob<XT> j1, int rows0) {
+__device__ __forceinline__ void stage_row(const StageJob<XT>& j, int row) {
   __shared__ float wmax[kThreadsM / 64];
-  const bool second = (int)blockIdx.x >= rows0;
-  const XT* __restrict__ x = second ? j1.x : j0.x;
-  const int K = second ? j1.K : j0.K;
-  const StagedRows out = second ? j1.out : j0.out;
-  const int row = second ? (int)blockIdx.x - rows0 : (int)blockIdx.x, t = threadIdx.x;
+  const XT* __restrict__ x = j.x;
+  const int K = j.K;
+  const StagedRows out = j.out;
+  const int t = threadIdx.x;
   const int nb = K / 8;
   const XT* xr = x + (int64_t)row * K;
   float v[kStageIt][8];
@@ -116,6 +115,28 @@ __global__ __launch_bounds__(kThreadsM) void stage_rows_kernel(StageJob<XT> j0, 
     }
   }
   if (t == 0) out.ef[row] = ldexpf(1.0f, e);
+}
+
+template <typename XT>
+__global__ __launch_bounds__(kThreadsM) void stage_rows_kernel(StageJob<XT> j0, StageJob<XT> j1, int rows0) {
+  const bool second = (int)blockIdx.x >= rows0;
+  stage_row<XT>(second ? j1 : j0, second ? (int)blockIdx.x - rows0 : (int)blockIdx.x);
+}
+
+// The grouping of the pairs (block 0) and the staging of the tokens (blocks 1 .. rows) in one launch: the
+// two are independent and each alone is a launch of a few microseconds.
+struct GroupJob {
+  const int32_t* ids;
+  int P, n_valid;
+  int32_t *n_groups, *perm, *n_chunks;
+  int4 *groups, *chunks;
+};
+
+template <typename XT>
+__global__ __launch_bounds__(kThreadsM) void group_and_stage_kernel(GroupJob g, StageJob<XT> j) {
+  static_assert(kThreadsM == kGroupThreads, "one block shape for both");
+  if (blockIdx.x == 0) group_pairs_block(g.ids, g.P, g.n_valid, g.n_groups, g.groups, g.perm, g.n_chunks, g.chunks);
+  else stage_row<XT>(j, (int)blockIdx.x - 1);
 }
 
 constexpr int kWavesG = 4;                 // wavefronts of a grouped-product block
@@ -418,6 +439,20 @@ moe_status launch_stage_rows(const void* x, bool x_bf16, int rows, int K, const 
     hipLaunchKernelGGL((stage_rows_kernel<float>), dim3(rows), dim3(kThreadsM), 0, s, j, j, rows);
   }
   return check_launch("stage_rows_kernel");
+}
+
+moe_status launch_group_and_stage(const int32_t* ids, int P, int n_valid, int32_t* n_groups, int4* groups,
+                                  int32_t* perm, int32_t* n_chunks, int4* chunks, const void* x, bool x_bf16, int rows,
+                                  int K, const StagedRows& out, hipStream_t s) {
+  const GroupJob g{ids, P, n_valid, n_groups, perm, n_chunks, groups, chunks};
+  if (x_bf16) {
+    const StageJob<uint16_t> j{static_cast<const uint16_t*>(x), K, out};
+    hipLaunchKernelGGL((group_and_stage_kernel<uint16_t>), dim3(rows + 1), dim3(kThreadsM), 0, s, g, j);
+  } else {
+    const StageJob<float> j{static_cast<const float*>(x), K, out};
+    hipLaunchKernelGGL((group_and_stage_kernel<float>), dim3(rows + 1), dim3(kThreadsM), 0, s, g, j);
+  }
+  return check_launch("group_and_stage_kernel");
 }
 
 moe_status launch_stage_rows2(const float* x0, int rows0, int K0, const StagedRows& out0, const float* x1, int rows1,
