@@ -236,3 +236,27 @@ def test_grouped_gemv_longest_rows_vs_oracle():
             err = max(err, H.max_rel_err(yr[t, i], moe.expert_ffn(decoded[ids_np[t, i]], u[t], moe.ACT_GELU_TANH)))
     print(f"d=8192 grouped expert gemv: max rel err {err:.3e}")
     assert err <= TOL
+
+
+def test_grouped_gemv_silu_ragged_batch_vs_oracle():
+    """SiLU activation, 7 tokens (a ragged token chunk), top-2 of the tiny pool with one expert taken by
+    every token (a 7-token run) and one by none; every output against the oracle."""
+    cfg = synth.TINY
+    dev = H.device_layer(cfg, 0)
+    orc = oin.oracle_layer(cfg, 0)
+    shape = H.shape_of(cfg)
+    rp, sp = _tiny_pools(cfg, dev, shape)
+    T, k = 7, cfg.k
+    ids_np = np.array([[3, 0], [3, 5], [1, 3], [3, 6], [2, 3], [3, 4], [0, 3]], dtype=np.int32)
+    x = H.token_batch(cfg, range(40, 40 + T))
+    yr, ys = _gemv(rp, sp, torch.from_numpy(ids_np).cuda(), k, x, q.MOE_F32, T, q.MOE_ACT_SILU, cfg.d)
+    torch.cuda.synchronize()
+    yr, ys = H.to_f64(yr), H.to_f64(ys)
+    err = 0.0
+    for t in range(T):
+        u = H.to_f64(x[t])
+        err = max(err, H.max_rel_err(ys[t], moe.expert_ffn(orc.decoded_shared(), u, moe.ACT_SILU)))
+        for i in range(k):
+            err = max(err, H.max_rel_err(yr[t, i], moe.expert_ffn(orc.decoded(int(ids_np[t, i])), u, moe.ACT_SILU)))
+    print(f"tiny grouped expert gemv, SiLU, 7 tokens: max rel err {err:.3e}")
+    assert err <= TOL
