@@ -68,6 +68,8 @@ def test_host_validation_errors():
     assert _status("moe_router_topk", *args(1, 60, 8, 2, 1 << 20)) == q.MOE_ERR_UNSUPPORTED
     assert _status("moe_router_topk", *args(1, 64, 8, 2, 16)) == q.MOE_ERR_INVALID_ARG      # workspace too small
     assert q.moe_router_workspace_bytes(1, 128) == 256 + 512
+    # one ticket counter per token, 256 bytes apart, then the logits [T][E] fp32
+    assert q.moe_router_workspace_bytes(32, 128) == 32 * 256 + 32 * 128 * 4
     # q4_expert_gemv: misaligned pool, mismatched d, k too large
     bad = q.pool(256 + 16, 61440, 8, 256, 128, 0)
     good = q.pool(256, 61440, 8, 256, 128, 0)
