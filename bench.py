@@ -11,8 +11,8 @@ graph; inputs are 256 seeded tokens already in HBM, rotated step by step.
 Prints one JSON line: decode tokens/s, plus the roofline of the dominant kernel (the single-launch
 layer, timed live with HIP events on its stream) and the CPU oracle's speed on a bounded sample.
 Alongside (not the headline value): per-launch times of the layer split in three kernels, a 32-token batched step
-and a 128-token prefill chunk through the same stack (grouped products on the matrix cores), and the same
-stack served from pinned host memory through 16-slot LFU expert caches (hit rates, host-to-device rate
+and a 128-token prefill chunk through the same stack (grouped products on the matrix cores), the same 4-bit
+row routine as one LM-head-sized GEMV (262,144 x 2816), and the same stack served from pinned host memory through 16-slot LFU expert caches (hit rates, host-to-device rate
 against a plain pinned copy).
 """
 from __future__ import annotations
@@ -208,6 +208,31 @@ def measure_batched(shape, layers, cfg, tokens, steps, warmup, T=32):
     return {"tokens_per_step": T, "tok_s": round(T / step_s, 1), "ms_per_step": round(step_s * 1e3, 4),
             "per_layer_us": round(step_s / len(layers) * 1e6, 2), "distinct_experts_per_layer": round(mean_distinct, 1),
             "weight_bytes_per_step": nbytes, "achieved_GBps": round(nbytes / step_s / 1e9, 1)}
+
+
+def measure_lm_head(steps=10, reps=10):
+    """q4_gemv (the experts' 4-bit row routine as a plain matrix GEMV) at LM-head scale: 262,144 rows (a
+    vocabulary) x 2816, bf16 scale/bias, one bf16 token, seeded random codes; graph-timed on its stream."""
+    import torch
+    from bit_quantized_expert_int8_amd import moeq4 as q
+
+    N, K = 262144, 2816
+    g = torch.Generator(device="cuda").manual_seed(5)
+    codes = torch.randint(0, 2**31 - 1, (N, K // 8), dtype=torch.int32, device="cuda", generator=g)
+    sb = (torch.rand((N, K // 64, 2), device="cuda", generator=g) * 0.01).to(torch.bfloat16)
+    x = torch.randn((1, K), device="cuda", generator=g).to(torch.bfloat16)
+    y = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+
+    def calls():
+        for _ in range(steps):
+            q.q4_gemv(x, q.MOE_BF16, 1, codes, sb, q.MOE_BF16, N, K, y, stream)
+
+    t = time_graph(calls, reps, stream) / steps
+    nbytes = N * (K // 2) + N * (K // 64) * 4
+    return {"rows": N, "cols": K, "us_per_call": round(t * 1e6, 2), "weight_bytes": nbytes,
+            "achieved_GBps": round(nbytes / t / 1e9, 1), "frac_of_8TBps": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def measure_streamed(shape, layers, cfg, dec, n_tokens):
@@ -407,6 +432,7 @@ def main():
     if not args.no_extras:
         out["batched"] = measure_batched(shape, layers, cfg, tokens.reshape(n_tok, cfg.d), 20, 3)
         out["prefill_chunk_128"] = measure_batched(shape, layers, cfg, tokens.reshape(n_tok, cfg.d), 8, 2, T=128)
+        out["lm_head_q4_gemv"] = measure_lm_head()
         out["streamed"] = measure_streamed(shape, layers, cfg, dec, args.stream_tokens)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_layers, args.cpu_repeats)
