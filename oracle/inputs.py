@@ -14,16 +14,26 @@ import synth
 from . import moe
 
 
+def expert_weights(cfg: synth.MoEConfig, layer: int, e: int, threads: int = 0):
+    """fp32 gate_up [2F][d] and down [d][F] of routed expert e (before quantization)."""
+    wgu = synth.weight_f32(cfg.weight_cfg, layer, synth.TAG_GATE_UP, e, 2 * cfg.F, cfg.d, threads=threads)
+    wd = synth.weight_f32(cfg.weight_cfg, layer, synth.TAG_DOWN, e, cfg.d, cfg.F, threads=threads)
+    return wgu, wd
+
+
+def shared_weights(cfg: synth.MoEConfig, layer: int, threads: int = 0):
+    """fp32 gate_up [2S][d] and down [d][S] of the shared expert (before quantization)."""
+    wgu = synth.weight_f32(cfg.weight_cfg, layer, synth.TAG_SHARED_GATE_UP, 0, 2 * cfg.S, cfg.d, threads=threads)
+    wd = synth.weight_f32(cfg.weight_cfg, layer, synth.TAG_SHARED_DOWN, 0, cfg.d, cfg.S, threads=threads)
+    return wgu, wd
+
+
 def expert_record(cfg: synth.MoEConfig, layer: int, e: int) -> np.ndarray:
-    wgu = synth.weight_f32(cfg.weight_cfg, layer, synth.TAG_GATE_UP, e, 2 * cfg.F, cfg.d)
-    wd = synth.weight_f32(cfg.weight_cfg, layer, synth.TAG_DOWN, e, cfg.d, cfg.F)
-    return moe.encode_record(wgu, wd, cfg.sb_bf16)
+    return moe.encode_record(*expert_weights(cfg, layer, e), cfg.sb_bf16)
 
 
 def shared_record(cfg: synth.MoEConfig, layer: int) -> np.ndarray:
-    wgu = synth.weight_f32(cfg.weight_cfg, layer, synth.TAG_SHARED_GATE_UP, 0, 2 * cfg.S, cfg.d)
-    wd = synth.weight_f32(cfg.weight_cfg, layer, synth.TAG_SHARED_DOWN, 0, cfg.d, cfg.S)
-    return moe.encode_record(wgu, wd, cfg.sb_bf16)
+    return moe.encode_record(*shared_weights(cfg, layer), cfg.sb_bf16)
 
 
 def oracle_layer(cfg: synth.MoEConfig, layer: int, cache_experts: int = 16, gamma_ones: bool = True) -> moe.OracleLayer:

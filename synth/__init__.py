@@ -25,7 +25,10 @@ the configured shapes stand in for it.
 """
 from __future__ import annotations
 
+import ctypes
 import dataclasses
+import os
+
 import numpy as np
 
 GOLDEN_GAMMA = np.uint64(0x9E3779B97F4A7C15)
@@ -70,8 +73,38 @@ def draws(seed: int, start: int, count: int) -> np.ndarray:
         return _mix(np.uint64(seed) + i * GOLDEN_GAMMA)
 
 
-def normals_f32(seed: int, start: int, count: int, sigma: float = 1.0, chunk: int = 1 << 21) -> np.ndarray:
-    """Irwin-Hall(12) normals number start .. start+count-1 of a stream, as fp32 (bit-exact spec)."""
+_HOST_LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsynth_host.so")
+_host = None
+
+
+def _host_lib():
+    """The C twin of this generator (synth_host.c, built by the package's build step), or None."""
+    global _host
+    if _host is None and os.path.exists(_HOST_LIB):
+        lib = ctypes.CDLL(_HOST_LIB)
+        lib.synth_host_normals_f32.restype = None
+        lib.synth_host_normals_f32.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_float,
+                                               ctypes.c_void_p, ctypes.c_int]
+        _host = lib
+    return _host
+
+
+def normals_f32(seed: int, start: int, count: int, sigma: float = 1.0, chunk: int = 1 << 21,
+                threads: int = 0) -> np.ndarray:
+    """Irwin-Hall(12) normals number start .. start+count-1 of a stream, as fp32 (bit-exact spec).
+
+    Drawn by the C twin (``synth_host.c``, same definition, ``threads`` OpenMP threads, 0 = all) when it
+    is built, else by ``normals_f32_numpy``; the two agree bit for bit."""
+    lib = _host_lib()
+    if lib is None or count == 0:
+        return normals_f32_numpy(seed, start, count, sigma, chunk)
+    out = np.empty(count, dtype=np.float32)
+    lib.synth_host_normals_f32(seed, start, count, sigma, out.ctypes.data, threads)
+    return out
+
+
+def normals_f32_numpy(seed: int, start: int, count: int, sigma: float = 1.0, chunk: int = 1 << 21) -> np.ndarray:
+    """The generator's definition in numpy (see normals_f32)."""
     out = np.empty(count, dtype=np.float32)
     scale = np.float32(np.float32(sigma) * np.float32(2.0 ** -16))
     mask = np.uint64(0xFFFF)
@@ -111,9 +144,9 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 # ----------------------------------------------------------------------------------------------
 
 def weight_f32(cfg: int, layer: int, tag: int, index: int, rows: int, cols: int,
-               sigma: float = SIGMA_WEIGHTS) -> np.ndarray:
+               sigma: float = SIGMA_WEIGHTS, threads: int = 0) -> np.ndarray:
     """fp32 [rows][cols] N(0, sigma) weights of one expert matrix (row-major draw order)."""
-    return normals_f32(stream_seed(cfg, layer, tag, index), 0, rows * cols, sigma).reshape(rows, cols)
+    return normals_f32(stream_seed(cfg, layer, tag, index), 0, rows * cols, sigma, threads=threads).reshape(rows, cols)
 
 
 def router_int8(cfg: int, layer: int, n_experts: int, d: int):

@@ -383,3 +383,86 @@ def test_group_pairs_brute_force_and_invariants():
         bs = [bucket_of[q] for q in p.tolist()]
         assert bs == sorted(bs)
         assert np.array_equal(np.bincount(bs, minlength=n + 1), np.bincount(bucket_of, minlength=n + 1))
+
+
+# ---------------------------------------------------------------------------------------------
+# the C expert FFN (oracle/fast.py) against the numpy definition, and the many-token evaluator
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("sb_bf16", [False, True])
+def test_c_quantizer_equals_numpy_bit_for_bit(sb_bf16):
+    from oracle import fast
+    w = synth.normals_f32(synth.stream_seed(7, 1, synth.TAG_GATE_UP, 3), 0, 96 * 256, 0.02).reshape(96, 256)
+    w[3, :64] = 0.25                                     # constant group: scale 0, codes 0
+    w[4, 64:128] = (0.5 * (np.arange(64) % 16) - 2.0)    # exact grid with ties at half steps
+    w[5, 128:192] = np.linspace(-1, 1, 64) ** 3
+    c1, s1, b1 = fast.quantize_q4(w, sb_bf16)
+    c2, s2, b2 = moe.quantize_affine_q4(w, sb_bf16)
+    assert np.array_equal(c1, c2)
+    assert np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+    assert np.array_equal(b1.view(np.uint32), b2.view(np.uint32))
+
+
+@pytest.mark.parametrize("act", [moe.ACT_GELU_TANH, moe.ACT_SILU])
+def test_c_expert_ffn_equals_numpy(act):
+    from oracle import fast
+    cfg = synth.TINY
+    U = np.stack([oin.token_input(cfg, t) for t in range(5)] + [np.zeros(cfg.d)])
+    for e in (0, 5):
+        wgu, wd = oin.expert_weights(cfg, 0, e)
+        ex = moe.decode_record(moe.encode_record(wgu, wd, cfg.sb_bf16), cfg.d, cfg.F, cfg.sb_bf16)
+        y, h = fast.expert_ffn_rows(wgu, wd, cfg.sb_bf16, U, act, want_h=True)
+        for t in range(len(U)):
+            ref = moe.expert_ffn(ex, U[t], act)
+            assert np.allclose(y[t], ref, rtol=0, atol=1e-12 * max(np.abs(ref).max(), 1e-300))
+            assert np.allclose(h[t], moe.expert_hidden(ex, U[t], act), rtol=0, atol=1e-12 * np.abs(h[t]).max() + 1e-300)
+        assert np.all(y[-1] == 0.0)                       # x = 0 -> y = 0 exactly
+
+
+def test_c_expert_ffn_lossless_grid_equals_loops():
+    # weights on the quantizer's grid, so the encoding is lossless: the C FFN must equal explicit loops over
+    # the fp32 weights (a computation that never sees the encoder)
+    from oracle import fast
+    rng = np.random.default_rng(1)
+    d, F = 128, 64
+    wgu, wd = _grid_weights(rng, 2 * F, d), _grid_weights(rng, d, F)
+    u = rng.standard_normal(d)
+    y = fast.expert_ffn_rows(wgu, wd, True, u[None, :], moe.ACT_SILU)[0]
+    h = []
+    for j in range(F):
+        g = sum(float(wgu[j, c]) * u[c] for c in range(d))
+        v = sum(float(wgu[F + j, c]) * u[c] for c in range(d))
+        h.append(g * scipy.special.expit(g) * v)
+    expect = [sum(float(wd[r, j]) * h[j] for j in range(F)) for r in range(d)]
+    assert np.allclose(y, expect, rtol=1e-12, atol=1e-12)
+
+
+def test_layer_tokens_equals_moe_layer_tiny(tiny_layer):
+    from oracle import fast
+    cfg = synth.TINY
+    X = np.stack([oin.token_input(cfg, t) for t in range(6)])
+    ids = np.stack([moe.select_topk(moe.router_logits(tiny_layer.router_w, tiny_layer.router_s, X[t]), cfg.k)
+                    for t in range(6)])
+    ids[2] = [7, 0]                                       # a forced selection in the middle
+    res = fast.layer_tokens(cfg, 0, X, ids, threads=3)
+    for t in range(6):
+        ref = moe.moe_layer(tiny_layer, X[t], cfg.k, forced_ids=ids[t])
+        assert np.array_equal(res[t].ids, ref.ids)
+        assert np.allclose(res[t].weights, ref.weights, rtol=0, atol=1e-15)
+        assert np.allclose(res[t].out, ref.out, rtol=0, atol=1e-12 * np.abs(ref.out).max())
+        assert np.array_equal(res[t].x_next, res[t].out)  # fp32 configuration: no output rounding
+
+
+def test_layer_tokens_equals_stack_step_full_size():
+    """One token through one full-size stacked layer (d=2816, 128 experts top-8, shared 2816, RMSNorm +
+    residual, bf16): the many-token evaluator equals moe.stack_layer_step (numpy) on the same routing."""
+    from oracle import fast
+    cfg = synth.STACK
+    orc = oin.oracle_layer(cfg, 3, cache_experts=8)
+    x = oin.token_input(cfg, 11)
+    u, ref, x_next = moe.stack_layer_step(orc, x, cfg.k)
+    res = fast.layer_tokens(cfg, 3, x[None, :], ref.ids[None, :])[0]
+    assert np.array_equal(res.u, u)
+    assert np.allclose(res.logits, ref.logits, rtol=0, atol=1e-12)
+    assert np.allclose(res.out, ref.out, rtol=0, atol=1e-12 * np.abs(ref.out).max())
+    assert np.array_equal(res.x_next, x_next)

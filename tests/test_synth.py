@@ -87,3 +87,12 @@ def test_configs():
     assert c["stack"].n_layers == 30 and c["stack"].n_tokens == 256 and c["stack"].rms_norm
     assert c["batched"].weight_cfg == c["layer"].weight_cfg and c["batched"].n_tokens == 32
     assert c["streamed"].weight_cfg == c["stack"].weight_cfg and c["streamed"].n_slots == 16
+
+
+def test_host_c_generator_equals_numpy_definition():
+    # the C twin (synth_host.c) and the numpy definition draw the same bits, at any offset and thread count
+    s = synth.stream_seed(2, 29, synth.TAG_DOWN, 127)
+    for start, n, threads in [(0, 1000, 1), (123457, 65537, 0), (3, 1 << 20, 3)]:
+        a = synth.normals_f32(s, start, n, 0.02, threads=threads)
+        b = synth.normals_f32_numpy(s, start, n, 0.02)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
