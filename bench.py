@@ -299,6 +299,7 @@ def measure_streamed(shape, layers, cfg, dec, n_tokens):
                 x = out
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        dec.check_status()
         hits, misses, nbytes = q.moe_expert_cache_stats(cache, -1)
     finally:
         q.moe_expert_cache_destroy(cache)
@@ -399,6 +400,7 @@ def main():
     wall = time.perf_counter() - t0
     gpu_s = e0.elapsed_time(e1) * 1e-3
     tok_s = args.steps / gpu_s
+    dec.check_status()      # every bounded wait inside the timed launches completed
 
     if args.calibration_copy_mib:
         src = torch.empty(args.calibration_copy_mib << 20, dtype=torch.uint8, device="cuda")
@@ -407,6 +409,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     dur, launches = time_layer_kernel(dec, xin, args.roofline_reps)
+    dec.check_status()
     nbytes = layer_bytes(cfg)
     achieved = nbytes / dur / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -3,9 +3,10 @@
 // The pages keep 16 expert slots per layer under a least-frequently-used policy and fetch the missing
 // experts while the shared expert computes.  Here the slow tier is pinned host memory; each miss is one
 // hipMemcpyAsync of a whole expert record on the caller's copy stream, ordered after `wait_event` (the
-// last kernel that read this layer's slots) and followed by `ready_event`.  Slot ids reach the device
-// through the arguments of a one-wave kernel on the copy stream, so no host staging buffer has to live
-// until the copy ends.
+// last kernel that read this layer's slots and slot ids) and followed by `ready_event`.  Slot ids reach the
+// device by one more copy on the same stream, from an entry of a pinned ring the handle owns: the copy
+// engine never switches to a kernel between a layer's record copies.  Each ring entry carries an event
+// recorded after its copy, and an entry is rewritten only once that event has completed.
 #include <string.h>
 
 #include <new>
@@ -28,20 +29,28 @@ struct moe_expert_cache {
   std::vector<char*> slot_pool;
   std::vector<Layer> layers;
   int32_t fail_after = -1;
+  // pinned staging ring for slot ids (device mode only)
+  int32_t* ring = nullptr;          // [kRing][kMaxIds]
+  std::vector<hipEvent_t> ring_ev;  // recorded after the copy out of each entry
+  std::vector<char> ring_used;
+  int ring_pos = 0;
 };
 
 namespace moeq4 {
 namespace {
 
 constexpr int kMaxIds = 32;
+constexpr int kRing = 1024;   // slot-id entries in flight before the host waits for the oldest copy
 
-struct SlotIds {
-  int32_t v[kMaxIds];
-  int32_t n;
-};
-
-__global__ void write_slot_ids(int32_t* dst, SlotIds ids) {
-  if ((int)threadIdx.x < ids.n) dst[threadIdx.x] = ids.v[threadIdx.x];
+void release_ring(moe_expert_cache* c) {
+  for (size_t i = 0; i < c->ring_ev.size(); ++i) {
+    if (c->ring_used[i]) (void)hipEventSynchronize(c->ring_ev[i]);
+    (void)hipEventDestroy(c->ring_ev[i]);
+  }
+  c->ring_ev.clear();
+  c->ring_used.clear();
+  if (c->ring) (void)hipHostFree(c->ring);
+  c->ring = nullptr;
 }
 
 // The policy step on a copy of the layer state.  Fills slot_of[i] for each requested id and the list of
@@ -120,11 +129,36 @@ extern "C" moe_status moe_expert_cache_create(int32_t n_layers, int32_t n_expert
     L.count.assign(n_slots, 0);
     L.last.assign(n_slots, -1);
   }
+  if (!(flags & MOE_CACHE_HOST_ONLY)) {
+    hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&c->ring), (size_t)kRing * kMaxIds * sizeof(int32_t),
+                                 hipHostMallocDefault);
+    if (e != hipSuccess) {
+      c->ring = nullptr;
+      delete c;
+      return fail(MOE_ERR_HIP, "moe_expert_cache_create: hipHostMalloc of the slot-id ring: %s", hipGetErrorString(e));
+    }
+    c->ring_ev.reserve(kRing);
+    for (int i = 0; i < kRing && e == hipSuccess; ++i) {
+      hipEvent_t ev = nullptr;
+      e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+      if (e == hipSuccess) c->ring_ev.push_back(ev);
+    }
+    c->ring_used.assign(c->ring_ev.size(), 0);
+    if (e != hipSuccess) {
+      release_ring(c);
+      delete c;
+      return fail(MOE_ERR_HIP, "moe_expert_cache_create: hipEventCreate: %s", hipGetErrorString(e));
+    }
+  }
   *out = c;
   return MOE_OK;
 }
 
-extern "C" void moe_expert_cache_destroy(moe_expert_cache* cache) { delete cache; }
+extern "C" void moe_expert_cache_destroy(moe_expert_cache* cache) {
+  if (!cache) return;
+  release_ring(cache);
+  delete cache;
+}
 
 extern "C" moe_status expert_cache_stage(moe_expert_cache* c, int32_t layer, const int32_t* ids_host, int32_t n,
                                          int32_t* slot_ids_dev, void* copy_stream, void* wait_event, void* ready_event) {
@@ -146,7 +180,10 @@ extern "C" moe_status expert_cache_stage(moe_expert_cache* c, int32_t layer, con
   int hits = 0;
   lfu_plan(next, c->n_slots, ids_host, n, slot_of, loads, &hits);
 
-  if (!host_only && wait_event && !loads.empty()) {
+  // Every write below (record copies and the slot ids) waits for the last reader of this layer's slots and
+  // slot ids, also when every id hits: a caller that runs ahead of the device may stage the next token while
+  // the previous token's kernel still reads slot_ids_dev.
+  if (!host_only && wait_event) {
     hipError_t e = hipStreamWaitEvent(cs, reinterpret_cast<hipEvent_t>(wait_event), 0);
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "expert_cache_stage: hipStreamWaitEvent: %s", hipGetErrorString(e));
   }
@@ -175,11 +212,21 @@ extern "C" moe_status expert_cache_stage(moe_expert_cache* c, int32_t layer, con
     if (host_only) {
       memcpy(slot_ids_dev, slot_of, (size_t)n * sizeof(int32_t));
     } else {
-      SlotIds a{};
-      for (int i = 0; i < n; ++i) a.v[i] = slot_of[i];
-      a.n = n;
-      hipLaunchKernelGGL(write_slot_ids, dim3(1), dim3(64), 0, cs, slot_ids_dev, a);
-      st = check_launch("expert_cache_stage(slot ids)");
+      const int pos = c->ring_pos;
+      hipError_t e = hipSuccess;
+      if (c->ring_used[pos]) e = hipEventSynchronize(c->ring_ev[pos]);   // the entry's previous copy has run
+      int32_t* entry = c->ring + (size_t)pos * kMaxIds;
+      if (e == hipSuccess) {
+        memcpy(entry, slot_of, (size_t)n * sizeof(int32_t));
+        e = hipMemcpyAsync(slot_ids_dev, entry, (size_t)n * sizeof(int32_t), hipMemcpyHostToDevice, cs);
+      }
+      if (e == hipSuccess) e = hipEventRecord(c->ring_ev[pos], cs);
+      if (e != hipSuccess) {
+        st = fail(MOE_ERR_HIP, "expert_cache_stage: slot ids: %s", hipGetErrorString(e));
+      } else {
+        c->ring_used[pos] = 1;
+        c->ring_pos = (pos + 1) % (int)c->ring_ev.size();
+      }
       if (st == MOE_OK && ready_event) {
         hipError_t e = hipEventRecord(reinterpret_cast<hipEvent_t>(ready_event), cs);
         if (e != hipSuccess) st = fail(MOE_ERR_HIP, "expert_cache_stage: hipEventRecord: %s", hipGetErrorString(e));

@@ -100,6 +100,7 @@ struct LayerArgs {
   int32_t* ids_out;
   float* weights_out;
   float* logits_out;
+  void* u_out;         // the normalized activation [d] in the activation dtype, or NULL
   void* out;
   int32_t x_ws, out_ws;    // activations exchanged through the workspace, in the activation dtype and read
                            // and written coherently (the layers between the first input and the last
@@ -318,6 +319,15 @@ __device__ __forceinline__ void norm_to_lds(const LayerArgs& a, float* u, NormLd
   }
 }
 
+// u[0..d) (LDS, values already rounded to the activation dtype) to a.u_out, by the whole block
+template <typename XT>
+__device__ __forceinline__ void write_u(const LayerArgs& a, const float* u) {
+  for (int j = threadIdx.x; j < a.d; j += kThreads) {
+    if (sizeof(XT) == 2) reinterpret_cast<uint16_t*>(a.u_out)[j] = (uint16_t)(__float_as_uint(u[j]) >> 16);
+    else reinterpret_cast<float*>(a.u_out)[j] = u[j];
+  }
+}
+
 // ------------------------------------------------------------------------------------------------
 // routing inside a block
 // ------------------------------------------------------------------------------------------------
@@ -450,6 +460,7 @@ __device__ __forceinline__ void router_block(const LayerArgs& a, int b, float* u
   const float rse = a.rs[__builtin_amdgcn_readfirstlane(e < a.E ? e : a.E - 1)];
   if (a.prev_x.base) wait_set(a.prev_x, blockIdx.x, a.tag, a.status);
   norm_to_lds<XT>(a, u, nl);
+  if (b == 0 && a.u_out && !a.has_shared) write_u<XT>(a, u);
   if (e < a.E) {
     float acc = 0.f;
     // three pieces at a time: their LDS reads are issued together
@@ -803,6 +814,7 @@ struct StackLayer {           // what differs between the layers of a launch
   int32_t* ids_out;
   float* weights_out;
   float* logits_out;
+  void* u_out;
 };
 
 struct WsLayout {
@@ -845,6 +857,7 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(const StackArgs 
   a.ids_out = L.ids_out;
   a.weights_out = L.weights_out;
   a.logits_out = L.logits_out;
+  a.u_out = L.u_out;
   char* ws = sa.ws + (int64_t)l * sa.w.total;
   a.x = l == 0 ? sa.x_in : static_cast<const void*>(ws - sa.w.total + sa.w.x_next);
   a.x_ws = l > 0;
@@ -898,6 +911,7 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(const StackArgs 
       // the shared expert needs only x: the norm (whose loads go out with the router's), then its code words
       if (a.prev_x.base) wait_set(a.prev_x, blockIdx.x, a.tag, a.status);
       norm_to_lds<XT>(a, u, nl);
+      if (b == 0 && a.u_out) write_u<XT>(a, u);   // off the routing path: the first shared gate/up block
       GuRegs<NBW, SB_BF16> g;
       gu_load<NBW, SB_BF16>(a, a.shared, 0, true, b, g);
       gu_finish<NBW, SB_BF16>(a, g, true, b, a.h_shared, a.shared_h, a.nSG, u, stage_for(a.d));
@@ -1079,12 +1093,13 @@ extern "C" moe_status moe_decode_layer(const void* x_dev, moe_dtype x_dtype, con
                                        int32_t residual, const int8_t* router_w_dev, const float* router_scale_dev,
                                        int32_t E, int32_t k, const int32_t* forced_ids_dev, const moe_q4_pool* routed,
                                        const int32_t* gemv_ids_dev, const moe_q4_pool* shared, moe_act act,
-                                       int32_t* ids_dev, float* weights_dev, float* logits_dev, void* out_dev,
-                                       void* workspace_dev, size_t workspace_bytes, void* stream) {
+                                       int32_t* ids_dev, float* weights_dev, float* logits_dev, void* u_dev,
+                                       void* out_dev, void* workspace_dev, size_t workspace_bytes, void* stream) {
   const char* who = "moe_decode_layer";
   if (!router_w_dev || !router_scale_dev) return fail(MOE_ERR_INVALID_ARG, "%s: NULL pointer", who);
   if (!aligned(router_w_dev, 16) || (gamma_dev && !aligned(gamma_dev, 16)))
     return fail(MOE_ERR_INVALID_ARG, "%s: router weights and gamma must be 16-byte aligned", who);
+  if (u_dev && (u_dev == x_dev || u_dev == out_dev)) return fail(MOE_ERR_INVALID_ARG, "%s: u must not alias x or out", who);
   StackArgs sa{};
   int nbw = 0;
   size_t lds = 0;
@@ -1095,7 +1110,7 @@ extern "C" moe_status moe_decode_layer(const void* x_dev, moe_dtype x_dtype, con
   sa.base.gemv_ids = gemv_ids_dev;
   sa.layer[0] = StackLayer{router_w_dev, router_scale_dev, gamma_dev, static_cast<const char*>(routed->base_dev),
                            shared ? static_cast<const char*>(shared->base_dev) : nullptr, ids_dev, weights_dev,
-                           logits_dev};
+                           logits_dev, u_dev};
   return launch(sa, x_dtype, routed->sb_dtype == MOE_BF16, nbw, lds, as_stream(stream), who);
 }
 
@@ -1127,7 +1142,8 @@ extern "C" moe_status moe_decode_stack(const moe_stack_layer* layers_host, int32
   for (int l = 0; l < n_layers; ++l) {
     const moe_stack_layer& L = layers_host[l];
     sa.layer[l] = StackLayer{L.router_w_dev, L.router_scale_dev, L.gamma_dev, static_cast<const char*>(L.routed_base_dev),
-                             static_cast<const char*>(L.shared_base_dev), L.ids_dev, L.weights_dev, L.logits_dev};
+                             static_cast<const char*>(L.shared_base_dev), L.ids_dev, L.weights_dev, L.logits_dev,
+                             L.u_dev};
   }
   return launch(sa, x_dtype, routed->sb_dtype == MOE_BF16, nbw, lds, as_stream(stream), who);
 }

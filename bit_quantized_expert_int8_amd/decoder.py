@@ -86,7 +86,8 @@ class MoEDecoder:
       "separate"  moe_rmsnorm, moe_router_topk, q4_expert_gemv, moe_combine
     "fused" and "separate" give the same routing and, on the same normalized input, the same output bits."""
 
-    def __init__(self, shape: Shape, layers: list, T: int = 1, device="cuda", mode: Optional[str] = None):
+    def __init__(self, shape: Shape, layers: list, T: int = 1, device="cuda", mode: Optional[str] = None,
+                 record_u: bool = False):
         self.shape, self.layers, self.T = shape, layers, T
         if mode is None:
             mode = "layer" if layer_kernel_fits(shape, T) else "fused"
@@ -107,6 +108,8 @@ class MoEDecoder:
         self.weights_all = torch.empty((L, T, s.k), dtype=torch.float32, device=device)
         self.logits_all = torch.empty((L, T, s.n_experts), dtype=torch.float32, device=device)
         self.ids, self.weights, self.logits = self.ids_all[0], self.weights_all[0], self.logits_all[0]
+        # with record_u, the single-launch modes also keep every layer's normalized activation (the last token's)
+        self.u_all = torch.empty((L, T, s.d), dtype=xdt, device=device) if record_u else None
         self.y_routed = torch.empty((T, s.k, s.d), dtype=torch.float32, device=device)
         self.y_shared = torch.empty((T, s.d), dtype=torch.float32, device=device)
         self.router_ws_bytes = q.moe_router_workspace_bytes(T, s.n_experts)
@@ -129,7 +132,8 @@ class MoEDecoder:
             self.stack_descs = q.stack_layers([
                 {"router_w_dev": W.router_w, "router_scale_dev": W.router_s,
                  "gamma_dev": W.gamma if s.rms_norm else None, "routed_base_dev": W.pool, "shared_base_dev": W.shared,
-                 "ids_dev": self.ids_all[l], "weights_dev": self.weights_all[l], "logits_dev": self.logits_all[l]}
+                 "ids_dev": self.ids_all[l], "weights_dev": self.weights_all[l], "logits_dev": self.logits_all[l],
+                 "u_dev": None if self.u_all is None else self.u_all[l]}
                 for l, W in enumerate(layers)])
         self.graph = None
 
@@ -161,7 +165,8 @@ class MoEDecoder:
         q.moe_decode_layer(x_in, s.x_dtype, L.gamma if s.rms_norm else None, s.eps, s.rms_norm, L.router_w, L.router_s,
                            s.n_experts, s.k, forced_ids, routed_pool or self.routed_pools[l], ids,
                            self.shared_pools[l], s.act, self.ids_all[l], self.weights_all[l], self.logits_all[l], x_out,
-                           self.layer_ws, self.layer_ws_bytes, stream)
+                           self.layer_ws, self.layer_ws_bytes, stream,
+                           u=None if self.u_all is None else self.u_all[l])
 
     def _layer_fused(self, l, x_in, x_out, forced_ids, routed_pool, ids, stream) -> None:
         s, L, T = self.shape, self.layers[l], self.T
@@ -196,6 +201,24 @@ class MoEDecoder:
             dst = bufs[l % 2]
             self.layer(l, src, dst, stream=stream)
             src = dst
+
+    def status(self) -> int:
+        """The sticky error word of the single-launch kernels' workspace (0 = every bounded wait inside them
+        completed; nonzero = a wait ran out and the results of that call are invalid).  Synchronizes."""
+        if self.mode == "stack":
+            ws = self.stack_ws
+        elif self.mode == "layer":
+            ws = self.layer_ws
+        else:
+            return 0
+        torch.cuda.synchronize()
+        return int(ws[:4].view(torch.int32).item())
+
+    def check_status(self) -> None:
+        """Raise if a bounded wait inside the single-launch kernels ran out since the workspace was zeroed."""
+        st = self.status()
+        if st:
+            raise RuntimeError(f"MoE decode kernel: a bounded wait ran out (status word {st:#x}); results are invalid")
 
     def capture(self, x: torch.Tensor, out: torch.Tensor) -> torch.cuda.CUDAGraph:
         """Capture one whole-stack step into a HIP graph (replay with graph.replay())."""

@@ -41,7 +41,8 @@ class moe_q4_pool(ctypes.Structure):
 
 class moe_stack_layer(ctypes.Structure):
     _fields_ = [("router_w_dev", _vp), ("router_scale_dev", _vp), ("gamma_dev", _vp), ("routed_base_dev", _vp),
-                ("shared_base_dev", _vp), ("ids_dev", _vp), ("weights_dev", _vp), ("logits_dev", _vp)]
+                ("shared_base_dev", _vp), ("ids_dev", _vp), ("weights_dev", _vp), ("logits_dev", _vp),
+                ("u_dev", _vp)]
 
 
 class MoeError(RuntimeError):
@@ -89,7 +90,7 @@ _c = {
     "moe_decode_layer": _sig("moe_decode_layer", _st,
                              [_vp, ctypes.c_int, _vp, ctypes.c_float, _i32, _vp, _vp, _i32, _i32, _vp,
                               ctypes.POINTER(moe_q4_pool), _vp, ctypes.POINTER(moe_q4_pool), ctypes.c_int, _vp, _vp,
-                              _vp, _vp, _vp, _sz, _vp]),
+                              _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_decode_stack_workspace_bytes": _sig("moe_decode_stack_workspace_bytes", _sz,
                                              [_i32, _i32, _i32, _i32, _i32, _i32]),
     "moe_decode_stack": _sig("moe_decode_stack", _st,
@@ -247,10 +248,11 @@ def moe_decode_layer_sync_bytes(d, k) -> int:
 
 
 def moe_decode_layer(x, x_dtype, gamma, eps, residual, router_w, router_scale, E, k, forced_ids, routed, gemv_ids,
-                     shared, act, ids, weights, logits, out, workspace, workspace_bytes, stream=None) -> None:
+                     shared, act, ids, weights, logits, out, workspace, workspace_bytes, stream=None, u=None) -> None:
     _check(_c["moe_decode_layer"](_p(x), x_dtype, _p(gamma), eps, int(residual), _p(router_w), _p(router_scale), E, k,
                                   _p(forced_ids), _pp(routed), _p(gemv_ids), _pp(shared), act, _p(ids), _p(weights),
-                                  _p(logits), _p(out), _p(workspace), workspace_bytes, _s(stream)), "moe_decode_layer")
+                                  _p(logits), _p(u), _p(out), _p(workspace), workspace_bytes, _s(stream)),
+           "moe_decode_layer")
 
 
 def moe_decode_stack_workspace_bytes(n_layers, d, E, k, F, S) -> int:

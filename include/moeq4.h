@@ -264,7 +264,8 @@ moe_status q4_expert_gemv_combine(const moe_q4_pool* routed, const int32_t* ids_
  * router as moe_router_topk; forced_ids_dev: int32 [k] or NULL; routed: pool of experts, indexed by the
  * selected ids, or by gemv_ids_dev[i] (int32 [k], e.g. cache slots from expert_cache_stage) when that is
  * non-NULL; shared: pool whose record 0 is the shared expert, or NULL; ids_dev / weights_dev / logits_dev:
- * optional outputs (int32 [k], fp32 [k], fp32 [E]).
+ * optional outputs (int32 [k], fp32 [k], fp32 [E]); u_dev: optional output x_dtype [d], the normalized
+ * activation u that the router and the experts consumed (must not alias x or out).
  * Limits: d <= 4096, shared width <= 4096, routed F <= 1024, E <= 256, 1 <= k <= min(E, 32).
  * Workspace: moe_decode_layer_workspace_bytes(d, E, k, F, S) bytes (S = 0 without shared expert), 256-byte
  * aligned, ZERO before its first use, and used with one shape (d, E, k, F, S and shared or not).  Its first
@@ -282,8 +283,8 @@ moe_status moe_decode_layer(const void* x_dev, moe_dtype x_dtype, const float* g
                             const int8_t* router_w_dev, const float* router_scale_dev, int32_t E, int32_t k,
                             const int32_t* forced_ids_dev, const moe_q4_pool* routed, const int32_t* gemv_ids_dev,
                             const moe_q4_pool* shared, moe_act act, int32_t* ids_dev, float* weights_dev,
-                            float* logits_dev, void* out_dev, void* workspace_dev, size_t workspace_bytes,
-                            void* stream);
+                            float* logits_dev, void* u_dev, void* out_dev, void* workspace_dev,
+                            size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------------
  * moe_decode_stack — n_layers consecutive layers of moe_decode_layer for one token in a single launch
@@ -295,8 +296,8 @@ moe_status moe_decode_layer(const void* x_dev, moe_dtype x_dtype, const float* g
  * must stay valid until the work completes).  routed / shared: the pools' shape (d, F, record_bytes,
  * n_records, sb_dtype; base_dev is ignored, every layer gives its own); shared may be NULL.
  * x_dev: x_dtype [d] input of layer 0; out_dev: x_dtype [d] output of the last layer (must not alias x_dev).
- * Per layer: router as moe_router_topk; gamma_dev fp32 [d] or NULL (no norm); ids/weights/logits optional
- * outputs.  Limits as moe_decode_layer, and 1 <= n_layers <= 32.
+ * Per layer: router as moe_router_topk; gamma_dev fp32 [d] or NULL (no norm); ids/weights/logits/u optional
+ * outputs (u: the layer's normalized activation, x_dtype [d]).  Limits as moe_decode_layer, and 1 <= n_layers <= 32.
  * Workspace: moe_decode_stack_workspace_bytes(...) bytes, 256-byte aligned, ZERO before first use; the
  * region of layer l is moe_decode_layer_workspace_bytes(d, E, k, F, S) bytes at offset l times that size,
  * laid out as moe_decode_layer's (word 0 of the whole workspace is the sticky error flag), with the same
@@ -311,6 +312,7 @@ typedef struct {
   int32_t* ids_dev;                /* int32 [k] or NULL */
   float* weights_dev;              /* fp32 [k] or NULL */
   float* logits_dev;               /* fp32 [E] or NULL */
+  void* u_dev;                     /* x_dtype [d] or NULL: the normalized activation of this layer */
 } moe_stack_layer;
 
 size_t moe_decode_stack_workspace_bytes(int32_t n_layers, int32_t d, int32_t E, int32_t k, int32_t F, int32_t S);

@@ -33,15 +33,18 @@ def _ws(cfg, shared=True):
     return torch.zeros(b, dtype=torch.uint8, device="cuda"), b
 
 
-def _run(cfg, dev, shape, x, ws, ws_b, gamma, residual, forced=None, routed=None, gemv_ids=None, shared=True):
+def _run(cfg, dev, shape, x, ws, ws_b, gamma, residual, forced=None, routed=None, gemv_ids=None, shared=True, u=None,
+         k=None, router_w=None, router_s=None):
     rp, sp = _pools(cfg, dev, shape, shared)
-    ids = torch.full((cfg.k,), -5, dtype=torch.int32, device="cuda")
-    w = torch.empty((cfg.k,), dtype=torch.float32, device="cuda")
+    k = k or cfg.k
+    ids = torch.full((k,), -5, dtype=torch.int32, device="cuda")
+    w = torch.empty((k,), dtype=torch.float32, device="cuda")
     lg = torch.empty((cfg.n_experts,), dtype=torch.float32, device="cuda")
     out = torch.empty_like(x)
     xdt = q.MOE_BF16 if cfg.x_bf16 else q.MOE_F32
-    q.moe_decode_layer(x, xdt, gamma, 1e-6, residual, dev.router_w, dev.router_s, cfg.n_experts, cfg.k, forced,
-                       routed or rp, gemv_ids, sp, shape.act, ids, w, lg, out, ws, ws_b)
+    q.moe_decode_layer(x, xdt, gamma, 1e-6, residual, dev.router_w if router_w is None else router_w,
+                       dev.router_s if router_s is None else router_s, cfg.n_experts, k, forced,
+                       routed or rp, gemv_ids, sp, shape.act, ids, w, lg, out, ws, ws_b, u=u)
     return ids, w, lg, out
 
 
@@ -60,33 +63,43 @@ def _check_clean(ws, cfg, calls):
 
 @pytest.mark.parametrize("gamma_ones", [True, False])
 def test_decode_layer_vs_oracle(stack_layer, gamma_ones):
-    """One d=2816 layer (RMSNorm, router, 8 of 128 experts + shared, residual) on four tokens, one call
-    each on one workspace: routing valid for the oracle's logits on the norm output, weights the softmax
-    of those logits, output within the parity bar of the oracle run on the GPU's routing."""
+    """One d=2816 layer (RMSNorm, router, 8 of 128 experts + shared, residual) on eight tokens, one call
+    each on one workspace.  The kernel's own normalized activation u (its optional output) is within one
+    bf16 step of the oracle's; the oracle's router run on that u gives the kernel's logits within 1e-4 and
+    ranks them like the kernel (exact ids when the 8th/9th gap exceeds 1e-3); the gate weights are the
+    softmax of the logits; the output is within the parity bar of the oracle on the kernel's routing."""
     cfg, dev, shape = stack_layer
     gamma_np = synth.rms_gamma(cfg.weight_cfg, 0, cfg.d, ones=gamma_ones)
     gamma = torch.from_numpy(gamma_np).cuda()
-    orc = oin.oracle_layer(cfg, 0, cache_experts=24)
+    orc = oin.oracle_layer(cfg, 0, cache_experts=48)
     orc.gamma = gamma_np.astype(np.float64)
     ws, ws_b = _ws(cfg)
-    for call, tok in enumerate((0, 5, 77, 200), 1):
+    u_dev = torch.empty((cfg.d,), dtype=torch.bfloat16, device="cuda")
+    for call, tok in enumerate((0, 5, 77, 200, 31, 32, 129, 255), 1):
         x = H.token_batch(cfg, [tok])[0]
-        ids, w, lg, out = _run(cfg, dev, shape, x, ws, ws_b, gamma, 1)
+        ids, w, lg, out = _run(cfg, dev, shape, x, ws, ws_b, gamma, 1, u=u_dev)
         _check_clean(ws, cfg, call)
         x64 = H.to_f64(x)
         u_ref = moe.f64_round_to_bf16(moe.rms_norm(x64, orc.gamma, 1e-6))
-        ref_lg = moe.router_logits(orc.router_w, orc.router_s, u_ref)
+        u_gpu = H.to_f64(u_dev)
+        assert H.bf16_steps(u_gpu, u_ref) <= 1, f"token {tok}: u off by more than one bf16 step"
+        ref_lg = moe.router_logits(orc.router_w, orc.router_s, u_gpu)
         got_lg = lg.cpu().numpy().astype(np.float64)
-        assert np.abs(got_lg - ref_lg).max() <= 2e-2 * max(1.0, np.abs(ref_lg).max()), f"token {tok}"
+        assert np.abs(got_lg - ref_lg).max() <= 1e-4 * max(1.0, np.abs(ref_lg).max()), f"token {tok}"
         ids_np = ids.cpu().numpy()
-        assert H.topk_consistent(ids_np.tolist(), ref_lg, cfg.k, gap=5e-3), f"token {tok}: {ids_np}"
+        assert H.topk_consistent(ids_np.tolist(), ref_lg, cfg.k), f"token {tok}: {ids_np}"
         assert np.allclose(w.cpu().numpy(), moe.gate_weights(got_lg, ids_np), rtol=0, atol=1e-6)
         _, res, x_next = moe.stack_layer_step(orc, x64, cfg.k, forced_ids=ids_np)
         got = H.to_f64(out)
-        allowed = TOL * np.abs(res.out - x64).max() + 2.0 ** -8 * np.abs(x_next)
+        moe_max = np.abs(res.out - x64).max()
+        allowed = TOL * moe_max + H.bf16_ulp(x_next)
         worst = float((np.abs(got - x_next) / allowed).max())
-        print(f"layer kernel token {tok}: rel err {H.max_rel_err(got, x_next):.2e}, error / allowance {worst:.2f}")
-        assert H.max_rel_err(got, x_next) <= TOL and worst <= 1.0
+        err = H.max_rel_err(got, x_next)
+        net = H.net_err(got, x_next, moe_max)
+        print(f"layer kernel token {tok}: rel err {err:.2e}, error / allowance {worst:.2f}, MoE-branch error "
+              f"beyond one output rounding {net:.2e}")
+        assert err <= TOL and worst <= 1.0
+        assert net <= H.REGRESSION["layer_kernel"], f"token {tok}: {net:.2e} above the measured-error bound"
 
 
 def test_decode_layer_repeatable_on_one_workspace(stack_layer):
@@ -152,7 +165,7 @@ def test_decode_layer_tiny_no_norm_vs_oracle(shared):
         ref = moe.moe_layer(orc, u, cfg.k, forced_ids=ids.cpu().numpy())
         worst = max(worst, H.max_rel_err(H.to_f64(out), ref.out))
     print(f"tiny layer kernel (shared={shared}): max rel err {worst:.3e}")
-    assert worst <= TOL
+    assert worst <= TOL and worst <= H.REGRESSION["tiny_layer"]
 
 
 def test_decode_stack_equals_chained_layers():
@@ -195,3 +208,92 @@ def test_decode_stack_equals_chained_layers():
             seg = words[l * region // 4: l * region // 4 + n].cpu().numpy()
             bad = np.nonzero((seg != 0) & (seg != call))[0]
             assert bad.size == 0, f"layer {l}: synchronisation words left at {seg[bad[:8]]} (call {call})"
+
+
+# ---------------------------------------------------------------------------------------------------
+# the method's degenerate cases on the single-launch layer (small configuration: d=256, 8 experts)
+# ---------------------------------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def tiny_layer():
+    cfg = synth.TINY
+    return cfg, H.device_layer(cfg, 0), H.shape_of(cfg), oin.oracle_layer(cfg, 0)
+
+
+def test_decode_layer_zero_input(tiny_layer, stack_layer):
+    """x = 0: every logit is 0, so the first k ids in order are chosen with weights 1/k, and every expert
+    output is exactly zero; with the norm (eps > 0) u = 0 too and the output is the residual, 0."""
+    for cfg, dev, shape, gamma, residual in ((tiny_layer[0], tiny_layer[1], tiny_layer[2], None, 0),
+                                             (stack_layer[0], stack_layer[1], stack_layer[2],
+                                              torch.ones(stack_layer[0].d, device="cuda"), 1)):
+        ws, ws_b = _ws(cfg)
+        x = torch.zeros((cfg.d,), dtype=torch.bfloat16 if cfg.x_bf16 else torch.float32, device="cuda")
+        ids, w, lg, out = _run(cfg, dev, shape, x, ws, ws_b, gamma, residual)
+        _check_clean(ws, cfg, 1)
+        assert ids.cpu().tolist() == list(range(cfg.k))
+        assert np.all(lg.cpu().numpy() == 0.0)
+        assert np.allclose(w.cpu().numpy(), 1.0 / cfg.k, rtol=0, atol=1e-7)
+        assert torch.count_nonzero(out).item() == 0
+
+
+@pytest.mark.parametrize("k", [1, 8])
+def test_decode_layer_k_one_and_k_all(tiny_layer, k):
+    """k = 1: the arg-max expert with weight exactly 1.  k = E = 8: every expert, ranked by logit (a full
+    sort), weights the softmax over all logits (the textbook dense softmax MoE).  Both against the oracle."""
+    cfg, dev, shape, orc = tiny_layer
+    b = q.moe_decode_layer_workspace_bytes(cfg.d, cfg.n_experts, k, cfg.F, cfg.S)
+    ws = torch.zeros(b, dtype=torch.uint8, device="cuda")
+    worst = 0.0
+    for tok in range(6):
+        x = H.token_batch(cfg, [tok])[0]
+        ids, w, lg, out = _run(cfg, dev, shape, x, ws, b, None, 0, k=k)
+        torch.cuda.synchronize()
+        assert int(ws[:4].view(torch.int32).item()) == 0
+        u = oin.token_input(cfg, tok)
+        ref_lg = moe.router_logits(orc.router_w, orc.router_s, u)
+        ids_np, w_np = ids.cpu().numpy(), w.cpu().numpy()
+        assert H.topk_consistent(ids_np.tolist(), ref_lg, k)
+        if k == 1:
+            assert w_np[0] == 1.0
+        else:
+            assert sorted(ids_np.tolist()) == list(range(cfg.n_experts))
+            p = np.exp(ref_lg - ref_lg.max())
+            p /= p.sum()
+            assert np.allclose(w_np, p[ids_np], rtol=0, atol=1e-6)
+        ref = moe.moe_layer(orc, u, k, forced_ids=ids_np)
+        worst = max(worst, H.max_rel_err(H.to_f64(out), ref.out))
+    print(f"tiny layer kernel k={k}: max rel err {worst:.2e}")
+    assert worst <= TOL and worst <= H.REGRESSION["tiny_layer"]
+
+
+def test_decode_layer_exact_logit_tie(tiny_layer):
+    """Two experts with identical router rows and scales have bit-identical logits: the lower id ranks
+    first (the selection rule), in the kernel and in the oracle, with equal gate weights."""
+    cfg, dev, shape, orc = tiny_layer
+    rw = dev.router_w.clone()
+    rs = dev.router_s.clone()
+    rw[6] = rw[2]
+    rs[6] = rs[2]
+    rw_np, rs_np = rw.cpu().numpy(), rs.cpu().numpy()
+    seen_tie = 0
+    for tok in range(12):
+        x = H.token_batch(cfg, [tok])[0]
+        for k in (cfg.k, cfg.n_experts):
+            b = q.moe_decode_layer_workspace_bytes(cfg.d, cfg.n_experts, k, cfg.F, cfg.S)
+            ws = torch.zeros(b, dtype=torch.uint8, device="cuda")
+            ids, w, lg, out = _run(cfg, dev, shape, x, ws, b, None, 0, k=k, router_w=rw, router_s=rs)
+            torch.cuda.synchronize()
+            lg_np = lg.cpu().numpy()
+            assert lg_np[2] == lg_np[6]
+            ids_l = ids.cpu().tolist()
+            ref = moe.select_topk(moe.router_logits(rw_np, rs_np, oin.token_input(cfg, tok)), k).tolist()
+            assert H.topk_consistent(ids_l, moe.router_logits(rw_np, rs_np, oin.token_input(cfg, tok)), k)
+            if 2 in ids_l and 6 in ids_l:
+                seen_tie += 1
+                assert ids_l.index(2) + 1 == ids_l.index(6), ids_l      # adjacent, lower id first
+                wl = w.cpu().numpy()
+                assert wl[ids_l.index(2)] == wl[ids_l.index(6)]
+                assert ref.index(2) + 1 == ref.index(6)
+            elif 6 in ids_l:
+                pytest.fail(f"expert 6 selected without its tie partner 2: {ids_l}")
+    assert seen_tie >= 12   # with k = E both are always selected

@@ -122,7 +122,7 @@ def test_expert_gemv_tiny_given_ids(tiny, act):
             worst = max(worst, H.max_rel_err(yr[t, i], ref))
         worst = max(worst, H.max_rel_err(ys[t], moe.expert_ffn(orc.decoded_shared(), u, act)))
     print(f"tiny expert gemv act={act}: max rel err {worst:.3e}")
-    assert worst <= TOL
+    assert worst <= TOL and worst <= H.REGRESSION["tiny_layer"]
 
 
 @pytest.mark.parametrize("mode", ["fused", "separate"])
@@ -144,7 +144,7 @@ def test_layer_tiny_end_to_end(tiny, mode):
         ref = moe.moe_layer(orc, u, cfg.k, forced_ids=ids[t])      # evaluate on the GPU's selection
         worst = max(worst, H.max_rel_err(got[t], ref.out))
     print(f"tiny layer: max rel err {worst:.3e}")
-    assert worst <= TOL
+    assert worst <= TOL and worst <= H.REGRESSION["tiny_layer"]
 
 
 def test_gemv_invalid_id_gives_nan(tiny):
@@ -188,3 +188,57 @@ def test_full_size_layer_sampled_tokens(full_layer, mode):
         worst = max(worst, H.max_rel_err(got[t], ref.out))
     print(f"full-size layer: max rel err {worst:.3e}")
     assert worst <= TOL
+
+
+def _single_token_gemv(dec, shape, x, ids_np, act):
+    ids = torch.from_numpy(ids_np.astype(np.int32).reshape(1, -1)).cuda()
+    q.q4_expert_gemv(dec.routed_pools[0], ids, ids_np.size, dec.shared_pools[0], x, shape.x_dtype, 1, act,
+                     dec.y_routed, dec.y_shared, dec.gemv_ws, dec.gemv_ws_bytes)
+    torch.cuda.synchronize()
+    return H.to_f64(dec.y_routed)[0], H.to_f64(dec.y_shared)[0]
+
+
+@pytest.mark.parametrize("act", [q.MOE_ACT_GELU_TANH, q.MOE_ACT_SILU])
+def test_expert_gemv_one_token_tiny_vs_oracle(tiny, act):
+    """q4_expert_gemv with T = 1 (the decode kernels, not the grouped ones) on the small configuration:
+    every selected expert's output and the shared expert's output against the oracle's expert FFN."""
+    cfg, dev, orc = tiny
+    shape = H.shape_of(cfg, act)
+    dec = decoder.MoEDecoder(shape, [dev], T=1, mode="separate")
+    rng = np.random.default_rng(10 + act)
+    worst = 0.0
+    for tok in range(12):
+        ids_np = rng.choice(cfg.n_experts, cfg.k, replace=False)
+        x = H.token_batch(cfg, [200 + tok])
+        yr, ys = _single_token_gemv(dec, shape, x, ids_np, act)
+        u = oin.token_input(cfg, 200 + tok)
+        for i, e in enumerate(ids_np):
+            worst = max(worst, H.max_rel_err(yr[i], moe.expert_ffn(orc.decoded(int(e)), u, act)))
+        worst = max(worst, H.max_rel_err(ys, moe.expert_ffn(orc.decoded_shared(), u, act)))
+    print(f"tiny one-token expert gemv act={act}: max rel err {worst:.3e}")
+    assert worst <= TOL and worst <= H.REGRESSION["tiny_layer"]
+
+
+@pytest.mark.parametrize("act", [q.MOE_ACT_GELU_TANH, q.MOE_ACT_SILU])
+def test_expert_gemv_one_token_full_size_vs_oracle(full_layer, act):
+    """q4_expert_gemv with T = 1 at d=2816 (8 routed experts of F=704 and the shared expert of width 2816,
+    bf16 activations and scale/bias): each expert's output against the oracle's expert FFN."""
+    from oracle import fast
+    cfg, dev, _ = full_layer
+    shape = H.shape_of(cfg, act)
+    dec = decoder.MoEDecoder(shape, [dev], T=1, mode="separate")
+    rng = np.random.default_rng(20 + act)
+    toks = [40, 41]
+    sel = [rng.choice(cfg.n_experts, cfg.k, replace=False) for _ in toks]
+    got = [_single_token_gemv(dec, shape, H.token_batch(cfg, [t]), ids_np, act) for t, ids_np in zip(toks, sel)]
+    U = np.stack([oin.token_input(cfg, t) for t in toks])
+    worst = 0.0
+    for j, (ids_np, (yr, ys)) in enumerate(zip(sel, got)):
+        for i, e in enumerate(ids_np):
+            ref = fast.expert_ffn_rows(*oin.expert_weights(cfg, 0, int(e)), cfg.sb_bf16, U[j:j + 1], act)[0]
+            worst = max(worst, H.max_rel_err(yr[i], ref))
+    ys_ref = fast.expert_ffn_rows(*oin.shared_weights(cfg, 0), cfg.sb_bf16, U, act)
+    for j, (_, ys) in enumerate(got):
+        worst = max(worst, H.max_rel_err(ys, ys_ref[j]))
+    print(f"full-size one-token expert gemv act={act}: max rel err {worst:.3e}")
+    assert worst <= TOL and worst <= H.REGRESSION["layer_gemv"]
