@@ -42,6 +42,8 @@
 //   u[j] = round_x( (x[j] * gamma[j]) * rinv ),  rinv = 1 / sqrt(sum_j x[j]^2 / d + eps)
 // The expert arithmetic is that of q4_expert_gemv (q4_device.h); the gate/up blocks split the row
 // between their four wavefronts, the routed down blocks give each wavefront 16 whole rows.
+#include <mutex>
+
 #include "q4_device.h"
 
 namespace moeq4 {
@@ -828,6 +830,7 @@ struct StackArgs {
   WsLayout w;
   const void* x_in;
   void* out;
+  uint32_t* status;           // the sticky status word (word 0 of the workspace, or the caller's word)
   int32_t n_layers, per_layer_blocks;
 };
 
@@ -864,7 +867,7 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(const StackArgs 
   a.out = last ? sa.out : static_cast<void*>(ws + sa.w.x_next);
   a.out_ws = !last;
   a.last_layer = last;
-  a.status = reinterpret_cast<uint32_t*>(sa.ws);
+  a.status = sa.status;
   uint32_t* sync = reinterpret_cast<uint32_t*>(ws);
   int line = 1;
   // The call's tag, without a call-wide counter: every block counts the calls in a word of its own (no
@@ -1020,6 +1023,7 @@ moe_status prepare_launch(const char* who, const void* x_dev, moe_dtype x_dtype,
   a.nSD = shared ? d / 16 : 0;
   a.nRD = k * (d / 64);
   sa->ws = static_cast<char*>(workspace_dev);
+  sa->status = static_cast<uint32_t*>(workspace_dev);
   sa->w = w;
   sa->x_in = x_dev;
   sa->out = out_dev;
@@ -1146,4 +1150,92 @@ extern "C" moe_status moe_decode_stack(const moe_stack_layer* layers_host, int32
                              L.u_dev};
   }
   return launch(sa, x_dtype, routed->sb_dtype == MOE_BF16, nbw, lds, as_stream(stream), who);
+}
+
+// ------------------------------------------------------------------------------------------------
+// moe_decode_layer_noalloc: moe_decode_layer with the workspace in a device array the library holds
+// ------------------------------------------------------------------------------------------------
+namespace moeq4 {
+namespace {
+
+constexpr size_t kScratchBytes = MOE_DECODE_LAYER_NOALLOC_MAX_BYTES;   // one layer's workspace
+constexpr int kMaxDevices = 64;
+
+// The workspace of moe_decode_layer_noalloc, one copy per GPU for the life of the process.  Host code never
+// uses this name as an address (on the host it is a stand-in, not device memory): the address of each
+// GPU's copy comes from hipGetSymbolAddress, once per device, and only that address reaches kernels.
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+__global__ void zero_kernel(uint4* __restrict__ p, size_t n16) {
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x) p[i] = z;
+}
+
+// The current device's copy of `scratch`, looked up on the first call on that device.
+moe_status scratch_for_current_device(void** out, const char* who) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: hipGetDevice: %s", who, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "%s: device %d (at most %d devices)", who, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOE_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", who, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moeq4
+
+extern "C" moe_status moe_decode_layer_noalloc(const void* x_dev, moe_dtype x_dtype, const float* gamma_dev, float eps,
+                                               int32_t residual, const int8_t* router_w_dev,
+                                               const float* router_scale_dev, int32_t E, int32_t k,
+                                               const int32_t* forced_ids_dev, const moe_q4_pool* routed,
+                                               const int32_t* gemv_ids_dev, const moe_q4_pool* shared, moe_act act,
+                                               int32_t* ids_dev, float* weights_dev, float* logits_dev, void* u_dev,
+                                               void* out_dev, uint32_t* status_dev, void* stream) {
+  const char* who = "moe_decode_layer_noalloc";
+  if (!routed) return fail(MOE_ERR_INVALID_ARG, "%s: routed is NULL", who);
+  const size_t need = moe_decode_layer_workspace_bytes(routed->d, E, k, routed->F, shared ? shared->F : 0);
+  if (need == 0) return fail(MOE_ERR_INVALID_ARG, "%s: bad shape (d=%d E=%d k=%d F=%d)", who, routed->d, E, k, routed->F);
+  if (need > kScratchBytes)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: this shape needs %zu bytes of workspace, more than the %zu bytes the library "
+                "holds per device (use moe_decode_layer with a caller workspace)", who, need, kScratchBytes);
+  if (!router_w_dev || !router_scale_dev) return fail(MOE_ERR_INVALID_ARG, "%s: NULL pointer", who);
+  if (!aligned(router_w_dev, 16) || (gamma_dev && !aligned(gamma_dev, 16)))
+    return fail(MOE_ERR_INVALID_ARG, "%s: router weights and gamma must be 16-byte aligned", who);
+  if (u_dev && (u_dev == x_dev || u_dev == out_dev)) return fail(MOE_ERR_INVALID_ARG, "%s: u must not alias x or out", who);
+  if (status_dev && !aligned(status_dev, 4)) return fail(MOE_ERR_INVALID_ARG, "%s: status not 4-byte aligned", who);
+  void* ws = nullptr;
+  moe_status st = scratch_for_current_device(&ws, who);
+  if (st != MOE_OK) return st;
+  StackArgs sa{};
+  int nbw = 0;
+  size_t lds = 0;
+  st = prepare_launch(who, x_dev, x_dtype, eps, gamma_dev != nullptr, residual, E, k, routed, shared, act, out_dev, ws,
+                      kScratchBytes, 1, &sa, &nbw, &lds);
+  if (st != MOE_OK) return st;
+  sa.base.forced = forced_ids_dev;
+  sa.base.gemv_ids = gemv_ids_dev;
+  sa.layer[0] = StackLayer{router_w_dev, router_scale_dev, gamma_dev, static_cast<const char*>(routed->base_dev),
+                           shared ? static_cast<const char*>(shared->base_dev) : nullptr, ids_dev, weights_dev,
+                           logits_dev, u_dev};
+  if (status_dev) sa.status = status_dev;
+  // The previous call on this device may have used another shape: start from a zeroed workspace (counters
+  // and call words zero, no stale tagged value), with a fill kernel on the call's stream.
+  hipStream_t s = as_stream(stream);
+  const size_t n16 = (need + 15) / 16;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024)), dim3(256), 0, s,
+                     static_cast<uint4*>(ws), n16);
+  st = check_launch(who);
+  if (st != MOE_OK) return st;
+  return launch(sa, x_dtype, routed->sb_dtype == MOE_BF16, nbw, lds, s, who);
 }

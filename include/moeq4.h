@@ -287,6 +287,31 @@ moe_status moe_decode_layer(const void* x_dev, moe_dtype x_dtype, const float* g
                             size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------------
+ * moe_decode_layer_noalloc — moe_decode_layer for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same computation, kernels
+ * and results, with the workspace in a device array the library holds instead of a caller workspace.
+ * Arguments, outputs, limits and errors as moe_decode_layer, without workspace_dev / workspace_bytes, and:
+ *   status_dev: optional uint32 (device, caller-owned, 4-byte aligned) into which the call ORs 1 if a wait
+ *   inside the kernel ran out (the results of that call are then invalid); NULL = not reported.
+ * The library's array holds MOE_DECODE_LAYER_NOALLOC_MAX_BYTES (1 MiB) per GPU, allocated with the library's
+ * code object and kept until the process ends; a shape whose moe_decode_layer_workspace_bytes(d, E, k, F, S)
+ * exceeds it is rejected with MOE_ERR_UNSUPPORTED before anything is enqueued (d = 2816, 128 experts, top-8,
+ * F = 704, S = 2816 needs about 317 KB).  Each call first clears the part of the array its shape uses (a
+ * fill kernel on `stream`, no memset node), then launches the layer kernel, so consecutive calls may use
+ * different shapes.  Every call on a GPU shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from several threads) race and give undefined results.  The call allocates nothing:
+ * no hipMalloc, hipFree or allocating library routine; the array's device address is looked up once per
+ * device with hipGetSymbolAddress on the first call made with that device current.
+ * ------------------------------------------------------------------------------------------------- */
+#define MOE_DECODE_LAYER_NOALLOC_MAX_BYTES (1u << 20)
+moe_status moe_decode_layer_noalloc(const void* x_dev, moe_dtype x_dtype, const float* gamma_dev, float eps,
+                                    int32_t residual, const int8_t* router_w_dev, const float* router_scale_dev,
+                                    int32_t E, int32_t k, const int32_t* forced_ids_dev, const moe_q4_pool* routed,
+                                    const int32_t* gemv_ids_dev, const moe_q4_pool* shared, moe_act act,
+                                    int32_t* ids_dev, float* weights_dev, float* logits_dev, void* u_dev,
+                                    void* out_dev, uint32_t* status_dev, void* stream);
+
+/* ---------------------------------------------------------------------------------------------------
  * moe_decode_stack — n_layers consecutive layers of moe_decode_layer for one token in a single launch
  * (the stacked decode: RMSNorm and the MoE block per layer, residual stream between them).  Layer l + 1's
  * blocks load their router rows and shared-expert weights while layer l finishes, then wait for layer l's
