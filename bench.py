@@ -5,11 +5,14 @@ top-8 of 128 -> 4-bit expert GEMVs (gate/up + GELU, down; 8 routed experts + the
 both in the same launches) -> routing-weighted combine + residual.  d=2816, F=704, shared width 2816,
 4-bit affine weights in groups of 64 with bf16 scale/bias, bf16 activations, fp32 accumulation.  All
 13.3 GB of expert records are resident in HBM; weights are seeded synthetic draws (no checkpoint).
-One step = one token through all 30 layers (one moe_decode_layer launch each), replayed from a HIP
-graph; inputs are 256 seeded tokens already in HBM, rotated step by step.
+One step = one token through all 30 layers in one moe_decode_stack launch (or, with --mode layer, one
+moe_decode_layer launch per layer), replayed from a HIP graph; inputs are 256 seeded tokens already in HBM,
+rotated step by step.
 
-Prints one JSON line: decode tokens/s, plus the roofline of the dominant kernel (the single-launch
-layer, timed live with HIP events on its stream) and the CPU oracle's speed on a bounded sample.
+Prints one JSON line: decode tokens/s, plus the roofline of the dominant kernel (the launch that decodes the
+token, timed live with HIP events on its stream), a plain streaming read of 2 GiB as the box's achievable
+read rate, and the CPU oracle on a bounded sample of the timed tokens (timed with all host cores and with
+one, and checked against the GPU's per-layer results: routing matches, near ties, largest errors).
 Alongside (not the headline value): per-launch times of the layer split in three kernels, a 32-token batched step
 and a 128-token prefill chunk through the same stack (grouped products on the matrix cores), the same 4-bit
 row routine as one LM-head-sized GEMV (262,144 x 2816), and the same stack served from pinned host memory through 16-slot LFU expert caches (hit rates, host-to-device rate
@@ -56,23 +59,29 @@ def build_stack(cfg, n_layers):
     return shape, layers
 
 
-# HBM traffic of one layer launch from rocprofv3 FETCH_SIZE and WRITE_SIZE counter runs of this script (2 steps,
-# --calibration-copy-mib 256), each scaled by what the counter reads for the plain 256 MiB device copy in the
-# same run (FETCH_SIZE x 1.9997, WRITE_SIZE x 1.0).  It is reported only while the kernel's sources are the
-# ones the counters were taken on.
-LAYER_TRAFFIC_BYTES = 42566437
-LAYER_TRAFFIC_SOURCES = ("bit_quantized_expert_int8_amd/csrc/layer.hip", "bit_quantized_expert_int8_amd/csrc/q4_device.h",
-                         "bit_quantized_expert_int8_amd/csrc/common.h")
-LAYER_TRAFFIC_SHA = "e2f0e1972e8c6818"
+# HBM traffic of one launch of the dominant kernel from rocprofv3 FETCH_SIZE and WRITE_SIZE counter runs of
+# this script (2 steps, --calibration-copy-mib 256), each scaled by what the counter reads for the plain
+# 256 MiB device copy in the same run.  Keyed by decode mode; reported only while the kernel's sources are
+# the ones the counters were taken on (first 16 hex digits of their sha256).
+TRAFFIC = {
+    # mode: (bytes per launch, sources sha)
+}
+TRAFFIC_SOURCES = ("bit_quantized_expert_int8_amd/csrc/layer.hip", "bit_quantized_expert_int8_amd/csrc/q4_device.h",
+                   "bit_quantized_expert_int8_amd/csrc/common.h")
 
 
-def layer_traffic():
+def sources_sha():
     import hashlib
     h = hashlib.sha256()
-    for p in LAYER_TRAFFIC_SOURCES:
+    for p in TRAFFIC_SOURCES:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
-    return LAYER_TRAFFIC_BYTES if h.hexdigest()[:16] == LAYER_TRAFFIC_SHA else None
+    return h.hexdigest()[:16]
+
+
+def kernel_traffic(mode):
+    t = TRAFFIC.get(mode)
+    return t[0] if t and t[1] == sources_sha() else None
 
 
 def record_data_bytes(d: int, F: int) -> int:
@@ -121,6 +130,41 @@ def time_layer_kernel(dec, xin, reps):
             dec.layer(l, bufs[l % 2], bufs[(l + 1) % 2], stream=stream)
 
     return time_graph(layers, reps, stream) / len(dec.layers), reps * len(dec.layers)
+
+
+def time_stack_kernel(dec, xin, reps):
+    """Average duration of one moe_decode_stack launch (every layer of the token in one launch), from HIP
+    events around a graph of replays of that launch on the stream it is captured on."""
+    import torch
+
+    out = torch.empty_like(xin)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    return time_graph(lambda: dec.step(xin, out, stream=stream), reps, stream), reps
+
+
+def measure_hbm_read(gib=2, reps=10):
+    """The box's achievable streaming read rate: moe_hbm_read_probe over a 2 GiB buffer (16-byte nontemporal
+    loads on every compute unit), HIP events around `reps` calls on one stream."""
+    import torch
+    from bit_quantized_expert_int8_amd import moeq4 as q
+
+    n = gib << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        q.moe_hbm_read_probe(buf, n, sink, stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            q.moe_hbm_read_probe(buf, n, sink, stream)
+        e1.record(stream)
+    e1.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    del buf
+    return {"bytes": n, "us_per_read": round(t * 1e6, 1), "GBps": round(n / t / 1e9, 1),
+            "frac_of_8TBps": round(n / t / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def time_split_kernels(dec, xin, reps):
@@ -312,35 +356,96 @@ def measure_streamed(shape, layers, cfg, dec, n_tokens):
             "pinned_copy_GBps": round(pinned_gbps, 2)}
 
 
-def cpu_baseline(cfg, n_layers_sample, repeats, token=0):
-    """The CPU oracle (float64 numpy) on a bounded sample: one token through the first layers of the
-    stack, repeated; the records of the experts it routes to are prepared beforehand (untimed)."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_leg(shape, layers, cfg, tokens, n_sample, st_layers, xout_graph=None):
+    """The CPU oracle on a bounded sample of the timed tokens, and the parity of the GPU's results on them.
+
+    The GPU runs the sampled tokens layer by layer (the single-layer launch, which equals the stack launch bit
+    for bit) and keeps every layer's input, normalized activation, routing and logits.  The oracle (float64;
+    its expert FFN in C, the experts of a layer on a thread pool) then evaluates every layer of every sampled
+    token on the GPU's input to that layer (teacher forcing), once with all host cores (timed: the value) and
+    for the first token over `st_layers` layers with one thread (timed, scaled to 30 layers)."""
     import numpy as np
+    import torch
     import synth
-    from oracle import inputs as oin
+    from bit_quantized_expert_int8_amd import decoder
+    from oracle import fast
     from oracle import moe
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = 1
-    layers = [oin.oracle_layer(cfg, l, cache_experts=16) for l in range(n_layers_sample)]
-    x0 = moe.f64_round_to_bf16(oin.token_input(cfg, token))
-    # untimed pass: draws and encodes the records this token needs
-    x = x0
-    for L in layers:
-        _, _, x = moe.stack_layer_step(L, x, cfg.k)
+    L = len(layers)
+    toks = list(range(0, len(tokens), max(1, len(tokens) // n_sample)))[:n_sample]
+    dec = decoder.MoEDecoder(shape, layers, T=1, mode="layer", record_u=True)
+    X = np.zeros((L + 1, len(toks), cfg.d))
+    U = np.zeros((L, len(toks), cfg.d))
+    IDS = np.zeros((L, len(toks), cfg.k), dtype=np.int64)
+    LG = np.zeros((L, len(toks), cfg.n_experts))
+    f64 = lambda t: t.detach().float().cpu().numpy().astype(np.float64)   # noqa: E731
+    for j, tok in enumerate(toks):
+        x = tokens[tok].clone()
+        X[0, j] = f64(x)[0]
+        for l in range(L):
+            out = torch.empty_like(x)
+            dec.layer(l, x, out)
+            torch.cuda.synchronize()
+            U[l, j], IDS[l, j], LG[l, j], X[l + 1, j] = f64(dec.u_all[l])[0], dec.ids_all[l].cpu().numpy()[0], \
+                dec.logits_all[l].cpu().numpy()[0], f64(out)[0]
+            x = out
+    dec.check_status()
+    threads = fast.default_threads()
     t0 = time.perf_counter()
-    for _ in range(repeats):
-        x = x0
-        for L in layers:
-            _, _, x = moe.stack_layer_step(L, x, cfg.k)
-    dt = time.perf_counter() - t0
-    per_layer = dt / (n_layers_sample * repeats)
-    return {"value": 1.0 / (per_layer * cfg.n_layers), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"token {token} through layers 0-{n_layers_sample - 1} of {cfg.n_layers}, {repeats} times "
-                      f"({dt:.1f} s), scaled to one 30-layer token"}
+    res = [fast.layer_tokens(cfg, l, X[l], IDS[l], threads=threads) for l in range(L)]
+    t_all = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for l in range(st_layers):
+        fast.layer_tokens(cfg, l, X[l, :1], IDS[l, :1], threads=1)
+    t_one = time.perf_counter() - t0
+    # parity of the sampled tokens
+    exact = ties = 0
+    worst = net = lg_err = 0.0
+    for l in range(L):
+        rw, rs = synth.router_int8(cfg.weight_cfg, l, cfg.n_experts, cfg.d)
+        for j in range(len(toks)):
+            r = res[l][j]
+            lg = moe.router_logits(rw, rs, U[l, j])
+            lg_err = max(lg_err, float(np.abs(LG[l, j] - lg).max() / max(1.0, np.abs(lg).max())))
+            order = np.lexsort((np.arange(cfg.n_experts), -lg))
+            if lg[order[cfg.k - 1]] - lg[order[cfg.k]] > 1e-3:
+                exact += int(list(IDS[l, j]) == list(order[:cfg.k]))
+            else:
+                ties += 1
+            got = X[l + 1, j]
+            worst = max(worst, float(np.abs(got - r.x_next).max() / np.abs(r.x_next).max()))
+            _, E = np.frexp(np.abs(r.x_next))
+            ulp = np.where(r.x_next != 0, np.ldexp(1.0, E - 8), 0.0)
+            excess = max(float((np.abs(got - r.x_next) - ulp).max()), 0.0)
+            net = max(net, excess / np.abs(r.out - X[l, j]).max())
+    n = L * len(toks)
+    same = None
+    if xout_graph is not None:   # the timed launch's output for the last sampled token equals the layer chain's
+        same = bool(np.array_equal(xout_graph, X[L, -1]))
+    cpu = {"value": len(toks) / t_all, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{len(toks)} of the {len(tokens)} timed tokens through all {L} layers, teacher-forced on the "
+                     f"GPU's per-layer inputs ({t_all:.1f} s with {threads} threads; float64, expert FFN in C, weights "
+                     f"drawn from the seeded generator and encoded inside the timed region)",
+           "single_thread_value": 1.0 / (t_one / st_layers * L),
+           "single_thread_sample": f"token {toks[0]} through layers 0-{st_layers - 1} with 1 thread ({t_one:.1f} s), "
+                                   f"scaled to {L} layers",
+           "nproc": os.cpu_count(), "cpu_model": cpu_model()}
+    parity = {"tokens": len(toks), "layers": L, "topk_exact": exact, "topk_compared": n - ties, "near_ties": ties,
+              "max_rel_err": round(worst, 5), "moe_branch_err_beyond_rounding": round(net, 6),
+              "max_logit_err": float(f"{lg_err:.2e}"), "bar": "top-k exact when the 8th/9th gap > 1e-3; "
+              "max relative error <= 1e-2", "timed_launch_equals_layer_chain": same}
+    return cpu, parity
 
 
 def main():
@@ -349,9 +454,11 @@ def main():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--layers", type=int, default=30)
+    ap.add_argument("--mode", choices=("stack", "layer"), default="stack",
+                    help="stack: one moe_decode_stack launch per token; layer: one moe_decode_layer launch per layer")
     ap.add_argument("--roofline-reps", type=int, default=20)
-    ap.add_argument("--cpu-layers", type=int, default=2)
-    ap.add_argument("--cpu-repeats", type=int, default=40)
+    ap.add_argument("--cpu-tokens", type=int, default=16, help="timed tokens the oracle leg checks (all layers)")
+    ap.add_argument("--cpu-single-layers", type=int, default=10, help="layers of the one-thread oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the batched and streamed measurements")
     ap.add_argument("--stream-tokens", type=int, default=512)
@@ -375,7 +482,7 @@ def main():
     shape, layers = build_stack(cfg, args.layers)
     torch.cuda.synchronize()
     t_build = time.perf_counter() - t_build
-    dec = decoder.MoEDecoder(shape, layers, T=1)
+    dec = decoder.MoEDecoder(shape, layers, T=1, mode=args.mode)
 
     n_tok = cfg.n_tokens
     bits = np.stack([synth.activation(cfg.act_cfg, t, cfg.d, bf16=True) for t in range(n_tok)]).astype(np.int16)
@@ -408,16 +515,25 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    dur, launches = time_layer_kernel(dec, xin, args.roofline_reps)
-    dec.check_status()
     nbytes = layer_bytes(cfg)
-    achieved = nbytes / dur / 1e9
+    lay_dur, lay_launches = time_layer_kernel(dec, xin, args.roofline_reps)
+    if args.mode == "stack":
+        dur, launches = time_stack_kernel(dec, xin, args.roofline_reps)
+        per_launch = nbytes * args.layers
+        kname = (f"decode_stack_kernel (moe_decode_stack: the {args.layers} layers of one token in one launch; per "
+                 "layer RMSNorm, int8 router + top-8, 8 routed + shared 4-bit expert FFNs, combine + residual)")
+    else:
+        dur, launches, per_launch = lay_dur, lay_launches, nbytes
+        kname = ("decode_stack_kernel (moe_decode_layer: RMSNorm, int8 router + top-8, 8 routed + shared 4-bit "
+                 "expert FFNs, combine + residual, one launch per layer)")
+    dec.check_status()
+    achieved = per_launch / dur / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": layer_traffic(),
-                "kernel": "decode_layer_kernel (moe_decode_layer: RMSNorm, int8 router + top-8, 8 routed + shared "
-                          "4-bit expert FFNs, combine + residual, one launch per layer)",
-                "bytes_per_launch": nbytes, "avg_launch_us": round(dur * 1e6, 3), "launches_timed": launches}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": kernel_traffic(args.mode), "kernel": kname,
+                "bytes_per_launch": per_launch, "avg_launch_us": round(dur * 1e6, 3), "launches_timed": launches,
+                "per_layer_us": round(dur / (args.layers if args.mode == "stack" else 1) * 1e6, 3)}
     split = time_split_kernels(dec, xin, args.roofline_reps)
+    split["layer_launch_us"] = round(lay_dur * 1e6, 3)
     step_bytes, _ = distinct_expert_bytes(dec, cfg)
 
     out = {"metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -431,14 +547,21 @@ def main():
            "roofline": roofline, "wall_s_timed_region": round(wall, 4), "build_s": round(t_build, 1),
            "step_weight_bytes": step_bytes, "step_achieved_GBps": round(step_bytes / (gpu_s / args.steps) / 1e9, 1),
            "per_layer_us": round(gpu_s / args.steps / args.layers * 1e6, 2),
-           "decode_mode": dec.mode, "split_kernels_us": split}
+           "decode_mode": dec.mode, "split_kernels_us": split, "hbm_read_2GiB": measure_hbm_read()}
     if not args.no_extras:
         out["batched"] = measure_batched(shape, layers, cfg, tokens.reshape(n_tok, cfg.d), 20, 3)
         out["prefill_chunk_128"] = measure_batched(shape, layers, cfg, tokens.reshape(n_tok, cfg.d), 8, 2, T=128)
         out["lm_head_q4_gemv"] = measure_lm_head()
         out["streamed"] = measure_streamed(shape, layers, cfg, dec, args.stream_tokens)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_layers, args.cpu_repeats)
+        # the timed launch's output for the last token the oracle leg samples
+        toks = list(range(0, n_tok, max(1, n_tok // args.cpu_tokens)))[:args.cpu_tokens]
+        xin.copy_(tokens[toks[-1]])
+        g.replay()
+        torch.cuda.synchronize()
+        xo = xout.float().cpu().numpy().astype(np.float64)[0]
+        out["cpu_baseline"], out["parity"] = oracle_leg(shape, layers, cfg, tokens, args.cpu_tokens,
+                                                        args.cpu_single_layers, xout_graph=xo)
     print(json.dumps(out), flush=True)
 
 

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-LIB_SOURCES = ["api.cpp", "quantize.hip", "router.hip", "q4_gemv.hip", "q4_grouped.hip", "q4_mfma.hip", "layer.hip", "cache.hip"]
+LIB_SOURCES = ["api.cpp", "quantize.hip", "router.hip", "q4_gemv.hip", "q4_grouped.hip", "q4_mfma.hip", "layer.hip", "cache.hip", "probe.hip"]
 LIB_OUT = os.path.join(PKG, "libmoeq4.so")
 SYNTH_SOURCES = [os.path.join(ROOT, "synth", "synth_gen.hip")]
 SYNTH_OUT = os.path.join(ROOT, "synth", "libsynth.so")

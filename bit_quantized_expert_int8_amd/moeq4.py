@@ -110,6 +110,7 @@ _c = {
                                                                    ctypes.POINTER(_u64)]),
     "moe_expert_cache_slots": _sig("moe_expert_cache_slots", _st, [_vp, _i32, ctypes.POINTER(_i32)]),
     "moe_expert_cache_inject_copy_failure": _sig("moe_expert_cache_inject_copy_failure", _st, [_vp, _i32]),
+    "moe_hbm_read_probe": _sig("moe_hbm_read_probe", _st, [_vp, _sz, _vp, _vp]),
     "moe_last_error": _sig("moe_last_error", ctypes.c_char_p, []),
     "moe_version": _sig("moe_version", ctypes.c_char_p, []),
 }
@@ -329,6 +330,10 @@ def moe_expert_cache_slots(cache, layer, n_slots) -> list:
 
 def moe_expert_cache_inject_copy_failure(cache, after_n_copies) -> None:
     _check(_c["moe_expert_cache_inject_copy_failure"](cache, after_n_copies), "moe_expert_cache_inject_copy_failure")
+
+
+def moe_hbm_read_probe(buf, nbytes, sink, stream=None) -> None:
+    _check(_c["moe_hbm_read_probe"](_p(buf), nbytes, _p(sink), _s(stream)), "moe_hbm_read_probe")
 
 
 def raw(name: str):

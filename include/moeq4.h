@@ -395,6 +395,13 @@ moe_status moe_expert_cache_slots(const moe_expert_cache* cache, int32_t layer, 
  * MOE_ERR_HIP without copying; -1 disables.  Used to force the failure path from the host. */
 moe_status moe_expert_cache_inject_copy_failure(moe_expert_cache* cache, int32_t after_n_copies);
 
+/* moe_hbm_read_probe — measurement aid, not a step of the layer: reads `bytes` of device memory once with
+ * 16-byte nontemporal loads spread over every compute unit (the plain streaming read that the 4-bit GEMVs'
+ * achieved bandwidth is compared with).  buf_dev: 16-byte aligned, bytes a nonzero multiple of 16; sink_dev:
+ * uint32 [1024] the kernel may write (it writes nothing in practice; the folded words only keep the loads).
+ * MOE_ERR_INVALID_ARG on bad arguments (nothing launched).  Asynchronous on `stream`. */
+moe_status moe_hbm_read_probe(const void* buf_dev, size_t bytes, uint32_t* sink_dev, void* stream);
+
 /* Thread-local message describing the last non-MOE_OK status returned on this thread. */
 const char* moe_last_error(void);
 
