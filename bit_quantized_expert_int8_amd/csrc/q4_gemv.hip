@@ -460,6 +460,8 @@ extern "C" moe_status q4_expert_gemv_combine(const moe_q4_pool* routed, const in
 namespace moeq4 {
 namespace {
 
+constexpr int kGemvBlocksPerCu = 4;   // persistent blocks of q4_gemv per compute unit
+
 struct MatArgs {
   const void* x;      // x dtype [T][K]
   const char* q;      // uint32 [N][K/8]
@@ -468,21 +470,150 @@ struct MatArgs {
   int32_t N, K, sb_row_bytes;
 };
 
+// One tile = 16 rows (rows r and r + 8 per 8-lane group of a wave, the waves splitting the row's chunk
+// iterations): this lane's code words and scale/bias words of a tile, loaded in one go.
+template <int NBW, bool SB_BF16>
+struct TileRegs {
+  SbWord<SB_BF16> sa[NBW], sb[NBW];
+  u32x4 qa[NBW], qb[NBW];
+};
+
+template <int NBW, bool SB_BF16>
+__device__ __forceinline__ void load_tile(const MatArgs& m, int tile, TileRegs<NBW, SB_BF16>& g) {
+  const int W = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63, ra = lane >> 3, j = lane & 7;
+  const int C = m.K / 32;
+  const int rA = min(tile * 16 + ra, m.N - 1), rB = min(tile * 16 + ra + 8, m.N - 1);
+  const char* qA = m.q + (int64_t)rA * (m.K / 2);
+  const char* qB = m.q + (int64_t)rB * (m.K / 2);
+  const char* sA = m.sb + (int64_t)rA * m.sb_row_bytes;
+  const char* sB = m.sb + (int64_t)rB * m.sb_row_bytes;
+#pragma unroll
+  for (int i = 0; i < NBW; ++i) {
+    const int c = (wave + W * i) * kLanesPerRow + j;
+    if (c < C) {
+      g.sa[i] = load_sb<SB_BF16>(sA, c >> 1);
+      g.sb[i] = load_sb<SB_BF16>(sB, c >> 1);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NBW; ++i) {
+    const int c = (wave + W * i) * kLanesPerRow + j;
+    if (c < C) {
+      g.qa[i] = load_nt(qA + c * 16);
+      g.qb[i] = load_nt(qB + c * 16);
+    }
+  }
+}
+
+// The tile's two row sums of this lane (before the 8-lane and the wave reductions), in rowpair_partial's order.
+template <int NBW, bool SB_BF16>
+__device__ __forceinline__ void tile_dot(const MatArgs& m, const TileRegs<NBW, SB_BF16>& g, Stage st, float& yA, float& yB) {
+  const int W = blockDim.x >> 6, wave = threadIdx.x >> 6, j = threadIdx.x & 7;
+  const int C = m.K / 32;
+  yA = 0.f;
+  yB = 0.f;
+  const Dequant dq = opaque_dequant();
+#pragma unroll
+  for (int i = 0; i < NBW; ++i) {
+    const int c = (wave + W * i) * kLanesPerRow + j;
+    if (c < C) {
+      const u32x4* xv = reinterpret_cast<const u32x4*>(st.xw + c * kHgStride);
+      const u32x4 x0 = xv[0], x1 = xv[1], x2 = xv[2], x3 = xv[3];
+      const float4 h = st.hg[c];
+      const float accA = chunk_dot(g.qa[i], x0, x1, x2, x3, dq, -h.y);
+      const float accB = chunk_dot(g.qb[i], x0, x1, x2, x3, dq, -h.y);
+      float s0, b0, s1, b1;
+      sb_values<SB_BF16>(g.sa[i], s0, b0);
+      sb_values<SB_BF16>(g.sb[i], s1, b1);
+      yA = fmaf(h.x, fmaf(s0, accA, b0 * h.z), yA);
+      yB = fmaf(h.x, fmaf(s1, accB, b1 * h.z), yB);
+    }
+  }
+}
+
+// Sum the tile's row pair over the block's waves in wave order (block_sum's order), with a reduction buffer
+// per parity of the tile count so that the next tile's writes never meet this tile's reads.
+__device__ __forceinline__ bool tile_sum(float& yA, float& yB, float (*red)[kMaxWaves][16], int parity) {
+  const int W = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63, ra = lane >> 3, j = lane & 7;
+  yA = reduce8(yA);
+  yB = reduce8(yB);
+  if (W == 1) return j == 0;
+  if (j == 0) {
+    red[parity][wave][ra] = yA;
+    red[parity][wave][8 + ra] = yB;
+  }
+  __syncthreads();
+  if (wave != 0 || j != 0) return false;
+  yA = red[parity][0][ra];
+  yB = red[parity][0][8 + ra];
+  for (int w = 1; w < W; ++w) {
+    yA += red[parity][w][ra];
+    yB += red[parity][w][8 + ra];
+  }
+  return true;
+}
+
+// A persistent grid over the matrix's 16-row tiles for token blockIdx.y: every block stages the token's
+// activation once (each wave its own half-groups, as rowpair_partial does), then walks the tiles
+// blockIdx.x, + gridDim.x, ... with the next tile's code words in flight while the current one is reduced
+// and stored.  Each row's arithmetic and summation order are those of rowpair_partial + block_sum, so the
+// results equal the expert kernels' row routine bit for bit.
 template <int NBW, typename XT, bool SB_BF16>
-__global__ __launch_bounds__(64 * kMaxWaves) void matrix_gemv_kernel(MatArgs m) {
+__global__ __launch_bounds__(64 * kMaxWaves) void matrix_gemv_kernel(MatArgs m, int n_tiles) {
   extern __shared__ __align__(16) uint32_t lds[];
-  const int C = m.K / 32, t = blockIdx.y, ra = (threadIdx.x & 63) >> 3;
-  const int rA = blockIdx.x * 16 + ra, rB = rA + 8;
-  const int lA = min(rA, m.N - 1), lB = min(rB, m.N - 1);
+  __shared__ float red[2][kMaxWaves][16];
+  const int W = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63, ra = lane >> 3;
+  const int C = m.K / 32, nit = (C + kLanesPerRow - 1) / kLanesPerRow, t = blockIdx.y;
   const Stage st{lds, reinterpret_cast<float4*>(lds + C * kHgStride)};
-  float yA, yB;
-  rowpair_partial<NBW, XT, SB_BF16>(m.q + (int64_t)lA * (m.K / 2), m.q + (int64_t)lB * (m.K / 2),
-                                    m.sb + (int64_t)lA * m.sb_row_bytes, m.sb + (int64_t)lB * m.sb_row_bytes,
-                                    reinterpret_cast<const XT*>(m.x) + (int64_t)t * m.K, m.K, st, true, yA, yB);
-  if (!block_sum(yA, yB)) return;
+  const XT* x = reinterpret_cast<const XT*>(m.x) + (int64_t)t * m.K;
+  int tile = blockIdx.x;
+  TileRegs<NBW, SB_BF16> g0, g1;
+  if (tile < n_tiles) load_tile<NBW, SB_BF16>(m, tile, g0);
+  // stage this wave's half-groups (slot mapping of rowpair_partial) while the first tile is in flight
+  constexpr int kPasses = (NBW * 32 + 63) / 64;
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int s = lane + 64 * p, mi = s >> 5, jj = (s >> 2) & 7, q = s & 3;
+    const int it = wave + W * mi;
+    const int hg = it * kLanesPerRow + jj;
+    const bool live = mi < NBW && it < nit && hg < C;
+    XWord<XT> xw;
+    float v[8];
+    if (live) {
+      load_word<XT>(x, hg, q, xw);
+      word_to_f32<XT>(xw, v);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.f;
+    }
+    stage_word(v, live, hg, q, st);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   float* y = m.y + (int64_t)t * m.N;
-  if (rA < m.N) y[rA] = yA;
-  if (rB < m.N) y[rB] = yB;
+  int parity = 0;
+  auto finish = [&](const TileRegs<NBW, SB_BF16>& g, int tl) {
+    float yA, yB;
+    tile_dot<NBW, SB_BF16>(m, g, st, yA, yB);
+    if (tile_sum(yA, yB, red, parity)) {
+      const int rA = tl * 16 + ra, rB = rA + 8;
+      if (rA < m.N) y[rA] = yA;
+      if (rB < m.N) y[rB] = yB;
+    }
+    parity ^= 1;
+  };
+  // two register sets alternate: the next tile loads into one while the other is computed
+  while (tile < n_tiles) {
+    const int t1 = tile + (int)gridDim.x;
+    if (t1 < n_tiles) load_tile<NBW, SB_BF16>(m, t1, g1);
+    finish(g0, tile);
+    if (t1 >= n_tiles) break;
+    const int t2 = t1 + (int)gridDim.x;
+    if (t2 < n_tiles) load_tile<NBW, SB_BF16>(m, t2, g0);
+    finish(g1, t1);
+    tile = t2;
+  }
 }
 
 }  // namespace
@@ -505,17 +636,22 @@ extern "C" moe_status q4_gemv(const void* x_dev, moe_dtype x_dtype, int32_t T, c
   const int sb_elem = sb_dtype == MOE_BF16 ? 2 : 4;
   const moeq4::MatArgs m{x_dev, reinterpret_cast<const char*>(codes_dev), reinterpret_cast<const char*>(sb_dev),
                          y_dev, N, K, (K / 64) * 2 * sb_elem};
-  const dim3 grid((N + 15) / 16, T), block(64 * waves);
+  const int n_tiles = (N + 15) / 16;
+  int dev = 0, cus = 0;
+  (void)hipGetDevice(&dev);
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  const int per_cu = kGemvBlocksPerCu;
+  const dim3 grid(n_tiles < cus * per_cu ? n_tiles : cus * per_cu, T), block(64 * waves);
   const size_t lds = lds_bytes(K);
   hipStream_t s = as_stream(stream);
   return dispatch_nbw(nbw, [&](auto nb) {
     constexpr int NB = decltype(nb)::value;
     if (x_dtype == MOE_BF16) {
-      if (sb_dtype == MOE_BF16) hipLaunchKernelGGL((moeq4::matrix_gemv_kernel<NB, uint16_t, true>), grid, block, lds, s, m);
-      else hipLaunchKernelGGL((moeq4::matrix_gemv_kernel<NB, uint16_t, false>), grid, block, lds, s, m);
+      if (sb_dtype == MOE_BF16) hipLaunchKernelGGL((moeq4::matrix_gemv_kernel<NB, uint16_t, true>), grid, block, lds, s, m, n_tiles);
+      else hipLaunchKernelGGL((moeq4::matrix_gemv_kernel<NB, uint16_t, false>), grid, block, lds, s, m, n_tiles);
     } else {
-      if (sb_dtype == MOE_BF16) hipLaunchKernelGGL((moeq4::matrix_gemv_kernel<NB, float, true>), grid, block, lds, s, m);
-      else hipLaunchKernelGGL((moeq4::matrix_gemv_kernel<NB, float, false>), grid, block, lds, s, m);
+      if (sb_dtype == MOE_BF16) hipLaunchKernelGGL((moeq4::matrix_gemv_kernel<NB, float, true>), grid, block, lds, s, m, n_tiles);
+      else hipLaunchKernelGGL((moeq4::matrix_gemv_kernel<NB, float, false>), grid, block, lds, s, m, n_tiles);
     }
     return check_launch(who);
   });
