@@ -279,10 +279,25 @@ def measure_lm_head(steps=10, reps=10):
             "achieved_GBps": round(nbytes / t / 1e9, 1), "frac_of_8TBps": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def measure_streamed(shape, layers, cfg, dec, n_tokens):
+def pinned_pools(layers):
+    """Every layer's expert records copied to pinned host memory (the slow tier of the expert cache)."""
+    import torch
+
+    host = [torch.empty(lay.pool.shape, dtype=torch.uint8, pin_memory=True) for lay in layers]
+    for h, lay in zip(host, layers):
+        h.copy_(lay.pool)
+    return host
+
+
+def measure_streamed(shape, layers, cfg, dec, n_tokens, overlap=True, copy_streams=1, pinned_gbps=None, host=None):
     """Experts served from pinned host memory through a 16-slot LFU cache per layer (routing forced by a
     Zipf(1.1) trace): tokens/s over all tokens and over the second half (warm cache), hit rates, and the
-    host-to-device rate against a plain pinned 1 GiB copy measured in the same process."""
+    host-to-device rate against a plain pinned 1 GiB copy measured in the same process.
+
+    With `overlap`, each layer runs as two launches: the router and the shared expert (moe_decode_layer_part
+    part 1) go ahead while the layer's missing experts are copied, and the routed experts and the combine
+    (part 2) wait for the copies; without, the whole layer waits for them.  Layers' copies go to
+    `copy_streams` streams in turn."""
     import numpy as np
     import torch
     import synth
@@ -290,23 +305,11 @@ def measure_streamed(shape, layers, cfg, dec, n_tokens):
 
     L, E, k, n_slots = len(layers), cfg.n_experts, cfg.k, 16
     rb = layers[0].pool.shape[1]
-    # pinned-copy reference rate
-    ref_h = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
-    ref_d = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    ref_d.copy_(ref_h, non_blocking=True)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(3):
-        ref_d.copy_(ref_h, non_blocking=True)
-    e1.record()
-    e1.synchronize()
-    pinned_gbps = 3 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del ref_h, ref_d
+    if pinned_gbps is None:
+        pinned_gbps = pinned_copy_gbps()
 
-    host = [torch.empty((E, rb), dtype=torch.uint8, pin_memory=True) for _ in range(L)]
-    for h, lay in zip(host, layers):
-        h.copy_(lay.pool)
+    if host is None:
+        host = pinned_pools(layers)
     slots = [torch.empty((n_slots, rb), dtype=torch.uint8, device="cuda") for _ in range(L)]
     cache = q.moe_expert_cache_create(L, E, n_slots, rb, [h.data_ptr() for h in host], [s_.data_ptr() for s_ in slots])
     try:
@@ -314,13 +317,13 @@ def measure_streamed(shape, layers, cfg, dec, n_tokens):
         forced = torch.from_numpy(trace.astype(np.int32)).cuda()
         slot_pools = [q.pool(s_, rb, n_slots, cfg.d, cfg.F, shape.sb_dtype) for s_ in slots]
         slot_ids = torch.empty((L, 1, k), dtype=torch.int32, device="cuda")
-        copy_stream = torch.cuda.Stream()
+        cstreams = [torch.cuda.Stream() for _ in range(copy_streams)]
         compute = torch.cuda.current_stream()
         ready = [torch.cuda.Event() for _ in range(L)]
         freed = [torch.cuda.Event() for _ in range(L)]
         for ev in ready + freed:
-            ev.record(copy_stream)
-        copy_stream.synchronize()
+            ev.record(cstreams[0])
+        cstreams[0].synchronize()
         bits = np.stack([synth.activation(cfg.act_cfg, t % 64, cfg.d, bf16=True) for t in range(64)]).astype(np.int16)
         toks = torch.from_numpy(bits).view(torch.bfloat16).cuda().reshape(64, 1, cfg.d)
         bufs = [torch.empty((1, cfg.d), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
@@ -335,10 +338,17 @@ def measure_streamed(shape, layers, cfg, dec, n_tokens):
                 bytes_half = q.moe_expert_cache_stats(cache, -1)[2]
             x = toks[t % 64]
             for l in range(L):
-                q.expert_cache_stage(cache, l, trace[t, l].tolist(), slot_ids[l], copy_stream, freed[l], ready[l])
-                compute.wait_event(ready[l])
+                q.expert_cache_stage(cache, l, trace[t, l].tolist(), slot_ids[l], cstreams[l % copy_streams], freed[l],
+                                     ready[l])
                 out = bufs[l % 2]
-                dec.layer(l, x, out, forced_ids=forced[t, l].reshape(1, k), routed_pool=slot_pools[l], ids=slot_ids[l])
+                fi = forced[t, l].reshape(1, k)
+                if overlap:
+                    dec.layer_part(1, l, x, out, forced_ids=fi, routed_pool=slot_pools[l], ids=slot_ids[l])
+                    compute.wait_event(ready[l])
+                    dec.layer_part(2, l, x, out, forced_ids=fi, routed_pool=slot_pools[l], ids=slot_ids[l])
+                else:
+                    compute.wait_event(ready[l])
+                    dec.layer(l, x, out, forced_ids=fi, routed_pool=slot_pools[l], ids=slot_ids[l])
                 freed[l].record(compute)
                 x = out
         torch.cuda.synchronize()
@@ -350,10 +360,32 @@ def measure_streamed(shape, layers, cfg, dec, n_tokens):
     req = n_tokens * L * k
     warm_req = (n_tokens - half) * L * k
     return {"tokens": n_tokens, "layers": L, "slots_per_layer": n_slots, "trace": "Zipf(1.1) forced routing",
+            "overlap": "shared expert during the copies (two launches per layer)" if overlap else "none",
+            "copy_streams": copy_streams,
             "tok_s_all": round(n_tokens / (t1 - t0), 2), "tok_s_warm": round((n_tokens - half) / (t1 - t_half), 2),
             "hit_rate_all": round(hits / req, 4), "hit_rate_warm": round((hits - hits_half) / warm_req, 4),
             "bytes_copied": int(nbytes), "h2d_GBps_effective_warm": round((nbytes - bytes_half) / (t1 - t_half) / 1e9, 2),
             "pinned_copy_GBps": round(pinned_gbps, 2)}
+
+
+def pinned_copy_gbps(reps=3):
+    """A plain pinned host -> device copy of 1 GiB: the host link's practical rate, the reference for the
+    expert cache's copies."""
+    import torch
+
+    ref_h = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+    ref_d = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    ref_d.copy_(ref_h, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        ref_d.copy_(ref_h, non_blocking=True)
+    e1.record()
+    e1.synchronize()
+    gbps = reps * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del ref_h, ref_d
+    return gbps
 
 
 def cpu_model():
@@ -462,6 +494,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the batched and streamed measurements")
     ap.add_argument("--stream-tokens", type=int, default=512)
+    ap.add_argument("--copy-streams", type=int, default=2, help="streams the expert cache's copies alternate over")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB (a reference for the HBM "
                          "traffic counters of a profiled run)")
@@ -552,7 +585,15 @@ def main():
         out["batched"] = measure_batched(shape, layers, cfg, tokens.reshape(n_tok, cfg.d), 20, 3)
         out["prefill_chunk_128"] = measure_batched(shape, layers, cfg, tokens.reshape(n_tok, cfg.d), 8, 2, T=128)
         out["lm_head_q4_gemv"] = measure_lm_head()
-        out["streamed"] = measure_streamed(shape, layers, cfg, dec, args.stream_tokens)
+        pinned = pinned_copy_gbps()
+        host = pinned_pools(layers)
+        out["streamed"] = measure_streamed(shape, layers, cfg, dec, args.stream_tokens, overlap=True,
+                                           copy_streams=args.copy_streams, pinned_gbps=pinned, host=host)
+        base = measure_streamed(shape, layers, cfg, dec, args.stream_tokens // 2, overlap=False,
+                                copy_streams=args.copy_streams, pinned_gbps=pinned, host=host)
+        del host
+        out["streamed"]["without_overlap"] = {kk: base[kk] for kk in ("tokens", "tok_s_all", "tok_s_warm",
+                                                                     "h2d_GBps_effective_warm")}
     if not args.no_cpu_baseline:
         # the timed launch's output for the last token the oracle leg samples
         toks = list(range(0, n_tok, max(1, n_tok // args.cpu_tokens)))[:args.cpu_tokens]

@@ -832,6 +832,9 @@ struct StackArgs {
   void* out;
   uint32_t* status;           // the sticky status word (word 0 of the workspace, or the caller's word)
   int32_t n_layers, per_layer_blocks;
+  // 0: the whole layer; 1: the router and the shared expert only; 2: the routed experts and the combine only
+  // (the roles of part 2 after those of part 1 on the same workspace make one call)
+  int32_t part;
 };
 
 __device__ __forceinline__ SyncSet layer_set(uint32_t* sync, int line, int n_sub, int n_flags, uint32_t total) {
@@ -848,6 +851,13 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(const StackArgs 
   __shared__ RouteLds r;
   const int l = MULTI ? (int)blockIdx.x / sa.per_layer_blocks : 0;
   int b = MULTI ? (int)blockIdx.x % sa.per_layer_blocks : (int)blockIdx.x;
+  if (!MULTI && sa.part) {
+    // a part's grid holds only its roles: map the block to its role index in the whole layer's layout
+    // [router | shared gate/up | routed gate/up | shared down | routed down]
+    const LayerArgs& c = sa.base;
+    if (sa.part == 1) b = b < c.nR + c.nSG ? b : b + c.nRG;
+    else b = b < c.nRG ? c.nR + c.nSG + b : c.nR + c.nSG + c.nRG + c.nSD + (b - c.nRG);
+  }
   const bool last = !MULTI || l == sa.n_layers - 1;
   // this block's layer
   LayerArgs a = sa.base;
@@ -1052,7 +1062,8 @@ moe_status prepare_launch(const char* who, const void* x_dev, moe_dtype x_dtype,
 
 moe_status launch(const StackArgs& sa, moe_dtype x_dtype, bool sb16, int nbw, size_t lds, hipStream_t s,
                   const char* who) {
-  const dim3 grid(sa.per_layer_blocks * sa.n_layers);
+  const LayerArgs& c = sa.base;
+  const dim3 grid(sa.part == 1 ? c.nR + c.nSG + c.nSD : sa.part == 2 ? c.nRG + c.nRD : sa.per_layer_blocks * sa.n_layers);
   if (grid.x == 0) return MOE_OK;
   return dispatch_nbw(nbw, [&](auto nb) {
     constexpr int N = decltype(nb)::value;
@@ -1119,6 +1130,34 @@ extern "C" moe_status moe_decode_layer(const void* x_dev, moe_dtype x_dtype, con
   sa.layer[0] = StackLayer{router_w_dev, router_scale_dev, gamma_dev, static_cast<const char*>(routed->base_dev),
                            shared ? static_cast<const char*>(shared->base_dev) : nullptr, ids_dev, weights_dev,
                            logits_dev, u_dev};
+  return launch(sa, x_dtype, routed->sb_dtype == MOE_BF16, nbw, lds, as_stream(stream), who);
+}
+
+extern "C" moe_status moe_decode_layer_part(int32_t part, const void* x_dev, moe_dtype x_dtype, const float* gamma_dev,
+                                            float eps, int32_t residual, const int8_t* router_w_dev,
+                                            const float* router_scale_dev, int32_t E, int32_t k,
+                                            const int32_t* forced_ids_dev, const moe_q4_pool* routed,
+                                            const int32_t* gemv_ids_dev, const moe_q4_pool* shared, moe_act act,
+                                            int32_t* ids_dev, float* weights_dev, float* logits_dev, void* u_dev,
+                                            void* out_dev, void* workspace_dev, size_t workspace_bytes, void* stream) {
+  const char* who = "moe_decode_layer_part";
+  if (part != 1 && part != 2) return fail(MOE_ERR_INVALID_ARG, "%s: part %d (1 or 2)", who, part);
+  if (!router_w_dev || !router_scale_dev) return fail(MOE_ERR_INVALID_ARG, "%s: NULL pointer", who);
+  if (!shared) return fail(MOE_ERR_INVALID_ARG, "%s: the parts split off the shared expert, which is NULL", who);
+  if (!aligned(router_w_dev, 16) || (gamma_dev && !aligned(gamma_dev, 16)))
+    return fail(MOE_ERR_INVALID_ARG, "%s: router weights and gamma must be 16-byte aligned", who);
+  if (u_dev && (u_dev == x_dev || u_dev == out_dev)) return fail(MOE_ERR_INVALID_ARG, "%s: u must not alias x or out", who);
+  StackArgs sa{};
+  int nbw = 0;
+  size_t lds = 0;
+  moe_status st = prepare_launch(who, x_dev, x_dtype, eps, gamma_dev != nullptr, residual, E, k, routed, shared, act,
+                                 out_dev, workspace_dev, workspace_bytes, 1, &sa, &nbw, &lds);
+  if (st != MOE_OK) return st;
+  sa.part = part;
+  sa.base.forced = forced_ids_dev;
+  sa.base.gemv_ids = gemv_ids_dev;
+  sa.layer[0] = StackLayer{router_w_dev, router_scale_dev, gamma_dev, static_cast<const char*>(routed->base_dev),
+                           static_cast<const char*>(shared->base_dev), ids_dev, weights_dev, logits_dev, u_dev};
   return launch(sa, x_dtype, routed->sb_dtype == MOE_BF16, nbw, lds, as_stream(stream), who);
 }
 

@@ -168,6 +168,18 @@ class MoEDecoder:
                            self.layer_ws, self.layer_ws_bytes, stream,
                            u=None if self.u_all is None else self.u_all[l])
 
+    def layer_part(self, part: int, l: int, x_in: torch.Tensor, x_out: torch.Tensor,
+                   forced_ids: Optional[torch.Tensor] = None, routed_pool=None, ids: Optional[torch.Tensor] = None,
+                   stream=None) -> None:
+        """One layer as two launches (moe_decode_layer_part): part 1 = router + shared expert, part 2 = routed
+        experts + combine; call 1 then 2 (an expert cache may fill the routed slots in between)."""
+        s, L = self.shape, self.layers[l]
+        q.moe_decode_layer_part(part, x_in, s.x_dtype, L.gamma if s.rms_norm else None, s.eps, s.rms_norm, L.router_w,
+                                L.router_s, s.n_experts, s.k, forced_ids, routed_pool or self.routed_pools[l], ids,
+                                self.shared_pools[l], s.act, self.ids_all[l], self.weights_all[l], self.logits_all[l],
+                                None if self.u_all is None else self.u_all[l], x_out, self.layer_ws,
+                                self.layer_ws_bytes, stream)
+
     def _layer_fused(self, l, x_in, x_out, forced_ids, routed_pool, ids, stream) -> None:
         s, L, T = self.shape, self.layers[l], self.T
         lid, lw, lg = self.ids_all[l], self.weights_all[l], self.logits_all[l]

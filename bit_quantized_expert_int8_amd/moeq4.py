@@ -91,6 +91,10 @@ _c = {
                              [_vp, ctypes.c_int, _vp, ctypes.c_float, _i32, _vp, _vp, _i32, _i32, _vp,
                               ctypes.POINTER(moe_q4_pool), _vp, ctypes.POINTER(moe_q4_pool), ctypes.c_int, _vp, _vp,
                               _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_decode_layer_part": _sig("moe_decode_layer_part", _st,
+                                  [_i32, _vp, ctypes.c_int, _vp, ctypes.c_float, _i32, _vp, _vp, _i32, _i32, _vp,
+                                   ctypes.POINTER(moe_q4_pool), _vp, ctypes.POINTER(moe_q4_pool), ctypes.c_int, _vp, _vp,
+                                   _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_decode_layer_noalloc": _sig("moe_decode_layer_noalloc", _st,
                                      [_vp, ctypes.c_int, _vp, ctypes.c_float, _i32, _vp, _vp, _i32, _i32, _vp,
                                       ctypes.POINTER(moe_q4_pool), _vp, ctypes.POINTER(moe_q4_pool), ctypes.c_int, _vp,
@@ -258,6 +262,15 @@ def moe_decode_layer(x, x_dtype, gamma, eps, residual, router_w, router_scale, E
                                   _p(forced_ids), _pp(routed), _p(gemv_ids), _pp(shared), act, _p(ids), _p(weights),
                                   _p(logits), _p(u), _p(out), _p(workspace), workspace_bytes, _s(stream)),
            "moe_decode_layer")
+
+
+def moe_decode_layer_part(part, x, x_dtype, gamma, eps, residual, router_w, router_scale, E, k, forced_ids, routed,
+                          gemv_ids, shared, act, ids, weights, logits, u, out, workspace, workspace_bytes,
+                          stream=None) -> None:
+    _check(_c["moe_decode_layer_part"](part, _p(x), x_dtype, _p(gamma), eps, int(residual), _p(router_w),
+                                       _p(router_scale), E, k, _p(forced_ids), _pp(routed), _p(gemv_ids), _pp(shared),
+                                       act, _p(ids), _p(weights), _p(logits), _p(u), _p(out), _p(workspace),
+                                       workspace_bytes, _s(stream)), "moe_decode_layer_part")
 
 
 MOE_DECODE_LAYER_NOALLOC_MAX_BYTES = 1 << 20

@@ -287,6 +287,27 @@ moe_status moe_decode_layer(const void* x_dev, moe_dtype x_dtype, const float* g
                             size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------------
+ * moe_decode_layer_part — moe_decode_layer as two launches, so that the routed experts' weights can arrive
+ * in between ([G26] "Concurrence pour masquer la latence": the shared expert computes while the missing
+ * experts are fetched, the two branches are merged once they are in; [DAILY] "3. Cache intelligent +
+ * Chevauchement temporel").  part 1 runs the router (logits, top-k) and the whole shared expert and leaves
+ * them in the workspace; part 2 runs the routed experts and the combine (with the residual) and writes
+ * out, ids and weights.  Arguments, limits and errors as moe_decode_layer; shared must not be NULL; logits
+ * and u are written by part 1, ids, weights and out by part 2.  A call of part 1 followed by part 2 with the
+ * same arguments on the same workspace (part 2 ordered after part 1, e.g. on the same stream) equals one
+ * moe_decode_layer call bit for bit; a workspace may alternate such pairs with whole calls, but every part 1
+ * must be followed by its part 2 before anything else uses the workspace.  The routed pool and gemv ids
+ * are read only by part 2: an expert cache may fill its slots between the parts (expert_cache_stage's
+ * ready event waited on before part 2).
+ * ------------------------------------------------------------------------------------------------- */
+moe_status moe_decode_layer_part(int32_t part, const void* x_dev, moe_dtype x_dtype, const float* gamma_dev,
+                                 float eps, int32_t residual, const int8_t* router_w_dev,
+                                 const float* router_scale_dev, int32_t E, int32_t k, const int32_t* forced_ids_dev,
+                                 const moe_q4_pool* routed, const int32_t* gemv_ids_dev, const moe_q4_pool* shared,
+                                 moe_act act, int32_t* ids_dev, float* weights_dev, float* logits_dev, void* u_dev,
+                                 void* out_dev, void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------------
  * moe_decode_layer_noalloc — moe_decode_layer for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same computation, kernels
  * and results, with the workspace in a device array the library holds instead of a caller workspace.

@@ -10,7 +10,7 @@ pytestmark = pytest.mark.gpu
 import synth  # noqa: E402
 from oracle import moe  # noqa: E402
 from oracle import inputs as oin  # noqa: E402
-from bit_quantized_expert_int8_amd import moeq4 as q  # noqa: E402
+from bit_quantized_expert_int8_amd import decoder, moeq4 as q  # noqa: E402
 import gpu_helpers as H  # noqa: E402
 
 TOL = 1e-2
@@ -297,3 +297,114 @@ def test_decode_layer_exact_logit_tie(tiny_layer):
             elif 6 in ids_l:
                 pytest.fail(f"expert 6 selected without its tie partner 2: {ids_l}")
     assert seen_tie >= 12   # with k = E both are always selected
+
+
+# ---------------------------------------------------------------------------------------------------
+# the layer in two launches (router + shared expert, then routed experts + combine)
+# ---------------------------------------------------------------------------------------------------
+
+def _run_parts(cfg, dev, shape, x, ws, ws_b, gamma, residual, forced=None, routed=None, gemv_ids=None, u=None):
+    rp, sp = _pools(cfg, dev, shape)
+    ids = torch.full((cfg.k,), -5, dtype=torch.int32, device="cuda")
+    w = torch.empty((cfg.k,), dtype=torch.float32, device="cuda")
+    lg = torch.empty((cfg.n_experts,), dtype=torch.float32, device="cuda")
+    out = torch.empty_like(x)
+    xdt = q.MOE_BF16 if cfg.x_bf16 else q.MOE_F32
+    for part in (1, 2):
+        q.moe_decode_layer_part(part, x, xdt, gamma, 1e-6, residual, dev.router_w, dev.router_s, cfg.n_experts, cfg.k,
+                                forced, routed or rp, gemv_ids, sp, shape.act, ids, w, lg, u, out, ws, ws_b)
+    return ids, w, lg, out
+
+
+def test_decode_layer_parts_equal_whole_calls(stack_layer):
+    """Part 1 then part 2 on one workspace equal one moe_decode_layer call bit for bit (routing, weights,
+    logits, normalized activation, output), with self-routing and with forced routing through cache slots,
+    alternating with whole calls on the same workspace; the synchronisation words stay consistent."""
+    cfg, dev, shape = stack_layer
+    gamma = torch.from_numpy(synth.rms_gamma(cfg.weight_cfg, 0, cfg.d, ones=False)).cuda()
+    trace = synth.zipf_trace(21, 2, 1, cfg.k, cfg.n_experts, 1.1)[:, 0, :]
+    rb = dev.pool.shape[1]
+    ws, ws_b = _ws(cfg)
+    ws2, _ = _ws(cfg)
+    calls = 0
+    for t, tok in enumerate((4, 90, 91, 250)):
+        x = H.token_batch(cfg, [tok])[0]
+        forced = routed = gemv_ids = None
+        if t >= 2:   # forced routing, experts read through slots
+            forced = torch.from_numpy(trace[t - 2].astype(np.int32)).cuda()
+            slots = torch.zeros((16, rb), dtype=torch.uint8, device="cuda")
+            slot_of = (np.arange(cfg.k) * 3 + 1 + t) % 16
+            for i, e in enumerate(trace[t - 2]):
+                slots[slot_of[i]].copy_(dev.pool[int(e)])
+            routed = q.pool(slots, rb, 16, cfg.d, cfg.F, shape.sb_dtype)
+            gemv_ids = torch.from_numpy(slot_of.astype(np.int32)).cuda()
+        ua = torch.empty((cfg.d,), dtype=torch.bfloat16, device="cuda")
+        ub = torch.empty_like(ua)
+        a = _run(cfg, dev, shape, x, ws2, ws_b, gamma, 1, forced=forced,
+                 routed=None if forced is None else q.pool(dev.pool, rb, cfg.n_experts, cfg.d, cfg.F, shape.sb_dtype),
+                 u=ua)
+        b = _run_parts(cfg, dev, shape, x, ws, ws_b, gamma, 1, forced, routed, gemv_ids, ub)
+        calls += 1
+        _check_clean(ws, cfg, calls)
+        for name, ta, tb in zip(("ids", "weights", "logits", "out"), a, b):
+            assert torch.equal(ta, tb), f"token {tok}: {name}"
+        assert torch.equal(ua, ub), f"token {tok}: u"
+        # a whole call on the same workspace in between
+        _run(cfg, dev, shape, x, ws, ws_b, gamma, 1)
+        calls += 1
+        _check_clean(ws, cfg, calls)
+
+
+def test_shared_expert_runs_inside_the_expert_copy_window():
+    """Expert-cache streaming with the layer in two launches: part 1 (router and shared expert) runs on the
+    compute stream while the layer's missing experts are copied from pinned host memory on the copy stream,
+    and part 2 waits for the copies.  Event timestamps: part 1 starts after the copies start and ends before
+    they end; the layer's output equals the resident run bit for bit."""
+    cfg = synth.STREAMED
+    dev = H.device_layer(cfg, 0)
+    shape = H.shape_of(cfg)
+    k, E, n_slots = cfg.k, cfg.n_experts, cfg.n_slots
+    rb = dev.pool.shape[1]
+    host = [dev.pool.cpu().pin_memory()]
+    slots = torch.empty((n_slots, rb), dtype=torch.uint8, device="cuda")
+    cache = q.moe_expert_cache_create(1, E, n_slots, rb, [host[0].data_ptr()], [slots.data_ptr()])
+    dec = decoder.MoEDecoder(shape, [dev], T=1)
+    slot_pool = q.pool(slots, rb, n_slots, cfg.d, cfg.F, shape.sb_dtype)
+    copy_stream = torch.cuda.Stream()
+    compute = torch.cuda.current_stream()
+    ready = torch.cuda.Event()
+    ready.record(copy_stream)
+    copy_stream.synchronize()
+    slot_ids = torch.empty((k,), dtype=torch.int32, device="cuda")
+    trace = synth.zipf_trace(31, 1, 1, k, E, 1.1)[0, 0]
+    forced = torch.from_numpy(trace.astype(np.int32)).cuda()
+    x = H.token_batch(cfg, [7])
+    out, ref = torch.empty_like(x), torch.empty_like(x)
+    ev = {n: torch.cuda.Event(enable_timing=True) for n in ("c0", "c1", "p0", "p1", "e")}
+    try:
+        torch.cuda.synchronize()
+        ev["c0"].record(copy_stream)
+        q.expert_cache_stage(cache, 0, trace.tolist(), slot_ids, copy_stream, None, ready)   # cold: 8 misses
+        ev["c1"].record(copy_stream)
+        compute.wait_event(ev["c0"])
+        ev["p0"].record(compute)
+        dec.layer_part(1, 0, x, out, forced_ids=forced.reshape(1, k), routed_pool=slot_pool, ids=slot_ids.reshape(1, k))
+        ev["p1"].record(compute)
+        compute.wait_event(ready)
+        dec.layer_part(2, 0, x, out, forced_ids=forced.reshape(1, k), routed_pool=slot_pool, ids=slot_ids.reshape(1, k))
+        ev["e"].record(compute)
+        torch.cuda.synchronize()
+        dec.check_status()
+        copy_ms = ev["c0"].elapsed_time(ev["c1"])
+        p1_ms = ev["p0"].elapsed_time(ev["p1"])
+        print(f"copies {copy_ms * 1e3:.0f} us; part 1 from {ev['c0'].elapsed_time(ev['p0']) * 1e3:.1f} to "
+              f"{ev['c0'].elapsed_time(ev['p1']) * 1e3:.1f} us; part 2 ends at {ev['c0'].elapsed_time(ev['e']) * 1e3:.0f} us")
+        assert ev["c0"].elapsed_time(ev["p0"]) >= 0.0           # part 1 starts after the copies start
+        assert ev["p1"].elapsed_time(ev["c1"]) > 0.0            # and ends before they end
+        assert p1_ms < copy_ms
+        assert ev["c1"].elapsed_time(ev["e"]) > 0.0             # part 2 ends after the copies
+        dec.layer(0, x, ref, forced_ids=forced.reshape(1, k))
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+    finally:
+        q.moe_expert_cache_destroy(cache)
