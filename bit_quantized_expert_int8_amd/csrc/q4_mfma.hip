@@ -24,6 +24,10 @@
 // within a group is a permutation shared by A and B).  The waves of a tile split the row's groups; their
 // 16 x 16 partial results are added in LDS in wave order.  Results match the one-token kernels within
 // rounding (the activation is scaled per token row, not per 32 values).
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "q4_grouping.h"
 
 namespace moeq4 {
@@ -383,15 +387,330 @@ __device__ __forceinline__ void mfma_item(const MfmaArgs& a, bool shared, int e,
   }
 }
 
-// The grid is one wave of resident blocks.  Routed work comes as chunks (runs of at most 16 pairs of one
-// expert, so a chunk is one pass of the token loop).  Each block reads the chunk count c and splits the
-// work the same way: the shared matrix gets blocks in proportion to its steps (times its token chunks)
-// against the routed steps of the c chunks, and splits its steps evenly over them; with R blocks left,
-// block b takes part b / c of chunk b % c when c < R (each chunk's steps split as evenly as the blocks
-// allow), else chunks b, b + R, ... whole.
+// ---------------------------------------------------------------------------------------------------------
+// The ring variant (at most 11 groups per wave, every row length up to 44 groups with 4 waves a tile).
+//
+// Streaming was the limit of the register-staged item above: with the activations of a chunk held in
+// registers a wave has room for one step of code words in flight, and at two waves per SIMD that is about
+// 48 KiB per compute unit, too little to cover the memory latency under full load.  Here the code words and
+// the scale/bias words go from memory straight into LDS (buffer loads with the LDS bit), two slots per wave:
+// while step s is multiplied, steps s + 1 and s + 2 are in flight, about 100 KiB per compute unit, and no
+// register holds them.  At the start of a step the wave waits for its slot's loads (a vmcnt that leaves the
+// next step's loads in flight), reads the slot into registers and refills it with step s + 2.
+//
+// The wait is written by hand: the compiler's own wait before an LDS read that a load may have written is
+// vmcnt(0) whenever a store is also outstanding, which would drain the ring at every step.  The slot reads
+// are therefore inline assembly (ending in their own lgkmcnt(0)), invisible to the compiler as LDS reads,
+// after an explicit vmcnt(N), N the loads issued after the slot's (the next step's).  Loads return in order,
+// so the wait holds whatever the stores do; the outputs of step s are stored at the start of step s + 1,
+// before its loads are issued, so that they are old by the time a wait could cover them.
+//
+// The products also drop the 1024 offset of the code-to-fp16 step: a code word masked with 0x000F000F (and
+// its siblings) is, as fp16 bits, the subnormal pair (n0 2^-24, n4 2^-24), which the matrix cores multiply
+// exactly.  A group's MFMA sum is then sum_c q_c x_c 2^-(e+24) with no cancellation, and
+//   y = 2^(e+24) (sum_g scale_g acc_g + sum_g bias_g Sx_g 2^-24),
+// the bias sum as fp32 MFMAs (16 tokens x 4 groups x 16 rows) on the chunk's Sx values.
 template <int NG, bool SB_BF16>
-__global__ __launch_bounds__(kThreadsG) void grouped_mfma_kernel(MfmaArgs a) {
-  extern __shared__ __align__(16) uint32_t lds[];
+struct Ring {
+  static constexpr int kSbWords = SB_BF16 ? 1 : 2;          // 32-bit scale/bias words per (row, group)
+  static constexpr int kCodeLoads = (NG + 1) / 2;           // 1 KiB loads (two groups of 16 rows each)
+  static constexpr int kCode = kCodeLoads * 1024;           // bytes of a wave's slot (the odd group's pad)
+  static constexpr int kSbUsed = 16 * NG * kSbWords;        // scale/bias words of a wave's step
+  static constexpr int kSbLoads = (kSbUsed + 63) / 64;      // 256-byte loads (one word a lane)
+  static constexpr int kSb = kSbLoads * 64;                 // words of a wave's slot
+  static constexpr int kBias = (NG + 3) / 4;                // bias MFMAs (4 groups each)
+  static constexpr int kLoads = kCodeLoads + kSbLoads;      // loads of one step
+  static_assert(kLoads <= 31, "two steps of loads must fit the 6-bit vmcnt");
+  static_assert(NG <= 11, "the slot reads are two asm blocks of at most 11 pairs");
+};
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt vmcnt(N) (the other counters not waited for), as a builtin so that the compiler counts it.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "6-bit vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// The block's LDS writes done, then the barrier.  __syncthreads would also wait for every load in flight
+// (the slot loads write LDS), which would drain the ring at each step.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Reads of a slot in inline assembly (the compiler does not see them as LDS reads, so it places no wait of
+// its own for the slot's loads): pairs of 32-bit words at byte offsets i * 512 and words at i * 4 * W from
+// two base addresses, after an explicit vmcnt(N); each block ends with its reads complete.
+#define MOE_RD64(i) "ds_read_b64 %" #i ", %[pa] offset:" #i "*512\n\t"
+template <int N, int NG, int W>
+__device__ __forceinline__ void read_slot(const char* pa, const uint32_t* pb, const uint32_t* pc, u32x2 (&q)[NG],
+                                          uint32_t (&sw)[NG], uint32_t (&bw)[(NG + 3) / 4]) {
+  static_assert(NG == 4 || NG == 8 || NG == 11, "slot shapes");
+  const uint32_t ua = (uint32_t)(uintptr_t)pa, ub = (uint32_t)(uintptr_t)pb, uc = (uint32_t)(uintptr_t)pc;
+  if constexpr (NG == 4) {
+    asm volatile("s_waitcnt vmcnt(%[n])\n\t" MOE_RD64(0) MOE_RD64(1) MOE_RD64(2) MOE_RD64(3) "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3])
+                 : [pa] "v"(ua), [n] "n"(N)
+                 : "memory");
+  } else if constexpr (NG == 8) {
+    asm volatile("s_waitcnt vmcnt(%[n])\n\t" MOE_RD64(0) MOE_RD64(1) MOE_RD64(2) MOE_RD64(3) MOE_RD64(4) MOE_RD64(5)
+                     MOE_RD64(6) MOE_RD64(7) "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3]), "=&v"(q[4]), "=&v"(q[5]), "=&v"(q[6]),
+                   "=&v"(q[7])
+                 : [pa] "v"(ua), [n] "n"(N)
+                 : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(%[n])\n\t" MOE_RD64(0) MOE_RD64(1) MOE_RD64(2) MOE_RD64(3) MOE_RD64(4) MOE_RD64(5)
+                     MOE_RD64(6) MOE_RD64(7) MOE_RD64(8) MOE_RD64(9) MOE_RD64(10) "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3]), "=&v"(q[4]), "=&v"(q[5]), "=&v"(q[6]),
+                   "=&v"(q[7]), "=&v"(q[8]), "=&v"(q[9]), "=&v"(q[10])
+                 : [pa] "v"(ua), [n] "n"(N)
+                 : "memory");
+  }
+  // scale words (group i at i * 4 W) and bias words (group 4 j + kb at pc + 16 j W); the slot's loads are
+  // already complete
+  constexpr int B = (NG + 3) / 4;
+  uint32_t t[11 + 3];
+#define MOE_S(i) "ds_read_b32 %" #i ", %[pb] offset:" #i "*%[w4]\n\t"
+  if constexpr (NG == 4) {
+    asm volatile(MOE_S(0) MOE_S(1) MOE_S(2) MOE_S(3) "ds_read_b32 %4, %[pc]\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4])
+                 : [pb] "v"(ub), [pc] "v"(uc), [w4] "n"(4 * W)
+                 : "memory");
+  } else if constexpr (NG == 8) {
+    asm volatile(MOE_S(0) MOE_S(1) MOE_S(2) MOE_S(3) MOE_S(4) MOE_S(5) MOE_S(6) MOE_S(7)
+                 "ds_read_b32 %8, %[pc]\n\tds_read_b32 %9, %[pc] offset:%[o1]\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]),
+                   "=&v"(t[7]), "=&v"(t[8]), "=&v"(t[9])
+                 : [pb] "v"(ub), [pc] "v"(uc), [o1] "n"(16 * W), [w4] "n"(4 * W)
+                 : "memory");
+  } else {
+    asm volatile(MOE_S(0) MOE_S(1) MOE_S(2) MOE_S(3) MOE_S(4) MOE_S(5) MOE_S(6) MOE_S(7) MOE_S(8) MOE_S(9) MOE_S(10)
+                 "ds_read_b32 %11, %[pc]\n\tds_read_b32 %12, %[pc] offset:%[o1]\n\t"
+                 "ds_read_b32 %13, %[pc] offset:%[o2]\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]),
+                   "=&v"(t[7]), "=&v"(t[8]), "=&v"(t[9]), "=&v"(t[10]), "=&v"(t[11]), "=&v"(t[12]), "=&v"(t[13])
+                 : [pb] "v"(ub), [pc] "v"(uc), [o1] "n"(16 * W), [o2] "n"(32 * W), [w4] "n"(4 * W)
+                 : "memory");
+  }
+#undef MOE_S
+#pragma unroll
+  for (int i = 0; i < NG; ++i) sw[i] = t[i];
+#pragma unroll
+  for (int j = 0; j < B; ++j) bw[j] = t[NG + j];
+}
+#undef MOE_RD64
+
+template <int NG, bool SB_BF16>
+__device__ __forceinline__ void ring_item(const MfmaArgs& a, bool shared, int e, bool valid, int start, int count,
+                                          int s0, int s1) {
+  using R = Ring<NG, SB_BF16>;
+  constexpr int W = R::kSbWords;
+  __shared__ __align__(16) char code0[kWavesG * R::kCode];
+  __shared__ __align__(16) char code1[kWavesG * R::kCode];
+  __shared__ __align__(16) uint32_t sbl0[kWavesG * R::kSb];
+  __shared__ __align__(16) uint32_t sbl1[kWavesG * R::kSb];
+  __shared__ float red0[kWavesG * 256], red1[kWavesG * 256];   // [wave][16 tokens][16 rows], by step parity
+  __shared__ float ef_l[16];
+  __shared__ int srow_l[16], orow_l[16];
+
+  const Pool P = shared ? a.shared : a.routed;
+  const StagedRows xs = shared ? a.xs_shared : a.xs_routed;
+  const int K = shared ? a.K_shared : a.K_routed, wk = shared ? a.wk_shared : a.wk_routed;
+  const int n_tiles = shared ? a.tiles_shared : a.tiles_routed;
+  float* const out = shared ? a.out_shared : a.out_routed;
+  const int out_len = shared ? a.out_len_shared : a.out_len_routed;
+  const int G = K / 64, tps = kWavesG / wk;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, n = lane & 15,
+            kb = lane >> 4;
+  const int part = wave % wk, wt = wave / wk;
+  const int g0 = (part * G) / wk, nw = ((part + 1) * G) / wk - g0;
+  const char* rec = P.base + (int64_t)e * P.record_bytes;
+  const int sb_row = G * 4 * W;
+  const int mat_rows = a.gate_up ? 2 * P.F : n_tiles * 16;
+  const __amdgpu_buffer_rsrc_t qr = buf_rsrc(rec + P.off_q, (uint32_t)mat_rows * (K / 2));
+  const __amdgpu_buffer_rsrc_t sr = buf_rsrc(rec + P.off_sb, (uint32_t)mat_rows * sb_row);
+  const __amdgpu_buffer_rsrc_t ar = buf_rsrc(xs.xq, (uint32_t)xs.rows * K * 2);
+  // row r of a tile: tile t's rows start t * rpt rows further (gate/up: 8 gate rows, then the 8 matching up
+  // rows F further)
+  const int rpt = a.gate_up ? 8 : 16;
+  auto row0 = [&](int r) { return a.gate_up ? (r < 8 ? r : P.F + r - 8) : r; };
+  // lane offsets of the loads into the slots.  Code load j, lane l: group 2 j + l / 32 of the wave, half
+  // (l / 16) % 2 of it, row l % 16 (so group i of the slot is 512 bytes at i * 512, half h at + 256 h, row r
+  // at + 16 r: an operand read of one group is 512 contiguous bytes).  Scale/bias load j, lane l: word
+  // 64 j + l of the wave's [16 rows][NG groups][W] words.  Lanes past the wave's groups read other bytes of
+  // the matrix, or zeros past its end, into the slot's padding or into groups that carry weight 0.
+  const uint32_t code_lane = (uint32_t)(row0(n) * (K / 2) + (lane >> 5) * 32 + ((lane >> 4) & 1) * 16 + g0 * 32);
+  uint32_t sb_lane[R::kSbLoads];
+#pragma unroll
+  for (int j = 0; j < R::kSbLoads; ++j) {
+    const int w = min(64 * j + lane, R::kSbUsed - 1);
+    const int r = w / (NG * W), c = w % (NG * W);
+    sb_lane[j] = (uint32_t)(row0(r) * sb_row + g0 * 4 * W + 4 * c);
+  }
+  // step s's words into slot SL; past the last step the offsets lie outside the buffers (zeros, no traffic),
+  // so that every step issues the same loads and the waits stay exact
+  auto issue = [&](auto slot_c, int s) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot_c)::value;
+    char* cb = (SL ? code1 : code0) + wave * R::kCode;
+    uint32_t* sbb = (SL ? sbl1 : sbl0) + wave * R::kSb;
+    const int t = min(s * tps + wt, n_tiles - 1);
+    const uint32_t cbase = s < s1 ? (uint32_t)(t * rpt) * (uint32_t)(K / 2) : 0x80000000u;
+    const uint32_t sbase = s < s1 ? (uint32_t)(t * rpt) * (uint32_t)sb_row : 0x80000000u;
+#pragma unroll
+    for (int j = 0; j < R::kCodeLoads; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_ptr_t)(cb + 1024 * j), 16, cbase + code_lane + 64 * j, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < R::kSbLoads; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_t)(sbb + 64 * j), 4, sbase + sb_lane[j], 0, 0, 0);
+  };
+
+  for (int c0 = 0; c0 < count; c0 += 16) {
+    const int nlive = min(16, count - c0);
+    // the first step's loads go out first (they depend on the expert only); then the chunk's tokens: staged
+    // row and output row (slots past the last token repeat the first token's staged row; their results are
+    // not stored)
+    issue(std::integral_constant<int, 0>(), s0);
+    if ((int)threadIdx.x < 16) {
+      const int m = threadIdx.x;
+      const int mm = m < nlive ? m : 0;
+      const int pr = shared ? c0 + mm : a.perm[start + c0 + mm];
+      srow_l[m] = (shared || !a.gate_up) ? pr : pr / a.k;
+      orow_l[m] = pr;
+    }
+    lds_barrier();
+    // A of this wave's groups for the whole chunk (indices clamped into the row past the wave's range), the
+    // bias MFMAs' A (Sx of token n, group 4 j + kb) and the tokens' 2^e; then the second step's loads, and a
+    // wait that leaves exactly those in flight (a wait the compiler sees, so it adds none of its own)
+    const int srow = srow_l[n];
+    const int a_off = (srow * K + 16 * kb) * 2;
+    half8 A0[NG], A1[NG];
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const int gi = min(g0 + i, G - 1);
+      A0[i] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(ar, a_off, gi * 128, 0));
+      A1[i] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(ar, a_off + 16, gi * 128, 0));
+    }
+    float sx[R::kBias];
+#pragma unroll
+    for (int j = 0; j < R::kBias; ++j) sx[j] = xs.os[(int64_t)srow * G + min(g0 + 4 * j + kb, G - 1)].y;
+    const float ef = xs.ef[srow_l[threadIdx.x & 15]];
+    __builtin_amdgcn_sched_barrier(0);   // the operand loads before the second step's
+    issue(std::integral_constant<int, 1>(), s0 + 1);
+    wait_vm<R::kLoads>();
+    // 2^(e + 24) per token (the products carry 2^-24), read in the steps' reductions after a barrier
+    if ((int)threadIdx.x < 16) ef_l[threadIdx.x] = (int)threadIdx.x < nlive ? ef * 16777216.0f : 0.f;
+#pragma unroll
+    for (int j = 0; j < R::kBias; ++j) sx[j] *= 0x1p-24f;
+
+    // a step's outputs (stored at the start of the next step): the reduction leaves output (m, nn) of tile
+    // tt in place of wave tt * wk's partial sum of it in red, which only this thread reads
+    auto out_slot = [&](int it, int s, int& m, int& nn, int& tile) __attribute__((always_inline)) {
+      const int idx = threadIdx.x + it * kThreadsG, tt = idx >> 8;
+      m = (idx >> 4) & 15;
+      nn = idx & 15;
+      tile = s * tps + tt;
+      return it < tps && m < nlive && tile < n_tiles && !(a.gate_up && nn >= 8);
+    };
+    auto flush = [&](const float* red, int s) __attribute__((always_inline)) {
+#pragma unroll
+      for (int it = 0; it < kWavesG; ++it) {
+        int m, nn, tile;
+        if (out_slot(it, s, m, nn, tile))
+          out[(int64_t)orow_l[m] * out_len + tile * (a.gate_up ? 8 : 16) + nn] =
+              red[((tile - s * tps) * wk) * 256 + m * 16 + nn];
+      }
+    };
+
+    auto step = [&](auto slot_c, int s) __attribute__((always_inline)) {
+      constexpr int SL = decltype(slot_c)::value;
+      const char* cb = (SL ? code1 : code0) + wave * R::kCode;
+      const uint32_t* sbb = (SL ? sbl1 : sbl0) + wave * R::kSb;
+      float* red = SL ? red1 : red0;
+      // the slot into registers (row n's words 2 kb, 2 kb + 1 of each group, its scale words, and the bias
+      // words of groups 4 j + kb), once the step's loads have arrived: at most the next step's are in flight
+      u32x2 qw[NG];
+      uint32_t sw[NG], bw[R::kBias];
+      const uint32_t* sp = sbb + n * NG * W;
+      read_slot<R::kLoads, NG, W>(cb + (kb >> 1) * 256 + n * 16 + (kb & 1) * 8, sp, sp + kb * W + (W - 1), qw, sw, bw);
+      // the previous step's outputs, then step s + 2's loads into the slot just read
+      if (s > s0) flush(SL ? red0 : red1, s - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(slot_c, s + 2);
+      const Dequant dq = opaque_dequant();
+      uint32_t sh8 = 8;
+      asm volatile("" : "+v"(sh8));
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        const uint32_t w0 = qw[i].x, w1 = qw[i].y, t0 = w0 >> sh8, t1 = w1 >> sh8;
+        u32x4 b0, b1;
+        b0.x = w0 & dq.lo;
+        b0.y = w0 & dq.hi;
+        b0.z = t0 & dq.lo;
+        b0.w = t0 & dq.hi;
+        b1.x = w1 & dq.lo;
+        b1.y = w1 & dq.hi;
+        b1.z = t1 & dq.lo;
+        b1.w = t1 & dq.hi;
+        float sc = SB_BF16 ? __uint_as_float(sw[i] << 16) : __uint_as_float(sw[i]);
+        if (i >= nw) sc = 0.f;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0[i], __builtin_bit_cast(half8, b0), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1[i], __builtin_bit_cast(half8, b1), acc, 0, 0, 0);
+        y[0] = fmaf(sc, acc[0], y[0]);
+        y[1] = fmaf(sc, acc[1], y[1]);
+        y[2] = fmaf(sc, acc[2], y[2]);
+        y[3] = fmaf(sc, acc[3], y[3]);
+      }
+#pragma unroll
+      for (int j = 0; j < R::kBias; ++j) {
+        const float b = SB_BF16 ? __uint_as_float(bw[j] & 0xffff0000u) : __uint_as_float(bw[j]);
+        y = __builtin_amdgcn_mfma_f32_16x16x4f32(sx[j], 4 * j + kb < nw ? b : 0.f, y, 0, 0, 0);
+      }
+      // the waves' partial tiles, added in wave order (red alternates with the step, so one barrier a step)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave * 256 + (4 * kb + i) * 16 + n] = y[i];
+      lds_barrier();
+#pragma unroll
+      for (int it = 0; it < kWavesG; ++it) {
+        int m, nn, tile;
+        if (!out_slot(it, s, m, nn, tile)) continue;
+        const int tt = tile - s * tps;
+        auto total = [&](int col) {
+          float v = red[(tt * wk) * 256 + m * 16 + col];
+          for (int w = 1; w < wk; ++w) v += red[(tt * wk + w) * 256 + m * 16 + col];
+          return v;
+        };
+        const float sc = ef_l[m];
+        float v;
+        if (!valid) v = __builtin_nanf("");
+        else if (a.gate_up) v = activation(sc * total(nn), a.act) * (sc * total(nn + 8));
+        else v = sc * total(nn);
+        red[(tt * wk) * 256 + m * 16 + nn] = v;
+      }
+    };
+    int s = s0;
+    for (; s + 1 < s1; s += 2) {
+      step(std::integral_constant<int, 0>(), s);
+      step(std::integral_constant<int, 1>(), s + 1);
+    }
+    if (s < s1) step(std::integral_constant<int, 0>(), s);
+    flush(((s1 - s0) & 1) ? red0 : red1, s1 - 1);
+    // the loads past the last step (zeros) land, and every wave is done with red and the token rows, before
+    // they are written again or the block ends
+    wait_vm<0>();
+    lds_barrier();
+  }
+}
+
+// The work of a block.  The grid is one wave of resident blocks.  Routed work comes as chunks (runs of at
+// most 16 pairs of one expert, so a chunk is one pass of the token loop).  Each block reads the chunk count
+// c and splits the work the same way: the shared matrix gets blocks in proportion to its steps (times its
+// token chunks) against the routed steps of the c chunks, and splits its steps evenly over them; with R
+// blocks left, block b takes part b / c of chunk b % c when c < R (each chunk's steps split as evenly as the
+// blocks allow), else chunks b, b + R, ... whole.
+template <typename Item>
+__device__ __forceinline__ void block_work(const MfmaArgs& a, Item&& item) {
   const int b = blockIdx.x, nb = gridDim.x;
   const int ng = a.steps_routed > 0 ? *a.n_chunks : 0;
   int nsb = 0;
@@ -407,7 +726,7 @@ __global__ __launch_bounds__(kThreadsG) void grouped_mfma_kernel(MfmaArgs a) {
   if (b < nsb) {
     const int spb = (a.steps_shared + nsb - 1) / nsb;
     const int s0 = b * spb, s1 = min(s0 + spb, a.steps_shared);
-    if (s0 < s1) mfma_item<NG, SB_BF16>(a, true, 0, true, 0, a.T, s0, s1, lds);
+    if (s0 < s1) item(true, 0, true, 0, a.T, s0, s1);
     return;
   }
   if (ng <= 0) return;
@@ -422,9 +741,24 @@ __global__ __launch_bounds__(kThreadsG) void grouped_mfma_kernel(MfmaArgs a) {
     }
     const int4 g = a.chunks[j];
     const bool valid = (unsigned)g.x < (unsigned)a.routed.n_records;
-    if (s0 < s1) mfma_item<NG, SB_BF16>(a, false, valid ? g.x : 0, valid, g.y, g.z, s0, s1, lds);
+    if (s0 < s1) item(false, valid ? g.x : 0, valid, g.y, g.z, s0, s1);
     if (ng < R) break;
   }
+}
+
+template <int NG, bool SB_BF16>
+__global__ __launch_bounds__(kThreadsG) void grouped_mfma_kernel(MfmaArgs a) {
+  extern __shared__ __align__(16) uint32_t lds[];
+  block_work(a, [&](bool shared, int e, bool valid, int start, int count, int s0, int s1) __attribute__((always_inline)) {
+    mfma_item<NG, SB_BF16>(a, shared, e, valid, start, count, s0, s1, lds);
+  });
+}
+
+template <int NG, bool SB_BF16>
+__global__ __launch_bounds__(kThreadsG, 2) void grouped_ring_kernel(MfmaArgs a) {
+  block_work(a, [&](bool shared, int e, bool valid, int start, int count, int s0, int s1) __attribute__((always_inline)) {
+    ring_item<NG, SB_BF16>(a, shared, e, valid, start, count, s0, s1);
+  });
 }
 
 }  // namespace
@@ -496,19 +830,36 @@ moe_status launch_grouped_mfma(MfmaArgs a, bool has_shared, bool has_routed, boo
     per_wave = max(per_wave, (a.K_routed / 64 + a.wk_routed - 1) / a.wk_routed);
     kmax = max(kmax, a.K_routed);
   }
+  // as many blocks as are resident at once, per (device, kernel, dynamic LDS): the count the runtime
+  // reports for this exact launch shape
+  auto resident = [](const void* kern, size_t lds) {
+    static std::mutex mu;
+    static std::map<std::tuple<int, const void*, size_t>, int> cache;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    std::lock_guard<std::mutex> lock(mu);
+    const auto key = std::make_tuple(dev, kern, lds);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreadsG, lds) != hipSuccess || per_cu < 1)
+      per_cu = 1;
+    cache.emplace(key, per_cu);
+    return per_cu;
+  };
   auto go = [&](auto ng) {
     constexpr int NG = decltype(ng)::value;
-    const size_t lds = mfma_lds_bytes(kmax, NG);
-    auto kern = sb_bf16 ? grouped_mfma_kernel<NG, true> : grouped_mfma_kernel<NG, false>;
-    // as many blocks as are resident at once
-    static int per_cu_cached[2] = {0, 0};   // per kernel instantiation (and scale/bias type)
-    int& per_cu = per_cu_cached[sb_bf16 ? 1 : 0];
-    if (per_cu == 0 && (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreadsG, lds) != hipSuccess ||
-                        per_cu < 1))
-      per_cu = 1;
-    const dim3 grid(max(2, per_cu * mfma_device_cus()));   // one wave of resident blocks (at least one per role)
+    void (*kern)(MfmaArgs);
+    size_t lds = 0;
+    if constexpr (NG <= 11) {
+      kern = sb_bf16 ? grouped_ring_kernel<NG, true> : grouped_ring_kernel<NG, false>;   // static LDS only
+    } else {
+      lds = mfma_lds_bytes(kmax, NG);
+      kern = sb_bf16 ? grouped_mfma_kernel<NG, true> : grouped_mfma_kernel<NG, false>;
+    }
+    const dim3 grid(max(2, resident(reinterpret_cast<const void*>(kern), lds) * mfma_device_cus()));
     hipLaunchKernelGGL(kern, grid, dim3(kThreadsG), lds, s, a);
-    return check_launch("grouped_mfma_kernel");
+    return check_launch(NG <= 11 ? "grouped_ring_kernel" : "grouped_mfma_kernel");
   };
   if (per_wave <= 4) return go(std::integral_constant<int, 4>());
   if (per_wave <= 8) return go(std::integral_constant<int, 8>());
