@@ -18,6 +18,8 @@ constexpr int kCounterStride = 64;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxK = 32;
 constexpr int kRouterChunks = 8;    // 16-byte chunks per lane: rows of up to 8192 int8
+// from this many tokens on, logits and selection as two launches; below, one launch (router_kernel)
+constexpr int kSplitRouterMinT = 2;
 
 template <typename T>
 __device__ __forceinline__ float load_act(const T* p, int64_t i);
@@ -260,6 +262,158 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
+// Router for several tokens: logits, then selection, as two launches
+// ------------------------------------------------------------------------------------------------
+// With a block per four experts and the selection in the last block to finish, a batch's tokens each
+// gather E / 4 blocks' logits through device-coherent stores and a ticket counter that those blocks
+// update one after another; for 32 or 128 tokens that hand-off dominates.  A block per token instead is
+// bound by one compute unit's arithmetic (E dot products of d int8 values).  So the logits come from a
+// block per (token, kLogitExperts experts), written with plain stores, and a second launch selects, a
+// block per token, after the kernel boundary has made them visible.  Every per-expert sum, the norm's
+// reduction and the ranking run exactly as in router_kernel (same lanes, same order): the results agree
+// bit for bit.
+constexpr int kLogitExperts = 16;   // experts per block: 4 per wavefront
+
+template <typename XT, int NCH>
+__global__ __launch_bounds__(256) void router_logits_kernel(RouterArgs a) {
+  extern __shared__ float xs[];   // [d] fp32 activation
+  __shared__ float rinv;
+  constexpr int kRows = kLogitExperts / 4;
+  const int64_t t = blockIdx.y;
+  const XT* x = reinterpret_cast<const XT*>(a.x) + t * a.d;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nch = a.d / 16;
+  const int e0 = blockIdx.x * kLogitExperts + wave * kRows;
+  // this wave's rows and scales first, then the activation (and the norm gain), all in one round trip
+  int4 q[kRows][NCH];
+  float sc[kRows];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    const int e = e0 + r;
+    const int8_t* row = a.w + (int64_t)(e < a.E ? e : 0) * a.d;
+    sc[r] = a.scale[e < a.E ? e : 0];
+#pragma unroll
+    for (int m = 0; m < NCH; ++m) {
+      const int c = lane + 64 * m;
+      if (c < nch) q[r][m] = *reinterpret_cast<const int4*>(row + c * 16);
+    }
+  }
+  constexpr int kPasses = 8192 / (8 * 256);
+  float v[kPasses][8], g[kPasses][8];
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int j0 = (threadIdx.x + 256 * p) * 8;
+    if (j0 < a.d) {
+      load8(x + j0, v[p]);
+      if (a.gamma) load8(a.gamma + j0, g[p]);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int j0 = (threadIdx.x + 256 * p) * 8;
+    if (j0 < a.d) {
+      *reinterpret_cast<float4*>(xs + j0) = make_float4(v[p][0], v[p][1], v[p][2], v[p][3]);
+      *reinterpret_cast<float4*>(xs + j0 + 4) = make_float4(v[p][4], v[p][5], v[p][6], v[p][7]);
+    }
+  }
+  __syncthreads();
+  if (a.gamma) {
+    // the norm as in router_kernel: wave 0, lane p sums elements p, p + 64, ..., then the xor tree
+    if (wave == 0) {
+      float ss = 0.f;
+      for (int j = lane; j < a.d; j += 64) ss += xs[j] * xs[j];
+      ss = wave_sum(ss);
+      if (lane == 0) rinv = 1.0f / sqrtf(ss / (float)a.d + a.eps);
+    }
+    __syncthreads();
+    const float r = rinv;
+    constexpr bool bf16 = sizeof(XT) == 2;
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int j0 = (threadIdx.x + 256 * p) * 8;
+      if (j0 < a.d) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float u = (v[p][i] * r) * g[p][i];
+          xs[j0 + i] = bf16 ? bf16_bits_to_f32(f32_to_bf16_bits(u)) : u;   // the norm output's bf16 rounding point
+          if (a.u_out && blockIdx.x == 0) store_act(a.u_out, bf16, t * a.d + j0 + i, u);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // a lane's 16-value slices of the activation are the same for all of the wave's experts: read once
+  float4 xr[NCH][4];
+#pragma unroll
+  for (int m = 0; m < NCH; ++m) {
+    const int c = lane + 64 * m;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      xr[m][i] = c < nch ? reinterpret_cast<const float4*>(xs + c * 16)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    const int e = e0 + r;
+    float acc = 0.f;
+#pragma unroll
+    for (int m = 0; m < NCH; ++m) {
+      const int c = lane + 64 * m;
+      if (c >= nch) break;
+      const int qw[4] = {q[r][m].x, q[r][m].y, q[r][m].z, q[r][m].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 xx = xr[m][i];
+        acc += (float)(int8_t)(qw[i] & 0xff) * xx.x;
+        acc += (float)(int8_t)((qw[i] >> 8) & 0xff) * xx.y;
+        acc += (float)(int8_t)((qw[i] >> 16) & 0xff) * xx.z;
+        acc += (float)(int8_t)((qw[i] >> 24) & 0xff) * xx.w;
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0 && e < a.E) a.logits[t * a.E + e] = acc * sc[r];
+  }
+}
+
+// A block per token: the token's logits into LDS, top-k by rank and the softmax, as in router_kernel.
+__global__ __launch_bounds__(256) void router_select_kernel(RouterArgs a) {
+  __shared__ float lgs[kMaxExperts];
+  __shared__ float sel_v[kMaxK];
+  __shared__ int sel_i[kMaxK];
+  const int64_t t = blockIdx.x;
+  for (int e = threadIdx.x; e < a.E; e += 256) lgs[e] = a.logits[t * a.E + e];
+  __syncthreads();
+  if (a.forced) {
+    if (threadIdx.x < a.k) {
+      const int i = a.forced[t * a.k + threadIdx.x];
+      sel_i[threadIdx.x] = i;
+      sel_v[threadIdx.x] = (i >= 0 && i < a.E) ? lgs[i] : NAN;
+    }
+  } else {
+    for (int c = threadIdx.x; c < a.E; c += 256) {
+      const float vc = lgs[c];
+      int rank = 0;
+      for (int e2 = 0; e2 < a.E; ++e2) {
+        const float u = lgs[e2];
+        rank += (u > vc) | ((u == vc) & (e2 < c));
+      }
+      if (rank < a.k) {
+        sel_i[rank] = c;
+        sel_v[rank] = vc;
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < a.k) {
+    float mx = sel_v[0];
+    for (int r = 1; r < a.k; ++r) mx = fmaxf(mx, sel_v[r]);
+    float den = 0.f;
+    for (int r = 0; r < a.k; ++r) den += expf(sel_v[r] - mx);
+    a.ids[t * a.k + threadIdx.x] = sel_i[threadIdx.x];
+    a.weights[t * a.k + threadIdx.x] = expf(sel_v[threadIdx.x] - mx) / den;
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
 // combine
 // ------------------------------------------------------------------------------------------------
 template <typename RT, int KT>
@@ -383,9 +537,30 @@ moe_status router_launch(const char* who, const void* x_dev, moe_dtype x_dtype, 
   a.eps = eps;
   a.u_out = u_dev;
   if (gamma_dev && !aligned(u_dev, 16)) return fail(MOE_ERR_INVALID_ARG, "%s: u not 16-byte aligned", who);
-  dim3 grid((E + kRouterWaves - 1) / kRouterWaves, T);
   const size_t lds = (size_t)d * sizeof(float);
   hipStream_t s = as_stream(stream);
+  if (T >= kSplitRouterMinT) {
+    // logits by (token, 16 experts), then the selection by token (the same results as the kernel below)
+    const int nch = (d / 16 + 63) / 64;
+    const dim3 grid_l((E + kLogitExperts - 1) / kLogitExperts, T);
+    auto go = [&](auto nc) {
+      constexpr int NCH = decltype(nc)::value;
+      if (x_dtype == MOE_BF16)
+        hipLaunchKernelGGL((router_logits_kernel<uint16_t, NCH>), grid_l, dim3(256), lds, s, a);
+      else
+        hipLaunchKernelGGL((router_logits_kernel<float, NCH>), grid_l, dim3(256), lds, s, a);
+      const moe_status st = check_launch(who);
+      if (st != MOE_OK) return st;
+      hipLaunchKernelGGL(router_select_kernel, dim3(T), dim3(256), 0, s, a);
+      return check_launch(who);
+    };
+    if (nch <= 1) return go(std::integral_constant<int, 1>());
+    if (nch <= 2) return go(std::integral_constant<int, 2>());
+    if (nch <= 3) return go(std::integral_constant<int, 3>());
+    if (nch <= 4) return go(std::integral_constant<int, 4>());
+    return go(std::integral_constant<int, 8>());
+  }
+  dim3 grid((E + kRouterWaves - 1) / kRouterWaves, T);
   if (x_dtype == MOE_BF16)
     hipLaunchKernelGGL(router_kernel<uint16_t>, grid, dim3(256), lds, s, a);
   else
