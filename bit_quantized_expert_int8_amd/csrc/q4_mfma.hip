@@ -566,16 +566,20 @@ __device__ __forceinline__ void ring_item(const MfmaArgs& a, bool shared, int e,
 
   for (int c0 = 0; c0 < count; c0 += 16) {
     const int nlive = min(16, count - c0);
-    // the first step's loads go out first (they depend on the expert only); then the chunk's tokens: staged
-    // row and output row (slots past the last token repeat the first token's staged row; their results are
-    // not stored)
-    issue(std::integral_constant<int, 0>(), s0);
+    // the chunk's tokens (staged row and output row; slots past the last token repeat the first token's
+    // staged row, their results are not stored), loaded before the first step's loads so that they do not
+    // wait behind them; the step's loads depend on the expert only
+    int pr = 0;
     if ((int)threadIdx.x < 16) {
       const int m = threadIdx.x;
       const int mm = m < nlive ? m : 0;
-      const int pr = shared ? c0 + mm : a.perm[start + c0 + mm];
-      srow_l[m] = (shared || !a.gate_up) ? pr : pr / a.k;
-      orow_l[m] = pr;
+      pr = shared ? start + c0 + mm : a.perm[start + c0 + mm];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    issue(std::integral_constant<int, 0>(), s0);
+    if ((int)threadIdx.x < 16) {
+      srow_l[threadIdx.x] = (shared || !a.gate_up) ? pr : pr / a.k;
+      orow_l[threadIdx.x] = pr;
     }
     lds_barrier();
     // A of this wave's groups for the whole chunk (indices clamped into the row past the wave's range), the
@@ -754,11 +758,79 @@ __global__ __launch_bounds__(kThreadsG) void grouped_mfma_kernel(MfmaArgs a) {
   });
 }
 
+// Item `it` of this block (false: no more).  The shared matrix gets blocks in proportion to its steps
+// times its token chunks, at least one per chunk, and each of them takes one token chunk and one step range
+// (so that no block runs the setup of several chunks in a row); the routed chunks share the other blocks,
+// each chunk split into as equal step ranges as the blocks allow, or, with more chunks than blocks, block
+// b takes chunks b, b + R, ... whole.
+struct WorkItem {
+  bool shared, valid;
+  int e, start, count, s0, s1;
+};
+__device__ __forceinline__ bool next_item(const MfmaArgs& a, int it, WorkItem& x) {
+  const int b = blockIdx.x, nb = gridDim.x;
+  const int ng = a.steps_routed > 0 ? *a.n_chunks : 0;
+  const int ss = a.steps_shared, tc = (a.T + 15) / 16;
+  int nsb = 0, rs = 1;
+  if (ss > 0) {
+    if (ng <= 0) {
+      nsb = nb;
+    } else {
+      const int64_t us = (int64_t)ss * tc, ur = (int64_t)a.steps_routed * ng;
+      nsb = (int)((nb * us + (us + ur) / 2) / (us + ur));
+      nsb = max(1, min(nsb, nb - 1));
+    }
+    rs = max(1, nsb / tc);
+    nsb = nsb < tc ? nsb : rs * tc;
+  }
+  if (b < nsb) {
+    if (nsb < tc) {
+      // fewer blocks than token chunks: block b takes chunks b, b + nsb, ... over all steps
+      const int c = b + it * nsb;
+      if (c >= tc) return false;
+      x = WorkItem{true, true, 0, 16 * c, min(16, a.T - 16 * c), 0, ss};
+      return true;
+    }
+    if (it > 0) return false;
+    const int c = b % tc, r = b / tc;
+    x = WorkItem{true, true, 0, 16 * c, min(16, a.T - 16 * c), (int)((int64_t)r * ss / rs),
+                 (int)((int64_t)(r + 1) * ss / rs)};
+    return true;
+  }
+  if (ng <= 0) return false;
+  const int o = b - nsb, R = nb - nsb, steps = a.steps_routed;
+  int j, s0 = 0, s1 = steps;
+  if (ng <= R) {
+    if (it > 0) return false;
+    const int q = R / ng, rem = R % ng;
+    int part, parts;
+    if (o < rem * (q + 1)) {
+      j = o / (q + 1);
+      part = o % (q + 1);
+      parts = q + 1;
+    } else {
+      const int o2 = o - rem * (q + 1);
+      j = rem + o2 / q;
+      part = o2 % q;
+      parts = q;
+    }
+    s0 = (int)((int64_t)part * steps / parts);
+    s1 = (int)((int64_t)(part + 1) * steps / parts);
+  } else {
+    j = o + it * R;
+    if (j >= ng) return false;
+  }
+  const int4 g = a.chunks[j];
+  const bool valid = (unsigned)g.x < (unsigned)a.routed.n_records;
+  x = WorkItem{false, valid, valid ? g.x : 0, g.y, g.z, s0, s1};
+  return true;
+}
+
 template <int NG, bool SB_BF16>
 __global__ __launch_bounds__(kThreadsG, 2) void grouped_ring_kernel(MfmaArgs a) {
-  block_work(a, [&](bool shared, int e, bool valid, int start, int count, int s0, int s1) __attribute__((always_inline)) {
-    ring_item<NG, SB_BF16>(a, shared, e, valid, start, count, s0, s1);
-  });
+  WorkItem x;
+  for (int it = 0; next_item(a, it, x); ++it)
+    if (x.s0 < x.s1) ring_item<NG, SB_BF16>(a, x.shared, x.e, x.valid, x.start, x.count, x.s0, x.s1);
 }
 
 }  // namespace
@@ -816,11 +888,37 @@ int mfma_device_cus() {
   return cus[dev];
 }
 
-moe_status launch_grouped_mfma(MfmaArgs a, bool has_shared, bool has_routed, bool sb_bf16, hipStream_t s) {
+namespace {
+// The kernel, dynamic LDS, grid and step counts of a grouped launch.
+struct LaunchShape {
+  void (*kern)(MfmaArgs);
+  size_t lds;
+  int nb, steps_shared, steps_routed;
+  bool ring;
+};
+
+// Resident blocks per compute unit for one kernel and dynamic LDS size, per device (queried once).
+int resident_blocks(const void* kern, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, const void*, size_t>, int> cache;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_tuple(dev, kern, lds);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreadsG, lds) != hipSuccess || per_cu < 1) per_cu = 1;
+  cache.emplace(key, per_cu);
+  return per_cu;
+}
+
+LaunchShape launch_shape(const MfmaArgs& a, bool has_shared, bool has_routed, bool sb_bf16) {
   // steps per matrix (a step: one tile per group of wk waves)
   auto steps_of = [](int tiles, int wk) { const int tps = kWavesG / wk; return (tiles + tps - 1) / tps; };
-  a.steps_shared = has_shared ? steps_of(a.tiles_shared, a.wk_shared) : 0;
-  a.steps_routed = has_routed ? steps_of(a.tiles_routed, a.wk_routed) : 0;
+  LaunchShape sh{};
+  sh.steps_shared = has_shared ? steps_of(a.tiles_shared, a.wk_shared) : 0;
+  sh.steps_routed = has_routed ? steps_of(a.tiles_routed, a.wk_routed) : 0;
   int per_wave = 0, kmax = 0;
   if (has_shared) {
     per_wave = (a.K_shared / 64 + a.wk_shared - 1) / a.wk_shared;
@@ -830,42 +928,36 @@ moe_status launch_grouped_mfma(MfmaArgs a, bool has_shared, bool has_routed, boo
     per_wave = max(per_wave, (a.K_routed / 64 + a.wk_routed - 1) / a.wk_routed);
     kmax = max(kmax, a.K_routed);
   }
-  // as many blocks as are resident at once, per (device, kernel, dynamic LDS): the count the runtime
-  // reports for this exact launch shape
-  auto resident = [](const void* kern, size_t lds) {
-    static std::mutex mu;
-    static std::map<std::tuple<int, const void*, size_t>, int> cache;
-    int dev = 0;
-    (void)hipGetDevice(&dev);
-    std::lock_guard<std::mutex> lock(mu);
-    const auto key = std::make_tuple(dev, kern, lds);
-    auto it = cache.find(key);
-    if (it != cache.end()) return it->second;
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreadsG, lds) != hipSuccess || per_cu < 1)
-      per_cu = 1;
-    cache.emplace(key, per_cu);
-    return per_cu;
-  };
-  auto go = [&](auto ng) {
+  auto pick = [&](auto ng) {
     constexpr int NG = decltype(ng)::value;
-    void (*kern)(MfmaArgs);
-    size_t lds = 0;
     if constexpr (NG <= 11) {
-      kern = sb_bf16 ? grouped_ring_kernel<NG, true> : grouped_ring_kernel<NG, false>;   // static LDS only
+      sh.kern = sb_bf16 ? grouped_ring_kernel<NG, true> : grouped_ring_kernel<NG, false>;   // static LDS only
+      sh.lds = 0;
+      sh.ring = true;
     } else {
-      lds = mfma_lds_bytes(kmax, NG);
-      kern = sb_bf16 ? grouped_mfma_kernel<NG, true> : grouped_mfma_kernel<NG, false>;
+      sh.kern = sb_bf16 ? grouped_mfma_kernel<NG, true> : grouped_mfma_kernel<NG, false>;
+      sh.lds = mfma_lds_bytes(kmax, NG);
+      sh.ring = false;
     }
-    const dim3 grid(max(2, resident(reinterpret_cast<const void*>(kern), lds) * mfma_device_cus()));
-    hipLaunchKernelGGL(kern, grid, dim3(kThreadsG), lds, s, a);
-    return check_launch(NG <= 11 ? "grouped_ring_kernel" : "grouped_mfma_kernel");
   };
-  if (per_wave <= 4) return go(std::integral_constant<int, 4>());
-  if (per_wave <= 8) return go(std::integral_constant<int, 8>());
-  if (per_wave <= 11) return go(std::integral_constant<int, 11>());
-  if (per_wave <= 16) return go(std::integral_constant<int, 16>());
-  return go(std::integral_constant<int, 32>());
+  if (per_wave <= 4) pick(std::integral_constant<int, 4>());
+  else if (per_wave <= 8) pick(std::integral_constant<int, 8>());
+  else if (per_wave <= 11) pick(std::integral_constant<int, 11>());
+  else if (per_wave <= 16) pick(std::integral_constant<int, 16>());
+  else pick(std::integral_constant<int, 32>());
+  // one wave of resident blocks (at least one per role)
+  const int per_cu = resident_blocks(reinterpret_cast<const void*>(sh.kern), sh.lds);
+  sh.nb = max(2, per_cu * mfma_device_cus());
+  return sh;
+}
+}  // namespace
+
+moe_status launch_grouped_mfma(MfmaArgs a, bool has_shared, bool has_routed, bool sb_bf16, hipStream_t s) {
+  const LaunchShape sh = launch_shape(a, has_shared, has_routed, sb_bf16);
+  a.steps_shared = sh.steps_shared;
+  a.steps_routed = sh.steps_routed;
+  hipLaunchKernelGGL(sh.kern, dim3(sh.nb), dim3(kThreadsG), sh.lds, s, a);
+  return check_launch(sh.ring ? "grouped_ring_kernel" : "grouped_mfma_kernel");
 }
 
 }  // namespace moeq4
