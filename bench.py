@@ -65,9 +65,16 @@ def build_stack(cfg, n_layers):
 # the ones the counters were taken on (first 16 hex digits of their sha256).
 TRAFFIC = {
     # mode: (bytes per launch, sources sha)
+    "stack": (1_261_649_577, "bdc27cc3efd56e2d"),   # 610,952.0 KiB fetched x 1.99966, 10,384.8 KiB written x 1.0
+    "layer": (42_296_921, "bdc27cc3efd56e2d"),      # 20,486.9 KiB fetched x 1.99966, 338.8 KiB written x 1.0
 }
 TRAFFIC_SOURCES = ("bit_quantized_expert_int8_amd/csrc/layer.hip", "bit_quantized_expert_int8_amd/csrc/q4_device.h",
                    "bit_quantized_expert_int8_amd/csrc/common.h")
+
+
+def log(msg):
+    """A progress line on stderr (the JSON result is the only line on stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def sources_sha():
@@ -355,6 +362,7 @@ def measure_streamed(shape, layers, cfg, dec, n_tokens, overlap=True, copy_strea
         t1 = time.perf_counter()
         dec.check_status()
         hits, misses, nbytes = q.moe_expert_cache_stats(cache, -1)
+        hits_per_layer = [int(q.moe_expert_cache_stats(cache, l)[0]) for l in range(L)]
     finally:
         q.moe_expert_cache_destroy(cache)
     req = n_tokens * L * k
@@ -365,7 +373,9 @@ def measure_streamed(shape, layers, cfg, dec, n_tokens, overlap=True, copy_strea
             "tok_s_all": round(n_tokens / (t1 - t0), 2), "tok_s_warm": round((n_tokens - half) / (t1 - t_half), 2),
             "hit_rate_all": round(hits / req, 4), "hit_rate_warm": round((hits - hits_half) / warm_req, 4),
             "bytes_copied": int(nbytes), "h2d_GBps_effective_warm": round((nbytes - bytes_half) / (t1 - t_half) / 1e9, 2),
-            "pinned_copy_GBps": round(pinned_gbps, 2)}
+            "pinned_copy_GBps": round(pinned_gbps, 2), "hits_per_layer": hits_per_layer,
+            "trace_args": {"seed": 4, "tokens": n_tokens, "layers": L, "k": k, "experts": E, "zipf_s": 1.1,
+                           "slots": n_slots}}
 
 
 def pinned_copy_gbps(reps=3):
@@ -397,6 +407,25 @@ def cpu_model():
     except OSError:
         pass
     return "unknown"
+
+
+def cache_hits_vs_oracle(streamed):
+    """The streamed run's per-layer cache hits against the oracle's LFU simulation of the same trace (every
+    token, every layer): they must be equal."""
+    import numpy as np
+    import synth
+    from oracle import moe
+
+    a = streamed["trace_args"]
+    trace = synth.zipf_trace(a["seed"], a["tokens"], a["layers"], a["k"], a["experts"], a["zipf_s"])
+    _, hits = moe.lfu_simulate(np.asarray(trace), a["slots"])
+    sim = [int(v) for v in hits.sum(axis=0)]
+    equal = sim == streamed["hits_per_layer"]
+    if not equal:
+        log(f"expert cache hits differ from the oracle's LFU simulation: gpu {streamed['hits_per_layer']} "
+            f"oracle {sim}")
+    return {"tokens": a["tokens"], "layers": a["layers"], "hits_gpu": sum(streamed["hits_per_layer"]),
+            "hits_oracle": sum(sim), "per_layer_equal": equal}
 
 
 def oracle_leg(shape, layers, cfg, tokens, n_sample, st_layers, xout_graph=None):
@@ -515,6 +544,7 @@ def main():
     shape, layers = build_stack(cfg, args.layers)
     torch.cuda.synchronize()
     t_build = time.perf_counter() - t_build
+    log(f"built {args.layers} layers in {t_build:.1f} s")
     dec = decoder.MoEDecoder(shape, layers, T=1, mode=args.mode)
 
     n_tok = cfg.n_tokens
@@ -541,6 +571,7 @@ def main():
     gpu_s = e0.elapsed_time(e1) * 1e-3
     tok_s = args.steps / gpu_s
     dec.check_status()      # every bounded wait inside the timed launches completed
+    log(f"timed {args.steps} steps: {tok_s:.1f} tokens/s")
 
     if args.calibration_copy_mib:
         src = torch.empty(args.calibration_copy_mib << 20, dtype=torch.uint8, device="cuda")
@@ -565,6 +596,7 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": kernel_traffic(args.mode), "kernel": kname,
                 "bytes_per_launch": per_launch, "avg_launch_us": round(dur * 1e6, 3), "launches_timed": launches,
                 "per_layer_us": round(dur / (args.layers if args.mode == "stack" else 1) * 1e6, 3)}
+    log(f"roofline launch: {dur * 1e6:.1f} us")
     split = time_split_kernels(dec, xin, args.roofline_reps)
     split["layer_launch_us"] = round(lay_dur * 1e6, 3)
     step_bytes, _ = distinct_expert_bytes(dec, cfg)
@@ -583,12 +615,16 @@ def main():
            "decode_mode": dec.mode, "split_kernels_us": split, "hbm_read_2GiB": measure_hbm_read()}
     if not args.no_extras:
         out["batched"] = measure_batched(shape, layers, cfg, tokens.reshape(n_tok, cfg.d), 20, 3)
+        log(f"batched: {out['batched']['tok_s']} tokens/s")
         out["prefill_chunk_128"] = measure_batched(shape, layers, cfg, tokens.reshape(n_tok, cfg.d), 8, 2, T=128)
+        log(f"prefill chunk: {out['prefill_chunk_128']['tok_s']} tokens/s")
         out["lm_head_q4_gemv"] = measure_lm_head()
+        log(f"lm head: {out['lm_head_q4_gemv']['achieved_GBps']} GB/s")
         pinned = pinned_copy_gbps()
         host = pinned_pools(layers)
         out["streamed"] = measure_streamed(shape, layers, cfg, dec, args.stream_tokens, overlap=True,
                                            copy_streams=args.copy_streams, pinned_gbps=pinned, host=host)
+        log(f"streamed: {out['streamed']['tok_s_all']} tokens/s")
         base = measure_streamed(shape, layers, cfg, dec, args.stream_tokens // 2, overlap=False,
                                 copy_streams=args.copy_streams, pinned_gbps=pinned, host=host)
         del host
@@ -601,8 +637,11 @@ def main():
         g.replay()
         torch.cuda.synchronize()
         xo = xout.float().cpu().numpy().astype(np.float64)[0]
+        log("oracle leg")
         out["cpu_baseline"], out["parity"] = oracle_leg(shape, layers, cfg, tokens, args.cpu_tokens,
                                                         args.cpu_single_layers, xout_graph=xo)
+        if "streamed" in out:
+            out["parity"]["expert_cache"] = cache_hits_vs_oracle(out["streamed"])
     print(json.dumps(out), flush=True)
 
 
