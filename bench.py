@@ -335,6 +335,7 @@ def measure_streamed(shape, layers, cfg, dec, n_tokens, overlap=True, copy_strea
         toks = torch.from_numpy(bits).view(torch.bfloat16).cuda().reshape(64, 1, cfg.d)
         bufs = [torch.empty((1, cfg.d), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
         half = n_tokens // 2
+        host_s = 0.0   # time the host spends issuing the layers' work (policy, copies, launches, events)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for t in range(n_tokens):
@@ -345,11 +346,17 @@ def measure_streamed(shape, layers, cfg, dec, n_tokens, overlap=True, copy_strea
                 bytes_half = q.moe_expert_cache_stats(cache, -1)[2]
             x = toks[t % 64]
             for l in range(L):
+                th = time.perf_counter()
                 q.expert_cache_stage(cache, l, trace[t, l].tolist(), slot_ids[l], cstreams[l % copy_streams], freed[l],
                                      ready[l])
                 out = bufs[l % 2]
                 fi = forced[t, l].reshape(1, k)
-                if overlap:
+                if overlap == "split":
+                    # the two launches of the overlap, both after the copies (isolates the launch split)
+                    compute.wait_event(ready[l])
+                    dec.layer_part(1, l, x, out, forced_ids=fi, routed_pool=slot_pools[l], ids=slot_ids[l])
+                    dec.layer_part(2, l, x, out, forced_ids=fi, routed_pool=slot_pools[l], ids=slot_ids[l])
+                elif overlap:
                     dec.layer_part(1, l, x, out, forced_ids=fi, routed_pool=slot_pools[l], ids=slot_ids[l])
                     compute.wait_event(ready[l])
                     dec.layer_part(2, l, x, out, forced_ids=fi, routed_pool=slot_pools[l], ids=slot_ids[l])
@@ -357,6 +364,7 @@ def measure_streamed(shape, layers, cfg, dec, n_tokens, overlap=True, copy_strea
                     compute.wait_event(ready[l])
                     dec.layer(l, x, out, forced_ids=fi, routed_pool=slot_pools[l], ids=slot_ids[l])
                 freed[l].record(compute)
+                host_s += time.perf_counter() - th
                 x = out
         torch.cuda.synchronize()
         t1 = time.perf_counter()
@@ -368,14 +376,174 @@ def measure_streamed(shape, layers, cfg, dec, n_tokens, overlap=True, copy_strea
     req = n_tokens * L * k
     warm_req = (n_tokens - half) * L * k
     return {"tokens": n_tokens, "layers": L, "slots_per_layer": n_slots, "trace": "Zipf(1.1) forced routing",
-            "overlap": "shared expert during the copies (two launches per layer)" if overlap else "none",
+            "overlap": ("two launches per layer after the copies" if overlap == "split" else
+                        "shared expert during the copies (two launches per layer)" if overlap else "none"),
             "copy_streams": copy_streams,
             "tok_s_all": round(n_tokens / (t1 - t0), 2), "tok_s_warm": round((n_tokens - half) / (t1 - t_half), 2),
             "hit_rate_all": round(hits / req, 4), "hit_rate_warm": round((hits - hits_half) / warm_req, 4),
             "bytes_copied": int(nbytes), "h2d_GBps_effective_warm": round((nbytes - bytes_half) / (t1 - t_half) / 1e9, 2),
-            "pinned_copy_GBps": round(pinned_gbps, 2), "hits_per_layer": hits_per_layer,
+            "pinned_copy_GBps": round(pinned_gbps, 2), "host_issue_us_per_layer": round(host_s / (n_tokens * L) * 1e6, 1),
+            "wall_us_per_layer": round((t1 - t0) / (n_tokens * L) * 1e6, 1), "hits_per_layer": hits_per_layer,
             "trace_args": {"seed": 4, "tokens": n_tokens, "layers": L, "k": k, "experts": E, "zipf_s": 1.1,
                            "slots": n_slots}}
+
+
+def lfu_misses(trace, n_slots):
+    """The experts each (token, layer) had to copy under the library's LFU policy (moe_expert_cache in its
+    host-only mode: the policy and the bookkeeping without a GPU), as a list of sets per token per layer."""
+    import numpy as np
+    from bit_quantized_expert_int8_amd import moeq4 as q
+
+    T, L, k = trace.shape
+    E = int(trace.max()) + 1
+    rb = 256
+    host = [np.zeros(E * rb, dtype=np.uint8) for _ in range(L)]
+    slots = [np.zeros(n_slots * rb, dtype=np.uint8) for _ in range(L)]
+    ids_out = np.zeros(k, dtype=np.int32)
+    cache = q.moe_expert_cache_create(L, E, n_slots, rb, [h.ctypes.data for h in host], [s_.ctypes.data for s_ in slots],
+                                      q.MOE_CACHE_HOST_ONLY)
+    missed = [[None] * L for _ in range(T)]
+    try:
+        for t in range(T):
+            for l in range(L):
+                before = q.moe_expert_cache_slots(cache, l, n_slots)
+                q.expert_cache_stage(cache, l, trace[t, l].tolist(), ids_out.ctypes.data)
+                after = q.moe_expert_cache_slots(cache, l, n_slots)
+                missed[t][l] = {e for b, e in zip(before, after) if e != b and e >= 0}
+    finally:
+        q.moe_expert_cache_destroy(cache)
+    return missed
+
+
+def predictor_stats(trace, missed):
+    """Cross-layer and temporal prefetch predictors on a routing trace: for each (token, layer) a predictor
+    names k experts before the layer's routing is known; precision = share of the named experts the layer
+    then uses, coverage = share of the layer's cache misses the named set contains (what a prefetch of it
+    would have hidden), waste = named experts that were neither used nor missing (bandwidth spent for
+    nothing if prefetched)."""
+    import numpy as np
+
+    T, L, k = trace.shape
+    preds = {
+        "cross_layer": lambda t, l: set(trace[t, l - 1].tolist()) if l > 0 else None,
+        "previous_token": lambda t, l: set(trace[t - 1, l].tolist()) if t > 0 else None,
+    }
+    counts = {}
+    for l in range(L):
+        counts[l] = np.zeros(int(trace.max()) + 1, dtype=np.int64)
+    out = {name: {"precision": 0.0, "coverage_hits": 0, "misses": 0, "named_not_used": 0, "cases": 0}
+           for name in list(preds) + ["popularity"]}
+    for t in range(T):
+        for l in range(L):
+            actual = set(trace[t, l].tolist())
+            miss = missed[t][l]
+            named = {name: f(t, l) for name, f in preds.items()}
+            if t > 0:
+                named["popularity"] = set(np.argsort(-counts[l], kind="stable")[:k].tolist())
+            for name, p in named.items():
+                if p is None:
+                    continue
+                o = out[name]
+                o["cases"] += 1
+                o["precision"] += len(p & actual) / k
+                o["coverage_hits"] += len(p & miss)
+                o["misses"] += len(miss)
+                o["named_not_used"] += len(p - actual)
+            counts[l][trace[t, l]] += 1
+    res = {}
+    for name, o in out.items():
+        n = max(1, o["cases"])
+        res[name] = {"precision": round(o["precision"] / n, 4),
+                     "miss_coverage": round(o["coverage_hits"] / max(1, o["misses"]), 4),
+                     "named_not_used_per_layer": round(o["named_not_used"] / n, 3)}
+    return res
+
+
+def prefetch_study(args):
+    """Cross-layer prefetch and overlap granularity on the expert-cache trace: one JSON line.
+
+    Overlap: the streamed decode of the same tokens without overlap (each layer waits for its copies, then
+    one launch) and with the per-layer (coarse) overlap (router + shared expert launched before the wait,
+    routed experts + combine after it), measured; and a bound for per-expert (fine) overlap, where each
+    routed expert would start as soon as its own record has landed: the compute it could hide is at most the
+    routed part's duration minus one expert's share, per layer with a miss (the durations measured here).
+    Predictors: lfu_misses + predictor_stats on the trace as the bench uses it (every layer ranks experts by
+    the same Zipf law) and on a copy whose layers each permute the expert ids (a popularity of their own)."""
+    import numpy as np
+    import torch
+    import synth
+    from bit_quantized_expert_int8_amd import decoder
+
+    cfg = synth.STACK
+    shape, layers = build_stack(cfg, args.layers)
+    dec = decoder.MoEDecoder(shape, layers, T=1, mode=args.mode)
+    L, E, k, n_tok = len(layers), cfg.n_experts, cfg.k, args.stream_tokens
+    log("stack built")
+    pinned = pinned_copy_gbps()
+    host = pinned_pools(layers)
+    runs = {}
+    for name, overlap in (("none", False), ("coarse", True), ("split_no_overlap", "split")):
+        runs[name] = measure_streamed(shape, layers, cfg, dec, n_tok, overlap=overlap, copy_streams=args.copy_streams,
+                                      pinned_gbps=pinned, host=host)
+        log(f"{name}: {runs[name]['tok_s_all']} tokens/s")
+    del host
+    # part durations of one layer (graph of 30 launches each, HIP events on the launch stream)
+    x = torch.zeros((1, cfg.d), dtype=torch.bfloat16, device="cuda")
+    bufs = [x, torch.empty_like(x)]
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    # part 2 consumes the routing of part 1 of the same call: it is timed as the pair minus part 1, and part 1
+    # alone runs on a decoder of its own (a workspace whose part 1 is not followed by part 2 is spent)
+    d1 = decoder.MoEDecoder(shape, layers, T=1, mode="layer")
+    part_us = {1: time_graph(lambda: [d1.layer_part(1, l, bufs[l % 2], bufs[(l + 1) % 2], stream=stream)
+                                      for l in range(L)], 10, stream) / L * 1e6}
+    del d1
+
+    def pairs():
+        for l in range(L):
+            dec.layer_part(1, l, bufs[l % 2], bufs[(l + 1) % 2], stream=stream)
+            dec.layer_part(2, l, bufs[l % 2], bufs[(l + 1) % 2], stream=stream)
+
+    part_us[2] = time_graph(pairs, 10, stream) / L * 1e6 - part_us[1]
+    dec.check_status()
+    # the host's cost of issuing one layer (Python binding and launch), eagerly, as the streamed loop does:
+    # one moe_decode_layer call against a part 1 + part 2 pair
+    issue_us = {}
+    for name, fn in (("layer", lambda l: dec.layer(l, bufs[l % 2], bufs[(l + 1) % 2], stream=stream)),
+                     ("parts", lambda l: (dec.layer_part(1, l, bufs[l % 2], bufs[(l + 1) % 2], stream=stream),
+                                          dec.layer_part(2, l, bufs[l % 2], bufs[(l + 1) % 2], stream=stream)))):
+        torch.cuda.synchronize()
+        th = time.perf_counter()
+        for _ in range(10):
+            for l in range(L):
+                fn(l)
+        issue_us[name] = round((time.perf_counter() - th) / (10 * L) * 1e6, 1)
+        torch.cuda.synchronize()
+    dec.check_status()
+    trace = synth.zipf_trace(4, n_tok, L, k, E, 1.1)
+    missed = lfu_misses(trace, 16)
+    layers_with_miss = sum(1 for t in range(n_tok) for l in range(L) if missed[t][l])
+    copy_us = layers[0].pool.shape[1] / (pinned * 1e9) * 1e6
+    fine_bound_us = layers_with_miss * part_us[2] * (1 - 1 / k)
+    coarse_s = n_tok / runs["coarse"]["tok_s_all"]
+    rng = np.random.default_rng(np.random.SeedSequence([4, 7]))
+    perm = np.stack([rng.permutation(E) for _ in range(L)])
+    trace_pl = np.stack([perm[l][trace[:, l]] for l in range(L)], axis=1).astype(np.int32)
+    missed_pl = lfu_misses(trace_pl, 16)
+    out = {"study": "expert cache: cross-layer prefetch and overlap granularity",
+           "trace": f"Zipf(1.1) forced routing, {n_tok} tokens x {L} layers, top-{k} of {E}, 16 slots per layer",
+           "overlap": {kk: {m: runs[kk][m] for m in ("tok_s_all", "tok_s_warm", "hit_rate_all", "h2d_GBps_effective_warm",
+                                                     "host_issue_us_per_layer", "wall_us_per_layer")}
+                       for kk in runs},
+           "pinned_copy_GBps": round(pinned, 2), "record_copy_us": round(copy_us, 1),
+           "part_us": {"router_shared": round(part_us[1], 2), "routed_combine": round(part_us[2], 2)},
+           "host_issue_us_per_layer_no_copies": issue_us,
+           "fine_bound": {"layers_with_a_miss": layers_with_miss,
+                          "hideable_us_total": round(fine_bound_us, 1),
+                          "tok_s_if_all_hidden": round(n_tok / max(1e-9, coarse_s - fine_bound_us * 1e-6), 2)},
+           "predictors_same_ranks": predictor_stats(trace, missed),
+           "predictors_per_layer_ranks": predictor_stats(trace_pl, missed_pl)}
+    print(json.dumps(out), flush=True)
 
 
 def pinned_copy_gbps(reps=3):
@@ -527,6 +695,8 @@ def main():
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB (a reference for the HBM "
                          "traffic counters of a profiled run)")
+    ap.add_argument("--study", choices=("prefetch",), default=None,
+                    help="instead of the bench line, the expert-cache study (cross-layer prefetch, overlap granularity)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -540,6 +710,9 @@ def main():
 
     cfg = synth.STACK
     torch.cuda.set_device(0)
+    if args.study == "prefetch":
+        prefetch_study(args)
+        return
     t_build = time.perf_counter()
     shape, layers = build_stack(cfg, args.layers)
     torch.cuda.synchronize()

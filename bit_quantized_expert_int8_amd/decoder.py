@@ -215,16 +215,16 @@ class MoEDecoder:
             src = dst
 
     def status(self) -> int:
-        """The sticky error word of the single-launch kernels' workspace (0 = every bounded wait inside them
-        completed; nonzero = a wait ran out and the results of that call are invalid).  Synchronizes."""
-        if self.mode == "stack":
-            ws = self.stack_ws
-        elif self.mode == "layer":
-            ws = self.layer_ws
-        else:
-            return 0
+        """The sticky error words of the single-launch kernels' workspaces, OR-ed (0 = every bounded wait inside
+        them completed; nonzero = a wait ran out and the results of that call are invalid): the layer workspace
+        (moe_decode_layer, its two parts) and the stack workspace (moe_decode_stack), whichever this decoder
+        holds, whatever its mode.  Synchronizes."""
         torch.cuda.synchronize()
-        return int(ws[:4].view(torch.int32).item())
+        st = 0
+        for ws in (getattr(self, "layer_ws", None), getattr(self, "stack_ws", None)):
+            if ws is not None:
+                st |= int(ws[:4].view(torch.int32).item())
+        return st
 
     def check_status(self) -> None:
         """Raise if a bounded wait inside the single-launch kernels ran out since the workspace was zeroed."""
