@@ -336,8 +336,8 @@ moe_status moe_decode_layer_noalloc(const void* x_dev, moe_dtype x_dtype, const 
  * moe_decode_stack — n_layers consecutive layers of moe_decode_layer for one token in a single launch
  * (the stacked decode: RMSNorm and the MoE block per layer, residual stream between them).  Layer l + 1's
  * blocks load their router rows and shared-expert weights while layer l finishes, then wait for layer l's
- * output; intermediate activations stay in the workspace as fp32 holding values already rounded to
- * x_dtype, so the result equals n_layers chained moe_decode_layer calls bit for bit.
+ * output; intermediate activations stay in the workspace in x_dtype, so the result equals n_layers chained
+ * moe_decode_layer calls bit for bit.
  * layers_host: host array of n_layers descriptors (copied into the launch; the device buffers they point to
  * must stay valid until the work completes).  routed / shared: the pools' shape (d, F, record_bytes,
  * n_records, sb_dtype; base_dev is ignored, every layer gives its own); shared may be NULL.
@@ -347,7 +347,11 @@ moe_status moe_decode_layer_noalloc(const void* x_dev, moe_dtype x_dtype, const 
  * Workspace: moe_decode_stack_workspace_bytes(...) bytes, 256-byte aligned, ZERO before first use; the
  * region of layer l is moe_decode_layer_workspace_bytes(d, E, k, F, S) bytes at offset l times that size,
  * laid out as moe_decode_layer's (word 0 of the whole workspace is the sticky error flag), with the same
- * state after every completed call: counters zero, flags zero or at the number of calls made.
+ * state after every completed call: counters zero, flags zero or at the number of calls made.  A workspace
+ * is bound to one n_layers and one shape for its life: every block of every layer counts the calls made on
+ * it and waits for the values tagged with that count, so a call with another n_layers, or a
+ * moe_decode_layer call on one layer's region, leaves the counts unequal and the next calls' waits run out
+ * (the sticky flag is set; nothing hangs).  Zero it before using it for another n_layers or shape.
  * ------------------------------------------------------------------------------------------------- */
 typedef struct {
   const int8_t* router_w_dev;      /* int8 [E][d] */
