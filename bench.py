@@ -65,8 +65,8 @@ def build_stack(cfg, n_layers):
 # the ones the counters were taken on (first 16 hex digits of their sha256).
 TRAFFIC = {
     # mode: (bytes per launch, sources sha)
-    "stack": (1_261_649_577, "bdc27cc3efd56e2d"),   # 610,952.0 KiB fetched x 1.99966, 10,384.8 KiB written x 1.0
-    "layer": (42_296_921, "bdc27cc3efd56e2d"),      # 20,486.9 KiB fetched x 1.99966, 338.8 KiB written x 1.0
+    "stack": (1_259_221_775, "7784cc6cbe2214d1"),   # 609,765.7 KiB fetched x 1.99966, 10,384.4 KiB written x 1.0
+    "layer": (42_268_500, "7784cc6cbe2214d1"),      # 20,473.0 KiB fetched x 1.99966, 338.8 KiB written x 1.0
 }
 TRAFFIC_SOURCES = ("bit_quantized_expert_int8_amd/csrc/layer.hip", "bit_quantized_expert_int8_amd/csrc/q4_device.h",
                    "bit_quantized_expert_int8_amd/csrc/common.h")
@@ -261,9 +261,10 @@ def measure_batched(shape, layers, cfg, tokens, steps, warmup, T=32):
             "weight_bytes_per_step": nbytes, "achieved_GBps": round(nbytes / step_s / 1e9, 1)}
 
 
-def measure_lm_head(steps=10, reps=10):
+def measure_lm_head(steps=10, reps=10, warm=200):
     """q4_gemv (the experts' 4-bit row routine as a plain matrix GEMV) at LM-head scale: 262,144 rows (a
-    vocabulary) x 2816, bf16 scale/bias, one bf16 token, seeded random codes; graph-timed on its stream."""
+    vocabulary) x 2816, bf16 scale/bias, one bf16 token, seeded random codes; graph-timed on its stream after
+    `warm` untimed launches (its duration settles only after about 150 back-to-back launches: --study lmhead)."""
     import torch
     from bit_quantized_expert_int8_amd import moeq4 as q
 
@@ -280,10 +281,50 @@ def measure_lm_head(steps=10, reps=10):
         for _ in range(steps):
             q.q4_gemv(x, q.MOE_BF16, 1, codes, sb, q.MOE_BF16, N, K, y, stream)
 
+    with torch.cuda.stream(stream):
+        for _ in range(warm):
+            q.q4_gemv(x, q.MOE_BF16, 1, codes, sb, q.MOE_BF16, N, K, y, stream)
     t = time_graph(calls, reps, stream) / steps
     nbytes = N * (K // 2) + N * (K // 64) * 4
-    return {"rows": N, "cols": K, "us_per_call": round(t * 1e6, 2), "weight_bytes": nbytes,
+    return {"rows": N, "cols": K, "warm_launches": warm, "us_per_call": round(t * 1e6, 2), "weight_bytes": nbytes,
             "achieved_GBps": round(nbytes / t / 1e9, 1), "frac_of_8TBps": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def lm_head_drift(launches=400, window=20):
+    """q4_gemv at the LM-head shape and a plain read of the same number of bytes (moe_hbm_read_probe), each
+    launched `launches` times back to back with a HIP event between launches: one JSON line with the mean
+    duration of every `window` consecutive launches (whether the duration holds under sustained load)."""
+    import torch
+    from bit_quantized_expert_int8_amd import moeq4 as q
+
+    N, K = 262144, 2816
+    g = torch.Generator(device="cuda").manual_seed(5)
+    codes = torch.randint(0, 2**31 - 1, (N, K // 8), dtype=torch.int32, device="cuda", generator=g)
+    sb = (torch.rand((N, K // 64, 2), device="cuda", generator=g) * 0.01).to(torch.bfloat16)
+    x = torch.randn((1, K), device="cuda", generator=g).to(torch.bfloat16)
+    y = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    nbytes = N * (K // 2) + N * (K // 64) * 4
+    buf = torch.empty(nbytes // 256 * 256, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream()
+
+    def per_launch(fn):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(launches + 1)]
+        ev[0].record(s)
+        for i in range(launches):
+            fn()
+            ev[i + 1].record(s)
+        torch.cuda.synchronize()
+        d = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(launches)]
+        return [round(sum(d[i:i + window]) / window, 1) for i in range(0, launches, window)]
+
+    out = {"weight_bytes": nbytes, "window": window}
+    for name, fn in (("q4_gemv_us", lambda: q.q4_gemv(x, q.MOE_BF16, 1, codes, sb, q.MOE_BF16, N, K, y, s)),
+                     ("read_probe_us", lambda: q.moe_hbm_read_probe(buf, buf.numel(), sink, s)),
+                     ("q4_gemv_again_us", lambda: q.q4_gemv(x, q.MOE_BF16, 1, codes, sb, q.MOE_BF16, N, K, y, s))):
+        out[name] = per_launch(fn)
+        log(f"{name}: {out[name]}")
+    print(json.dumps(out), flush=True)
 
 
 def pinned_pools(layers):
@@ -695,8 +736,9 @@ def main():
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB (a reference for the HBM "
                          "traffic counters of a profiled run)")
-    ap.add_argument("--study", choices=("prefetch",), default=None,
-                    help="instead of the bench line, the expert-cache study (cross-layer prefetch, overlap granularity)")
+    ap.add_argument("--study", choices=("prefetch", "lmhead"), default=None,
+                    help="instead of the bench line: the expert-cache study (prefetch: cross-layer prefetch, overlap "
+                         "granularity) or the LM-head GEMV's duration over sustained launches (lmhead)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -712,6 +754,9 @@ def main():
     torch.cuda.set_device(0)
     if args.study == "prefetch":
         prefetch_study(args)
+        return
+    if args.study == "lmhead":
+        lm_head_drift()
         return
     t_build = time.perf_counter()
     shape, layers = build_stack(cfg, args.layers)
