@@ -3,8 +3,8 @@
 // Router: each block holds the token's activation in LDS as fp32 and each of its four wavefronts
 // computes one expert's logit with 16-byte int8 loads (coalesced along the row) and a wave reduction.
 // The last block to finish for a token (agent-scope ticket counter in the caller's workspace) reads the
-// token's logits back into LDS, ranks every candidate against all logits (ties: lower id first), keeps
-// the k best in rank order and takes the softmax over them.  It resets the counter, so the workspace is
+// token's logits back into LDS, takes the k best in rank order (larger first, ties: lower id first) and
+// the softmax over them.  It resets the counter, so the workspace is
 // reusable.  Logits travel between blocks by device-coherent stores and loads.
 #include "common.h"
 
@@ -51,6 +51,91 @@ __device__ __forceinline__ void store_act(void* out, bool bf16, int64_t i, float
     reinterpret_cast<float*>(out)[i] = v;
 }
 
+// The normalized activation of a router block, from this thread's 8-value pieces v[p] (elements
+// (threadIdx.x + 256 p) * 8 ..) and the gain g[p], into xs [d] (LDS) and, if u_out, to memory:
+// u[j] = round_x((x[j] * gamma[j]) * rinv), rinv = 1 / sqrt(sum_j x[j]^2 / d + eps).  The sum runs in the
+// order of the single-launch layer's norm (per thread an fma chain over its pieces in index order, the
+// wavefront sum, then the four wavefronts' sums in order), so both compute the same u.  Ends with a barrier.
+template <typename XT, int P>
+__device__ __forceinline__ void router_norm(const float (&v)[P][8], const float (&g)[P][8], int d, float eps, float* xs,
+                                            void* u_out, int64_t u_off, float* wsum) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float ss = 0.f;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int j0 = (threadIdx.x + 256 * p) * 8;
+    float si = ss;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) si = fmaf(v[p][i], v[p][i], si);
+    ss = j0 < d ? si : ss;
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) wsum[wave] = ss;
+  __syncthreads();
+  float tot = wsum[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) tot += wsum[w];
+  const float rinv = 1.0f / sqrtf(tot / (float)d + eps);
+  constexpr bool bf16 = sizeof(XT) == 2;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int j0 = (threadIdx.x + 256 * p) * 8;
+    if (j0 < d) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float u = (v[p][i] * g[p][i]) * rinv;
+        xs[j0 + i] = bf16 ? bf16_bits_to_f32(f32_to_bf16_bits(u)) : u;   // the norm output's rounding point
+        if (u_out) store_act(u_out, bf16, u_off + j0 + i, u);
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// The k best of lgs[0..E) (larger first, equal values -> lower id) into sel_i / sel_v in rank order, by the
+// block: wavefront 0 takes them with topk_wave for E <= 256, every thread ranks its candidates against all E
+// values otherwise (the same selection and order).  Ends with a barrier.
+__device__ __forceinline__ void router_rank(const float* lgs, int E, int k, int* sel_i, float* sel_v) {
+  if (E <= 256) {
+    if (threadIdx.x < 64) {
+      int id = -1;
+      float val = 0.f;
+      auto run = [&](auto per) {
+        constexpr int PER = decltype(per)::value;
+        float v[PER];
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+          const int e = threadIdx.x + 64 * m;
+          v[m] = e < E ? lgs[e] : 0.f;
+        }
+        topk_wave<PER>(v, E, k, id, val);
+      };
+      if (E <= 64) run(std::integral_constant<int, 1>());
+      else if (E <= 128) run(std::integral_constant<int, 2>());
+      else if (E <= 192) run(std::integral_constant<int, 3>());
+      else run(std::integral_constant<int, 4>());
+      if ((int)threadIdx.x < k) {
+        sel_i[threadIdx.x] = id;
+        sel_v[threadIdx.x] = val;
+      }
+    }
+  } else {
+    for (int c = threadIdx.x; c < E; c += 256) {
+      const float vc = lgs[c];
+      int rank = 0;
+      for (int e2 = 0; e2 < E; ++e2) {
+        const float u = lgs[e2];
+        rank += (u > vc) | ((u == vc) & (e2 < c));
+      }
+      if (rank < k) {
+        sel_i[rank] = c;
+        sel_v[rank] = vc;
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // ------------------------------------------------------------------------------------------------
 // RMSNorm: one block per token
 // ------------------------------------------------------------------------------------------------
@@ -68,27 +153,36 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const XT* __restrict__ x, 
     const int j0 = (threadIdx.x + 256 * p) * 8;
     if (j0 < d) load8(xt + j0, v[p]);
   }
+  float g[kPasses][8];
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int j0 = (threadIdx.x + 256 * p) * 8;
+    if (j0 < d) load8(gamma + j0, g[p]);
+  }
+  // the order of the single-launch layer's norm (router_norm): fma chain per thread, the wavefront sum,
+  // the four wavefronts' sums in order; u = (x * gamma) * rinv
   float ss = 0.f;
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     const int j0 = (threadIdx.x + 256 * p) * 8;
-    if (j0 < d)
+    float si = ss;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ss += v[p][i] * v[p][i];
+    for (int i = 0; i < 8; ++i) si = fmaf(v[p][i], v[p][i], si);
+    ss = j0 < d ? si : ss;
   }
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) partial[threadIdx.x >> 6] = ss;
   __syncthreads();
-  const float tot = (partial[0] + partial[1]) + (partial[2] + partial[3]);
+  float tot = partial[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) tot += partial[w];
   const float r = 1.0f / sqrtf(tot / (float)d + eps);
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     const int j0 = (threadIdx.x + 256 * p) * 8;
     if (j0 < d) {
-      const float4 g0 = reinterpret_cast<const float4*>(gamma + j0)[0], g1 = reinterpret_cast<const float4*>(gamma + j0)[1];
-      const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) store_act(out, out_bf16, t * d + j0 + i, (v[p][i] * r) * g[i]);
+      for (int i = 0; i < 8; ++i) store_act(out, out_bf16, t * d + j0 + i, (v[p][i] * g[p][i]) * r);
     }
   }
 }
@@ -141,41 +235,20 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
       if (a.gamma) load8(a.gamma + j0, g[p]);
     }
   }
-#pragma unroll
-  for (int p = 0; p < kPasses; ++p) {
-    const int j0 = (threadIdx.x + 256 * p) * 8;
-    if (j0 < a.d) {
-      *reinterpret_cast<float4*>(xs + j0) = make_float4(v[p][0], v[p][1], v[p][2], v[p][3]);
-      *reinterpret_cast<float4*>(xs + j0 + 4) = make_float4(v[p][4], v[p][5], v[p][6], v[p][7]);
-    }
-  }
-  __syncthreads();
-  if (a.gamma) {
-    // RMSNorm fused in: every block reduces x in the same fixed order (wave 0: lane p sums elements
-    // p, p+64, ... then a fixed xor tree), so all blocks obtain the same u bit for bit.
-    __shared__ float rinv;
-    if (wave == 0) {
-      float ss = 0.f;
-      for (int j = lane; j < a.d; j += 64) ss += xs[j] * xs[j];
-      ss = wave_sum(ss);
-      if (lane == 0) rinv = 1.0f / sqrtf(ss / (float)a.d + a.eps);
-    }
-    __syncthreads();
-    const float r = rinv;
-    constexpr bool bf16 = sizeof(XT) == 2;
+  if (!a.gamma) {
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
       const int j0 = (threadIdx.x + 256 * p) * 8;
       if (j0 < a.d) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float u = (v[p][i] * r) * g[p][i];
-          xs[j0 + i] = bf16 ? bf16_bits_to_f32(f32_to_bf16_bits(u)) : u;   // the norm output's bf16 rounding point
-          if (a.u_out && blockIdx.x == 0) store_act(a.u_out, bf16, t * a.d + j0 + i, u);
-        }
+        *reinterpret_cast<float4*>(xs + j0) = make_float4(v[p][0], v[p][1], v[p][2], v[p][3]);
+        *reinterpret_cast<float4*>(xs + j0 + 4) = make_float4(v[p][4], v[p][5], v[p][6], v[p][7]);
       }
     }
     __syncthreads();
+  } else {
+    // RMSNorm fused in: every block reduces x in the same fixed order, so all blocks obtain the same u
+    __shared__ float wsum[4];
+    router_norm<XT, kPasses>(v, g, a.d, a.eps, xs, blockIdx.x == 0 ? a.u_out : nullptr, t * a.d, wsum);
   }
 
   if (e < a.E) {
@@ -211,9 +284,8 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
   __syncthreads();
   if (!last_flag) return;
 
-  // The last block selects.  Top-k by rank: candidate e is kept iff fewer than k logits beat it
-  // (larger value, or equal value and lower id), and its rank is its position in the output.  Every
-  // comparison reads LDS by broadcast; there are no dependent cross-lane shuffle chains.
+  // The last block selects: candidate e is kept iff fewer than k logits beat it (larger value, or equal
+  // value and lower id), and its rank is its position in the output (router_rank).
   __shared__ float lgs[kMaxExperts];
   __shared__ float sel_v[kMaxK];
   __shared__ int sel_i[kMaxK];
@@ -230,25 +302,10 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
       sel_i[threadIdx.x] = i;
       sel_v[threadIdx.x] = (i >= 0 && i < a.E) ? lgs[i] : NAN;
     }
+    __syncthreads();
   } else {
-#pragma unroll
-    for (int p = 0; p < kMaxExperts / 256; ++p) {
-      const int c = threadIdx.x + 256 * p;
-      if (c < a.E) {
-        const float v = lgs[c];
-        int rank = 0;
-        for (int e2 = 0; e2 < a.E; ++e2) {
-          const float u = lgs[e2];
-          rank += (u > v) | ((u == v) & (e2 < c));
-        }
-        if (rank < a.k) {
-          sel_i[rank] = c;
-          sel_v[rank] = v;
-        }
-      }
-    }
+    router_rank(lgs, a.E, a.k, sel_i, sel_v);
   }
-  __syncthreads();
   // softmax over the k kept logits; every lane sums the same terms in the same order
   if (threadIdx.x < a.k) {
     float mx = sel_v[0];
@@ -277,7 +334,6 @@ constexpr int kLogitExperts = 16;   // experts per block: 4 per wavefront
 template <typename XT, int NCH>
 __global__ __launch_bounds__(256) void router_logits_kernel(RouterArgs a) {
   extern __shared__ float xs[];   // [d] fp32 activation
-  __shared__ float rinv;
   constexpr int kRows = kLogitExperts / 4;
   const int64_t t = blockIdx.y;
   const XT* x = reinterpret_cast<const XT*>(a.x) + t * a.d;
@@ -308,39 +364,20 @@ __global__ __launch_bounds__(256) void router_logits_kernel(RouterArgs a) {
       if (a.gamma) load8(a.gamma + j0, g[p]);
     }
   }
-#pragma unroll
-  for (int p = 0; p < kPasses; ++p) {
-    const int j0 = (threadIdx.x + 256 * p) * 8;
-    if (j0 < a.d) {
-      *reinterpret_cast<float4*>(xs + j0) = make_float4(v[p][0], v[p][1], v[p][2], v[p][3]);
-      *reinterpret_cast<float4*>(xs + j0 + 4) = make_float4(v[p][4], v[p][5], v[p][6], v[p][7]);
-    }
-  }
-  __syncthreads();
-  if (a.gamma) {
-    // the norm as in router_kernel: wave 0, lane p sums elements p, p + 64, ..., then the xor tree
-    if (wave == 0) {
-      float ss = 0.f;
-      for (int j = lane; j < a.d; j += 64) ss += xs[j] * xs[j];
-      ss = wave_sum(ss);
-      if (lane == 0) rinv = 1.0f / sqrtf(ss / (float)a.d + a.eps);
-    }
-    __syncthreads();
-    const float r = rinv;
-    constexpr bool bf16 = sizeof(XT) == 2;
+  if (!a.gamma) {
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
       const int j0 = (threadIdx.x + 256 * p) * 8;
       if (j0 < a.d) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float u = (v[p][i] * r) * g[p][i];
-          xs[j0 + i] = bf16 ? bf16_bits_to_f32(f32_to_bf16_bits(u)) : u;   // the norm output's bf16 rounding point
-          if (a.u_out && blockIdx.x == 0) store_act(a.u_out, bf16, t * a.d + j0 + i, u);
-        }
+        *reinterpret_cast<float4*>(xs + j0) = make_float4(v[p][0], v[p][1], v[p][2], v[p][3]);
+        *reinterpret_cast<float4*>(xs + j0 + 4) = make_float4(v[p][4], v[p][5], v[p][6], v[p][7]);
       }
     }
     __syncthreads();
+  } else {
+    // the norm as in router_kernel
+    __shared__ float wsum[4];
+    router_norm<XT, kPasses>(v, g, a.d, a.eps, xs, blockIdx.x == 0 ? a.u_out : nullptr, t * a.d, wsum);
   }
   // a lane's 16-value slices of the activation are the same for all of the wave's experts: read once
   float4 xr[NCH][4];
@@ -388,21 +425,10 @@ __global__ __launch_bounds__(256) void router_select_kernel(RouterArgs a) {
       sel_i[threadIdx.x] = i;
       sel_v[threadIdx.x] = (i >= 0 && i < a.E) ? lgs[i] : NAN;
     }
+    __syncthreads();
   } else {
-    for (int c = threadIdx.x; c < a.E; c += 256) {
-      const float vc = lgs[c];
-      int rank = 0;
-      for (int e2 = 0; e2 < a.E; ++e2) {
-        const float u = lgs[e2];
-        rank += (u > vc) | ((u == vc) & (e2 < c));
-      }
-      if (rank < a.k) {
-        sel_i[rank] = c;
-        sel_v[rank] = vc;
-      }
-    }
+    router_rank(lgs, a.E, a.k, sel_i, sel_v);
   }
-  __syncthreads();
   if (threadIdx.x < a.k) {
     float mx = sel_v[0];
     for (int r = 1; r < a.k; ++r) mx = fmaxf(mx, sel_v[r]);

@@ -129,8 +129,9 @@ def _ws(rp, sp, k, T):
 
 @pytest.mark.parametrize("gamma_ones", [True, False])
 def test_norm_router_vs_separate_and_oracle(gamma_ones):
-    """moe_norm_router_topk: u within one bf16 ulp of moe_rmsnorm's and of the oracle's RMSNorm; ids a valid
-    top-8 of the oracle's logits on that u; weights the softmax of those logits; forced ids honoured."""
+    """moe_norm_router_topk: u equal to moe_rmsnorm's bit for bit (one token alone or four together, with
+    the same logits, ids and weights) and within one bf16 ulp of the oracle's RMSNorm; ids a valid top-8 of
+    the oracle's logits on that u; weights the softmax of those logits; forced ids honoured."""
     cfg = synth.STACK
     d, E, k, T = cfg.d, cfg.n_experts, cfg.k, 4
     rw, rs = synth.router_int8(cfg.weight_cfg, 0, E, d)
@@ -149,7 +150,19 @@ def test_norm_router_vs_separate_and_oracle(gamma_ones):
     q.moe_rmsnorm(x, q.MOE_BF16, gamma, 1e-6, T, d, u_sep, q.MOE_BF16)
     torch.cuda.synchronize()
     uf, us = H.to_f64(u), H.to_f64(u_sep)
-    assert (np.abs(uf - us) <= 2.0 ** -7 * np.abs(us)).all()     # at most one bf16 ulp apart
+    assert torch.equal(u, u_sep)     # the same summation order: bit for bit
+    # the one-token launch (router_kernel) normalizes the same way as the batched one
+    u1 = torch.empty_like(x[:1])
+    ids1 = torch.empty((1, k), dtype=torch.int32, device="cuda")
+    wts1 = torch.empty((1, k), dtype=torch.float32, device="cuda")
+    lg1 = torch.empty((1, E), dtype=torch.float32, device="cuda")
+    ws1_b = q.moe_router_workspace_bytes(1, E)
+    ws1 = torch.zeros(ws1_b, dtype=torch.uint8, device="cuda")
+    q.moe_norm_router_topk(x[:1].contiguous(), q.MOE_BF16, gamma, 1e-6, 1, d, w_dev, s_dev, E, k, None, ids1, wts1, lg1,
+                           u1, ws1, ws1_b)
+    torch.cuda.synchronize()
+    assert torch.equal(u1[0], u[0])
+    assert torch.equal(ids1[0], ids[0]) and torch.equal(wts1[0], wts[0]) and torch.equal(lg1[0], lg[0])
     xs = H.to_f64(x)
     for t in range(T):
         u_ref = moe.rms_norm(xs[t], gamma_np.astype(np.float64), 1e-6)

@@ -65,7 +65,8 @@ def _check_clean(ws, cfg, calls):
 def test_decode_layer_vs_oracle(stack_layer, gamma_ones):
     """One d=2816 layer (RMSNorm, router, 8 of 128 experts + shared, residual) on eight tokens, one call
     each on one workspace.  The kernel's own normalized activation u (its optional output) is within one
-    bf16 step of the oracle's; the oracle's router run on that u gives the kernel's logits within 1e-4 and
+    bf16 step of the oracle's and equals moe_rmsnorm's bit for bit (the same summation order); the oracle's
+    router run on that u gives the kernel's logits within 1e-4 and
     ranks them like the kernel (exact ids when the 8th/9th gap exceeds 1e-3); the gate weights are the
     softmax of the logits; the output is within the parity bar of the oracle on the kernel's routing."""
     cfg, dev, shape = stack_layer
@@ -83,6 +84,10 @@ def test_decode_layer_vs_oracle(stack_layer, gamma_ones):
         u_ref = moe.f64_round_to_bf16(moe.rms_norm(x64, orc.gamma, 1e-6))
         u_gpu = H.to_f64(u_dev)
         assert H.bf16_steps(u_gpu, u_ref) <= 1, f"token {tok}: u off by more than one bf16 step"
+        u_sep = torch.empty_like(u_dev)
+        q.moe_rmsnorm(x, q.MOE_BF16, gamma, 1e-6, 1, cfg.d, u_sep, q.MOE_BF16)
+        torch.cuda.synchronize()
+        assert torch.equal(u_dev, u_sep), f"token {tok}: the layer's u differs from moe_rmsnorm's"
         ref_lg = moe.router_logits(orc.router_w, orc.router_s, u_gpu)
         got_lg = lg.cpu().numpy().astype(np.float64)
         assert np.abs(got_lg - ref_lg).max() <= 1e-4 * max(1.0, np.abs(ref_lg).max()), f"token {tok}"
