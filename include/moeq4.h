@@ -114,7 +114,10 @@ moe_status q4_gemv(const void* x_dev, moe_dtype x_dtype, int32_t T, const uint32
                    moe_dtype sb_dtype, int32_t N, int32_t K, float* y_dev, void* stream);
 
 /* ---------------------------------------------------------------------------------------------------
- * moe_rmsnorm — u[t] = x[t] / sqrt(mean(x[t]^2) + eps) * gamma, fp32 math, rounded to out_dtype (RNE).
+ * moe_rmsnorm — u[t] = (x[t] * gamma) * (1 / sqrt(mean(x[t]^2) + eps)), fp32 math, rounded to out_dtype
+ * (RNE).  The sum of squares runs in one fixed order (each thread an fma chain over its 8-value pieces
+ * (thread + 256 p) * 8, the wavefront sums, then the four wavefronts' sums in order), the order of
+ * moe_norm_router_topk and of the single-launch layer, so all three produce the same u.
  * The pages list a normalisation (RMSNorm) kernel ([LEAF] "Du code sur-mesure sans dépendance externe";
  * [DEVT] "Geen afhankelijkheden van llama.cpp en MLX"); it precedes each MoE block in the stacked decode.
  * x_dev: x_dtype [T][d]; gamma_dev: fp32 [d]; out_dev: out_dtype [T][d].  d % 8 == 0, d <= 16384, T >= 1;
@@ -149,9 +152,9 @@ moe_status moe_router_topk(const void* x_dev, moe_dtype x_dtype, int32_t T, int3
  * the RMSNorm and router kernels of the engine).  Every router block normalizes x itself:
  *   u[t] = round_x( x[t] / sqrt(mean(x[t]^2) + eps) * gamma )      (fp32 math, RNE to x_dtype)
  * and routes u[t] exactly as moe_router_topk routes its x; block 0 also writes u to u_dev (x_dtype [T][d],
- * 16-byte aligned) for the expert GEMVs.  The sum of squares is reduced in a fixed order that differs from
- * moe_rmsnorm's, so u may differ from moe_rmsnorm's output in the last bit.  gamma_dev: fp32 [d], 16-byte
- * aligned; eps >= 0.  Other arguments, limits and the workspace rule as moe_router_topk. */
+ * 16-byte aligned) for the expert GEMVs.  The norm is moe_rmsnorm's, in the same order: u equals
+ * moe_rmsnorm's output bit for bit, and a token's logits, ids and weights do not depend on T.  gamma_dev:
+ * fp32 [d], 16-byte aligned; eps >= 0.  Other arguments, limits and the workspace rule as moe_router_topk. */
 moe_status moe_norm_router_topk(const void* x_dev, moe_dtype x_dtype, const float* gamma_dev, float eps, int32_t T,
                                 int32_t d, const int8_t* w_dev, const float* row_scale_dev, int32_t E, int32_t k,
                                 const int32_t* forced_ids_dev, int32_t* ids_dev, float* weights_dev,
@@ -257,9 +260,9 @@ moe_status q4_expert_gemv_combine(const moe_q4_pool* routed, const int32_t* ids_
  *   u       = gamma ? round_x((x * gamma) * rsqrt(mean(x^2) + eps)) : x
  *   logits  = row_scale[e] * (w[e] . u);  ids = top-k (or forced ids);  weights = softmax over ids
  *   out     = round_x( sum_i weights[i] * FFN_{ids[i]}(u) + FFN_shared(u) + (residual ? x : 0) )
- * with the selection rule, weights and expert arithmetic of moe_router_topk / q4_expert_gemv.  The norm's
- * sum of squares and the router's dot products use their own fixed orders, so u may differ from
- * moe_rmsnorm's in the last bit and the logits from moe_router_topk's in the last bits.
+ * with the selection rule, weights and expert arithmetic of moe_router_topk / q4_expert_gemv.  u equals
+ * moe_rmsnorm's bit for bit (the same summation order); the router's dot products use an order of their own,
+ * so the logits may differ from moe_router_topk's in the last bits.
  * x_dev, out_dev: x_dtype [d] (16-byte aligned, must not alias); gamma_dev: fp32 [d] or NULL;
  * router as moe_router_topk; forced_ids_dev: int32 [k] or NULL; routed: pool of experts, indexed by the
  * selected ids, or by gemv_ids_dev[i] (int32 [k], e.g. cache slots from expert_cache_stage) when that is
