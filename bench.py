@@ -732,7 +732,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the batched and streamed measurements")
     ap.add_argument("--stream-tokens", type=int, default=512)
-    ap.add_argument("--copy-streams", type=int, default=2, help="streams the expert cache's copies alternate over")
+    ap.add_argument("--copy-streams", type=int, default=4,
+                    help="streams the expert cache's copies alternate over (4: the overlap schedule's best of 1-8)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB (a reference for the HBM "
                          "traffic counters of a profiled run)")
