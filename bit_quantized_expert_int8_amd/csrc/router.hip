@@ -18,8 +18,11 @@ constexpr int kCounterStride = 64;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxK = 32;
 constexpr int kRouterChunks = 8;    // 16-byte chunks per lane: rows of up to 8192 int8
-// from this many tokens on, logits and selection as two launches; below, one launch (router_kernel)
+// from this many tokens on, logits by (token, 16 experts) blocks; below, one launch of router_kernel
 constexpr int kSplitRouterMinT = 2;
+// up to this many tokens the last logit block of a token selects (ticket, one launch); above, a second launch
+// selects (measured: 123.3 against 124.6 us per layer at 32 tokens, 180.1 against 179.3 at 128)
+constexpr int kTicketRouterMaxT = 32;
 
 template <typename T>
 __device__ __forceinline__ float load_act(const T* p, int64_t i);
@@ -319,19 +322,20 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// Router for several tokens: logits, then selection, as two launches
+// Router for several tokens: logits by (token, 16 experts), then the selection
 // ------------------------------------------------------------------------------------------------
 // With a block per four experts and the selection in the last block to finish, a batch's tokens each
 // gather E / 4 blocks' logits through device-coherent stores and a ticket counter that those blocks
 // update one after another; for 32 or 128 tokens that hand-off dominates.  A block per token instead is
 // bound by one compute unit's arithmetic (E dot products of d int8 values).  So the logits come from a
-// block per (token, kLogitExperts experts), written with plain stores, and a second launch selects, a
-// block per token, after the kernel boundary has made them visible.  Every per-expert sum, the norm's
-// reduction and the ranking run exactly as in router_kernel (same lanes, same order): the results agree
-// bit for bit.
+// block per (token, kLogitExperts experts).  With TICKET (up to kTicketRouterMaxT tokens) they go out by
+// device-coherent stores and the last of a token's E / 16 blocks (ticket) selects, as router_kernel does;
+// otherwise they go out with plain stores and a second launch selects, a block per token, after the kernel
+// boundary has made them visible.  Every per-expert sum, the norm's reduction and the ranking run exactly as
+// in router_kernel (same lanes, same order): the results agree bit for bit.
 constexpr int kLogitExperts = 16;   // experts per block: 4 per wavefront
 
-template <typename XT, int NCH>
+template <typename XT, int NCH, bool TICKET>
 __global__ __launch_bounds__(256) void router_logits_kernel(RouterArgs a) {
   extern __shared__ float xs[];   // [d] fp32 activation
   constexpr int kRows = kLogitExperts / 4;
@@ -407,8 +411,46 @@ __global__ __launch_bounds__(256) void router_logits_kernel(RouterArgs a) {
       }
     }
     acc = wave_sum(acc);
-    if (lane == 0 && e < a.E) a.logits[t * a.E + e] = acc * sc[r];
+    if (lane == 0 && e < a.E) {
+      if (TICKET) __hip_atomic_store(a.logits + t * a.E + e, acc * sc[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else a.logits[t * a.E + e] = acc * sc[r];
+    }
   }
+  if (!TICKET) return;
+  __shared__ uint32_t last_flag;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t ticket = __hip_atomic_fetch_add(a.counters + t * kCounterStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_flag = (ticket == gridDim.x - 1) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (!last_flag) return;
+  __shared__ float lgs[kMaxExperts];
+  __shared__ float sel_v[kMaxK];
+  __shared__ int sel_i[kMaxK];
+  const float* lg = a.logits + t * a.E;
+  for (int e2 = threadIdx.x; e2 < a.E; e2 += 256) lgs[e2] = __hip_atomic_load(lg + e2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (a.forced) {
+    if (threadIdx.x < a.k) {
+      const int i = a.forced[t * a.k + threadIdx.x];
+      sel_i[threadIdx.x] = i;
+      sel_v[threadIdx.x] = (i >= 0 && i < a.E) ? lgs[i] : NAN;
+    }
+    __syncthreads();
+  } else {
+    router_rank(lgs, a.E, a.k, sel_i, sel_v);
+  }
+  if (threadIdx.x < a.k) {
+    float mx = sel_v[0];
+    for (int rr = 1; rr < a.k; ++rr) mx = fmaxf(mx, sel_v[rr]);
+    float den = 0.f;
+    for (int rr = 0; rr < a.k; ++rr) den += expf(sel_v[rr] - mx);
+    a.ids[t * a.k + threadIdx.x] = sel_i[threadIdx.x];
+    a.weights[t * a.k + threadIdx.x] = expf(sel_v[threadIdx.x] - mx) / den;
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(a.counters + t * kCounterStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // A block per token: the token's logits into LDS, top-k by rank and the softmax, as in router_kernel.
@@ -571,10 +613,17 @@ moe_status router_launch(const char* who, const void* x_dev, moe_dtype x_dtype, 
     const dim3 grid_l((E + kLogitExperts - 1) / kLogitExperts, T);
     auto go = [&](auto nc) {
       constexpr int NCH = decltype(nc)::value;
+      if (T <= kTicketRouterMaxT) {
+        if (x_dtype == MOE_BF16)
+          hipLaunchKernelGGL((router_logits_kernel<uint16_t, NCH, true>), grid_l, dim3(256), lds, s, a);
+        else
+          hipLaunchKernelGGL((router_logits_kernel<float, NCH, true>), grid_l, dim3(256), lds, s, a);
+        return check_launch(who);
+      }
       if (x_dtype == MOE_BF16)
-        hipLaunchKernelGGL((router_logits_kernel<uint16_t, NCH>), grid_l, dim3(256), lds, s, a);
+        hipLaunchKernelGGL((router_logits_kernel<uint16_t, NCH, false>), grid_l, dim3(256), lds, s, a);
       else
-        hipLaunchKernelGGL((router_logits_kernel<float, NCH>), grid_l, dim3(256), lds, s, a);
+        hipLaunchKernelGGL((router_logits_kernel<float, NCH, false>), grid_l, dim3(256), lds, s, a);
       const moe_status st = check_launch(who);
       if (st != MOE_OK) return st;
       hipLaunchKernelGGL(router_select_kernel, dim3(T), dim3(256), 0, s, a);
