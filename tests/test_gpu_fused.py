@@ -178,3 +178,35 @@ def test_norm_router_vs_separate_and_oracle(gamma_ones):
     for t in range(T):
         ref_lg = moe.router_logits(rw, rs, uf[t])
         assert np.allclose(wts[t].cpu().numpy(), moe.gate_weights(ref_lg, forced[t].cpu().numpy()), rtol=0, atol=1e-6)
+
+
+@pytest.mark.parametrize("T", [2, 32, 33])
+def test_norm_router_paths_agree_bit_for_bit(T):
+    """moe_norm_router_topk runs one launch per token block for T = 1, a launch whose last logit block of each
+    token selects for 2 <= T <= 32, and logits then selection (two launches) above: every token's u, logits,
+    ids and weights equal the one-token call's bit for bit (same norm order, same dot products, same ranking)."""
+    cfg = synth.STACK
+    d, E, k = cfg.d, cfg.n_experts, cfg.k
+    rw, rs = synth.router_int8(cfg.weight_cfg, 1, E, d)
+    gamma = torch.from_numpy(synth.rms_gamma(cfg.weight_cfg, 1, d, ones=False)).cuda()
+    w_dev, s_dev = torch.from_numpy(rw).cuda(), torch.from_numpy(rs).cuda()
+    x = H.token_batch(cfg, range(40, 40 + T))
+
+    def run(xs):
+        n = xs.shape[0]
+        ws_b = q.moe_router_workspace_bytes(n, E)
+        ws = torch.zeros(ws_b, dtype=torch.uint8, device="cuda")
+        u = torch.empty_like(xs)
+        ids = torch.empty((n, k), dtype=torch.int32, device="cuda")
+        wts = torch.empty((n, k), dtype=torch.float32, device="cuda")
+        lg = torch.empty((n, E), dtype=torch.float32, device="cuda")
+        q.moe_norm_router_topk(xs, q.MOE_BF16, gamma, 1e-6, n, d, w_dev, s_dev, E, k, None, ids, wts, lg, u, ws, ws_b)
+        return u, ids, wts, lg
+
+    u, ids, wts, lg = run(x)
+    torch.cuda.synchronize()
+    for t in range(T):
+        u1, ids1, wts1, lg1 = run(x[t:t + 1].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(u1[0], u[t]) and torch.equal(lg1[0], lg[t]), f"token {t}"
+        assert torch.equal(ids1[0], ids[t]) and torch.equal(wts1[0], wts[t]), f"token {t}"
