@@ -30,6 +30,20 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == set(q.EXPORTED)
 
 
+@pytest.mark.parametrize("compiler,flags", [("gcc", ["-x", "c", "-std=c99"]), ("g++", ["-x", "c++", "-std=c++17"])])
+def test_header_compiles_alone(compiler, flags, tmp_path):
+    """include/moeq4.h is a self-contained C header: it compiles on its own as C99 and as C++17, warning-free."""
+    import shutil
+    import subprocess
+    if shutil.which(compiler) is None:
+        pytest.skip(f"{compiler} not found")
+    src = tmp_path / "use_header.c"
+    src.write_text('#include "moeq4.h"\nint main(void) { return 0; }\n')
+    r = subprocess.run([compiler, *flags, "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
+                        "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
 @pytest.mark.parametrize("d,F,sb", [(256, 128, 0), (2816, 704, 1), (2816, 2816, 1), (64, 64, 0), (4096, 1536, 1)])
 def test_record_layout_matches_oracle(d, F, sb):
     lay = moe.record_layout(d, F, sb == 1)
