@@ -215,6 +215,45 @@ def test_decode_stack_equals_chained_layers():
             assert bad.size == 0, f"layer {l}: synchronisation words left at {seg[bad[:8]]} (call {call})"
 
 
+@pytest.mark.parametrize("shared", [True, False])
+def test_decode_stack_small_fp32_equals_chained_layers(shared):
+    """Six layers of the small configuration (d=256, 8 experts top-2, fp32 activations and scale/bias, RMSNorm
+    with a seeded gain, residual) in one moe_decode_stack launch, with and without the shared expert: the
+    multi-layer instantiations for fp32 activations and without the shared expert's roles equal six chained
+    moe_decode_layer calls bit for bit (output, ids, weights, logits), twice in a row on one workspace, and
+    leave the error flag clear."""
+    cfg = synth.TINY
+    L = 6
+    devs = [H.device_layer(cfg, l) for l in range(L)]
+    shape = H.shape_of(cfg)
+    rp, sp = _pools(cfg, devs[0], shape, shared)
+    E, k, d = cfg.n_experts, cfg.k, cfg.d
+    S = cfg.S if shared else 0
+    gammas = [torch.from_numpy(synth.rms_gamma(cfg.weight_cfg, l, d, ones=False)).cuda() for l in range(L)]
+    ids = torch.full((L, k), -1, dtype=torch.int32, device="cuda")
+    wts = torch.zeros((L, k), dtype=torch.float32, device="cuda")
+    lgs = torch.zeros((L, E), dtype=torch.float32, device="cuda")
+    descs = q.stack_layers([{"router_w_dev": W.router_w, "router_scale_dev": W.router_s, "gamma_dev": gammas[l],
+                             "routed_base_dev": W.pool, "shared_base_dev": W.shared if shared else None,
+                             "ids_dev": ids[l], "weights_dev": wts[l], "logits_dev": lgs[l]}
+                            for l, W in enumerate(devs)])
+    sb = q.moe_decode_stack_workspace_bytes(L, d, E, k, cfg.F, S)
+    ws = torch.zeros(sb, dtype=torch.uint8, device="cuda")
+    lws, lwb = _ws(cfg, shared)
+    for call, tok in enumerate((3, 4), 1):
+        x = H.token_batch(cfg, [tok])[0]
+        out = torch.empty_like(x)
+        q.moe_decode_stack(descs, L, x, q.MOE_F32, 1e-6, 1, E, k, rp, sp, shape.act, out, ws, sb)
+        xs = x
+        for l, W in enumerate(devs):
+            i1, w1, g1, o1 = _run(cfg, W, shape, xs, lws, lwb, gammas[l], 1, shared=shared)
+            torch.cuda.synchronize()
+            assert torch.equal(i1, ids[l]) and torch.equal(w1, wts[l]) and torch.equal(g1, lgs[l]), f"layer {l}"
+            xs = o1
+        assert torch.equal(xs, out), f"token {tok}"
+        assert int(ws.view(torch.int32)[0].item()) == 0, "a wait inside the stack kernel ran out"
+
+
 # ---------------------------------------------------------------------------------------------------
 # the method's degenerate cases on the single-launch layer (small configuration: d=256, 8 experts)
 # ---------------------------------------------------------------------------------------------------
