@@ -215,10 +215,11 @@ def test_decode_stack_equals_chained_layers():
             assert bad.size == 0, f"layer {l}: synchronisation words left at {seg[bad[:8]]} (call {call})"
 
 
-@pytest.mark.parametrize("shared", [True, False])
-def test_decode_stack_small_fp32_equals_chained_layers(shared):
+@pytest.mark.parametrize("shared,k", [(True, 2), (False, 2), (True, 8)])
+def test_decode_stack_small_fp32_equals_chained_layers(shared, k):
     """Six layers of the small configuration (d=256, 8 experts top-2, fp32 activations and scale/bias, RMSNorm
-    with a seeded gain, residual) in one moe_decode_stack launch, with and without the shared expert: the
+    with a seeded gain, residual) in one moe_decode_stack launch, with and without the shared expert, top-2 and
+    top-8 (every expert): the
     multi-layer instantiations for fp32 activations and without the shared expert's roles equal six chained
     moe_decode_layer calls bit for bit (output, ids, weights, logits), twice in a row on one workspace, and
     leave the error flag clear."""
@@ -227,7 +228,7 @@ def test_decode_stack_small_fp32_equals_chained_layers(shared):
     devs = [H.device_layer(cfg, l) for l in range(L)]
     shape = H.shape_of(cfg)
     rp, sp = _pools(cfg, devs[0], shape, shared)
-    E, k, d = cfg.n_experts, cfg.k, cfg.d
+    E, d = cfg.n_experts, cfg.d
     S = cfg.S if shared else 0
     gammas = [torch.from_numpy(synth.rms_gamma(cfg.weight_cfg, l, d, ones=False)).cuda() for l in range(L)]
     ids = torch.full((L, k), -1, dtype=torch.int32, device="cuda")
@@ -239,14 +240,15 @@ def test_decode_stack_small_fp32_equals_chained_layers(shared):
                             for l, W in enumerate(devs)])
     sb = q.moe_decode_stack_workspace_bytes(L, d, E, k, cfg.F, S)
     ws = torch.zeros(sb, dtype=torch.uint8, device="cuda")
-    lws, lwb = _ws(cfg, shared)
+    lwb = q.moe_decode_layer_workspace_bytes(d, E, k, cfg.F, S)
+    lws = torch.zeros(lwb, dtype=torch.uint8, device="cuda")
     for call, tok in enumerate((3, 4), 1):
         x = H.token_batch(cfg, [tok])[0]
         out = torch.empty_like(x)
         q.moe_decode_stack(descs, L, x, q.MOE_F32, 1e-6, 1, E, k, rp, sp, shape.act, out, ws, sb)
         xs = x
         for l, W in enumerate(devs):
-            i1, w1, g1, o1 = _run(cfg, W, shape, xs, lws, lwb, gammas[l], 1, shared=shared)
+            i1, w1, g1, o1 = _run(cfg, W, shape, xs, lws, lwb, gammas[l], 1, shared=shared, k=k)
             torch.cuda.synchronize()
             assert torch.equal(i1, ids[l]) and torch.equal(w1, wts[l]) and torch.equal(g1, lgs[l]), f"layer {l}"
             xs = o1
