@@ -337,7 +337,8 @@ def pinned_pools(layers):
     return host
 
 
-def measure_streamed(shape, layers, cfg, dec, n_tokens, overlap=True, copy_streams=1, pinned_gbps=None, host=None):
+def measure_streamed(shape, layers, cfg, dec, n_tokens, overlap=True, copy_streams=1, pinned_gbps=None, host=None,
+                     run_ahead=False):
     """Experts served from pinned host memory through a 16-slot LFU cache per layer (routing forced by a
     Zipf(1.1) trace): tokens/s over all tokens and over the second half (warm cache), hit rates, and the
     host-to-device rate against a plain pinned 1 GiB copy measured in the same process.
@@ -345,7 +346,9 @@ def measure_streamed(shape, layers, cfg, dec, n_tokens, overlap=True, copy_strea
     With `overlap`, each layer runs as two launches: the router and the shared expert (moe_decode_layer_part
     part 1) go ahead while the layer's missing experts are copied, and the routed experts and the combine
     (part 2) wait for the copies; without, the whole layer waits for them.  Layers' copies go to
-    `copy_streams` streams in turn."""
+    `copy_streams` streams in turn.  Unless `run_ahead`, the host stages layer l of a token once layer l of the
+    previous token has run (a host-side wait, so the copies are enqueued without a device-side wait; the
+    copy streams still hold up to a token of work)."""
     import numpy as np
     import torch
     import synth
@@ -388,6 +391,8 @@ def measure_streamed(shape, layers, cfg, dec, n_tokens, overlap=True, copy_strea
             x = toks[t % 64]
             for l in range(L):
                 th = time.perf_counter()
+                if not run_ahead:
+                    freed[l].synchronize()
                 q.expert_cache_stage(cache, l, trace[t, l].tolist(), slot_ids[l], cstreams[l % copy_streams], freed[l],
                                      ready[l])
                 out = bufs[l % 2]
@@ -605,6 +610,38 @@ def pinned_copy_gbps(reps=3):
     gbps = reps * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del ref_h, ref_d
     return gbps
+
+
+def record_copy_gbps(host, copy_streams, n_copies=240, per_group=4):
+    """Back-to-back copies of single expert records (pinned host -> HBM), in groups of `per_group` on one stream,
+    the groups on `copy_streams` streams in turn, as the expert cache issues a layer's misses: the host
+    link's rate at the cache's copy size, next to the plain 1 GiB copy."""
+    import torch
+
+    rb = host[0].shape[1]
+    dst = torch.empty((16, rb), dtype=torch.uint8, device="cuda")
+    streams = [torch.cuda.Stream() for _ in range(copy_streams)]
+    main = torch.cuda.current_stream()
+
+    def run():
+        for st in streams:
+            st.wait_stream(main)
+        for i in range(n_copies):
+            st = streams[(i // per_group) % copy_streams]
+            h = host[i % len(host)]
+            with torch.cuda.stream(st):
+                dst[i % 16].copy_(h[(7 * i) % h.shape[0]], non_blocking=True)
+        for st in streams:
+            main.wait_stream(st)
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run()
+    e1.record()
+    e1.synchronize()
+    return n_copies * rb / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
 def cpu_model():
@@ -846,6 +883,7 @@ def main():
         log(f"streamed: {out['streamed']['tok_s_all']} tokens/s")
         base = measure_streamed(shape, layers, cfg, dec, args.stream_tokens // 2, overlap=False,
                                 copy_streams=args.copy_streams, pinned_gbps=pinned, host=host)
+        out["streamed"]["record_copy_GBps"] = {str(n): round(record_copy_gbps(host, n), 2) for n in (1, args.copy_streams)}
         del host
         out["streamed"]["without_overlap"] = {kk: base[kk] for kk in ("tokens", "tok_s_all", "tok_s_warm",
                                                                      "h2d_GBps_effective_warm")}

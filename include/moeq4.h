@@ -403,7 +403,8 @@ void moe_expert_cache_destroy(moe_expert_cache* cache);
 /* expert_cache_stage — make the n experts ids_host[0..n) of `layer` resident.
  * Runs the policy on the host, enqueues one hipMemcpyAsync per miss (pinned host record -> HBM slot) on
  * copy_stream after waiting on wait_event (if not NULL: the event recorded after the last kernel that read
- * this layer's slots, so a slot is never overwritten while it is read), writes the slot index of each id
+ * this layer's slots, so a slot is never overwritten while it is read; an event already complete at the
+ * call is not waited on, the copies then start without a device-side wait), writes the slot index of each id
  * to slot_ids_dev (int32 [n], copied on copy_stream), then records ready_event (if not NULL) on
  * copy_stream.  Kernels that read the slots must wait on ready_event.
  * Errors: duplicate ids or n > n_slots -> MOE_ERR_CACHE; id outside [0, n_experts) -> MOE_ERR_OUT_OF_RANGE;
