@@ -612,38 +612,6 @@ def pinned_copy_gbps(reps=3):
     return gbps
 
 
-def record_copy_gbps(host, copy_streams, n_copies=240, per_group=4):
-    """Back-to-back copies of single expert records (pinned host -> HBM), in groups of `per_group` on one stream,
-    the groups on `copy_streams` streams in turn, as the expert cache issues a layer's misses: the host
-    link's rate at the cache's copy size, next to the plain 1 GiB copy."""
-    import torch
-
-    rb = host[0].shape[1]
-    dst = torch.empty((16, rb), dtype=torch.uint8, device="cuda")
-    streams = [torch.cuda.Stream() for _ in range(copy_streams)]
-    main = torch.cuda.current_stream()
-
-    def run():
-        for st in streams:
-            st.wait_stream(main)
-        for i in range(n_copies):
-            st = streams[(i // per_group) % copy_streams]
-            h = host[i % len(host)]
-            with torch.cuda.stream(st):
-                dst[i % 16].copy_(h[(7 * i) % h.shape[0]], non_blocking=True)
-        for st in streams:
-            main.wait_stream(st)
-
-    run()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    run()
-    e1.record()
-    e1.synchronize()
-    return n_copies * rb / (e0.elapsed_time(e1) * 1e-3) / 1e9
-
-
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -883,7 +851,6 @@ def main():
         log(f"streamed: {out['streamed']['tok_s_all']} tokens/s")
         base = measure_streamed(shape, layers, cfg, dec, args.stream_tokens // 2, overlap=False,
                                 copy_streams=args.copy_streams, pinned_gbps=pinned, host=host)
-        out["streamed"]["record_copy_GBps"] = {str(n): round(record_copy_gbps(host, n), 2) for n in (1, args.copy_streams)}
         del host
         out["streamed"]["without_overlap"] = {kk: base[kk] for kk in ("tokens", "tok_s_all", "tok_s_warm",
                                                                      "h2d_GBps_effective_warm")}
