@@ -47,6 +47,36 @@ __device__ __forceinline__ void load8(const float* p, float v[8]) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// 8 consecutive activations as loaded (16 or 32 bytes), converted to fp32 where they are used: a load issued
+// a token ahead is not waited for before the conversion
+template <typename XT>
+struct Raw8;
+template <>
+struct Raw8<uint16_t> {
+  uint4 r;
+  __device__ __forceinline__ void load(const uint16_t* p) { r = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void to_f32(float v[8]) const {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+template <>
+struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ void to_f32(float v[8]) const {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
 __device__ __forceinline__ void store_act(void* out, bool bf16, int64_t i, float v) {
   if (bf16)
     reinterpret_cast<uint16_t*>(out)[i] = (uint16_t)f32_to_bf16_bits(v);
@@ -59,7 +89,11 @@ __device__ __forceinline__ void store_act(void* out, bool bf16, int64_t i, float
 // u[j] = round_x((x[j] * gamma[j]) * rinv), rinv = 1 / sqrt(sum_j x[j]^2 / d + eps).  The sum runs in the
 // order of the single-launch layer's norm (per thread an fma chain over its pieces in index order, the
 // wavefront sum, then the four wavefronts' sums in order), so both compute the same u.  Ends with a barrier.
-template <typename XT, int P>
+// Barrier for LDS only: the block's LDS writes are complete and visible; loads and stores to memory stay in
+// flight (__syncthreads also waits for those)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <typename XT, int P, bool LDSB = false>
 __device__ __forceinline__ void router_norm(const float (&v)[P][8], const float (&g)[P][8], int d, float eps, float* xs,
                                             void* u_out, int64_t u_off, float* wsum) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -74,7 +108,8 @@ __device__ __forceinline__ void router_norm(const float (&v)[P][8], const float 
   }
   ss = wave_sum(ss);
   if (lane == 0) wsum[wave] = ss;
-  __syncthreads();
+  if (LDSB) lds_barrier();
+  else __syncthreads();
   float tot = wsum[0];
 #pragma unroll
   for (int w = 1; w < 4; ++w) tot += wsum[w];
@@ -92,7 +127,8 @@ __device__ __forceinline__ void router_norm(const float (&v)[P][8], const float 
       }
     }
   }
-  __syncthreads();
+  if (LDSB) lds_barrier();
+  else __syncthreads();
 }
 
 // The k best of lgs[0..E) (larger first, equal values -> lower id) into sel_i / sel_v in rank order, by the
@@ -206,6 +242,7 @@ struct RouterArgs {
   const float* gamma;    // RMSNorm gain [d], or NULL: the router reads x as is
   float eps;
   void* u_out;           // [T][d] normalized activation (x dtype), written by block 0; NULL = not wanted
+  int T;
 };
 
 __device__ __forceinline__ bool better(float v, int i, float v2, int i2) { return v > v2 || (v == v2 && i < i2); }
@@ -331,22 +368,55 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
 // block per (token, kLogitExperts experts).  With TICKET (up to kTicketRouterMaxT tokens) they go out by
 // device-coherent stores and the last of a token's E / 16 blocks (ticket) selects, as router_kernel does;
 // otherwise they go out with plain stores and a second launch selects, a block per token, after the kernel
-// boundary has made them visible.  Every per-expert sum, the norm's reduction and the ranking run exactly as
-// in router_kernel (same lanes, same order): the results agree bit for bit.
+// boundary has made them visible.  Every per-expert sum, the norm's reduction and the ranking run exactly
+// as in router_kernel (same lanes, same order): the results agree bit for bit.  (Blocks that keep their
+// rows for several tokens, the activations staged in LDS, were measured slower: a token's norm and dot
+// products take a block about 3.5 us, so four tokens in turn cost more than the second round of blocks.)
 constexpr int kLogitExperts = 16;   // experts per block: 4 per wavefront
 
-template <typename XT, int NCH, bool TICKET>
-__global__ __launch_bounds__(256) void router_logits_kernel(RouterArgs a) {
-  extern __shared__ float xs[];   // [d] fp32 activation
-  constexpr int kRows = kLogitExperts / 4;
-  const int64_t t = blockIdx.y;
-  const XT* x = reinterpret_cast<const XT*>(a.x) + t * a.d;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nch = a.d / 16;
-  const int e0 = blockIdx.x * kLogitExperts + wave * kRows;
-  // this wave's rows and scales first, then the activation (and the norm gain), all in one round trip
-  int4 q[kRows][NCH];
-  float sc[kRows];
+// The dot products of a wavefront's kRows rows with the activation in LDS (xs, fp32): lane l takes the
+// 16-value slices l, l + 64, ... of each row; the rows' sums run side by side (independent chains), each in
+// the same order as alone; returns the wavefront sums.
+template <int NCH, int kRows>
+__device__ __forceinline__ void logit_rows(const int4 (&q)[kRows][NCH], const float* xs, int nch, float (&out)[kRows]) {
+  const int lane = threadIdx.x & 63;
+  // a lane's 16-value slices of the activation are the same for all of the wave's experts: read once
+  float4 xr[NCH][4];
+#pragma unroll
+  for (int m = 0; m < NCH; ++m) {
+    const int c = lane + 64 * m;
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4)
+      xr[m][k4] = c < nch ? reinterpret_cast<const float4*>(xs + c * 16)[k4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float acc[kRows];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int m = 0; m < NCH; ++m) {
+    const int c = lane + 64 * m;
+    if (c >= nch) break;
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      const float4 xx = xr[m][k4];
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) {
+        const int qw = k4 == 0 ? q[r][m].x : k4 == 1 ? q[r][m].y : k4 == 2 ? q[r][m].z : q[r][m].w;
+        acc[r] += (float)(int8_t)(qw & 0xff) * xx.x;
+        acc[r] += (float)(int8_t)((qw >> 8) & 0xff) * xx.y;
+        acc[r] += (float)(int8_t)((qw >> 16) & 0xff) * xx.z;
+        acc[r] += (float)(int8_t)((qw >> 24) & 0xff) * xx.w;
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) out[r] = wave_sum(acc[r]);
+}
+
+// This wavefront's kRows rows of int8 weights (16-byte slices, as logit_rows reads them) and their scales
+template <int NCH, int kRows>
+__device__ __forceinline__ void load_logit_rows(const RouterArgs& a, int e0, int nch, int4 (&q)[kRows][NCH], float (&sc)[kRows]) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int r = 0; r < kRows; ++r) {
     const int e = e0 + r;
@@ -358,13 +428,27 @@ __global__ __launch_bounds__(256) void router_logits_kernel(RouterArgs a) {
       if (c < nch) q[r][m] = *reinterpret_cast<const int4*>(row + c * 16);
     }
   }
-  constexpr int kPasses = 8192 / (8 * 256);
+}
+
+template <typename XT, int NCH, bool TICKET>
+__global__ __launch_bounds__(256) void router_logits_kernel(RouterArgs a) {
+  extern __shared__ float xs[];   // [d] fp32 activation
+  constexpr int kRows = kLogitExperts / 4;
+  const int64_t t = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nch = a.d / 16;
+  const int e0 = blockIdx.x * kLogitExperts + wave * kRows;
+  // this wave's rows and scales first, then the activation (and the norm gain), all in one round trip
+  int4 q[kRows][NCH];
+  float sc[kRows];
+  load_logit_rows<NCH, kRows>(a, e0, nch, q, sc);
+  constexpr int kPasses = (NCH + 1) / 2;   // 8 values per thread and pass: rows of d <= 1024 NCH
   float v[kPasses][8], g[kPasses][8];
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     const int j0 = (threadIdx.x + 256 * p) * 8;
     if (j0 < a.d) {
-      load8(x + j0, v[p]);
+      load8(reinterpret_cast<const XT*>(a.x) + t * a.d + j0, v[p]);
       if (a.gamma) load8(a.gamma + j0, g[p]);
     }
   }
@@ -383,37 +467,14 @@ __global__ __launch_bounds__(256) void router_logits_kernel(RouterArgs a) {
     __shared__ float wsum[4];
     router_norm<XT, kPasses>(v, g, a.d, a.eps, xs, blockIdx.x == 0 ? a.u_out : nullptr, t * a.d, wsum);
   }
-  // a lane's 16-value slices of the activation are the same for all of the wave's experts: read once
-  float4 xr[NCH][4];
-#pragma unroll
-  for (int m = 0; m < NCH; ++m) {
-    const int c = lane + 64 * m;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      xr[m][i] = c < nch ? reinterpret_cast<const float4*>(xs + c * 16)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  float lgt[kRows];
+  logit_rows<NCH, kRows>(q, xs, nch, lgt);
 #pragma unroll
   for (int r = 0; r < kRows; ++r) {
     const int e = e0 + r;
-    float acc = 0.f;
-#pragma unroll
-    for (int m = 0; m < NCH; ++m) {
-      const int c = lane + 64 * m;
-      if (c >= nch) break;
-      const int qw[4] = {q[r][m].x, q[r][m].y, q[r][m].z, q[r][m].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 xx = xr[m][i];
-        acc += (float)(int8_t)(qw[i] & 0xff) * xx.x;
-        acc += (float)(int8_t)((qw[i] >> 8) & 0xff) * xx.y;
-        acc += (float)(int8_t)((qw[i] >> 16) & 0xff) * xx.z;
-        acc += (float)(int8_t)((qw[i] >> 24) & 0xff) * xx.w;
-      }
-    }
-    acc = wave_sum(acc);
     if (lane == 0 && e < a.E) {
-      if (TICKET) __hip_atomic_store(a.logits + t * a.E + e, acc * sc[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      else a.logits[t * a.E + e] = acc * sc[r];
+      if (TICKET) __hip_atomic_store(a.logits + t * a.E + e, lgt[r] * sc[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else a.logits[t * a.E + e] = lgt[r] * sc[r];
     }
   }
   if (!TICKET) return;
@@ -604,26 +665,27 @@ moe_status router_launch(const char* who, const void* x_dev, moe_dtype x_dtype, 
   a.gamma = gamma_dev;
   a.eps = eps;
   a.u_out = u_dev;
+  a.T = T;
   if (gamma_dev && !aligned(u_dev, 16)) return fail(MOE_ERR_INVALID_ARG, "%s: u not 16-byte aligned", who);
   const size_t lds = (size_t)d * sizeof(float);
   hipStream_t s = as_stream(stream);
   if (T >= kSplitRouterMinT) {
     // logits by (token, 16 experts), then the selection by token (the same results as the kernel below)
     const int nch = (d / 16 + 63) / 64;
-    const dim3 grid_l((E + kLogitExperts - 1) / kLogitExperts, T);
+    const int ne = (E + kLogitExperts - 1) / kLogitExperts;
     auto go = [&](auto nc) {
       constexpr int NCH = decltype(nc)::value;
       if (T <= kTicketRouterMaxT) {
         if (x_dtype == MOE_BF16)
-          hipLaunchKernelGGL((router_logits_kernel<uint16_t, NCH, true>), grid_l, dim3(256), lds, s, a);
+          hipLaunchKernelGGL((router_logits_kernel<uint16_t, NCH, true>), dim3(ne, T), dim3(256), lds, s, a);
         else
-          hipLaunchKernelGGL((router_logits_kernel<float, NCH, true>), grid_l, dim3(256), lds, s, a);
+          hipLaunchKernelGGL((router_logits_kernel<float, NCH, true>), dim3(ne, T), dim3(256), lds, s, a);
         return check_launch(who);
       }
       if (x_dtype == MOE_BF16)
-        hipLaunchKernelGGL((router_logits_kernel<uint16_t, NCH, false>), grid_l, dim3(256), lds, s, a);
+        hipLaunchKernelGGL((router_logits_kernel<uint16_t, NCH, false>), dim3(ne, T), dim3(256), lds, s, a);
       else
-        hipLaunchKernelGGL((router_logits_kernel<float, NCH, false>), grid_l, dim3(256), lds, s, a);
+        hipLaunchKernelGGL((router_logits_kernel<float, NCH, false>), dim3(ne, T), dim3(256), lds, s, a);
       const moe_status st = check_launch(who);
       if (st != MOE_OK) return st;
       hipLaunchKernelGGL(router_select_kernel, dim3(T), dim3(256), 0, s, a);
