@@ -210,3 +210,43 @@ def test_norm_router_paths_agree_bit_for_bit(T):
         torch.cuda.synchronize()
         assert torch.equal(u1[0], u[t]) and torch.equal(lg1[0], lg[t]), f"token {t}"
         assert torch.equal(ids1[0], ids[t]) and torch.equal(wts1[0], wts[t]), f"token {t}"
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("d,E,k,x_f32", [(512, 16, 2, False), (1536, 72, 8, True), (4096, 128, 8, False),
+                                         (5120, 256, 16, True), (8192, 40, 4, False)])
+def test_router_launch_paths_agree_across_row_lengths(d, E, k, x_f32):
+    """Every row-length instantiation of the several-token router (d <= 1024 NCH, the norm's register passes
+    sized from it) gives, for 3 tokens (one launch, ticket selection) and 37 tokens (logits, then selection),
+    each token's u, logits, ids and weights equal to the one-token launch's, bit for bit."""
+    g = torch.Generator().manual_seed(d + E)
+    w_dev = torch.randint(-127, 128, (E, d), dtype=torch.int8, generator=g).cuda()
+    s_dev = (torch.rand(E, generator=g) * 4e-3 + 1e-3).cuda()
+    gamma = (torch.rand(d, generator=g) + 0.5).cuda()
+    dt, xd = (torch.float32, q.MOE_F32) if x_f32 else (torch.bfloat16, q.MOE_BF16)
+    x = torch.randn(37, d, generator=g).to(dt).cuda()
+
+    def run(xs):
+        n = xs.shape[0]
+        ws_b = q.moe_router_workspace_bytes(n, E)
+        ws = torch.zeros(ws_b, dtype=torch.uint8, device="cuda")
+        u = torch.empty_like(xs)
+        ids = torch.empty((n, k), dtype=torch.int32, device="cuda")
+        wts = torch.empty((n, k), dtype=torch.float32, device="cuda")
+        lg = torch.empty((n, E), dtype=torch.float32, device="cuda")
+        q.moe_norm_router_topk(xs, xd, gamma, 1e-6, n, d, w_dev, s_dev, E, k, None, ids, wts, lg, u, ws, ws_b)
+        torch.cuda.synchronize()
+        return u, ids, wts, lg
+
+    one = [run(x[t:t + 1].contiguous()) for t in range(37)]
+    for T in (3, 37):
+        u, ids, wts, lg = run(x[:T].contiguous())
+        for t in range(T):
+            u1, ids1, wts1, lg1 = one[t]
+            assert torch.equal(u1[0], u[t]) and torch.equal(lg1[0], lg[t]), f"T={T} token {t}"
+            assert torch.equal(ids1[0], ids[t]) and torch.equal(wts1[0], wts[t]), f"T={T} token {t}"
+    # and the one-token logits are the int8 dot products of the call's own u (fp64, rounding-level bound)
+    u1, _, _, lg1 = one[0]
+    ref = (w_dev.double().cpu() @ u1[0].double().cpu()) * s_dev.double().cpu()
+    bound = 1e-5 * (w_dev.double().abs().cpu() @ u1[0].double().abs().cpu()) * s_dev.double().cpu() + 1e-30
+    assert torch.all((lg1[0].double().cpu() - ref).abs() <= bound)
