@@ -47,36 +47,6 @@ __device__ __forceinline__ void load8(const float* p, float v[8]) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-// 8 consecutive activations as loaded (16 or 32 bytes), converted to fp32 where they are used: a load issued
-// a token ahead is not waited for before the conversion
-template <typename XT>
-struct Raw8;
-template <>
-struct Raw8<uint16_t> {
-  uint4 r;
-  __device__ __forceinline__ void load(const uint16_t* p) { r = *reinterpret_cast<const uint4*>(p); }
-  __device__ __forceinline__ void to_f32(float v[8]) const {
-    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(w[i] << 16);
-      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
-  }
-};
-template <>
-struct Raw8<float> {
-  float4 a, b;
-  __device__ __forceinline__ void load(const float* p) {
-    a = reinterpret_cast<const float4*>(p)[0];
-    b = reinterpret_cast<const float4*>(p)[1];
-  }
-  __device__ __forceinline__ void to_f32(float v[8]) const {
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-};
-
 __device__ __forceinline__ void store_act(void* out, bool bf16, int64_t i, float v) {
   if (bf16)
     reinterpret_cast<uint16_t*>(out)[i] = (uint16_t)f32_to_bf16_bits(v);
@@ -89,11 +59,7 @@ __device__ __forceinline__ void store_act(void* out, bool bf16, int64_t i, float
 // u[j] = round_x((x[j] * gamma[j]) * rinv), rinv = 1 / sqrt(sum_j x[j]^2 / d + eps).  The sum runs in the
 // order of the single-launch layer's norm (per thread an fma chain over its pieces in index order, the
 // wavefront sum, then the four wavefronts' sums in order), so both compute the same u.  Ends with a barrier.
-// Barrier for LDS only: the block's LDS writes are complete and visible; loads and stores to memory stay in
-// flight (__syncthreads also waits for those)
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-template <typename XT, int P, bool LDSB = false>
+template <typename XT, int P>
 __device__ __forceinline__ void router_norm(const float (&v)[P][8], const float (&g)[P][8], int d, float eps, float* xs,
                                             void* u_out, int64_t u_off, float* wsum) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -108,8 +74,7 @@ __device__ __forceinline__ void router_norm(const float (&v)[P][8], const float 
   }
   ss = wave_sum(ss);
   if (lane == 0) wsum[wave] = ss;
-  if (LDSB) lds_barrier();
-  else __syncthreads();
+  __syncthreads();
   float tot = wsum[0];
 #pragma unroll
   for (int w = 1; w < 4; ++w) tot += wsum[w];
@@ -127,8 +92,7 @@ __device__ __forceinline__ void router_norm(const float (&v)[P][8], const float 
       }
     }
   }
-  if (LDSB) lds_barrier();
-  else __syncthreads();
+  __syncthreads();
 }
 
 // The k best of lgs[0..E) (larger first, equal values -> lower id) into sel_i / sel_v in rank order, by the
@@ -242,7 +206,6 @@ struct RouterArgs {
   const float* gamma;    // RMSNorm gain [d], or NULL: the router reads x as is
   float eps;
   void* u_out;           // [T][d] normalized activation (x dtype), written by block 0; NULL = not wanted
-  int T;
 };
 
 __device__ __forceinline__ bool better(float v, int i, float v2, int i2) { return v > v2 || (v == v2 && i < i2); }
@@ -665,7 +628,6 @@ moe_status router_launch(const char* who, const void* x_dev, moe_dtype x_dtype, 
   a.gamma = gamma_dev;
   a.eps = eps;
   a.u_out = u_dev;
-  a.T = T;
   if (gamma_dev && !aligned(u_dev, 16)) return fail(MOE_ERR_INVALID_ARG, "%s: u not 16-byte aligned", who);
   const size_t lds = (size_t)d * sizeof(float);
   hipStream_t s = as_stream(stream);
