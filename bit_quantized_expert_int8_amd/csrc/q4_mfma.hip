@@ -425,6 +425,7 @@ struct Ring {
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+constexpr int kNt = 2;   // cache-policy operand of a buffer load: nontemporal
 
 // s_waitcnt vmcnt(N) (the other counters not waited for), as a builtin so that the compiler counts it.
 template <int N>
@@ -438,10 +439,10 @@ __device__ __forceinline__ void wait_vm() {
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Reads of a slot in inline assembly (the compiler does not see them as LDS reads, so it places no wait of
-// its own for the slot's loads): pairs of 32-bit words at byte offsets i * 512 and words at i * 4 * W from
+// its own for the slot's loads): pairs of 32-bit words at byte offsets i * GS and words at i * 4 * W from
 // two base addresses, after an explicit vmcnt(N); each block ends with its reads complete.
-#define MOE_RD64(i) "ds_read_b64 %" #i ", %[pa] offset:" #i "*512\n\t"
-template <int N, int NG, int W>
+#define MOE_RD64(i) "ds_read_b64 %" #i ", %[pa] offset:" #i "*%[gs]\n\t"
+template <int N, int NG, int W, int GS>
 __device__ __forceinline__ void read_slot(const char* pa, const uint32_t* pb, const uint32_t* pc, u32x2 (&q)[NG],
                                           uint32_t (&sw)[NG], uint32_t (&bw)[(NG + 3) / 4]) {
   static_assert(NG == 4 || NG == 8 || NG == 11, "slot shapes");
@@ -449,21 +450,21 @@ __device__ __forceinline__ void read_slot(const char* pa, const uint32_t* pb, co
   if constexpr (NG == 4) {
     asm volatile("s_waitcnt vmcnt(%[n])\n\t" MOE_RD64(0) MOE_RD64(1) MOE_RD64(2) MOE_RD64(3) "s_waitcnt lgkmcnt(0)"
                  : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3])
-                 : [pa] "v"(ua), [n] "n"(N)
+                 : [pa] "v"(ua), [n] "n"(N), [gs] "n"(GS)
                  : "memory");
   } else if constexpr (NG == 8) {
     asm volatile("s_waitcnt vmcnt(%[n])\n\t" MOE_RD64(0) MOE_RD64(1) MOE_RD64(2) MOE_RD64(3) MOE_RD64(4) MOE_RD64(5)
                      MOE_RD64(6) MOE_RD64(7) "s_waitcnt lgkmcnt(0)"
                  : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3]), "=&v"(q[4]), "=&v"(q[5]), "=&v"(q[6]),
                    "=&v"(q[7])
-                 : [pa] "v"(ua), [n] "n"(N)
+                 : [pa] "v"(ua), [n] "n"(N), [gs] "n"(GS)
                  : "memory");
   } else {
     asm volatile("s_waitcnt vmcnt(%[n])\n\t" MOE_RD64(0) MOE_RD64(1) MOE_RD64(2) MOE_RD64(3) MOE_RD64(4) MOE_RD64(5)
                      MOE_RD64(6) MOE_RD64(7) MOE_RD64(8) MOE_RD64(9) MOE_RD64(10) "s_waitcnt lgkmcnt(0)"
                  : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3]), "=&v"(q[4]), "=&v"(q[5]), "=&v"(q[6]),
                    "=&v"(q[7]), "=&v"(q[8]), "=&v"(q[9]), "=&v"(q[10])
-                 : [pa] "v"(ua), [n] "n"(N)
+                 : [pa] "v"(ua), [n] "n"(N), [gs] "n"(GS)
                  : "memory");
   }
   // scale words (group i at i * 4 W) and bias words (group 4 j + kb at pc + 16 j W); the slot's loads are
@@ -500,18 +501,36 @@ __device__ __forceinline__ void read_slot(const char* pa, const uint32_t* pb, co
 }
 #undef MOE_RD64
 
+// The LDS of a block of the ring kernel: each wave's two slots of code and scale/bias words, the partial
+// tiles by step parity ([wave][16 tokens][16 rows]), and the chunk's token scales and rows.
 template <int NG, bool SB_BF16>
+struct RingLds {
+  using R = Ring<NG, SB_BF16>;
+  __align__(16) char code0[kWavesG * R::kCode];
+  __align__(16) char code1[kWavesG * R::kCode];
+  __align__(16) uint32_t sbl0[kWavesG * R::kSb];
+  __align__(16) uint32_t sbl1[kWavesG * R::kSb];
+  float red0[kWavesG * 256], red1[kWavesG * 256];
+  float ef_l[16];
+  int srow_l[16], orow_l[16];
+};
+
+// CONTIG: the item's tiles are contiguous runs of whole rows (below); the two forms are separate
+// instantiations, each with the registers of one.
+template <int NG, bool SB_BF16, bool CONTIG>
 __device__ __forceinline__ void ring_item(const MfmaArgs& a, bool shared, int e, bool valid, int start, int count,
-                                          int s0, int s1) {
+                                          int s0, int s1, RingLds<NG, SB_BF16>& lds) {
   using R = Ring<NG, SB_BF16>;
   constexpr int W = R::kSbWords;
-  __shared__ __align__(16) char code0[kWavesG * R::kCode];
-  __shared__ __align__(16) char code1[kWavesG * R::kCode];
-  __shared__ __align__(16) uint32_t sbl0[kWavesG * R::kSb];
-  __shared__ __align__(16) uint32_t sbl1[kWavesG * R::kSb];
-  __shared__ float red0[kWavesG * 256], red1[kWavesG * 256];   // [wave][16 tokens][16 rows], by step parity
-  __shared__ float ef_l[16];
-  __shared__ int srow_l[16], orow_l[16];
+  char* const code0 = lds.code0;
+  char* const code1 = lds.code1;
+  uint32_t* const sbl0 = lds.sbl0;
+  uint32_t* const sbl1 = lds.sbl1;
+  float* const red0 = lds.red0;
+  float* const red1 = lds.red1;
+  float* const ef_l = lds.ef_l;
+  int* const srow_l = lds.srow_l;
+  int* const orow_l = lds.orow_l;
 
   const Pool P = shared ? a.shared : a.routed;
   const StagedRows xs = shared ? a.xs_shared : a.xs_routed;
@@ -539,7 +558,17 @@ __device__ __forceinline__ void ring_item(const MfmaArgs& a, bool shared, int e,
   // at + 16 r: an operand read of one group is 512 contiguous bytes).  Scale/bias load j, lane l: word
   // 64 j + l of the wave's [16 rows][NG groups][W] words.  Lanes past the wave's groups read other bytes of
   // the matrix, or zeros past its end, into the slot's padding or into groups that carry weight 0.
-  const uint32_t code_lane = (uint32_t)(row0(n) * (K / 2) + (lane >> 5) * 32 + ((lane >> 4) & 1) * 16 + g0 * 32);
+  //
+  // A wave that multiplies whole rows of the plain 16-row layout (down, wk == 1) owns a tile that is one
+  // contiguous run of 16 K / 2 bytes, starting on a 128-byte line (K is a multiple of 64 and records are
+  // 256-byte aligned).  It is loaded as is, 1 KiB per load, so that every load covers whole lines and can be
+  // marked nontemporal (a streaming probe moved 7.0 TB/s so against 6.2 with the default policy; half-line
+  // pieces do not gain); the slot then holds the tile row-major (row r at r K / 2, group i at + 32 i), and
+  // the last load's lanes past the tile's end read nothing.
+  constexpr bool contig = CONTIG;
+  const uint32_t tile_bytes = 16u * (uint32_t)(K / 2);
+  const uint32_t code_lane = contig ? 16u * (uint32_t)lane
+                                    : (uint32_t)(row0(n) * (K / 2) + (lane >> 5) * 32 + ((lane >> 4) & 1) * 16 + g0 * 32);
   uint32_t sb_lane[R::kSbLoads];
 #pragma unroll
   for (int j = 0; j < R::kSbLoads; ++j) {
@@ -556,9 +585,19 @@ __device__ __forceinline__ void ring_item(const MfmaArgs& a, bool shared, int e,
     const int t = min(s * tps + wt, n_tiles - 1);
     const uint32_t cbase = s < s1 ? (uint32_t)(t * rpt) * (uint32_t)(K / 2) : 0x80000000u;
     const uint32_t sbase = s < s1 ? (uint32_t)(t * rpt) * (uint32_t)sb_row : 0x80000000u;
+    if constexpr (contig) {
+      constexpr int L = R::kCodeLoads;
+      const uint32_t vo = cbase + code_lane;
+      const uint32_t vl = code_lane + 1024u * (L - 1) < tile_bytes ? vo + 1024u * (L - 1) : 0x80000000u;
 #pragma unroll
-    for (int j = 0; j < R::kCodeLoads; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_ptr_t)(cb + 1024 * j), 16, cbase + code_lane + 64 * j, 0, 0, 0);
+      for (int j = 0; j < L - 1; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_ptr_t)(cb + 1024 * j), 16, vo, 1024 * j, 0, kNt);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_ptr_t)(cb + 1024 * (L - 1)), 16, vl, 0, 0, kNt);
+    } else {
+#pragma unroll
+      for (int j = 0; j < R::kCodeLoads; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_ptr_t)(cb + 1024 * j), 16, cbase + code_lane + 64 * j, 0, 0, 0);
+    }
 #pragma unroll
     for (int j = 0; j < R::kSbLoads; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_t)(sbb + 64 * j), 4, sbase + sb_lane[j], 0, 0, 0);
@@ -635,7 +674,11 @@ __device__ __forceinline__ void ring_item(const MfmaArgs& a, bool shared, int e,
       u32x2 qw[NG];
       uint32_t sw[NG], bw[R::kBias];
       const uint32_t* sp = sbb + n * NG * W;
-      read_slot<R::kLoads, NG, W>(cb + (kb >> 1) * 256 + n * 16 + (kb & 1) * 8, sp, sp + kb * W + (W - 1), qw, sw, bw);
+      if constexpr (contig)
+        read_slot<R::kLoads, NG, W, 32>(cb + n * (K / 2) + kb * 8, sp, sp + kb * W + (W - 1), qw, sw, bw);
+      else
+        read_slot<R::kLoads, NG, W, 512>(cb + (kb >> 1) * 256 + n * 16 + (kb & 1) * 8, sp, sp + kb * W + (W - 1), qw, sw,
+                                         bw);
       // the previous step's outputs, then step s + 2's loads into the slot just read
       if (s > s0) flush(SL ? red0 : red1, s - 1);
       __builtin_amdgcn_sched_barrier(0);
@@ -829,8 +872,14 @@ __device__ __forceinline__ bool next_item(const MfmaArgs& a, int it, WorkItem& x
 template <int NG, bool SB_BF16>
 __global__ __launch_bounds__(kThreadsG, 2) void grouped_ring_kernel(MfmaArgs a) {
   WorkItem x;
-  for (int it = 0; next_item(a, it, x); ++it)
-    if (x.s0 < x.s1) ring_item<NG, SB_BF16>(a, x.shared, x.e, x.valid, x.start, x.count, x.s0, x.s1);
+  __shared__ RingLds<NG, SB_BF16> lds;
+  for (int it = 0; next_item(a, it, x); ++it) {
+    if (x.s0 >= x.s1) continue;
+    if (!a.gate_up && (x.shared ? a.wk_shared : a.wk_routed) == 1)
+      ring_item<NG, SB_BF16, true>(a, x.shared, x.e, x.valid, x.start, x.count, x.s0, x.s1, lds);
+    else
+      ring_item<NG, SB_BF16, false>(a, x.shared, x.e, x.valid, x.start, x.count, x.s0, x.s1, lds);
+  }
 }
 
 }  // namespace
