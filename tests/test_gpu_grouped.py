@@ -260,3 +260,37 @@ def test_grouped_gemv_silu_ragged_batch_vs_oracle():
             err = max(err, H.max_rel_err(yr[t, i], moe.expert_ffn(orc.decoded(int(ids_np[t, i])), u, moe.ACT_SILU)))
     print(f"tiny grouped expert gemv, SiLU, 7 tokens: max rel err {err:.3e}")
     assert err <= TOL
+
+
+@pytest.mark.parametrize("cfg_name,T", [("tiny", 24), ("batched", 32), ("batched", 128)])
+def test_split_calls_equal_whole_call(cfg_name, T):
+    """q4_expert_gate_up followed by q4_expert_down on the same workspace (the hidden vectors left there as
+    fp32) equals q4_expert_gemv bit for bit with several tokens.  The batch holds a zero token (every hidden
+    value 0), a token scaled by 2^-40 (hidden vectors near 2^-80, staged with exponents near -93) and, on
+    the tiny pool, an id outside the pool (NaN rows on both)."""
+    cfg = synth.TINY if cfg_name == "tiny" else synth.BATCHED
+    dev = H.device_layer(cfg, 0)
+    shape = H.shape_of(cfg)
+    rp, sp = _tiny_pools(cfg, dev, shape)
+    k, E = cfg.k, cfg.n_experts
+    ids_np = synth.zipf_trace(T, T, 1, k, E, 1.1)[:, 0, :].astype(np.int32)
+    if cfg_name == "tiny":
+        ids_np[5, 0] = E + 2
+    ids = torch.from_numpy(ids_np).cuda()
+    x = H.token_batch(cfg, range(500, 500 + T)).clone()
+    x[2] = 0
+    x[7] = x[7] * 2.0 ** -40
+    xdt = q.MOE_BF16 if cfg.x_bf16 else q.MOE_F32
+    yr, ys = _gemv(rp, sp, ids, k, x, xdt, T, shape.act, cfg.d)
+    wb = q.q4_expert_gemv_workspace_bytes(rp, k, sp, T)
+    ws = torch.empty(wb, dtype=torch.uint8, device="cuda")
+    yr2 = torch.full_like(yr, 7.0)
+    ys2 = torch.full_like(ys, 7.0)
+    q.q4_expert_gate_up(rp, ids, k, sp, x, xdt, T, shape.act, ws, wb)
+    q.q4_expert_down(rp, ids, k, sp, T, yr2, ys2, ws, wb)
+    torch.cuda.synchronize()
+    bad = torch.from_numpy(ids_np >= E).cuda()
+    assert torch.isnan(yr[bad]).all() and torch.isnan(yr2[bad]).all()
+    assert torch.equal(yr[~bad], yr2[~bad]) and torch.equal(ys, ys2)
+    assert torch.isfinite(yr[~bad]).all() and torch.isfinite(ys).all()
+    assert torch.all(ys[2] == 0) and torch.all(yr[2][~bad[2]] == 0)
