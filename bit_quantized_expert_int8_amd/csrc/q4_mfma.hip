@@ -835,7 +835,20 @@ __device__ __forceinline__ bool next_item(const MfmaArgs& a, int it, WorkItem& x
       return true;
     }
     if (it > 0) return false;
-    const int c = b % tc, r = b / tc;
+    // the tc chunks of a step range on one XCD (block b runs on XCD b % 8): ranges in octets, octet o's
+    // blocks [8 tc o, 8 tc (o + 1)), chunk c of range 8 o + x at 8 tc o + 8 c + x; ranges past the last
+    // full octet as before
+    const int full = (rs / 8) * 8;
+    int c, r;
+    if (b < full * tc) {
+      const int o = b / (8 * tc), w = b % (8 * tc);
+      c = w / 8;
+      r = 8 * o + w % 8;
+    } else {
+      const int b2 = b - full * tc;
+      c = b2 % tc;
+      r = full + b2 / tc;
+    }
     x = WorkItem{true, true, 0, 16 * c, min(16, a.T - 16 * c), (int)((int64_t)r * ss / rs),
                  (int)((int64_t)(r + 1) * ss / rs)};
     return true;

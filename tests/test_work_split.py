@@ -1,0 +1,139 @@
+"""CPU model of how the persistent blocks of the grouped matrix-core kernel (q4_mfma.hip, next_item) split a
+launch's work: the shared matrix's (token chunk, step) pairs and the routed chunks' steps.  The function
+below restates the kernel's integer arithmetic; the tests check that every piece of work is done exactly
+once for grids of 2 to 1024 blocks and 0 to 700 routed chunks, that a block never holds more than one
+item unless there are more chunks (or token chunks) than blocks, and that the token chunks of one shared
+step range run on one XCD (block b runs on XCD b mod 8) wherever the ranges fill octets."""
+import itertools
+
+import pytest
+
+
+def next_item(b, nb, it, T, steps_shared, steps_routed, ng):
+    """(shared, chunk or token chunk, s0, s1) of item `it` of block b, or None; the kernel's arithmetic."""
+    ng = ng if steps_routed > 0 else 0
+    ss, tc = steps_shared, (T + 15) // 16
+    nsb, rs = 0, 1
+    if ss > 0:
+        if ng <= 0:
+            nsb = nb
+        else:
+            us, ur = ss * tc, steps_routed * ng
+            nsb = (nb * us + (us + ur) // 2) // (us + ur)
+            nsb = max(1, min(nsb, nb - 1))
+        rs = max(1, nsb // tc)
+        nsb = nsb if nsb < tc else rs * tc
+    if b < nsb:
+        if nsb < tc:
+            c = b + it * nsb
+            return None if c >= tc else (True, c, 0, ss)
+        if it > 0:
+            return None
+        full = (rs // 8) * 8
+        if b < full * tc:
+            o, w = divmod(b, 8 * tc)
+            c, r = w // 8, 8 * o + w % 8
+        else:
+            b2 = b - full * tc
+            c, r = b2 % tc, full + b2 // tc
+        return True, c, r * ss // rs, (r + 1) * ss // rs
+    if ng <= 0:
+        return None
+    o, R, steps = b - nsb, nb - nsb, steps_routed
+    s0, s1 = 0, steps
+    if ng <= R:
+        if it > 0:
+            return None
+        q, rem = divmod(R, ng)
+        if o < rem * (q + 1):
+            j, part, parts = o // (q + 1), o % (q + 1), q + 1
+        else:
+            o2 = o - rem * (q + 1)
+            j, part, parts = rem + o2 // q, o2 % q, q
+        s0, s1 = part * steps // parts, (part + 1) * steps // parts
+    else:
+        j = o + it * R
+        if j >= ng:
+            return None
+    return False, j, s0, s1
+
+
+def items_of(nb, T, ss, sr, ng):
+    out = {}
+    for b in range(nb):
+        lst = []
+        for it in itertools.count():
+            x = next_item(b, nb, it, T, ss, sr, ng)
+            if x is None:
+                break
+            lst.append(x)
+        out[b] = lst
+    return out
+
+
+def check(nb, T, ss, sr, ng):
+    tc = (T + 15) // 16
+    items = items_of(nb, T, ss, sr, ng)
+    shared, routed = {}, {}
+    for b, lst in items.items():
+        for sh, j, s0, s1 in lst:
+            assert 0 <= s0 <= s1
+            for s in range(s0, s1):
+                key = (j, s)
+                d = shared if sh else routed
+                assert key not in d, f"nb={nb} T={T}: {('shared', 'routed')[not sh]} {key} twice"
+                d[key] = b
+    if ss > 0:
+        assert set(shared) == {(c, s) for c in range(tc) for s in range(ss)}
+    else:
+        assert not shared
+    if sr > 0 and ng > 0:
+        assert set(routed) == {(j, s) for j in range(ng) for s in range(sr)}
+    else:
+        assert not routed
+    return items, shared
+
+
+CASES = [(nb, T, ss, sr, ng)
+         for nb in (2, 3, 8, 64, 255, 512, 1024)
+         for T in (2, 16, 17, 32, 128, 300)
+         for ss, sr in ((0, 88), (352, 0), (352, 88), (176, 44), (1, 1), (704, 22))
+         for ng in (0, 1, 5, 107, 135, 700)]
+
+
+@pytest.mark.parametrize("nb,T,ss,sr,ng", CASES)
+def test_every_step_once(nb, T, ss, sr, ng):
+    if ss == 0 and (sr == 0 or ng == 0):
+        return
+    check(nb, T, ss, sr, ng)
+
+
+@pytest.mark.parametrize("T,ng", [(32, 107), (128, 135), (64, 120), (256, 128)])
+def test_token_chunks_of_a_range_share_an_xcd(T, ng):
+    """The bench's launches (512 blocks; gate/up: 352 shared steps and 88 per routed chunk; down: 176 and
+    44): in every octet of full step ranges, the tc token chunks of a range are on blocks with the same
+    index mod 8, so that the L2 of one XCD serves the matrix's rows to all of them."""
+    for ss, sr in ((352, 88), (176, 44)):
+        nb, tc = 512, (T + 15) // 16
+        items, shared = check(nb, T, ss, sr, ng)
+        by_range = {}
+        for b, lst in items.items():
+            for sh, c, s0, s1 in lst:
+                if sh:
+                    by_range.setdefault((s0, s1), set()).add(b % 8)
+        nsb = sum(1 for lst in items.values() if lst and lst[0][0])
+        rs = nsb // tc
+        full = (rs // 8) * 8
+        assert full >= 1 or rs < 8
+        ranges = sorted(by_range)
+        for r in range(full):
+            assert len(by_range[ranges[r]]) == 1, f"T={T}: range {ranges[r]} on XCDs {by_range[ranges[r]]}"
+
+
+def test_one_item_per_block_when_blocks_suffice():
+    """With at least as many routed blocks as chunks (the bench's launches), every block holds one item, so
+    no block pays a second chunk's setup."""
+    for T, ss, sr, ng in ((32, 352, 88, 107), (128, 352, 88, 135), (32, 176, 44, 107), (128, 176, 44, 135)):
+        items = items_of(512, T, ss, sr, ng)
+        assert max(len(v) for v in items.values()) == 1
+        assert sum(len(v) for v in items.values()) == 512
