@@ -361,6 +361,8 @@ struct GemvArgs {
   int32_t* n_chunks;       // [1] the groups' runs of at most 16 pairs (written by the grouping kernel)
   int4* chunks;            // [chunks_max] (expert or n_records, first index into perm, count <= 16, 0)
   char* stage;             // activations staged for the matrix cores (StagedRows), T > 1
+  int4* plan_gu;           // [kPlanMaxBlocks] work descriptors of the grouped gate/up and down launches, T > 1
+  int4* plan_dn;
 };
 
 // The combine of one 16-row tile of token t, summed in the order i = 0..k-1, shared, residual (the
@@ -441,6 +443,9 @@ struct MfmaArgs {
   float* out_routed;            // gate_up: h [pairs][F]; down: y [pairs][d]
   float* out_shared;            // gate_up: h [T][S];     down: y [T][d]
   int32_t out_len_routed, out_len_shared;
+  // one work descriptor per block of the launch, written by the grouping launch (see q4_grouping.h), or NULL
+  // (the blocks split the work themselves)
+  const int4* plan;
   // set by launch_grouped_mfma
   int32_t steps_routed, steps_shared;   // steps of a matrix (0: no such matrix)
 };

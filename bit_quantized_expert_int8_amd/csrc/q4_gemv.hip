@@ -1,6 +1,10 @@
 // q4_expert_gemv and its halves: the single-token (decode) kernels and the C entry points.  The
 // arithmetic, the work mapping and the dequantization are described in q4_device.h; batches of more
 // than one token go through the grouped kernels of q4_grouped.hip.
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "q4_grouping.h"
 
 namespace moeq4 {
@@ -132,10 +136,11 @@ int groups_max(int n_records, int T, int k) {
 
 // Bytes of the grouping tables of a grouped call: group count, groups, pair permutation.
 int chunks_max(int n_records, int T, int k) { return groups_max(n_records, T, k) + T * k / kChunkPairs; }
-// the group count and chunk count (one 256-byte slot), groups, chunks, perm
+// the group count and chunk count (one 256-byte slot), groups, chunks, perm, then the work descriptors of the
+// grouped gate/up and down launches
 size_t group_table_bytes(int n_records, int T, int k) {
   return 256 + align256((size_t)groups_max(n_records, T, k) * 16) + align256((size_t)chunks_max(n_records, T, k) * 16) +
-         align256((size_t)T * k * 4);
+         align256((size_t)T * k * 4) + 2 * (size_t)kPlanMaxBlocks * 16;
 }
 
 }  // namespace
@@ -238,10 +243,59 @@ moe_status prepare(const char* who, const moe_q4_pool* routed, const int32_t* id
     a->groups = reinterpret_cast<int4*>(g + 256);
     a->chunks = reinterpret_cast<int4*>(g + 256 + gb);
     a->perm = reinterpret_cast<int32_t*>(g + 256 + gb + cb);
+    char* pl = g + 256 + gb + cb + align256((size_t)T * k * 4);
+    a->plan_gu = reinterpret_cast<int4*>(pl);
+    a->plan_dn = reinterpret_cast<int4*>(pl + (size_t)kPlanMaxBlocks * 16);
     g += group_table_bytes(routed->n_records, T, k);
   }
   a->stage = T > 1 ? g : nullptr;
   return MOE_OK;
+}
+
+// The grouped products' arguments that fix their launch shapes (T > 1).
+MfmaArgs gate_up_mfma(const GemvArgs& a, int T) {
+  MfmaArgs m{};
+  m.routed = a.routed;
+  m.shared = a.shared;
+  m.K_routed = m.K_shared = a.d;
+  m.wk_routed = m.wk_shared = mfma_waves_per_tile(a.d);
+  m.gate_up = 1;
+  m.act = a.act;
+  m.T = T;
+  m.k = a.k;
+  m.tiles_shared = a.shared.base ? a.shared.F / 8 : 0;   // 8 features a tile
+  m.tiles_routed = a.routed.F / 8;
+  return m;
+}
+MfmaArgs down_mfma(const GemvArgs& a, int T) {
+  MfmaArgs m{};
+  m.routed = a.routed;
+  m.shared = a.shared;
+  m.K_routed = a.routed.F;
+  m.K_shared = a.shared.F;
+  m.wk_routed = a.k > 0 ? mfma_waves_per_tile(a.routed.F) : 1;
+  m.wk_shared = a.shared.base ? mfma_waves_per_tile(a.shared.F) : 1;
+  m.T = T;
+  m.k = a.k;
+  m.tiles_shared = m.tiles_routed = a.d / 16;   // 16 rows a tile
+  return m;
+}
+// Whether a grouped launch runs from descriptors the grouping launch writes: the ring kernel, and no block
+// with more than one item for any chunk count the call can produce.  Both the gate/up call (which asks the
+// grouping for them) and the down call (which reads them) decide the same way.
+bool use_plan(const MfmaArgs& m, bool has_shared, bool has_routed, bool sb_bf16, int n_records, int T, int k,
+              SplitShape* sh) {
+  if (!has_routed || !mfma_plan_shape(m, has_shared, has_routed, sb_bf16, sh)) return false;
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, int, int, int>, bool> cache;
+  const int cmax = chunks_max(n_records, T, k);
+  const auto key = std::make_tuple(sh->nb, sh->T, sh->ss, sh->sr, cmax);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  const bool ok = split_single_item(*sh, cmax);
+  cache.emplace(key, ok);
+  return ok;
 }
 
 // gate_up: 8 features per block; its waves split the iterations of rows of K = d
@@ -260,22 +314,18 @@ moe_status run_gate_up(GemvArgs a, const RecordOffsets& orr, const RecordOffsets
     // grouped on the matrix cores: sort the pairs by expert and stage the T tokens (one launch), then the
     // products, every selected expert's and the shared expert's rows streamed once per chunk of tokens
     const StagedRows xs = staged_rows_at(a.stage, T, a.d);
+    MfmaArgs m = gate_up_mfma(a, T);
+    // the work descriptors of this launch and of the down launch that follows, written by the grouping
+    SplitShape shg{}, shd{};
+    const bool pg = use_plan(m, a.nb_shared > 0, a.k > 0, sb_bf16, a.routed.n_records, T, a.k, &shg);
+    const bool pd = use_plan(down_mfma(a, T), a.shared.base != nullptr, a.k > 0, sb_bf16, a.routed.n_records, T, a.k, &shd);
     const moe_status st =
         a.k > 0 ? launch_group_and_stage(a.ids, T * a.k, a.routed.n_records, a.n_groups, a.groups, a.perm, a.n_chunks,
-                                         a.chunks, a.in, x_dtype == MOE_BF16, T, a.d, xs, s)
+                                         a.chunks, a.in, x_dtype == MOE_BF16, T, a.d, xs, s, pg ? a.plan_gu : nullptr,
+                                         &shg, pd ? a.plan_dn : nullptr, &shd)
                 : launch_stage_rows(a.in, x_dtype == MOE_BF16, T, a.d, xs, s);
     if (st != MOE_OK) return st;
-    MfmaArgs m{};
-    m.routed = a.routed;
-    m.shared = a.shared;
-    m.K_routed = m.K_shared = a.d;
-    m.wk_routed = m.wk_shared = mfma_waves_per_tile(a.d);
-    m.gate_up = 1;
-    m.act = a.act;
-    m.T = T;
-    m.k = a.k;
-    m.tiles_shared = a.nb_shared;   // 8 features a tile
-    m.tiles_routed = a.nb_routed;
+    if (pg) m.plan = a.plan_gu;
     m.n_chunks = a.n_chunks;
     m.chunks = a.chunks;
     m.perm = a.perm;
@@ -323,16 +373,9 @@ moe_status run_down(GemvArgs a, const RecordOffsets& orr, const RecordOffsets& o
     const moe_status st =
         launch_stage_rows2(a.h_routed, has_routed ? P : 0, Fr, xr, a.h_shared, has_shared ? T : 0, Fs, xsh, s);
     if (st != MOE_OK) return st;
-    MfmaArgs m{};
-    m.routed = a.routed;
-    m.shared = a.shared;
-    m.K_routed = Fr;
-    m.K_shared = Fs;
-    m.wk_routed = has_routed ? mfma_waves_per_tile(Fr) : 1;
-    m.wk_shared = has_shared ? mfma_waves_per_tile(Fs) : 1;
-    m.T = T;
-    m.k = a.k;
-    m.tiles_shared = m.tiles_routed = a.d / 16;   // 16 rows a tile
+    MfmaArgs m = down_mfma(a, T);
+    SplitShape shd{};
+    if (use_plan(m, has_shared, has_routed, sb_bf16, a.routed.n_records, T, a.k, &shd)) m.plan = a.plan_dn;
     m.n_chunks = a.n_chunks;
     m.chunks = a.chunks;
     m.perm = a.perm;

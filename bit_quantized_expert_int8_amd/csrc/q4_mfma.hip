@@ -129,18 +129,32 @@ __global__ __launch_bounds__(kThreadsM) void stage_rows_kernel(StageJob<XT> j0, 
 
 // The grouping of the pairs (block 0) and the staging of the tokens (blocks 1 .. rows) in one launch: the
 // two are independent and each alone is a launch of a few microseconds.
+constexpr int kPlanBlocks = 8;   // blocks of the grouping launch that write the products' descriptors (half each)
 struct GroupJob {
   const int32_t* ids;
   int P, n_valid;
   int32_t *n_groups, *perm, *n_chunks;
   int4 *groups, *chunks;
+  int4 *plan0, *plan1;    // work descriptors of the two product launches that follow, or NULL
+  SplitShape shape0, shape1;
 };
 
 template <typename XT>
 __global__ __launch_bounds__(kThreadsM) void group_and_stage_kernel(GroupJob g, StageJob<XT> j) {
   static_assert(kThreadsM == kGroupThreads, "one block shape for both");
-  if (blockIdx.x == 0) group_pairs_block(g.ids, g.P, g.n_valid, g.n_groups, g.groups, g.perm, g.n_chunks, g.chunks);
-  else stage_row<XT>(j, (int)blockIdx.x - 1);
+  // blocks: 0 groups, 1 .. rows stage, the last kPlanBlocks (with descriptors) write the descriptors
+  const int rows = (int)gridDim.x - 1 - ((g.plan0 || g.plan1) ? kPlanBlocks : 0);
+  if (blockIdx.x == 0) {
+    group_pairs_block(g.ids, g.P, g.n_valid, g.n_groups, g.groups, g.perm, g.n_chunks, g.chunks);
+  } else if ((int)blockIdx.x <= rows) {
+    stage_row<XT>(j, (int)blockIdx.x - 1);
+  } else {
+    // the first half of these blocks write the first launch's descriptors, the second half the second's
+    const int q = (int)blockIdx.x - 1 - rows, half = kPlanBlocks / 2, i = q / half;
+    PlanOut po{{nullptr, nullptr}, {g.shape0, g.shape1}};
+    po.plan[i] = i == 0 ? g.plan0 : g.plan1;
+    plan_share(po, g.ids, g.P, g.n_valid, q % half, half);
+  }
 }
 
 constexpr int kWavesG = 4;                 // wavefronts of a grouped-product block
@@ -801,97 +815,46 @@ __global__ __launch_bounds__(kThreadsG) void grouped_mfma_kernel(MfmaArgs a) {
   });
 }
 
-// Item `it` of this block (false: no more).  The shared matrix gets blocks in proportion to its steps
-// times its token chunks, at least one per chunk, and each of them takes one token chunk and one step range
-// (so that no block runs the setup of several chunks in a row); the routed chunks share the other blocks,
-// each chunk split into as equal step ranges as the blocks allow, or, with more chunks than blocks, block
-// b takes chunks b, b + R, ... whole.
+// Item `it` of this block (false: no more): the split of q4_grouping.h on the chunk count the grouping wrote.
 struct WorkItem {
   bool shared, valid;
   int e, start, count, s0, s1;
 };
 __device__ __forceinline__ bool next_item(const MfmaArgs& a, int it, WorkItem& x) {
-  const int b = blockIdx.x, nb = gridDim.x;
   const int ng = a.steps_routed > 0 ? *a.n_chunks : 0;
-  const int ss = a.steps_shared, tc = (a.T + 15) / 16;
-  int nsb = 0, rs = 1;
-  if (ss > 0) {
-    if (ng <= 0) {
-      nsb = nb;
-    } else {
-      const int64_t us = (int64_t)ss * tc, ur = (int64_t)a.steps_routed * ng;
-      nsb = (int)((nb * us + (us + ur) / 2) / (us + ur));
-      nsb = max(1, min(nsb, nb - 1));
-    }
-    rs = max(1, nsb / tc);
-    nsb = nsb < tc ? nsb : rs * tc;
-  }
-  if (b < nsb) {
-    if (nsb < tc) {
-      // fewer blocks than token chunks: block b takes chunks b, b + nsb, ... over all steps
-      const int c = b + it * nsb;
-      if (c >= tc) return false;
-      x = WorkItem{true, true, 0, 16 * c, min(16, a.T - 16 * c), 0, ss};
-      return true;
-    }
-    if (it > 0) return false;
-    // the tc chunks of a step range on one XCD (block b runs on XCD b % 8): ranges in octets, octet o's
-    // blocks [8 tc o, 8 tc (o + 1)), chunk c of range 8 o + x at 8 tc o + 8 c + x; ranges past the last
-    // full octet as before
-    const int full = (rs / 8) * 8;
-    int c, r;
-    if (b < full * tc) {
-      const int o = b / (8 * tc), w = b % (8 * tc);
-      c = w / 8;
-      r = 8 * o + w % 8;
-    } else {
-      const int b2 = b - full * tc;
-      c = b2 % tc;
-      r = full + b2 / tc;
-    }
-    x = WorkItem{true, true, 0, 16 * c, min(16, a.T - 16 * c), (int)((int64_t)r * ss / rs),
-                 (int)((int64_t)(r + 1) * ss / rs)};
-    return true;
-  }
-  if (ng <= 0) return false;
-  const int o = b - nsb, R = nb - nsb, steps = a.steps_routed;
-  int j, s0 = 0, s1 = steps;
-  if (ng <= R) {
-    if (it > 0) return false;
-    const int q = R / ng, rem = R % ng;
-    int part, parts;
-    if (o < rem * (q + 1)) {
-      j = o / (q + 1);
-      part = o % (q + 1);
-      parts = q + 1;
-    } else {
-      const int o2 = o - rem * (q + 1);
-      j = rem + o2 / q;
-      part = o2 % q;
-      parts = q;
-    }
-    s0 = (int)((int64_t)part * steps / parts);
-    s1 = (int)((int64_t)(part + 1) * steps / parts);
+  SplitItem si;
+  if (!split_item(SplitShape{(int)gridDim.x, a.T, a.steps_shared, a.steps_routed}, ng, (int)blockIdx.x, it, si))
+    return false;
+  if (si.shared) {
+    x = WorkItem{true, true, 0, 16 * si.j, min(16, a.T - 16 * si.j), si.s0, si.s1};
   } else {
-    j = o + it * R;
-    if (j >= ng) return false;
+    const int4 g = a.chunks[si.j];
+    const bool valid = (unsigned)g.x < (unsigned)a.routed.n_records;
+    x = WorkItem{false, valid, valid ? g.x : 0, g.y, g.z, si.s0, si.s1};
   }
-  const int4 g = a.chunks[j];
-  const bool valid = (unsigned)g.x < (unsigned)a.routed.n_records;
-  x = WorkItem{false, valid, valid ? g.x : 0, g.y, g.z, s0, s1};
   return true;
 }
 
-template <int NG, bool SB_BF16>
+// PLAN: each block's one item from the descriptor the grouping launch wrote (a.plan); else the blocks split
+// the work themselves (any number of items per block).
+template <int NG, bool SB_BF16, bool PLAN>
 __global__ __launch_bounds__(kThreadsG, 2) void grouped_ring_kernel(MfmaArgs a) {
-  WorkItem x;
   __shared__ RingLds<NG, SB_BF16> lds;
-  for (int it = 0; next_item(a, it, x); ++it) {
-    if (x.s0 >= x.s1) continue;
+  auto run = [&](const WorkItem& x) __attribute__((always_inline)) {
     if (!a.gate_up && (x.shared ? a.wk_shared : a.wk_routed) == 1)
       ring_item<NG, SB_BF16, true>(a, x.shared, x.e, x.valid, x.start, x.count, x.s0, x.s1, lds);
     else
       ring_item<NG, SB_BF16, false>(a, x.shared, x.e, x.valid, x.start, x.count, x.s0, x.s1, lds);
+  };
+  if constexpr (PLAN) {
+    const int4 p = a.plan[blockIdx.x];
+    const uint32_t w = (uint32_t)p.w;
+    const int s0 = (int)(w & 0x7fffu), s1 = (int)((w >> 15) & 0x7fffu);
+    if (s0 < s1) run(WorkItem{(w >> 30 & 1u) != 0, (w >> 31) != 0, p.x, p.y, p.z, s0, s1});
+  } else {
+    WorkItem x;
+    for (int it = 0; next_item(a, it, x); ++it)
+      if (x.s0 < x.s1) run(x);
   }
 }
 
@@ -911,14 +874,17 @@ moe_status launch_stage_rows(const void* x, bool x_bf16, int rows, int K, const 
 
 moe_status launch_group_and_stage(const int32_t* ids, int P, int n_valid, int32_t* n_groups, int4* groups,
                                   int32_t* perm, int32_t* n_chunks, int4* chunks, const void* x, bool x_bf16, int rows,
-                                  int K, const StagedRows& out, hipStream_t s) {
-  const GroupJob g{ids, P, n_valid, n_groups, perm, n_chunks, groups, chunks};
+                                  int K, const StagedRows& out, hipStream_t s, int4* plan0, const SplitShape* shape0,
+                                  int4* plan1, const SplitShape* shape1) {
+  const GroupJob g{ids, P, n_valid, n_groups, perm, n_chunks, groups, chunks, plan0, plan1,
+                   plan0 ? *shape0 : SplitShape{}, plan1 ? *shape1 : SplitShape{}};
+  const int np = (plan0 || plan1) ? kPlanBlocks : 0;
   if (x_bf16) {
     const StageJob<uint16_t> j{static_cast<const uint16_t*>(x), K, out};
-    hipLaunchKernelGGL((group_and_stage_kernel<uint16_t>), dim3(rows + 1), dim3(kThreadsM), 0, s, g, j);
+    hipLaunchKernelGGL((group_and_stage_kernel<uint16_t>), dim3(rows + 1 + np), dim3(kThreadsM), 0, s, g, j);
   } else {
     const StageJob<float> j{static_cast<const float*>(x), K, out};
-    hipLaunchKernelGGL((group_and_stage_kernel<float>), dim3(rows + 1), dim3(kThreadsM), 0, s, g, j);
+    hipLaunchKernelGGL((group_and_stage_kernel<float>), dim3(rows + 1 + np), dim3(kThreadsM), 0, s, g, j);
   }
   return check_launch("group_and_stage_kernel");
 }
@@ -993,7 +959,9 @@ LaunchShape launch_shape(const MfmaArgs& a, bool has_shared, bool has_routed, bo
   auto pick = [&](auto ng) {
     constexpr int NG = decltype(ng)::value;
     if constexpr (NG <= 11) {
-      sh.kern = sb_bf16 ? grouped_ring_kernel<NG, true> : grouped_ring_kernel<NG, false>;   // static LDS only
+      // static LDS only
+      if (a.plan) sh.kern = sb_bf16 ? grouped_ring_kernel<NG, true, true> : grouped_ring_kernel<NG, false, true>;
+      else sh.kern = sb_bf16 ? grouped_ring_kernel<NG, true, false> : grouped_ring_kernel<NG, false, false>;
       sh.lds = 0;
       sh.ring = true;
     } else {
@@ -1013,6 +981,15 @@ LaunchShape launch_shape(const MfmaArgs& a, bool has_shared, bool has_routed, bo
   return sh;
 }
 }  // namespace
+
+bool mfma_plan_shape(MfmaArgs a, bool has_shared, bool has_routed, bool sb_bf16, SplitShape* out) {
+  a.plan = reinterpret_cast<const int4*>(alignof(int4));   // any non-NULL pointer selects the instantiation
+  const LaunchShape sh = launch_shape(a, has_shared, has_routed, sb_bf16);
+  if (!sh.ring || sh.nb > kPlanMaxBlocks || sh.steps_shared >= kPlanMaxSteps || sh.steps_routed >= kPlanMaxSteps)
+    return false;
+  *out = SplitShape{sh.nb, a.T, sh.steps_shared, sh.steps_routed};
+  return true;
+}
 
 moe_status launch_grouped_mfma(MfmaArgs a, bool has_shared, bool has_routed, bool sb_bf16, hipStream_t s) {
   const LaunchShape sh = launch_shape(a, has_shared, has_routed, sb_bf16);

@@ -294,3 +294,31 @@ def test_split_calls_equal_whole_call(cfg_name, T):
     assert torch.equal(yr[~bad], yr2[~bad]) and torch.equal(ys, ys2)
     assert torch.isfinite(yr[~bad]).all() and torch.isfinite(ys).all()
     assert torch.all(ys[2] == 0) and torch.all(yr[2][~bad[2]] == 0)
+
+
+def test_grouped_gemv_many_chunks_split_on_device_vs_oracle():
+    """4096 tokens on the tiny pool (top-2 of 8: 256 token chunks of the shared expert, 512 routed chunks):
+    more chunks than the launch can give one block each, so the blocks split the work themselves instead of
+    reading descriptors from the grouping launch.  Sampled tokens' expert outputs against the
+    oracle; every output finite."""
+    cfg = synth.TINY
+    dev = H.device_layer(cfg, 0)
+    orc = oin.oracle_layer(cfg, 0)
+    shape = H.shape_of(cfg)
+    rp, sp = _tiny_pools(cfg, dev, shape)
+    T, k = 4096, cfg.k
+    rng = np.random.default_rng(4096)
+    ids_np = np.stack([rng.permutation(cfg.n_experts)[:k] for _ in range(T)]).astype(np.int32)
+    x = torch.from_numpy(rng.standard_normal((T, cfg.d)).astype(np.float32)).cuda()
+    yr, ys = _gemv(rp, sp, torch.from_numpy(ids_np).cuda(), k, x, q.MOE_F32, T, shape.act, cfg.d)
+    torch.cuda.synchronize()
+    assert torch.isfinite(yr).all() and torch.isfinite(ys).all()
+    yr, ys, u = H.to_f64(yr), H.to_f64(ys), H.to_f64(x)
+    act = _oracle_act(shape)
+    err = 0.0
+    for t in sorted({0, 1, 15, 16, 17, 511, 1024, 2047, 4094, 4095, *rng.integers(0, T, 20).tolist()}):
+        err = max(err, H.max_rel_err(ys[t], moe.expert_ffn(orc.decoded_shared(), u[t], act)))
+        for i in range(k):
+            err = max(err, H.max_rel_err(yr[t, i], moe.expert_ffn(orc.decoded(int(ids_np[t, i])), u[t], act)))
+    print(f"4096 tokens, tiny pool: max rel err {err:.3e}")
+    assert err <= TOL

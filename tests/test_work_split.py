@@ -1,9 +1,11 @@
-"""CPU model of how the persistent blocks of the grouped matrix-core kernel (q4_mfma.hip, next_item) split a
-launch's work: the shared matrix's (token chunk, step) pairs and the routed chunks' steps.  The function
-below restates the kernel's integer arithmetic; the tests check that every piece of work is done exactly
-once for grids of 2 to 1024 blocks and 0 to 700 routed chunks, that a block never holds more than one
-item unless there are more chunks (or token chunks) than blocks, and that the token chunks of one shared
-step range run on one XCD (block b runs on XCD b mod 8) wherever the ranges fill octets."""
+"""CPU model of how the persistent blocks of the grouped matrix-core kernel split a launch's work (split_item in
+q4_grouping.h: run by the blocks themselves, or by the grouping launch to write one descriptor per block): the
+shared matrix's (token chunk, step) pairs and the routed chunks' steps.  The function below restates the
+integer arithmetic; the tests check that every piece of work is done exactly once for grids of 2 to 1024
+blocks and 0 to 700 routed chunks, that a block never holds more than one item unless there are more chunks
+(or token chunks) than blocks, that the host's single-item check (split_single_item) agrees with that, and
+that the token chunks of one shared step range run on one XCD (block b runs on XCD b mod 8) wherever the
+ranges fill octets, and on 8 / L XCDs for the L ranges after the last full octet when that divides evenly."""
 import itertools
 
 import pytest
@@ -30,12 +32,18 @@ def next_item(b, nb, it, T, steps_shared, steps_routed, ng):
         if it > 0:
             return None
         full = (rs // 8) * 8
+        L = rs - full
         if b < full * tc:
             o, w = divmod(b, 8 * tc)
             c, r = w // 8, 8 * o + w % 8
         else:
             b2 = b - full * tc
-            c, r = b2 % tc, full + b2 // tc
+            g = 8 // L
+            if 8 % L == 0 and tc % g == 0:
+                m, x = b2 // 8, b2 % 8
+                r, c = full + x % L, (x // L) * (tc // g) + m
+            else:
+                c, r = b2 % tc, full + b2 // tc
         return True, c, r * ss // rs, (r + 1) * ss // rs
     if ng <= 0:
         return None
@@ -128,6 +136,10 @@ def test_token_chunks_of_a_range_share_an_xcd(T, ng):
         ranges = sorted(by_range)
         for r in range(full):
             assert len(by_range[ranges[r]]) == 1, f"T={T}: range {ranges[r]} on XCDs {by_range[ranges[r]]}"
+        L = rs - full
+        if L and 8 % L == 0 and tc % (8 // L) == 0:
+            for r in range(full, rs):
+                assert len(by_range[ranges[r]]) == 8 // L, f"T={T}: range {ranges[r]} on XCDs {by_range[ranges[r]]}"
 
 
 def test_one_item_per_block_when_blocks_suffice():
@@ -137,3 +149,97 @@ def test_one_item_per_block_when_blocks_suffice():
         items = items_of(512, T, ss, sr, ng)
         assert max(len(v) for v in items.values()) == 1
         assert sum(len(v) for v in items.values()) == 512
+
+
+def split_counts(nb, T, ss, sr, ng):
+    ng = ng if sr > 0 else 0
+    tc = (T + 15) // 16
+    nsb, rs = 0, 1
+    if ss > 0:
+        if ng <= 0:
+            nsb = nb
+        else:
+            us, ur = ss * tc, sr * ng
+            nsb = max(1, min((nb * us + (us + ur) // 2) // (us + ur), nb - 1))
+        rs = max(1, nsb // tc)
+        nsb = nsb if nsb < tc else rs * tc
+    return nsb, rs
+
+
+def split_single_item(nb, T, ss, sr, ng_max):
+    """The host's check (q4_grouping.h) that no block gets a second item for any chunk count up to ng_max."""
+    tc = (T + 15) // 16
+    for ng in (range(1, ng_max + 1) if sr > 0 else [0]):
+        nsb, rs = split_counts(nb, T, ss, sr, ng)
+        if ss > 0 and nsb < tc and tc > 1:
+            return False
+        if ng > nb - nsb:
+            return False
+    return True
+
+
+@pytest.mark.parametrize("nb,T,ss,sr", [(512, 32, 352, 88), (512, 128, 176, 44), (64, 300, 352, 88), (8, 2, 44, 88),
+                                        (512, 4096, 16, 16), (3, 17, 1, 1), (512, 1000, 352, 88)])
+def test_single_item_check_matches_the_split(nb, T, ss, sr):
+    """Whenever the host's check passes for chunk counts up to ng_max, every block of every such launch holds at
+    most one item (the descriptor launch would be exact); when it fails, some chunk count needs a second item."""
+    for ng_max in (1, 5, 107, 145, 193, 600):
+        ok = split_single_item(nb, T, ss, sr, ng_max)
+        worst = max(max(len(v) for v in items_of(nb, T, ss, sr, ng).values()) for ng in range(1, ng_max + 1))
+        assert ok == (worst <= 1), (nb, T, ss, sr, ng_max, ok, worst)
+
+
+def split_shared_block(rs, tc, r, c):
+    full = (rs // 8) * 8
+    L = rs - full
+    if r < full:
+        return 8 * tc * (r // 8) + 8 * c + r % 8
+    g = 8 // L
+    if 8 % L == 0 and tc % g == 0:
+        return full * tc + 8 * (c % (tc // g)) + (r - full) + L * (c // (tc // g))
+    return full * tc + c + tc * (r - full)
+
+
+def build_plan(nb, T, ss, sr, ng):
+    """The grouping block's descriptors (build_plan in q4_grouping.h): per routed chunk its parts, per shared
+    step range its token chunks; block -> (shared, chunk or token chunk, s0, s1)."""
+    nsb, rs = split_counts(nb, T, ss, sr, ng)
+    ng = ng if sr > 0 else 0
+    tc = (T + 15) // 16
+    plan = {}
+    if ng > 0:
+        R = nb - nsb
+        q, rem = divmod(R, ng)
+        for j in range(ng):
+            parts = q + 1 if j < rem else q
+            o0 = j * (q + 1) if j < rem else rem * (q + 1) + (j - rem) * q
+            s0 = 0
+            for part in range(parts):
+                s1 = (part + 1) * sr // parts
+                b = nsb + o0 + part
+                assert b not in plan
+                plan[b] = (False, j, s0, s1)
+                s0 = s1
+    if ss > 0:
+        for r in range(rs):
+            for c in range(tc):
+                b = split_shared_block(rs, tc, r, c)
+                assert b not in plan
+                plan[b] = (True, c, r * ss // rs, (r + 1) * ss // rs)
+    return plan
+
+
+@pytest.mark.parametrize("nb,T,ss,sr", [(512, 32, 352, 88), (512, 32, 176, 44), (512, 128, 352, 88), (512, 128, 176, 44),
+                                        (512, 24, 4, 4), (768, 64, 4, 4), (512, 200, 352, 88), (64, 16, 44, 22)])
+def test_descriptors_equal_the_split(nb, T, ss, sr):
+    """Wherever the host allows descriptors, the grouping block's per-chunk construction gives every block
+    exactly the item the per-block split gives it."""
+    for ng in (1, 2, 7, 50, 107, 135, 193):
+        if not split_single_item(nb, T, ss, sr, ng):
+            continue
+        items = items_of(nb, T, ss, sr, ng)
+        plan = build_plan(nb, T, ss, sr, ng)
+        assert set(plan) == {b for b, v in items.items() if v}
+        for b, v in items.items():
+            if v:
+                assert plan[b] == v[0], (nb, T, ss, sr, ng, b)
