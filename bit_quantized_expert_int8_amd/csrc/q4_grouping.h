@@ -165,15 +165,6 @@ constexpr int kPlanMaxBlocks = 4096;   // descriptors reserved per launch in a g
 // when the launch would not use the ring kernel, or its shape does not fit the descriptors.
 bool mfma_plan_shape(MfmaArgs a, bool has_shared, bool has_routed, bool sb_bf16, SplitShape* out);
 
-// Block of shared step range r, token chunk c (the inverse of split_item's placement; every block of the
-// launch holds exactly one item when the descriptors are used).
-__host__ __device__ inline int split_shared_block(int rs, int tc, int r, int c) {
-  const int full = (rs / 8) * 8, L = rs - full;
-  if (r < full) return 8 * tc * (r / 8) + 8 * c + r % 8;
-  const int g = 8 / L;
-  if (8 % L == 0 && tc % g == 0) return full * tc + 8 * (c % (tc / g)) + (r - full) + L * (c / (tc / g));
-  return full * tc + c + tc * (r - full);
-}
 
 
 __device__ __forceinline__ int bucket_of(int32_t e, int n_valid) { return (unsigned)e < (unsigned)n_valid ? e : n_valid; }

@@ -189,57 +189,78 @@ def test_single_item_check_matches_the_split(nb, T, ss, sr):
         assert ok == (worst <= 1), (nb, T, ss, sr, ng_max, ok, worst)
 
 
-def split_shared_block(rs, tc, r, c):
-    full = (rs // 8) * 8
-    L = rs - full
-    if r < full:
-        return 8 * tc * (r // 8) + 8 * c + r % 8
-    g = 8 // L
-    if 8 % L == 0 and tc % g == 0:
-        return full * tc + 8 * (c % (tc // g)) + (r - full) + L * (c // (tc // g))
-    return full * tc + c + tc * (r - full)
+def grouping_chunks(ids, n_valid):
+    """The grouping's chunk table: experts in order (ids outside the pool last), each expert's pairs in runs of
+    16: (record or n_valid, first index into the grouped pair order, count)."""
+    bucket = [i if 0 <= i < n_valid else n_valid for i in ids]
+    cnt = [bucket.count(b) for b in range(n_valid + 1)]
+    out, start = [], 0
+    for b in range(n_valid + 1):
+        for c in range(0, cnt[b], 16):
+            out.append((b, start + c, min(16, cnt[b] - c)))
+        start += cnt[b]
+    return out
 
 
-def build_plan(nb, T, ss, sr, ng):
-    """The grouping block's descriptors (build_plan in q4_grouping.h): per routed chunk its parts, per shared
-    step range its token chunks; block -> (shared, chunk or token chunk, s0, s1)."""
-    nsb, rs = split_counts(nb, T, ss, sr, ng)
-    ng = ng if sr > 0 else 0
-    tc = (T + 15) // 16
-    plan = {}
-    if ng > 0:
-        R = nb - nsb
-        q, rem = divmod(R, ng)
-        for j in range(ng):
-            parts = q + 1 if j < rem else q
-            o0 = j * (q + 1) if j < rem else rem * (q + 1) + (j - rem) * q
-            s0 = 0
-            for part in range(parts):
-                s1 = (part + 1) * sr // parts
-                b = nsb + o0 + part
-                assert b not in plan
-                plan[b] = (False, j, s0, s1)
-                s0 = s1
-    if ss > 0:
-        for r in range(rs):
-            for c in range(tc):
-                b = split_shared_block(rs, tc, r, c)
-                assert b not in plan
-                plan[b] = (True, c, r * ss // rs, (r + 1) * ss // rs)
-    return plan
+def plan_share_descriptor(ids, n_valid, nb, T, ss, sr, b):
+    """One block's descriptor as a descriptor block writes it (plan_share in q4_grouping.h): the chunk table
+    rebuilt from per-expert counts and their prefix sums, chunk j found by a binary search for the last
+    expert whose first chunk is at most j; the item from split_item."""
+    nbk = n_valid + 1
+    pcnt = [0] * nbk
+    for i in ids:
+        pcnt[i if 0 <= i < n_valid else n_valid] += 1
+    pre_x, pre_z, x, z = [], [], 0, 0
+    for b2 in range(nbk):
+        pre_x.append(x)
+        pre_z.append(z)
+        x += pcnt[b2]
+        z += (pcnt[b2] + 15) // 16
+    ng = z
+    item = next_item(b, nb, 0, T, ss, sr, ng)
+    if item is None or item[2] >= item[3]:
+        return None
+    shared, j, s0, s1 = item
+    if shared:
+        return (True, 0, 16 * j, min(16, T - 16 * j), s0, s1)
+    lo, hi = 0, nbk - 1
+    while lo < hi:
+        mid = (lo + hi + 1) >> 1
+        if pre_z[mid] <= j:
+            lo = mid
+        else:
+            hi = mid - 1
+    k0 = (j - pre_z[lo]) * 16
+    return (False, lo, pre_x[lo] + k0, min(16, pcnt[lo] - k0), s0, s1)
 
 
-@pytest.mark.parametrize("nb,T,ss,sr", [(512, 32, 352, 88), (512, 32, 176, 44), (512, 128, 352, 88), (512, 128, 176, 44),
-                                        (512, 24, 4, 4), (768, 64, 4, 4), (512, 200, 352, 88), (64, 16, 44, 22)])
-def test_descriptors_equal_the_split(nb, T, ss, sr):
-    """Wherever the host allows descriptors, the grouping block's per-chunk construction gives every block
-    exactly the item the per-block split gives it."""
-    for ng in (1, 2, 7, 50, 107, 135, 193):
-        if not split_single_item(nb, T, ss, sr, ng):
+@pytest.mark.parametrize("T,k,E,ss,sr,kind", [(32, 8, 128, 352, 88, "perm"), (128, 8, 128, 176, 44, "zipf"),
+                                              (24, 2, 8, 4, 4, "perm"), (7, 2, 8, 4, 4, "invalid"),
+                                              (200, 4, 16, 352, 88, "zipf")])
+def test_descriptors_equal_the_grouping(T, k, E, ss, sr, kind):
+    """Every block's descriptor, as the descriptor blocks rebuild it from the ids, names the chunk of the
+    grouping's own table that split_item assigns to the block (record, first pair, count) and its steps."""
+    import numpy as np
+    rng = np.random.default_rng(T * 7 + k)
+    if kind == "perm":
+        ids = np.concatenate([rng.permutation(E)[:k] for _ in range(T)])
+    elif kind == "zipf":
+        r = np.arange(1, E + 1, dtype=np.float64) ** -1.1
+        ids = rng.choice(E, size=T * k, p=r / r.sum())
+    else:
+        ids = rng.integers(-2, E + 2, size=T * k)
+    ids = ids.tolist()
+    table = grouping_chunks(ids, E)
+    ng = len(table)
+    nb = 512
+    assert split_single_item(nb, T, ss, sr, ng)
+    for b in range(nb):
+        d = plan_share_descriptor(ids, E, nb, T, ss, sr, b)
+        it = next_item(b, nb, 0, T, ss, sr, ng)
+        if d is None:
+            assert it is None or it[2] >= it[3]
             continue
-        items = items_of(nb, T, ss, sr, ng)
-        plan = build_plan(nb, T, ss, sr, ng)
-        assert set(plan) == {b for b, v in items.items() if v}
-        for b, v in items.items():
-            if v:
-                assert plan[b] == v[0], (nb, T, ss, sr, ng, b)
+        shared, rec, start, count, s0, s1 = d
+        assert (shared, s0, s1) == (it[0], it[2], it[3])
+        if not shared:
+            assert (rec, start, count) == table[it[1]], (b, it)
